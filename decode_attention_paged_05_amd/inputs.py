@@ -1,0 +1,297 @@
+"""Seeded synthetic inputs for single-token paged decode attention.
+
+This module draws values and lays them out; it holds none of the attention
+arithmetic.  It serves both the tests (which feed the same arrays to the CPU
+oracle and to the GPU library) and the benchmark.
+
+Storage formats on the host:
+  * ``"f32"``  -> ``numpy.float32``
+  * ``"bf16"`` -> ``numpy.uint16`` holding the bfloat16 bit pattern
+
+The KV pool layout is ``[num_blocks, num_kv_heads, block_size, head_size]``
+for both K and V (the 4-D layout the second page's hardware-test message
+reports as accepted for the split kernel).  ``block_tables[s, j]`` names the
+physical block that holds logical tokens ``[j*block_size, (j+1)*block_size)``
+of sequence ``s``; unused entries hold -1.
+
+Every random stream is derived from one integer seed through
+``numpy.random.SeedSequence(seed, spawn_key=(stream, ...))`` so that any
+(sequence, KV head) slice can be regenerated on its own, in any order and on
+any number of threads, with identical bits.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Callable, Dict, List, Optional, Sequence
+
+import numpy as np
+
+BF16_NAN = np.uint16(0x7FC0)
+
+# stream identifiers for SeedSequence spawn keys
+_S_TABLE, _S_LENS, _S_QUERY, _S_KEY, _S_VALUE, _S_OUTLIER = range(6)
+
+
+@dataclasses.dataclass(frozen=True)
+class ConfigSpec:
+    """Shape and value recipe of one synthetic workload."""
+
+    name: str
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_size: int
+    block_size: int
+    num_blocks: int           # physical blocks in the pool
+    max_blocks_per_seq: int   # block-table width W
+    partition_size: int       # 0 = one-pass
+    dtype: str                # "f32" | "bf16"
+    seed: int
+    seq_len: Optional[int] = None          # fixed length for every sequence
+    seq_len_range: Optional[tuple] = None  # inclusive (lo, hi) uniform integers
+    outlier_rate: float = 0.0              # Bernoulli rate of outlier key positions
+    outlier_scale: float = 1.0             # multiplier of K at outlier positions
+    scale: Optional[float] = None          # default 1/sqrt(head_size)
+
+    @property
+    def softmax_scale(self) -> float:
+        return float(np.float32(self.scale if self.scale is not None
+                                else 1.0 / math.sqrt(self.head_size)))
+
+
+# The five workloads.  Shapes follow the model attention shape the pages
+# describe (24 query heads, 4 KV heads, head size 256) and their 100K-token
+# long-context case; the value distributions are synthetic N(0, 1).
+CONFIGS: Dict[str, ConfigSpec] = {
+    "tiny": ConfigSpec("tiny", num_seqs=1, num_heads=4, num_kv_heads=1, head_size=64,
+                       block_size=16, num_blocks=16, max_blocks_per_seq=7,
+                       partition_size=32, dtype="f32", seed=1, seq_len=100,
+                       scale=0.125),
+    "short": ConfigSpec("short", num_seqs=1, num_heads=24, num_kv_heads=4, head_size=256,
+                        block_size=16, num_blocks=1024, max_blocks_per_seq=512,
+                        partition_size=0, dtype="bf16", seed=2, seq_len=8192),
+    "long": ConfigSpec("long", num_seqs=1, num_heads=24, num_kv_heads=4, head_size=256,
+                       block_size=16, num_blocks=12500, max_blocks_per_seq=6250,
+                       partition_size=512, dtype="bf16", seed=3, seq_len=100000),
+    "mixed": ConfigSpec("mixed", num_seqs=32, num_heads=24, num_kv_heads=4, head_size=256,
+                        block_size=16, num_blocks=65536, max_blocks_per_seq=2048,
+                        partition_size=512, dtype="bf16", seed=4,
+                        seq_len_range=(1, 32768)),
+    "stress": ConfigSpec("stress", num_seqs=8, num_heads=24, num_kv_heads=24, head_size=256,
+                         block_size=16, num_blocks=65536, max_blocks_per_seq=8192,
+                         partition_size=1024, dtype="bf16", seed=5, seq_len=131072,
+                         outlier_rate=0.01, outlier_scale=20.0),
+}
+
+
+@dataclasses.dataclass
+class Problem:
+    """Host-side metadata and the small arrays of one decode step.
+
+    The KV pool is not stored here: it is produced on demand by
+    :func:`build_pool` (whole pool) or :func:`fill_pool` (streamed per
+    sequence), so that very large pools need not sit in host memory twice.
+    """
+
+    spec: ConfigSpec
+    seq_lens: np.ndarray      # int32 [S]
+    block_tables: np.ndarray  # int32 [S, W], -1 where unused
+    query: np.ndarray         # [S, H, D] storage format
+
+    # convenient aliases
+    @property
+    def num_seqs(self): return self.spec.num_seqs
+    @property
+    def num_heads(self): return self.spec.num_heads
+    @property
+    def num_kv_heads(self): return self.spec.num_kv_heads
+    @property
+    def head_size(self): return self.spec.head_size
+    @property
+    def block_size(self): return self.spec.block_size
+    @property
+    def num_blocks(self): return self.spec.num_blocks
+    @property
+    def max_blocks_per_seq(self): return self.spec.max_blocks_per_seq
+    @property
+    def partition_size(self): return self.spec.partition_size
+    @property
+    def dtype(self): return self.spec.dtype
+    @property
+    def scale(self): return self.spec.softmax_scale
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V that one decode step must read (each element once)."""
+        elem = 4 if self.dtype == "f32" else 2
+        return int(self.seq_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_size * 2 * elem
+
+
+def _rng(seed: int, *key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=tuple(key))))
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return round_to_bf16_bits(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def poison_value(dtype: str):
+    return np.float32(np.nan) if dtype == "f32" else BF16_NAN
+
+
+def storage_dtype(dtype: str):
+    return np.float32 if dtype == "f32" else np.uint16
+
+
+def make_problem(spec: ConfigSpec | str, seq_lens: Optional[Sequence[int]] = None,
+                 seed: Optional[int] = None, **overrides) -> Problem:
+    """Build metadata, block tables and queries for a workload.
+
+    ``seq_lens`` and ``seed`` override the spec's; other keyword arguments
+    replace spec fields (e.g. ``partition_size=0``).
+    """
+    if isinstance(spec, str):
+        spec = CONFIGS[spec]
+    if seed is not None:
+        overrides["seed"] = seed
+    if overrides:
+        spec = dataclasses.replace(spec, **overrides)
+    S, W, bs = spec.num_seqs, spec.max_blocks_per_seq, spec.block_size
+    if seq_lens is None:
+        if spec.seq_len is not None:
+            lens = np.full(S, spec.seq_len, dtype=np.int64)
+        else:
+            lo, hi = spec.seq_len_range
+            lens = _rng(spec.seed, _S_LENS).integers(lo, hi + 1, size=S)
+    else:
+        lens = np.asarray(seq_lens, dtype=np.int64)
+        if lens.shape != (S,):
+            raise ValueError("seq_lens must have num_seqs entries")
+    if (lens < 0).any() or (lens > W * bs).any():
+        raise ValueError("seq_lens must lie in [0, max_blocks_per_seq*block_size]")
+    nblk = (lens + bs - 1) // bs
+    if int(nblk.sum()) > spec.num_blocks:
+        raise ValueError("pool too small for the sequences")
+    perm = _rng(spec.seed, _S_TABLE).permutation(spec.num_blocks)
+    tables = np.full((S, W), -1, dtype=np.int32)
+    off = 0
+    for s in range(S):
+        n = int(nblk[s])
+        tables[s, :n] = perm[off:off + n]
+        off += n
+    q = _rng(spec.seed, _S_QUERY).standard_normal(
+        (S, spec.num_heads, spec.head_size), dtype=np.float32)
+    return Problem(spec=spec, seq_lens=lens.astype(np.int32), block_tables=tables,
+                   query=to_storage(q, spec.dtype))
+
+
+def sequence_kv_f32(problem: Problem, s: int, kv_head: int):
+    """Logical K and V rows of (sequence s, KV head g) as float32, before rounding.
+
+    Returns two arrays of shape [seq_len, head_size].
+    """
+    spec = problem.spec
+    L, D = int(problem.seq_lens[s]), spec.head_size
+    k = _rng(spec.seed, _S_KEY, s, kv_head).standard_normal((L, D), dtype=np.float32)
+    v = _rng(spec.seed, _S_VALUE, s, kv_head).standard_normal((L, D), dtype=np.float32)
+    if spec.outlier_rate > 0.0:
+        mask = outlier_positions(problem, s)
+        k[mask] *= np.float32(spec.outlier_scale)
+    return k, v
+
+
+def outlier_positions(problem: Problem, s: int) -> np.ndarray:
+    """Boolean [seq_len] mask of the key positions scaled as outliers (shared by all KV heads)."""
+    spec = problem.spec
+    L = int(problem.seq_lens[s])
+    if spec.outlier_rate <= 0.0:
+        return np.zeros(L, dtype=bool)
+    return _rng(spec.seed, _S_OUTLIER, s).random(L) < spec.outlier_rate
+
+
+def sequence_kv(problem: Problem, s: int, kv_head: int):
+    """Logical K and V rows of (s, kv_head) in storage format, shape [seq_len, head_size]."""
+    k, v = sequence_kv_f32(problem, s, kv_head)
+    return to_storage(k, problem.dtype), to_storage(v, problem.dtype)
+
+
+def _sequence_blocks(problem: Problem, s: int, poison: bool):
+    """K and V of sequence s as pool blocks [nblk, Hkv, bs, D] (tail slots poisoned or zero)."""
+    Hkv, D, bs = problem.num_kv_heads, problem.head_size, problem.block_size
+    L = int(problem.seq_lens[s])
+    nb = (L + bs - 1) // bs
+    sd = storage_dtype(problem.dtype)
+    fill = poison_value(problem.dtype) if poison else sd(0)
+    kb = np.full((Hkv, nb * bs, D), fill, dtype=sd)
+    vb = np.full((Hkv, nb * bs, D), fill, dtype=sd)
+    for g in range(Hkv):
+        k, v = sequence_kv(problem, s, g)
+        kb[g, :L] = k
+        vb[g, :L] = v
+    kb = np.ascontiguousarray(kb.reshape(Hkv, nb, bs, D).transpose(1, 0, 2, 3))
+    vb = np.ascontiguousarray(vb.reshape(Hkv, nb, bs, D).transpose(1, 0, 2, 3))
+    return problem.block_tables[s, :nb].copy(), kb, vb
+
+
+def default_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def fill_pool(problem: Problem, sink: Callable[[np.ndarray, np.ndarray, np.ndarray], None],
+              poison: bool = True, threads: Optional[int] = None) -> None:
+    """Stream the pool contents sequence by sequence.
+
+    ``sink(block_ids, k_blocks, v_blocks)`` receives int32 [n] physical ids and
+    the matching [n, Hkv, bs, D] blocks.  Blocks that no table references are
+    never passed; the caller decides their contents (poison in the tests).
+    Sequences are generated on a thread pool; ``sink`` is called from the
+    calling thread in sequence order.
+    """
+    threads = threads or default_threads()
+    S = problem.num_seqs
+    if threads <= 1 or S == 1:
+        for s in range(S):
+            sink(*_sequence_blocks(problem, s, poison))
+        return
+    with ThreadPoolExecutor(max_workers=min(threads, S)) as ex:
+        futs = [ex.submit(_sequence_blocks, problem, s, poison) for s in range(S)]
+        for f in futs:
+            sink(*f.result())
+
+
+def build_pool(problem: Problem, poison: bool = True, threads: Optional[int] = None):
+    """Whole K and V pools on the host, unreferenced blocks filled with poison (NaN)."""
+    shape = (problem.num_blocks, problem.num_kv_heads, problem.block_size, problem.head_size)
+    sd = storage_dtype(problem.dtype)
+    fill = poison_value(problem.dtype) if poison else sd(0)
+    kc = np.full(shape, fill, dtype=sd)
+    vc = np.full(shape, fill, dtype=sd)
+
+    def sink(ids, kb, vb):
+        kc[ids] = kb
+        vc[ids] = vb
+
+    fill_pool(problem, sink, poison=poison, threads=threads)
+    return kc, vc
+
+
+def logical_kv(problem: Problem, s: int) -> List[tuple]:
+    """[(K_g, V_g) for each KV head] of sequence s in storage format."""
+    return [sequence_kv(problem, s, g) for g in range(problem.num_kv_heads)]
