@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+One step is one whole decode-attention call over one batch: phase 1 (per
+partition attention) and phase 2 (log-sum-exp merge) for the split workloads,
+the single one-pass kernel for P = 0.  The default workload is the 100K-token
+split decode (1 sequence x 100000 tokens, 24 query / 4 KV heads, head size
+256, bf16 K/V, partition size 512 -> 196 partitions).
+
+Inputs are generated on the host from a fixed seed, uploaded once, and stay
+resident in HBM.  The KV pool is held in several copies and consecutive steps
+read different copies, so every step streams its K/V from HBM rather than from
+the 256 MB memory-side cache (4 x 820 MB rotate for the default workload).
+
+Prints one JSON line (rank 0) with the step time, the KV-read bandwidth
+(algorithmic bytes: every K and V element of every sequence read once), the
+phase-1 kernel's roofline fraction against 8 TB/s, the oracle's CPU baseline on
+the same workload, and the max abs error of the timed output against the oracle.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/step + achieved KV-read HBM GB/s (% roofline) at 100K ctx"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "decode_attention_paged_05_amd", "csrc", "*"))
+                   + glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per phase-1 launch from the committed rocprofv3 counter runs,
+    or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def describe(p) -> str:
+    lens = p.seq_lens
+    L = f"{int(lens[0])} tokens" if (lens == lens[0]).all() else f"{int(lens.min())}-{int(lens.max())} tokens"
+    P = p.partition_size
+    return (f"{p.spec.name}: {p.num_seqs} seq x {L}, {p.num_heads} q / {p.num_kv_heads} KV heads, "
+            f"head {p.head_size}, {p.dtype} KV, block {p.block_size}, "
+            + (f"split P={P}" if P else "one-pass"))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="long", help="tiny | short | long | mixed | stress")
+    ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
+    ap.add_argument("--copies", type=int, default=0, help="KV pool copies to rotate (0: enough for 1.5 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the decode path is sharded by sequence or KV head with no exchange, so N GPUs run N "
+              "independent copies of this step", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import decode_attention_paged_05_amd as pad
+    from decode_attention_paged_05_amd import inputs as gen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    overrides = {}
+    if args.partition_size is not None:
+        overrides["partition_size"] = args.partition_size
+    p = gen.make_problem(args.config, **overrides)
+    P = p.partition_size
+    kv_bytes = p.kv_bytes()
+    need_host = not (args.no_parity and args.no_cpu_baseline)
+
+    # ---- inputs: generate on the host, upload once --------------------------------
+    t0 = time.perf_counter()
+    shape = (p.num_blocks, p.num_kv_heads, p.block_size, p.head_size)
+    tdt = torch.float32 if p.dtype == "f32" else torch.bfloat16
+    kc = torch.full(shape, float("nan"), dtype=tdt, device=dev)
+    vc = torch.full(shape, float("nan"), dtype=tdt, device=dev)
+    host_k = host_v = None
+    if need_host:
+        host_k = np.full(shape, gen.poison_value(p.dtype), dtype=gen.storage_dtype(p.dtype))
+        host_v = np.full(shape, gen.poison_value(p.dtype), dtype=gen.storage_dtype(p.dtype))
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if p.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    def sink(ids, kb, vb):
+        idx = torch.from_numpy(ids.astype(np.int64)).to(dev)
+        kc.index_copy_(0, idx, up(kb))
+        vc.index_copy_(0, idx, up(vb))
+        if need_host:
+            host_k[ids] = kb
+            host_v[ids] = vb
+
+    gen.fill_pool(p, sink)
+    q = up(p.query)
+    tables = torch.from_numpy(p.block_tables).to(dev)
+    lens = torch.from_numpy(p.seq_lens).to(dev)
+    pool_bytes = 2 * kc.numel() * kc.element_size()
+    copies = args.copies or max(1, min(8, -(-1536 * 2**20 // pool_bytes)))
+    pools = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    print(f"[bench] {describe(p)}; inputs ready in {time.perf_counter() - t0:.1f}s; "
+          f"{copies} pool copies of {pool_bytes / 2**20:.0f} MiB", file=sys.stderr, flush=True)
+
+    out = torch.empty((p.num_seqs, p.num_heads, p.head_size), dtype=torch.float32, device=dev)
+    ws = None
+    dims = pad.make_dims(q, kc, tables)
+    if P:
+        ws = pad.alloc_workspace(p.num_seqs, p.num_heads, p.head_size, p.max_blocks_per_seq, p.block_size, P,
+                                 device=dev)
+
+    def step(i, ev=None):
+        k, v = pools[i % copies]
+        if P == 0:
+            if ev:
+                ev[0].record()
+            pad.paged_attention_decode(out, q, k, v, tables, lens, p.scale, p.num_kv_heads, p.block_size, 0)
+            if ev:
+                ev[1].record()
+            return
+        if ev:
+            ev[0].record()
+        pad.paged_attention_decode_phase1(q, k, v, tables, lens, p.scale, p.num_kv_heads, p.block_size, P, ws)
+        if ev:
+            ev[1].record()
+        pad.paged_attention_decode_phase2(out, lens, p.block_size, P, ws, dims)
+        if ev:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, per-kernel HIP events on the launch stream -------
+    K = args.steps
+    n_ev = 2 if P == 0 else 3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
+    torch.cuda.synchronize()  # one GPU: the barrier is the synchronisation
+    t_start = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_start) * 1e3
+    ms_per_step = wall_ms / K
+    k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if n_ev == 3 else 0.0
+    result_gpu = out.detach().cpu().numpy().astype(np.float64)
+
+    # the same K steps without events, for the event overhead
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    ms_no_events = (time.perf_counter() - t_start) * 1e3 / K
+
+    gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    k1_gbs = kv_bytes / (k1_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.config)
+
+    # ---- oracle: parity of the timed output and the CPU baseline ---------------
+    max_err = None
+    cpu = None
+    if need_host:
+        import oracle
+
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # noqa: BLE001 - reporting only
+            blas_threads = 1
+        t_or = time.perf_counter()
+        ref = oracle.decode_attention(p.query, host_k, host_v, p.block_tables, p.seq_lens, p.scale, p.num_kv_heads,
+                                      p.block_size, p.dtype)
+        or_s = time.perf_counter() - t_or
+        max_err = float(np.max(np.abs(result_gpu - ref)))
+        if not args.no_cpu_baseline:
+            cpu = {"value": round(kv_bytes / or_s / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+                   "kind": "oracle", "sample": f"one full step of the same workload ({describe(p)}), "
+                                               f"{or_s:.2f} s, fp64 NumPy"}
+        print(f"[bench] oracle {or_s:.1f}s, max |gpu - oracle| = {max_err:.3e}", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_hbm_roofline": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": describe(p),
+            "num_seqs": p.num_seqs,
+            "seq_len": int(p.seq_lens.max()),
+            "num_heads": p.num_heads,
+            "num_kv_heads": p.num_kv_heads,
+            "head_size": p.head_size,
+            "partition_size": P,
+            "kv_bytes_per_step": kv_bytes,
+            "seed": p.spec.seed,
+            "pool_copies": copies,
+            "accumulate": "fp32",
+        },
+        "kernels_ms": {"phase1" if P else "one_pass": round(k1_ms, 5), **({"phase2": round(k2_ms, 5)} if P else {})},
+        "ms_per_step_without_events": round(ms_no_events, 5),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(k1_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "phase1" if P else "one_pass",
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+        "cpu_baseline": cpu,
+        "max_abs_err_vs_oracle": max_err,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

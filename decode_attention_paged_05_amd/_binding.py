@@ -1,0 +1,256 @@
+"""ctypes binding of ``libpad.so``: argument marshalling only.
+
+Every entry point of ``include/paged_attention_decode.h`` has a Python function
+of the same name.  Tensors are torch tensors on the current CUDA (HIP) device;
+torch supplies device memory and the stream, all arithmetic runs in the
+library's HIP kernels.  A missing library raises at import of this module, and
+a non-zero status raises ``RuntimeError`` with the library's message.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpad.so")
+
+PAD_DTYPE_F32 = 0
+PAD_DTYPE_BF16 = 1
+
+STATUS = {
+    0: "PAD_OK", -1: "PAD_ERR_NULL", -2: "PAD_ERR_DTYPE", -3: "PAD_ERR_SHAPE",
+    -4: "PAD_ERR_UNSUPPORTED", -5: "PAD_ERR_PARTITION", -6: "PAD_ERR_WORKSPACE", -7: "PAD_ERR_ALIGN",
+}
+
+EXPORTED = [
+    "paged_attention_decode",
+    "paged_attention_decode_phase1",
+    "paged_attention_decode_phase2",
+    "paged_attention_decode_workspace_size",
+    "paged_attention_decode_workspace_layout",
+    "paged_attention_decode_workspace_init",
+    "paged_attention_decode_choose_partition",
+    "paged_attention_decode_strerror",
+]
+
+
+class PadDims(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("max_blocks_per_seq", ctypes.c_int32),
+    ]
+
+
+class PadError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {strerror(status)}")
+
+
+def _load() -> ctypes.CDLL:
+    # torch's HIP runtime must be the one libpad.so binds to: streams and
+    # device memory are objects of that runtime.  Loading torch first makes
+    # the dynamic linker resolve libpad's libamdhip64.so.7 to torch's copy
+    # instead of loading a second runtime from /opt/rocm.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m decode_attention_paged_05_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    dims = ctypes.POINTER(PadDims)
+    lib.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, sz, dims, vp]
+    lib.paged_attention_decode.restype = i32
+    lib.paged_attention_decode_phase1.argtypes = [vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, sz, dims, vp]
+    lib.paged_attention_decode_phase1.restype = i32
+    lib.paged_attention_decode_phase2.argtypes = [vp, vp, i32, i32, vp, sz, dims, vp]
+    lib.paged_attention_decode_phase2.restype = i32
+    lib.paged_attention_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_attention_decode_workspace_size.restype = sz
+    lib.paged_attention_decode_workspace_layout.argtypes = [i32, i32, i32, i32, i32, i32,
+                                                             ctypes.POINTER(sz), ctypes.POINTER(sz),
+                                                             ctypes.POINTER(sz)]
+    lib.paged_attention_decode_workspace_layout.restype = i32
+    lib.paged_attention_decode_workspace_init.argtypes = [vp, sz, i32, i32, i32, i32, i32, i32, vp]
+    lib.paged_attention_decode_workspace_init.restype = i32
+    lib.paged_attention_decode_choose_partition.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_attention_decode_choose_partition.restype = i32
+    lib.paged_attention_decode_strerror.argtypes = [i32]
+    lib.paged_attention_decode_strerror.restype = ctypes.c_char_p
+    del i64
+    return lib
+
+
+LIB = _load()
+
+
+def strerror(status: int) -> str:
+    return LIB.paged_attention_decode_strerror(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise PadError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PAD_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return PAD_DTYPE_BF16
+    raise TypeError(f"query/key/value must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_dims(query, key_cache, block_tables) -> PadDims:
+    if query.dim() != 3 or key_cache.dim() != 4 or block_tables.dim() != 2:
+        raise ValueError("expected query [S,H,D], key_cache [NB,Hkv,bs,D], block_tables [S,W]")
+    S, H, D = query.shape
+    return PadDims(_dtype_code(query), S, H, D, key_cache.shape[0], block_tables.shape[1])
+
+
+def _check_tensors(out, query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, block_size):
+    torch = _torch()
+    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+        raise TypeError("query, key_cache and value_cache must share a dtype")
+    if key_cache.shape != value_cache.shape:
+        raise ValueError("key_cache and value_cache shapes differ")
+    S, H, D = query.shape
+    if tuple(key_cache.shape[1:]) != (num_kv_heads, block_size, D):
+        raise ValueError(f"key_cache must be [num_blocks, {num_kv_heads}, {block_size}, {D}], got {tuple(key_cache.shape)}")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    if block_tables.shape[0] != S or tuple(seq_lens.shape) != (S,):
+        raise ValueError("block_tables / seq_lens disagree with num_seqs")
+    if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (S, H, D)):
+        raise ValueError("out must be float32 [num_seqs, num_heads, head_size]")
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def paged_attention_decode(out, query, key_cache, value_cache, block_tables, seq_lens, scale: float,
+                           num_kv_heads: int, block_size: int, partition_size: int, workspace=None,
+                           stream=None) -> None:
+    """Decode attention into ``out`` (float32 [S, H, D]); see the C header for the contract."""
+    _check_tensors(out, query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, block_size)
+    dims = make_dims(query, key_cache, block_tables)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = LIB.paged_attention_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                    _ptr(block_tables), _ptr(seq_lens), float(scale), int(num_kv_heads),
+                                    int(block_size), int(partition_size), ws_ptr, ws_bytes,
+                                    ctypes.byref(dims), _stream(stream))
+    _check(st, "paged_attention_decode")
+
+
+def paged_attention_decode_phase1(query, key_cache, value_cache, block_tables, seq_lens, scale: float,
+                                  num_kv_heads: int, block_size: int, partition_size: int, workspace,
+                                  stream=None) -> None:
+    _check_tensors(None, query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, block_size)
+    dims = make_dims(query, key_cache, block_tables)
+    st = LIB.paged_attention_decode_phase1(_ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+                                           _ptr(seq_lens), float(scale), int(num_kv_heads), int(block_size),
+                                           int(partition_size), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), ctypes.byref(dims),
+                                           _stream(stream))
+    _check(st, "paged_attention_decode_phase1")
+
+
+def paged_attention_decode_phase2(out, seq_lens, block_size: int, partition_size: int, workspace, dims: PadDims,
+                                  stream=None) -> None:
+    st = LIB.paged_attention_decode_phase2(_ptr(out), _ptr(seq_lens), int(block_size), int(partition_size),
+                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           ctypes.byref(dims), _stream(stream))
+    _check(st, "paged_attention_decode_phase2")
+
+
+def paged_attention_decode_workspace_size(num_seqs: int, num_heads: int, head_size: int, max_blocks_per_seq: int,
+                                          block_size: int, partition_size: int) -> int:
+    n = LIB.paged_attention_decode_workspace_size(num_seqs, num_heads, head_size, max_blocks_per_seq, block_size,
+                                                  partition_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid workspace-size arguments")
+    return int(n)
+
+
+def paged_attention_decode_workspace_layout(num_seqs, num_heads, head_size, max_blocks_per_seq, block_size,
+                                            partition_size):
+    """(max_logits, exp_sums, tmp_output) byte offsets inside the workspace."""
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    st = LIB.paged_attention_decode_workspace_layout(num_seqs, num_heads, head_size, max_blocks_per_seq,
+                                                     block_size, partition_size, ctypes.byref(a), ctypes.byref(b),
+                                                     ctypes.byref(c))
+    _check(st, "paged_attention_decode_workspace_layout")
+    return a.value, b.value, c.value
+
+
+def paged_attention_decode_workspace_init(workspace, num_seqs, num_heads, head_size, max_blocks_per_seq, block_size,
+                                          partition_size, stream=None) -> None:
+    st = LIB.paged_attention_decode_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                   num_seqs, num_heads, head_size, max_blocks_per_seq, block_size,
+                                                   partition_size, _stream(stream))
+    _check(st, "paged_attention_decode_workspace_init")
+
+
+def paged_attention_decode_choose_partition(num_seqs, num_heads, num_kv_heads, max_context_len, block_size,
+                                            num_cus=256) -> int:
+    r = LIB.paged_attention_decode_choose_partition(num_seqs, num_heads, num_kv_heads, max_context_len, block_size,
+                                                    num_cus)
+    if r < 0:
+        raise PadError(r, "paged_attention_decode_choose_partition")
+    return int(r)
+
+
+def paged_attention_decode_strerror(status: int) -> str:
+    return strerror(status)
+
+
+def alloc_workspace(num_seqs, num_heads, head_size, max_blocks_per_seq, block_size, partition_size, device=None,
+                    init=True, stream=None):
+    """Allocate (torch, uint8) and optionally initialise a workspace for split calls."""
+    torch = _torch()
+    n = paged_attention_decode_workspace_size(num_seqs, num_heads, head_size, max_blocks_per_seq, block_size,
+                                              partition_size)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
+    if init and n:
+        paged_attention_decode_workspace_init(ws, num_seqs, num_heads, head_size, max_blocks_per_seq, block_size,
+                                              partition_size, stream)
+    return ws

@@ -1,0 +1,255 @@
+// Host side of the C ABI: argument validation (before any HIP call), the
+// workspace layout, the one-pass/split choice and the launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "paged_attention_decode.h"
+#include "pad_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+  size_t ml, es, tmp, total;
+  int64_t np;
+  size_t n_stats, n_tmp;
+};
+
+// Workspace layout for a split call; returns false on invalid sizes.
+bool workspace_layout(int32_t S, int32_t H, int32_t D, int32_t W, int32_t bs, int32_t P, Layout* out) {
+  if (S < 0 || H <= 0 || D <= 0 || W <= 0 || bs <= 0 || P < 0) return false;
+  if (P == 0) {
+    *out = Layout{0, 0, 0, 0, 0, 0, 0};
+    return true;
+  }
+  if (P % bs) return false;
+  const int64_t tokens = (int64_t)W * bs;
+  const int64_t np = (tokens + P - 1) / P;
+  const size_t n_stats = (size_t)S * (size_t)H * (size_t)np;
+  const size_t n_tmp = n_stats * (size_t)D;
+  Layout l;
+  l.np = np;
+  l.n_stats = n_stats;
+  l.n_tmp = n_tmp;
+  l.ml = 0;
+  l.es = round_up(n_stats * sizeof(float), kAlign);
+  l.tmp = l.es + round_up(n_stats * sizeof(float), kAlign);
+  l.total = l.tmp + round_up(n_tmp * sizeof(float), kAlign);
+  *out = l;
+  return true;
+}
+
+// Validation shared by the attention entry points.
+int32_t validate(const void* query, const void* key_cache, const void* value_cache, const int32_t* block_tables,
+                 const int32_t* seq_lens, float scale, int32_t num_kv_heads, int32_t block_size,
+                 int32_t partition_size, const pad_dims_t* dims) {
+  if (!dims) return PAD_ERR_NULL;
+  if (dims->dtype != PAD_DTYPE_F32 && dims->dtype != PAD_DTYPE_BF16) return PAD_ERR_DTYPE;
+  if (dims->num_seqs < 0 || dims->num_heads <= 0 || num_kv_heads <= 0 || dims->num_blocks <= 0 ||
+      dims->max_blocks_per_seq <= 0 || dims->head_size <= 0)
+    return PAD_ERR_SHAPE;
+  if (dims->num_heads % num_kv_heads != 0) return PAD_ERR_SHAPE;
+  if (!std::isfinite(scale)) return PAD_ERR_SHAPE;
+  if (dims->head_size != 64 && dims->head_size != 128 && dims->head_size != 256) return PAD_ERR_UNSUPPORTED;
+  if (block_size != pad::kBlockTokens) return PAD_ERR_UNSUPPORTED;
+  // grid limits: y = KV heads x head chunks, z = sequences
+  const int group = dims->num_heads / num_kv_heads;
+  const int chunks = (group + pad::kMaxHeadsPerGroup - 1) / pad::kMaxHeadsPerGroup;
+  if ((int64_t)num_kv_heads * chunks > 65535 || dims->num_seqs > 65535) return PAD_ERR_UNSUPPORTED;
+  // token counts must fit int32 inside the kernels
+  if ((int64_t)dims->max_blocks_per_seq * block_size > INT32_MAX / 2) return PAD_ERR_UNSUPPORTED;
+  if (partition_size < 0 || partition_size % block_size) return PAD_ERR_PARTITION;
+  if (dims->num_seqs == 0) return PAD_OK;
+  if (!query || !key_cache || !value_cache || !block_tables || !seq_lens) return PAD_ERR_NULL;
+  if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) || (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return PAD_ERR_ALIGN;
+  return PAD_OK;
+}
+
+pad::Plan make_plan(float scale, int32_t num_kv_heads, int32_t partition_size, const pad_dims_t* dims) {
+  pad::Plan p{};
+  p.dtype = dims->dtype;
+  p.num_seqs = dims->num_seqs;
+  p.num_heads = dims->num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = dims->num_heads / num_kv_heads;
+  p.head_chunks = (p.group + pad::kMaxHeadsPerGroup - 1) / pad::kMaxHeadsPerGroup;
+  p.heads_per_wg = p.group < pad::kMaxHeadsPerGroup ? p.group : pad::kMaxHeadsPerGroup;
+  p.head_size = dims->head_size;
+  p.num_blocks = dims->num_blocks;
+  p.max_blocks = dims->max_blocks_per_seq;
+  p.partition = partition_size;
+  p.scale = scale;
+  return p;
+}
+
+// Attach the workspace arrays; false if it is missing or too small.
+bool attach_workspace(pad::Plan* p, void* workspace, size_t workspace_bytes) {
+  Layout l;
+  if (!workspace_layout(p->num_seqs, p->num_heads, p->head_size, p->max_blocks, pad::kBlockTokens, p->partition, &l))
+    return false;
+  if (!workspace || workspace_bytes < l.total || !aligned16(workspace)) return false;
+  char* base = static_cast<char*>(workspace);
+  p->num_partitions = (int)l.np;
+  p->max_logits = reinterpret_cast<float*>(base + l.ml);
+  p->exp_sums = reinterpret_cast<float*>(base + l.es);
+  p->tmp_out = reinterpret_cast<float*>(base + l.tmp);
+  return true;
+}
+
+int32_t status_of(hipError_t e) { return e == hipSuccess ? PAD_OK : (int32_t)e; }
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                             int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size) {
+  Layout l;
+  if (!workspace_layout(num_seqs, num_heads, head_size, max_blocks_per_seq, block_size, partition_size, &l))
+    return (size_t)-1;
+  return l.total;
+}
+
+int32_t paged_attention_decode_workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                                int32_t max_blocks_per_seq, int32_t block_size,
+                                                int32_t partition_size, size_t* max_logits_offset,
+                                                size_t* exp_sums_offset, size_t* tmp_output_offset) {
+  Layout l;
+  if (!workspace_layout(num_seqs, num_heads, head_size, max_blocks_per_seq, block_size, partition_size, &l))
+    return partition_size < 0 || (block_size > 0 && partition_size % block_size) ? PAD_ERR_PARTITION : PAD_ERR_SHAPE;
+  if (max_logits_offset) *max_logits_offset = l.ml;
+  if (exp_sums_offset) *exp_sums_offset = l.es;
+  if (tmp_output_offset) *tmp_output_offset = l.tmp;
+  return PAD_OK;
+}
+
+int32_t paged_attention_decode_workspace_init(void* workspace, size_t workspace_bytes, int32_t num_seqs,
+                                              int32_t num_heads, int32_t head_size, int32_t max_blocks_per_seq,
+                                              int32_t block_size, int32_t partition_size, void* stream) {
+  Layout l;
+  if (partition_size < 0 || (block_size > 0 && partition_size % block_size)) return PAD_ERR_PARTITION;
+  if (!workspace_layout(num_seqs, num_heads, head_size, max_blocks_per_seq, block_size, partition_size, &l))
+    return PAD_ERR_SHAPE;
+  if (l.total == 0) return PAD_OK;
+  if (!workspace) return PAD_ERR_WORKSPACE;
+  if (workspace_bytes < l.total) return PAD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PAD_ERR_ALIGN;
+  char* base = static_cast<char*>(workspace);
+  return status_of(pad::launch_workspace_fill(reinterpret_cast<float*>(base + l.ml),
+                                              reinterpret_cast<float*>(base + l.es),
+                                              reinterpret_cast<float*>(base + l.tmp), l.n_stats, l.n_tmp,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int32_t paged_attention_decode_phase1(const void* query, const void* key_cache, const void* value_cache,
+                                      const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                                      int32_t num_kv_heads, int32_t block_size, int32_t partition_size,
+                                      void* workspace, size_t workspace_bytes, const pad_dims_t* dims,
+                                      void* stream) {
+  int32_t st = validate(query, key_cache, value_cache, block_tables, seq_lens, scale, num_kv_heads, block_size,
+                        partition_size, dims);
+  if (st != PAD_OK) return st;
+  if (partition_size == 0) return PAD_ERR_PARTITION;
+  if (dims->num_seqs == 0) return PAD_OK;
+  pad::Plan plan = make_plan(scale, num_kv_heads, partition_size, dims);
+  if (!attach_workspace(&plan, workspace, workspace_bytes)) return PAD_ERR_WORKSPACE;
+  return status_of(pad::launch_phase1(plan, query, key_cache, value_cache, block_tables, seq_lens,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32_t block_size,
+                                      int32_t partition_size, const void* workspace, size_t workspace_bytes,
+                                      const pad_dims_t* dims, void* stream) {
+  if (!dims) return PAD_ERR_NULL;
+  if (dims->dtype != PAD_DTYPE_F32 && dims->dtype != PAD_DTYPE_BF16) return PAD_ERR_DTYPE;
+  if (dims->num_seqs < 0 || dims->num_heads <= 0 || dims->max_blocks_per_seq <= 0) return PAD_ERR_SHAPE;
+  if (dims->head_size != 64 && dims->head_size != 128 && dims->head_size != 256) return PAD_ERR_UNSUPPORTED;
+  if (block_size != pad::kBlockTokens) return PAD_ERR_UNSUPPORTED;
+  if (dims->num_seqs > 65535 || dims->num_heads > 65535) return PAD_ERR_UNSUPPORTED;
+  if ((int64_t)dims->max_blocks_per_seq * block_size > INT32_MAX / 2) return PAD_ERR_UNSUPPORTED;
+  if (partition_size <= 0 || partition_size % block_size) return PAD_ERR_PARTITION;
+  if (dims->num_seqs == 0) return PAD_OK;
+  if (!out || !seq_lens) return PAD_ERR_NULL;
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u)) return PAD_ERR_ALIGN;
+  pad::Plan plan{};
+  plan.dtype = dims->dtype;
+  plan.num_seqs = dims->num_seqs;
+  plan.num_heads = dims->num_heads;
+  plan.head_size = dims->head_size;
+  plan.max_blocks = dims->max_blocks_per_seq;
+  plan.partition = partition_size;
+  if (!attach_workspace(&plan, const_cast<void*>(workspace), workspace_bytes)) return PAD_ERR_WORKSPACE;
+  return status_of(pad::launch_phase2(plan, out, seq_lens, static_cast<hipStream_t>(stream)));
+}
+
+int32_t paged_attention_decode(float* out, const void* query, const void* key_cache, const void* value_cache,
+                               const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                               int32_t num_kv_heads, int32_t block_size, int32_t partition_size, void* workspace,
+                               size_t workspace_bytes, const pad_dims_t* dims, void* stream) {
+  int32_t st = validate(query, key_cache, value_cache, block_tables, seq_lens, scale, num_kv_heads, block_size,
+                        partition_size, dims);
+  if (st != PAD_OK) return st;
+  if (dims->num_seqs == 0) return PAD_OK;
+  if (!out) return PAD_ERR_NULL;
+  if (!aligned16(out)) return PAD_ERR_ALIGN;
+  pad::Plan plan = make_plan(scale, num_kv_heads, partition_size, dims);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (partition_size == 0)
+    return status_of(pad::launch_one_pass(plan, out, query, key_cache, value_cache, block_tables, seq_lens, s));
+  if (!attach_workspace(&plan, workspace, workspace_bytes)) return PAD_ERR_WORKSPACE;
+  hipError_t e = pad::launch_phase1(plan, query, key_cache, value_cache, block_tables, seq_lens, s);
+  if (e != hipSuccess) return status_of(e);
+  return status_of(pad::launch_phase2(plan, out, seq_lens, s));
+}
+
+int32_t paged_attention_decode_choose_partition(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                                int32_t max_context_len, int32_t block_size, int32_t num_cus) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || max_context_len < 0 ||
+      num_cus <= 0)
+    return PAD_ERR_SHAPE;
+  if (block_size != pad::kBlockTokens) return PAD_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_context_len == 0) return 0;
+  const int64_t group = num_heads / num_kv_heads;
+  const int64_t chunks = (group + pad::kMaxHeadsPerGroup - 1) / pad::kMaxHeadsPerGroup;
+  const int64_t wg_one_pass = (int64_t)num_seqs * num_kv_heads * chunks;
+  // Enough independent workgroups to keep every compute unit streaming: the
+  // one-pass form when the batch alone provides them or the context is too
+  // short to split; otherwise the largest partition that still provides them.
+  const int64_t target = 2 * (int64_t)num_cus;
+  if (wg_one_pass >= target || max_context_len <= 2 * 128) return 0;
+  static const int32_t kSizes[] = {2048, 1024, 512, 256, 128};
+  for (int32_t p : kSizes) {
+    if (p % block_size) continue;
+    const int64_t parts = (max_context_len + p - 1) / p;
+    if (parts >= 2 && wg_one_pass * parts >= target) return p;
+  }
+  return 128;
+}
+
+const char* paged_attention_decode_strerror(int32_t status) {
+  switch (status) {
+    case PAD_OK: return "success";
+    case PAD_ERR_NULL: return "a required pointer is NULL";
+    case PAD_ERR_DTYPE: return "dtype must be PAD_DTYPE_F32 or PAD_DTYPE_BF16";
+    case PAD_ERR_SHAPE: return "invalid sizes: need num_seqs >= 0, num_heads, num_kv_heads, num_blocks, max_blocks_per_seq >= 1, num_heads % num_kv_heads == 0, finite scale";
+    case PAD_ERR_UNSUPPORTED: return "unsupported shape: head_size must be 64, 128 or 256 and block_size 16 (or a grid limit is exceeded)";
+    case PAD_ERR_PARTITION: return "partition_size must be >= 0 and a multiple of block_size (> 0 for phase calls)";
+    case PAD_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than paged_attention_decode_workspace_size()";
+    case PAD_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    default: break;
+  }
+  if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));
+  return "unknown status";
+}
+
+}  // extern "C"

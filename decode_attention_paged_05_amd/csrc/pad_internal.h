@@ -1,0 +1,52 @@
+// Internal interface between the C-ABI host layer (pad_api.cpp) and the
+// kernel launchers (pad_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pad {
+
+// Tokens per KV block handled by the kernels.
+constexpr int kBlockTokens = 16;
+// Query heads one workgroup serves: the N width of the 16x16 matrix-core tile.
+constexpr int kMaxHeadsPerGroup = 16;
+
+// Everything the launchers need, validated and derived on the host.
+struct Plan {
+  int dtype;          // PAD_DTYPE_*
+  int num_seqs;       // S
+  int num_heads;      // H
+  int num_kv_heads;   // Hkv
+  int group;          // G = H / Hkv query heads per KV head
+  int head_chunks;    // ceil(G / 16): workgroups per KV head
+  int heads_per_wg;   // min(G, 16)
+  int head_size;      // D
+  int64_t num_blocks; // NB
+  int max_blocks;     // W
+  int partition;      // P tokens (0 = one-pass)
+  int num_partitions; // NP = ceil(W * 16 / P) (0 for one-pass)
+  float scale;        // softmax scale
+  // workspace arrays (split only)
+  float* max_logits;  // [S, H, NP]
+  float* exp_sums;    // [S, H, NP]
+  float* tmp_out;     // [S, H, NP, D]
+};
+
+hipError_t launch_phase1(const Plan& plan, const void* query, const void* key_cache,
+                         const void* value_cache, const int32_t* block_tables,
+                         const int32_t* seq_lens, hipStream_t stream);
+
+hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens,
+                         hipStream_t stream);
+
+hipError_t launch_one_pass(const Plan& plan, float* out, const void* query,
+                           const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           hipStream_t stream);
+
+hipError_t launch_workspace_fill(float* max_logits, float* exp_sums, float* tmp_out,
+                                 size_t n_stats, size_t n_tmp, hipStream_t stream);
+
+}  // namespace pad

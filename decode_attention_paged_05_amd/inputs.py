@@ -228,21 +228,33 @@ def sequence_kv(problem: Problem, s: int, kv_head: int):
     return to_storage(k, problem.dtype), to_storage(v, problem.dtype)
 
 
-def _sequence_blocks(problem: Problem, s: int, poison: bool):
-    """K and V of sequence s as pool blocks [nblk, Hkv, bs, D] (tail slots poisoned or zero)."""
-    Hkv, D, bs = problem.num_kv_heads, problem.head_size, problem.block_size
+def _head_rows(problem: Problem, s: int, g: int, poison: bool):
+    """K and V rows of (s, g) padded to whole blocks: [nblk*bs, D] each, tail slots poisoned or zero."""
+    D, bs = problem.head_size, problem.block_size
     L = int(problem.seq_lens[s])
     nb = (L + bs - 1) // bs
     sd = storage_dtype(problem.dtype)
     fill = poison_value(problem.dtype) if poison else sd(0)
-    kb = np.full((Hkv, nb * bs, D), fill, dtype=sd)
-    vb = np.full((Hkv, nb * bs, D), fill, dtype=sd)
-    for g in range(Hkv):
-        k, v = sequence_kv(problem, s, g)
-        kb[g, :L] = k
-        vb[g, :L] = v
-    kb = np.ascontiguousarray(kb.reshape(Hkv, nb, bs, D).transpose(1, 0, 2, 3))
-    vb = np.ascontiguousarray(vb.reshape(Hkv, nb, bs, D).transpose(1, 0, 2, 3))
+    k, v = sequence_kv(problem, s, g)
+    if nb * bs == L:
+        return k, v
+    kp = np.full((nb * bs, D), fill, dtype=sd)
+    vp = np.full((nb * bs, D), fill, dtype=sd)
+    kp[:L] = k
+    vp[:L] = v
+    return kp, vp
+
+
+def _assemble(problem: Problem, s: int, rows):
+    """Per-head padded rows -> (block ids, K blocks, V blocks) with blocks [nblk, Hkv, bs, D]."""
+    Hkv, D, bs = problem.num_kv_heads, problem.head_size, problem.block_size
+    nb = (int(problem.seq_lens[s]) + bs - 1) // bs
+    sd = storage_dtype(problem.dtype)
+    kb = np.empty((nb, Hkv, bs, D), dtype=sd)
+    vb = np.empty((nb, Hkv, bs, D), dtype=sd)
+    for g, (k, v) in enumerate(rows):
+        kb[:, g] = k.reshape(nb, bs, D)
+        vb[:, g] = v.reshape(nb, bs, D)
     return problem.block_tables[s, :nb].copy(), kb, vb
 
 
@@ -261,19 +273,29 @@ def fill_pool(problem: Problem, sink: Callable[[np.ndarray, np.ndarray, np.ndarr
     ``sink(block_ids, k_blocks, v_blocks)`` receives int32 [n] physical ids and
     the matching [n, Hkv, bs, D] blocks.  Blocks that no table references are
     never passed; the caller decides their contents (poison in the tests).
-    Sequences are generated on a thread pool; ``sink`` is called from the
-    calling thread in sequence order.
+    (sequence, KV head) slices are generated on a thread pool, at most two
+    sequences ahead of the one being handed to ``sink`` (called from the
+    calling thread, in sequence order).
     """
     threads = threads or default_threads()
-    S = problem.num_seqs
-    if threads <= 1 or S == 1:
+    S, Hkv = problem.num_seqs, problem.num_kv_heads
+    if threads <= 1:
         for s in range(S):
-            sink(*_sequence_blocks(problem, s, poison))
+            sink(*_assemble(problem, s, [_head_rows(problem, s, g, poison) for g in range(Hkv)]))
         return
-    with ThreadPoolExecutor(max_workers=min(threads, S)) as ex:
-        futs = [ex.submit(_sequence_blocks, problem, s, poison) for s in range(S)]
-        for f in futs:
-            sink(*f.result())
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        pending = {}
+
+        def submit(s):
+            if s < S:
+                pending[s] = [ex.submit(_head_rows, problem, s, g, poison) for g in range(Hkv)]
+
+        submit(0)
+        submit(1)
+        for s in range(S):
+            submit(s + 2)
+            rows = [f.result() for f in pending.pop(s)]
+            sink(*_assemble(problem, s, rows))
 
 
 def build_pool(problem: Problem, poison: bool = True, threads: Optional[int] = None):

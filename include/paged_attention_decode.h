@@ -1,0 +1,191 @@
+/*
+ * paged_attention_decode.h - C ABI of the MI355X (gfx950) paged decode-attention library.
+ *
+ * Operation (second page, "V2 implementation" message; first page, two-pass
+ * message): for every sequence s and query head h, one new query row attends
+ * over the sequence's cached keys and values, which live in a pool of
+ * fixed-size blocks addressed through a per-sequence block table:
+ *
+ *     x_t      = scale * <query[s,h,:], K_s[g(h), t, :]>      for t < seq_lens[s]
+ *     out[s,h] = sum_t exp(x_t - max x) V_s[g(h), t, :] / sum_t exp(x_t - max x)
+ *
+ * with g(h) = h / (num_heads / num_kv_heads) (query heads grouped contiguously
+ * per KV head) and K_s[g, t, :] = key_cache[block_tables[s, t / block_size], g,
+ * t % block_size, :] (likewise V).
+ *
+ * The split form computes this in two passes.  Phase 1 runs one workgroup per
+ * (sequence, KV head, partition of partition_size tokens) and stores, for each
+ * query head of the group, the partition's max logit, its exp-sum and its
+ * normalised partial output.  Phase 2 merges the partitions by log-sum-exp:
+ * weight_p = exp_sum_p * exp(max_p - max over p), out = sum_p weight_p *
+ * partial_p / sum_p weight_p.  partition_size == 0 selects the one-pass path,
+ * which walks the whole context in one workgroup per (sequence, KV head) with
+ * an online softmax and needs no workspace.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers named as device pointers must be device memory of the current HIP
+ * device (e.g. torch CUDA tensors), contiguous, 16-byte aligned.  Layouts
+ * (row-major, innermost last):
+ *   out          float32 [num_seqs, num_heads, head_size]
+ *   query        dtype   [num_seqs, num_heads, head_size]
+ *   key_cache    dtype   [num_blocks, num_kv_heads, block_size, head_size]
+ *   value_cache  dtype   [num_blocks, num_kv_heads, block_size, head_size]
+ *   block_tables int32   [num_seqs, max_blocks_per_seq]
+ *   seq_lens     int32   [num_seqs]
+ * The second page's hardware-test message names this 4-D layout for both
+ * caches of the split kernel; each (block, KV head) tile is block_size *
+ * head_size contiguous elements.
+ *
+ * Ownership: every buffer belongs to the caller.  The library allocates no
+ * memory and keeps no per-call state; calls only enqueue kernels on `stream`
+ * (a hipStream_t; NULL = the null stream) and return without synchronising.
+ * Buffers must stay valid until that work completes.  One workspace must not
+ * be used by two calls whose work may overlap.
+ *
+ * Errors: 0 = success.  A negative status is an argument error found on the
+ * host before any HIP call: nothing is enqueued and no buffer is touched.  A
+ * positive status is the hipError_t of a failed launch.  No function throws.
+ *
+ * Device-side contract (not checkable without a synchronisation): 0 <=
+ * seq_lens[s] <= max_blocks_per_seq * block_size, and block_tables[s, j] lies in
+ * [0, num_blocks) for j < ceil(seq_lens[s] / block_size); other table entries
+ * are never read.  A violation does not fault: a length outside the range or a
+ * block id outside the pool makes that sequence's output rows NaN.
+ */
+#ifndef PAGED_ATTENTION_DECODE_H
+#define PAGED_ATTENTION_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types of query, key_cache and value_cache */
+#define PAD_DTYPE_F32 0
+#define PAD_DTYPE_BF16 1
+
+/* status codes */
+#define PAD_OK 0
+#define PAD_ERR_NULL (-1)        /* a required pointer is NULL */
+#define PAD_ERR_DTYPE (-2)       /* dtype is neither PAD_DTYPE_F32 nor PAD_DTYPE_BF16 */
+#define PAD_ERR_SHAPE (-3)       /* a size is out of range or sizes disagree (e.g. num_heads % num_kv_heads != 0) */
+#define PAD_ERR_UNSUPPORTED (-4) /* head_size not 64/128/256, or block_size not 16 */
+#define PAD_ERR_PARTITION (-5)   /* partition_size negative or not a multiple of block_size */
+#define PAD_ERR_WORKSPACE (-6)   /* split call with a NULL or too small workspace */
+#define PAD_ERR_ALIGN (-7)       /* a device pointer is not 16-byte aligned */
+
+/*
+ * Problem sizes shared by the entry points.
+ *   dtype              PAD_DTYPE_F32 | PAD_DTYPE_BF16 (query, key_cache, value_cache)
+ *   num_seqs           S >= 0 (0 makes every call a no-op)
+ *   num_heads          H >= 1, a multiple of num_kv_heads
+ *   head_size          D in {64, 128, 256}
+ *   num_blocks         physical blocks in the KV pool, >= 1
+ *   max_blocks_per_seq W >= 1, the block-table row width
+ */
+typedef struct pad_dims {
+  int32_t dtype;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t head_size;
+  int64_t num_blocks;
+  int32_t max_blocks_per_seq;
+} pad_dims_t;
+
+/*
+ * Decode attention for one new token per sequence (both phases, or the
+ * one-pass path), written to `out` (float32).
+ *   scale          multiplies every query-key dot product (usually 1/sqrt(D)); finite
+ *   num_kv_heads   KV heads in the pool (>= 1, divides num_heads)
+ *   block_size     tokens per block; must be 16
+ *   partition_size 0 = one-pass; else tokens per partition, a multiple of block_size
+ *   workspace      device buffer of >= paged_attention_decode_workspace_size(...)
+ *                  bytes, used only when partition_size > 0 (may be NULL otherwise).
+ *                  It needs no initialisation: phase 1 writes every entry phase 2
+ *                  reads.  paged_attention_decode_workspace_init gives it the
+ *                  defined starting contents (-inf / 0 / 0) all the same.
+ * Sequences with seq_lens[s] == 0 get all-zero output rows.
+ */
+int32_t paged_attention_decode(float* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               const int32_t* seq_lens, float scale, int32_t num_kv_heads,
+                               int32_t block_size, int32_t partition_size, void* workspace,
+                               size_t workspace_bytes, const pad_dims_t* dims, void* stream);
+
+/*
+ * Phase 1 alone (partition_size > 0): per (sequence, KV head, partition)
+ * workgroup, the partition's max logit, exp-sum and normalised partial output
+ * for each query head of the group, written into `workspace`.  Arguments as in
+ * paged_attention_decode.  Partitions at or beyond ceil(seq_lens[s] /
+ * partition_size) are left untouched.
+ */
+int32_t paged_attention_decode_phase1(const void* query, const void* key_cache,
+                                      const void* value_cache, const int32_t* block_tables,
+                                      const int32_t* seq_lens, float scale, int32_t num_kv_heads,
+                                      int32_t block_size, int32_t partition_size, void* workspace,
+                                      size_t workspace_bytes, const pad_dims_t* dims, void* stream);
+
+/*
+ * Phase 2 alone: log-sum-exp merge of the first ceil(seq_lens[s] /
+ * partition_size) partitions of each (sequence, head) in `workspace` into
+ * `out`.  Reads only entries phase 1 wrote for the same seq_lens.
+ */
+int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32_t block_size,
+                                      int32_t partition_size, const void* workspace,
+                                      size_t workspace_bytes, const pad_dims_t* dims, void* stream);
+
+/*
+ * Bytes of workspace a split call needs: three float32 arrays, each starting on
+ * a 256-byte boundary,
+ *   max_logits [S, H, NP] | exp_sums [S, H, NP] | tmp_output [S, H, NP, D]
+ * with NP = ceil(max_blocks_per_seq * block_size / partition_size), the most
+ * partitions any sequence can have (the pages' tmp_output, exp_sums and
+ * max_logits, second page, workspace-initialisation message).  Returns 0 when
+ * partition_size == 0 and (size_t)-1 for invalid arguments.
+ */
+size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                             int32_t max_blocks_per_seq, int32_t block_size,
+                                             int32_t partition_size);
+
+/* Byte offsets of the three workspace arrays (same arguments); each may be NULL. */
+int32_t paged_attention_decode_workspace_layout(int32_t num_seqs, int32_t num_heads,
+                                                int32_t head_size, int32_t max_blocks_per_seq,
+                                                int32_t block_size, int32_t partition_size,
+                                                size_t* max_logits_offset, size_t* exp_sums_offset,
+                                                size_t* tmp_output_offset);
+
+/*
+ * Enqueue the workspace's defined starting contents on `stream`: max_logits =
+ * -inf, exp_sums = 0, tmp_output = 0 (second page, workspace-initialisation
+ * message).  Done with a fill kernel, so the call may be captured in a HIP graph.
+ */
+int32_t paged_attention_decode_workspace_init(void* workspace, size_t workspace_bytes,
+                                              int32_t num_seqs, int32_t num_heads,
+                                              int32_t head_size, int32_t max_blocks_per_seq,
+                                              int32_t block_size, int32_t partition_size,
+                                              void* stream);
+
+/*
+ * One-pass versus split choice for a batch, sized for a GPU with `num_cus`
+ * compute units (256 on MI355X).  Returns 0 (one-pass) when the batch's
+ * (sequence, KV head) workgroups already fill the GPU or the context is short,
+ * otherwise the partition size (a multiple of block_size) that gives enough
+ * workgroups.  The first page's two-pass message weighs partition count
+ * against workgroups per compute unit for a 16-unit GPU; this rule redoes that
+ * for num_cus units.  Negative status on invalid arguments.
+ */
+int32_t paged_attention_decode_choose_partition(int32_t num_seqs, int32_t num_heads,
+                                                int32_t num_kv_heads, int32_t max_context_len,
+                                                int32_t block_size, int32_t num_cus);
+
+/* Static text for a status code (never NULL). */
+const char* paged_attention_decode_strerror(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTENTION_DECODE_H */

@@ -1,0 +1,118 @@
+"""Upload of seeded problems to the GPU and the oracle comparisons the GPU tests share."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import decode_attention_paged_05_amd as pad
+import oracle
+from decode_attention_paged_05_amd import inputs as gen
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a ROCm GPU (run with -m 'not gpu' on a CPU-only host)")
+
+
+def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def torch_dtype(dtype: str):
+    return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+class DeviceProblem:
+    """A problem's inputs on the GPU (pool poisoned with NaN outside referenced rows),
+    optionally with the host pool kept for the oracle."""
+
+    def __init__(self, problem: gen.Problem, keep_host: bool = True, device="cuda", pool_copies: int = 1):
+        require_gpu()
+        self.p = problem
+        shape = (problem.num_blocks, problem.num_kv_heads, problem.block_size, problem.head_size)
+        td = torch_dtype(problem.dtype)
+        self.kc = torch.full(shape, float("nan"), dtype=td, device=device)
+        self.vc = torch.full(shape, float("nan"), dtype=td, device=device)
+        self.kc_host = self.vc_host = None
+        if keep_host:
+            sd = gen.storage_dtype(problem.dtype)
+            fill = gen.poison_value(problem.dtype)
+            self.kc_host = np.full(shape, fill, dtype=sd)
+            self.vc_host = np.full(shape, fill, dtype=sd)
+
+        def sink(ids, kb, vb):
+            idx = torch.from_numpy(ids.astype(np.int64)).to(device)
+            self.kc.index_copy_(0, idx, to_device(kb, problem.dtype, device))
+            self.vc.index_copy_(0, idx, to_device(vb, problem.dtype, device))
+            if keep_host:
+                self.kc_host[ids] = kb
+                self.vc_host[ids] = vb
+
+        gen.fill_pool(problem, sink)
+        self.query = to_device(problem.query, problem.dtype, device)
+        self.tables = torch.from_numpy(problem.block_tables).to(device)
+        self.lens = torch.from_numpy(problem.seq_lens).to(device)
+        torch.cuda.synchronize()
+
+    def workspace(self, partition_size: int, init: bool = True):
+        p = self.p
+        return pad.alloc_workspace(p.num_seqs, p.num_heads, p.head_size, p.max_blocks_per_seq, p.block_size,
+                                   partition_size, init=init)
+
+    def run(self, partition_size: int | None = None, workspace=None, out=None, kc=None, vc=None, tables=None,
+            lens=None) -> torch.Tensor:
+        p = self.p
+        P = p.partition_size if partition_size is None else partition_size
+        if out is None:
+            out = torch.full((p.num_seqs, p.num_heads, p.head_size), float("nan"), dtype=torch.float32,
+                             device=self.query.device)
+        if P and workspace is None:
+            workspace = self.workspace(P)
+        pad.paged_attention_decode(out, self.query, self.kc if kc is None else kc, self.vc if vc is None else vc,
+                                   self.tables if tables is None else tables, self.lens if lens is None else lens,
+                                   p.scale, p.num_kv_heads, p.block_size, P, workspace)
+        return out
+
+    def oracle(self) -> np.ndarray:
+        p = self.p
+        return oracle.decode_attention(p.query, self.kc_host, self.vc_host, p.block_tables, p.seq_lens, p.scale,
+                                       p.num_kv_heads, p.block_size, p.dtype)
+
+    def oracle_split(self, partition_size: int):
+        p = self.p
+        return oracle.decode_attention_split(p.query, self.kc_host, self.vc_host, p.block_tables, p.seq_lens,
+                                             p.scale, p.num_kv_heads, p.block_size, p.dtype, partition_size)
+
+
+def max_err(gpu: torch.Tensor, ref: np.ndarray) -> float:
+    g = gpu.detach().cpu().numpy().astype(np.float64)
+    assert g.shape == ref.shape
+    assert np.isfinite(g).all(), f"non-finite GPU output at {np.argwhere(~np.isfinite(g))[:5].tolist()}"
+    return float(np.max(np.abs(g - ref))) if g.size else 0.0
+
+
+def assert_close(gpu: torch.Tensor, ref: np.ndarray, dtype: str, what: str = ""):
+    err = max_err(gpu, ref)
+    tol = TOL[dtype]
+    if err > tol:
+        g = gpu.detach().cpu().numpy().astype(np.float64)
+        idx = np.unravel_index(np.argmax(np.abs(g - ref)), ref.shape)
+        raise AssertionError(f"{what}: max |gpu - oracle| = {err:.3e} > {tol:.0e} at {idx}: "
+                             f"gpu {g[idx]!r} oracle {ref[idx]!r}")
+    return err
+
+
+def workspace_views(ws: torch.Tensor, p: gen.Problem, partition_size: int):
+    """(max_logits [S,H,NP], exp_sums [S,H,NP], tmp_output [S,H,NP,D]) float32 views of a workspace."""
+    ml, es, tmp = pad.paged_attention_decode_workspace_layout(p.num_seqs, p.num_heads, p.head_size,
+                                                              p.max_blocks_per_seq, p.block_size, partition_size)
+    NP = -(-p.max_blocks_per_seq * p.block_size // partition_size)
+    S, H, D = p.num_seqs, p.num_heads, p.head_size
+    n = S * H * NP
+    f = lambda off, count: ws[off: off + 4 * count].view(torch.float32)
+    return (f(ml, n).view(S, H, NP), f(es, n).view(S, H, NP), f(tmp, n * D).view(S, H, NP, D))
