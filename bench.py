@@ -10,7 +10,7 @@ split decode (1 sequence x 100000 tokens, 24 query / 4 KV heads, head size
 Inputs are generated on the host from a fixed seed, uploaded once, and stay
 resident in HBM.  The KV pool is held in several copies and consecutive steps
 read different copies, so every step streams its K/V from HBM rather than from
-the 256 MB memory-side cache (4 x 820 MB rotate for the default workload).
+the 256 MB memory-side cache (at least 1.5 GiB of pool copies rotate).
 
 Prints one JSON line (rank 0) with the step time, the KV-read bandwidth
 (algorithmic bytes: every K and V element of every sequence read once), the
@@ -60,13 +60,13 @@ def load_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def describe(p) -> str:
+def describe(p, layout: str = "") -> str:
     lens = p.seq_lens
     L = f"{int(lens[0])} tokens" if (lens == lens[0]).all() else f"{int(lens.min())}-{int(lens.max())} tokens"
     P = p.partition_size
     return (f"{p.spec.name}: {p.num_seqs} seq x {L}, {p.num_heads} q / {p.num_kv_heads} KV heads, "
             f"head {p.head_size}, {p.dtype} KV, block {p.block_size}, "
-            + (f"split P={P}" if P else "one-pass"))
+            + (f"split P={P}" if P else "one-pass") + (f", {layout} layout" if layout else ""))
 
 
 def main() -> int:
@@ -76,7 +76,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="long", help="tiny | short | long | mixed | stress")
     ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
+    ap.add_argument("--seq-len", type=int, default=None,
+                    help="override every sequence's length (table width and pool follow)")
     ap.add_argument("--copies", type=int, default=0, help="KV pool copies to rotate (0: enough for 1.5 GB)")
+    ap.add_argument("--layout", default="tiled", choices=["tiled", "rows"],
+                    help="KV cache layout: tiled (K 16-byte chunks x tokens, V dims x tokens) or rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     args = ap.parse_args()
@@ -103,6 +107,11 @@ def main() -> int:
     overrides = {}
     if args.partition_size is not None:
         overrides["partition_size"] = args.partition_size
+    if args.seq_len is not None:
+        spec = gen.CONFIGS[args.config]
+        W = -(-args.seq_len // spec.block_size)
+        overrides.update(seq_len=args.seq_len, seq_len_range=None, max_blocks_per_seq=W,
+                         num_blocks=max(spec.num_blocks, spec.num_seqs * W))
     p = gen.make_problem(args.config, **overrides)
     P = p.partition_size
     kv_bytes = p.kv_bytes()
@@ -112,8 +121,14 @@ def main() -> int:
     t0 = time.perf_counter()
     shape = (p.num_blocks, p.num_kv_heads, p.block_size, p.head_size)
     tdt = torch.float32 if p.dtype == "f32" else torch.bfloat16
-    kc = torch.full(shape, float("nan"), dtype=tdt, device=dev)
-    vc = torch.full(shape, float("nan"), dtype=tdt, device=dev)
+    if args.layout == "tiled":
+        x = 16 // (4 if p.dtype == "f32" else 2)
+        k_shape = (p.num_blocks, p.num_kv_heads, p.head_size // x, p.block_size, x)
+        v_shape = (p.num_blocks, p.num_kv_heads, p.head_size, p.block_size)
+    else:
+        k_shape = v_shape = shape
+    kc = torch.full(k_shape, float("nan"), dtype=tdt, device=dev)
+    vc = torch.full(v_shape, float("nan"), dtype=tdt, device=dev)
     host_k = host_v = None
     if need_host:
         host_k = np.full(shape, gen.poison_value(p.dtype), dtype=gen.storage_dtype(p.dtype))
@@ -127,8 +142,9 @@ def main() -> int:
 
     def sink(ids, kb, vb):
         idx = torch.from_numpy(ids.astype(np.int64)).to(dev)
-        kc.index_copy_(0, idx, up(kb))
-        vc.index_copy_(0, idx, up(vb))
+        kd, vd = gen.to_tiled(kb, vb, p.dtype) if args.layout == "tiled" else (kb, vb)
+        kc.index_copy_(0, idx, up(kd))
+        vc.index_copy_(0, idx, up(vd))
         if need_host:
             host_k[ids] = kb
             host_v[ids] = vb
@@ -141,7 +157,7 @@ def main() -> int:
     copies = args.copies or max(1, min(8, -(-1536 * 2**20 // pool_bytes)))
     pools = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(copies - 1)]
     torch.cuda.synchronize()
-    print(f"[bench] {describe(p)}; inputs ready in {time.perf_counter() - t0:.1f}s; "
+    print(f"[bench] {describe(p, args.layout)}; inputs ready in {time.perf_counter() - t0:.1f}s; "
           f"{copies} pool copies of {pool_bytes / 2**20:.0f} MiB", file=sys.stderr, flush=True)
 
     out = torch.empty((p.num_seqs, p.num_heads, p.head_size), dtype=torch.float32, device=dev)
@@ -218,7 +234,7 @@ def main() -> int:
         max_err = float(np.max(np.abs(result_gpu - ref)))
         if not args.no_cpu_baseline:
             cpu = {"value": round(kv_bytes / or_s / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
-                   "kind": "oracle", "sample": f"one full step of the same workload ({describe(p)}), "
+                   "kind": "oracle", "sample": f"one full step of the same workload ({describe(p, args.layout)}), "
                                                f"{or_s:.2f} s, fp64 NumPy"}
         print(f"[bench] oracle {or_s:.1f}s, max |gpu - oracle| = {max_err:.3e}", file=sys.stderr, flush=True)
 
@@ -238,7 +254,7 @@ def main() -> int:
         "dtype": p.dtype,
         "data": "synthetic",
         "config": {
-            "workload": describe(p),
+            "workload": describe(p, args.layout),
             "num_seqs": p.num_seqs,
             "seq_len": int(p.seq_lens.max()),
             "num_heads": p.num_heads,
@@ -249,6 +265,7 @@ def main() -> int:
             "seed": p.spec.seed,
             "pool_copies": copies,
             "accumulate": "fp32",
+            "kv_layout": args.layout,
         },
         "kernels_ms": {"phase1" if P else "one_pass": round(k1_ms, 5), **({"phase2": round(k2_ms, 5)} if P else {})},
         "ms_per_step_without_events": round(ms_no_events, 5),

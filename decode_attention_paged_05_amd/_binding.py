@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(PKG, "libpad.so")
 
 PAD_DTYPE_F32 = 0
 PAD_DTYPE_BF16 = 1
+PAD_KV_ROWS = 0
+PAD_KV_TILED = 1
 
 STATUS = {
     0: "PAD_OK", -1: "PAD_ERR_NULL", -2: "PAD_ERR_DTYPE", -3: "PAD_ERR_SHAPE",
@@ -44,6 +46,7 @@ class PadDims(ctypes.Structure):
         ("head_size", ctypes.c_int32),
         ("num_blocks", ctypes.c_int64),
         ("max_blocks_per_seq", ctypes.c_int32),
+        ("kv_layout", ctypes.c_int32),
     ]
 
 
@@ -53,7 +56,7 @@ class PadError(RuntimeError):
         super().__init__(f"{where}: {STATUS.get(status, status)}: {strerror(status)}")
 
 
-def _load() -> ctypes.CDLL:
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     # torch's HIP runtime must be the one libpad.so binds to: streams and
     # device memory are objects of that runtime.  Loading torch first makes
     # the dynamic linker resolve libpad's libamdhip64.so.7 to torch's copy
@@ -62,11 +65,11 @@ def _load() -> ctypes.CDLL:
         import torch  # noqa: F401
     except ImportError:
         pass
-    if not os.path.exists(LIB_PATH):
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m decode_attention_paged_05_amd.build` "
+            f"{path} is missing: build it with `python -m decode_attention_paged_05_amd.build` "
             "(there is no fallback implementation)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     dims = ctypes.POINTER(PadDims)
     lib.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, sz, dims, vp]
@@ -138,22 +141,39 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def make_dims(query, key_cache, block_tables) -> PadDims:
-    if query.dim() != 3 or key_cache.dim() != 4 or block_tables.dim() != 2:
-        raise ValueError("expected query [S,H,D], key_cache [NB,Hkv,bs,D], block_tables [S,W]")
+def cache_layout(key_cache, value_cache) -> int:
+    """PAD_KV_ROWS for 4-D K [NB,Hkv,bs,D]; PAD_KV_TILED for 5-D K [NB,Hkv,D/x,bs,x] with V [NB,Hkv,D,bs]."""
+    if key_cache.dim() == 4:
+        return PAD_KV_ROWS
+    if key_cache.dim() == 5 and value_cache.dim() == 4:
+        return PAD_KV_TILED
+    raise ValueError("key_cache must be 4-D (rows layout) or 5-D (tiled layout)")
+
+
+def make_dims(query, key_cache, block_tables, value_cache=None) -> PadDims:
+    if query.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("expected query [S,H,D] and block_tables [S,W]")
     S, H, D = query.shape
-    return PadDims(_dtype_code(query), S, H, D, key_cache.shape[0], block_tables.shape[1])
+    layout = PAD_KV_TILED if key_cache.dim() == 5 else PAD_KV_ROWS
+    return PadDims(_dtype_code(query), S, H, D, key_cache.shape[0], block_tables.shape[1], layout)
 
 
 def _check_tensors(out, query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, block_size):
     torch = _torch()
     if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
         raise TypeError("query, key_cache and value_cache must share a dtype")
-    if key_cache.shape != value_cache.shape:
-        raise ValueError("key_cache and value_cache shapes differ")
     S, H, D = query.shape
-    if tuple(key_cache.shape[1:]) != (num_kv_heads, block_size, D):
-        raise ValueError(f"key_cache must be [num_blocks, {num_kv_heads}, {block_size}, {D}], got {tuple(key_cache.shape)}")
+    layout = cache_layout(key_cache, value_cache)
+    NB = key_cache.shape[0]
+    if layout == PAD_KV_ROWS:
+        want_k = want_v = (NB, num_kv_heads, block_size, D)
+    else:
+        x = 16 // query.element_size()
+        want_k = (NB, num_kv_heads, D // x, block_size, x)
+        want_v = (NB, num_kv_heads, D, block_size)
+    if tuple(key_cache.shape) != want_k or tuple(value_cache.shape) != want_v:
+        raise ValueError(f"caches must be K {want_k} and V {want_v}, got {tuple(key_cache.shape)} and "
+                         f"{tuple(value_cache.shape)}")
     if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise TypeError("block_tables and seq_lens must be int32")
     if block_tables.shape[0] != S or tuple(seq_lens.shape) != (S,):

@@ -45,14 +45,14 @@ def _run(cmd, verbose):
         print("\n".join(lines), flush=True)
 
 
-DEVICE_SOURCES = ["pad_kernels.hip", "pad_attn_bf16_split.hip", "pad_attn_bf16_one_pass.hip",
-                  "pad_attn_f32_split.hip", "pad_attn_f32_one_pass.hip"]
+DEVICE_SOURCES = ["pad_kernels.hip"] + [f"pad_attn_{dt}_{lay}_{form}.hip" for dt in ("bf16", "f32")
+                                         for lay in ("rows", "tiled") for form in ("split", "one_pass")]
 HOST_SOURCES = ["pad_api.cpp"]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+def build(verbose: bool = False, extra_flags=(), out: str = None) -> str:
     cc = hipcc()
-    out = os.path.join(PKG, LIB_NAME)
+    out = out or os.path.join(PKG, LIB_NAME)
     with tempfile.TemporaryDirectory(prefix="pad_build_") as tmp:
         jobs, objs = [], []
         for src in DEVICE_SOURCES:

@@ -53,6 +53,7 @@ int32_t validate(const void* query, const void* key_cache, const void* value_cac
                  int32_t partition_size, const pad_dims_t* dims) {
   if (!dims) return PAD_ERR_NULL;
   if (dims->dtype != PAD_DTYPE_F32 && dims->dtype != PAD_DTYPE_BF16) return PAD_ERR_DTYPE;
+  if (dims->kv_layout != PAD_KV_ROWS && dims->kv_layout != PAD_KV_TILED) return PAD_ERR_DTYPE;
   if (dims->num_seqs < 0 || dims->num_heads <= 0 || num_kv_heads <= 0 || dims->num_blocks <= 0 ||
       dims->max_blocks_per_seq <= 0 || dims->head_size <= 0)
     return PAD_ERR_SHAPE;
@@ -78,6 +79,7 @@ int32_t validate(const void* query, const void* key_cache, const void* value_cac
 pad::Plan make_plan(float scale, int32_t num_kv_heads, int32_t partition_size, const pad_dims_t* dims) {
   pad::Plan p{};
   p.dtype = dims->dtype;
+  p.layout = dims->kv_layout;
   p.num_seqs = dims->num_seqs;
   p.num_heads = dims->num_heads;
   p.num_kv_heads = num_kv_heads;
@@ -240,7 +242,7 @@ const char* paged_attention_decode_strerror(int32_t status) {
   switch (status) {
     case PAD_OK: return "success";
     case PAD_ERR_NULL: return "a required pointer is NULL";
-    case PAD_ERR_DTYPE: return "dtype must be PAD_DTYPE_F32 or PAD_DTYPE_BF16";
+    case PAD_ERR_DTYPE: return "dtype must be PAD_DTYPE_F32 or PAD_DTYPE_BF16 and kv_layout PAD_KV_ROWS or PAD_KV_TILED";
     case PAD_ERR_SHAPE: return "invalid sizes: need num_seqs >= 0, num_heads, num_kv_heads, num_blocks, max_blocks_per_seq >= 1, num_heads % num_kv_heads == 0, finite scale";
     case PAD_ERR_UNSUPPORTED: return "unsupported shape: head_size must be 64, 128 or 256 and block_size 16 (or a grid limit is exceeded)";
     case PAD_ERR_PARTITION: return "partition_size must be >= 0 and a multiple of block_size (> 0 for phase calls)";

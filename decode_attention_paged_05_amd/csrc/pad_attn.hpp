@@ -1,6 +1,6 @@
 // Attention kernel template for paged single-token decode on CDNA4 (gfx950).
 // Included by the pad_attn_*.hip translation units, each of which
-// instantiates one (element type, split/one-pass) family.
+// instantiates one (element type, split/one-pass, layout) family.
 //
 // Split form (second page, "V2 implementation" message; first page, two-pass
 // message):
@@ -19,29 +19,42 @@
 // log2(NW)-step tree through LDS, fixed order, so results are bitwise
 // repeatable).
 //
+// Two cache layouts (second page, hardware-test message, lists both):
+//   rows   K and V [blocks, kv_heads, block_size, D]: every token's row is
+//          contiguous.
+//   tiled  K [blocks, kv_heads, D/x, block_size, x] with x = 16 bytes of
+//          elements, V [blocks, kv_heads, D, block_size].
 // Per 16-token block a wave:
-//   * loads the K tile (16 rows x D) and the V tile with 16-byte buffer loads
-//     whose bounds (num_records) are the block's valid rows: tail slots of the
-//     last block read as zero and never reach the arithmetic, and a block id
-//     outside the pool reads nothing at all;
+//   * loads the block's K and V tile (8 KB each for bf16 D=256) with buffer
+//     loads bounded to the tile (a block id outside the pool reads nothing);
 //   * forms the 16 tokens x 16 heads logit tile on the matrix cores: A = K
 //     (rows = tokens), B = Q^T (columns = the group's heads), contracting over
-//     head_size.  The K tile's 16-byte pieces are already in the operand
-//     layout (lane l holds token l%16 and a 16-byte run of dims; the same run
-//     of Q supplies the B operand), so K goes from the load into the MFMA;
-//   * updates the running max per head (a 4-lane shuffle reduction), turns
-//     the logits into exp2 weights and publishes them through a 1 KB per-wave
-//     LDS tile;
-//   * accumulates P.V in fp32 on the vector ALUs: lane l owns a 16-byte run
-//     of dims of one token per load, so each V load is one contiguous 1 KB
-//     wave access.  Probabilities stay fp32 (bf16 probabilities would cost up
-//     to 2^-9 relative per weight).
-// Loads run R-1 blocks ahead of the arithmetic through a register ring.
+//     D.  Lane l supplies token l%16 and one 16-byte run of dims, exactly one
+//     16-byte load: in the tiled layout the runs of one MFMA step are a
+//     contiguous 1 KB, in the rows layout 16 rows x 64 B;
+//   * updates the running max per head (a 4-lane shuffle reduction) and turns
+//     the logits into exp2 weights p, still in the tile layout: lane l holds
+//     tokens 4*(l/16)+i of head l%16;
+//   * accumulates P.V:
+//       tiled: on the matrix cores.  That p layout is the A operand of a
+//       16x16x16 bf16 MFMA (rows = heads, k = tokens), and a V load of 8 bytes
+//       (4 consecutive tokens of one dim) is its B operand, so nothing moves
+//       through LDS.  p is split into bf16 hi + lo parts (two MFMAs), which
+//       keeps ~2^-17 relative precision; fp32 caches use the fp32 MFMA on p
+//       directly.
+//       rows: on the vector ALUs in fp32: p goes through a 1 KB per-wave LDS
+//       tile, lane l owns a 16-byte run of dims of one token per V load.
+//     Tail tokens of the last block are masked by select: logits to -inf,
+//     and (tiled) their V elements to zero before the MFMA, so NaN padding
+//     never reaches the output.
+// Loads run up to R-1 blocks ahead of the arithmetic through a register ring.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "pad_internal.h"
 
@@ -77,16 +90,6 @@ struct Geom {
   static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
   static constexpr int kVLoads = kBlockTokens / kRowsPerLoad;
   static constexpr int kElemsPerLane = 16 / DT::kBytes;
-  // registers of one in-flight block (K and V)
-  static constexpr int kStageVgprs = 2 * kSteps * 4;
-  // blocks in flight per wave: as many (up to 3) as fit next to the Q operand
-  // and a GH-head accumulator in ~400 of the 512 registers one wave per SIMD owns
-  template <int GH>
-  static constexpr int ring() {
-    constexpr int fixed = kSteps * 4 + GH * kElemsPerLane + 48;
-    constexpr int r = (400 - fixed) / kStageVgprs;
-    return r < 1 ? 1 : (r > 3 ? 3 : r);
-  }
   static_assert(kVLoads == kSteps, "K and V load counts agree");
   static_assert(kRowsPerLoad >= 1, "row fits in a wave");
 };
@@ -156,21 +159,128 @@ __device__ inline void widen(F32, u32x4_t w, float* f) {
   for (int i = 0; i < 4; ++i) f[i] = v[i];
 }
 
-template <class DT, int D, int GH, int NW, bool kSplit>
+// Cache layouts of the K and V pools.
+constexpr int kLayoutRows = 0;
+// Log2 headroom of the lazy softmax reference (weights stay <= 2^8).
+constexpr float kLazyLog2 = 8.0f;
+
+// Build-time tuning knobs (defaults are the tuned values).
+#ifndef PAD_RING_MAX
+#define PAD_RING_MAX 2  // most blocks a wave keeps in flight
+#endif
+#ifndef PAD_SPLIT_WAVES
+#define PAD_SPLIT_WAVES 1  // waves per phase-1 workgroup
+#endif
+#ifndef PAD_KV_LOAD_POLICY
+// cache-policy bits of the K/V buffer loads: non-temporal (each byte is read
+// once; measured ~11 % faster than the default policy on the 100K workload)
+#define PAD_KV_LOAD_POLICY 2
+#endif
+constexpr int kLayoutTiled = 1;
+
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+
+// Where lane `lane` finds its pieces of one tile, per layout.
+template <class DT, int D, int LAYOUT>
+struct TileMap {
+  using G_ = Geom<DT, D>;
+  static constexpr bool kMfmaPV = LAYOUT == kLayoutTiled;
+  // K: kSteps 16-byte loads per lane; step s covers dims [32 s, 32 s + 32)
+  // (bf16) of all 16 tokens
+  __device__ static int k_off(int lane) {
+    return LAYOUT == kLayoutTiled ? 16 * lane : (lane & 15) * G_::kRowBytes + 16 * (lane >> 4);
+  }
+  static constexpr int kKStepBytes = LAYOUT == kLayoutTiled ? 1024 : 64;
+  // V: rows layout, kSteps 16-byte loads (1 KB contiguous per wave load);
+  // tiled layout, one load per 16-dim slice: 4 tokens of one dim per lane
+  // (8 bytes bf16, 16 bytes fp32)
+  static constexpr int kVLoads = LAYOUT == kLayoutTiled ? D / 16 : G_::kSteps;
+  static constexpr int kVBytes = (LAYOUT == kLayoutTiled && DT::kBytes == 2) ? 8 : 16;
+  using VReg = typename std::conditional<kVBytes == 8, u32x2_t, u32x4_t>::type;
+  __device__ static int v_off(int lane) {
+    if (LAYOUT != kLayoutTiled) return 16 * lane;
+    // dim-major tile [D][16 tokens]: dim (lane%16), tokens 4*(lane/16) ...
+    return (lane & 15) * kBlockTokens * DT::kBytes + 4 * DT::kBytes * (lane >> 4);
+  }
+  static constexpr int kVLoadStride = LAYOUT == kLayoutTiled ? 16 * kBlockTokens * DT::kBytes : 1024;
+  static constexpr int kStageVgprs = G_::kSteps * 4 + kVLoads * kVBytes / 4;
+  // accumulator registers per lane
+  template <int GH>
+  static constexpr int acc_vgprs() { return kMfmaPV ? (D / 16) * 4 : GH * G_::kElemsPerLane; }
+  // blocks in flight per wave: as many (up to 3) as fit next to the Q operand
+  // and the accumulator in ~400 of the 512 registers one wave per SIMD owns
+  template <int GH>
+  static constexpr int ring() {
+    constexpr int fixed = G_::kSteps * 4 + acc_vgprs<GH>() + 48;
+    constexpr int r = (400 - fixed) / kStageVgprs;
+    return r < 1 ? 1 : (r > PAD_RING_MAX ? PAD_RING_MAX : r);
+  }
+};
+
+template <int N>
+__device__ inline u32x4_t buffer_load(__amdgpu_buffer_rsrc_t r, int off, u32x4_t*) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, PAD_KV_LOAD_POLICY);
+}
+template <int N>
+__device__ inline u32x2_t buffer_load(__amdgpu_buffer_rsrc_t r, int off, u32x2_t*) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, PAD_KV_LOAD_POLICY);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ inline uint32_t bf16_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// P.V step of the tiled layout for one 16-dim slice: C[head][dim] += sum over
+// the block's 16 tokens of p[head][token] * V[token][dim].
+__device__ inline f32x4_t pv_step(BF16, s16x4_t p_hi, s16x4_t p_lo, const float*, u32x2_t v, f32x4_t c) {
+  const s16x4_t vb = __builtin_bit_cast(s16x4_t, v);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi, vb, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo, vb, c, 0, 0, 0);
+}
+__device__ inline f32x4_t pv_step(F32, s16x4_t, s16x4_t, const float* p, u32x4_t v, f32x4_t c) {
+  const f32x4_t vf = __builtin_bit_cast(f32x4_t, v);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(p[i], vf[i], c, 0, 0, 0);
+  return c;
+}
+
+// Zero the V elements of tokens >= rows (lane holds tokens 4*(lane/16)+e).
+__device__ inline u32x2_t mask_tail(u32x2_t v, int t0, int rows) {
+  const uint32_t m0 = (t0 < rows ? 0xffffu : 0u) | (t0 + 1 < rows ? 0xffff0000u : 0u);
+  const uint32_t m1 = (t0 + 2 < rows ? 0xffffu : 0u) | (t0 + 3 < rows ? 0xffff0000u : 0u);
+  return u32x2_t{v[0] & m0, v[1] & m1};
+}
+__device__ inline u32x4_t mask_tail(u32x4_t v, int t0, int rows) {
+  return u32x4_t{t0 < rows ? v[0] : 0u, t0 + 1 < rows ? v[1] : 0u, t0 + 2 < rows ? v[2] : 0u,
+                 t0 + 3 < rows ? v[3] : 0u};
+}
+
+template <class DT, int D, int GH, int NW, bool kSplit, int LAYOUT>
 __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
   using G_ = Geom<DT, D>;
-  constexpr int R = G_::template ring<GH>();
+  using TM = TileMap<DT, D, LAYOUT>;
+  using VReg = typename TM::VReg;
+  constexpr bool kMfmaPV = TM::kMfmaPV;
+  constexpr int R = TM::template ring<GH>();
   constexpr int kSteps = G_::kSteps;
+  constexpr int kVLoads = TM::kVLoads;
   constexpr int LPR = G_::kLanesPerRow;
   constexpr int RPL = G_::kRowsPerLoad;
   constexpr int EPL = G_::kElemsPerLane;
-  constexpr int kPTile = kBlockTokens * kMaxHeadsPerGroup;  // floats per wave
-  constexpr int kTreeFloats = (NW / 2) * GH * D;             // tree-merge buffer
-  constexpr int kLdsFloats = (NW * kPTile > kTreeFloats) ? NW * kPTile : kTreeFloats;
+  constexpr int kSlices = D / 16;                               // tiled: 16-dim output slices
+  constexpr int kRowsHeld = kMfmaPV ? kMaxHeadsPerGroup : GH;   // head rows an accumulator covers
+  constexpr int kPTile = kMfmaPV ? 0 : kBlockTokens * kMaxHeadsPerGroup;  // floats per wave
+  constexpr int kTreeFloats = (NW / 2) * kRowsHeld * D;                  // tree-merge buffer
+  constexpr int kLdsFloats1 = (NW * kPTile > kTreeFloats) ? NW * kPTile : kTreeFloats;
+  constexpr int kLdsFloats = kLdsFloats1 > 0 ? kLdsFloats1 : 1;
   static_assert((NW & (NW - 1)) == 0, "NW is a power of two");
 
-  __shared__ float lds[kLdsFloats];  // p tiles in the loop, then the tree-merge buffer
+  __shared__ float lds[kLdsFloats];  // rows layout: p tiles in the loop; then the tree-merge buffer
   __shared__ float m_lds[NW][kMaxHeadsPerGroup];
+  __shared__ float t_lds[NW][kMaxHeadsPerGroup];
   __shared__ float l_lds[NW > 1 ? NW / 2 : 1][kMaxHeadsPerGroup];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -204,8 +314,8 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
   const int blk_begin = tok_begin / kBlockTokens;
   const int blk_end = (tok_end + kBlockTokens - 1) / kBlockTokens;
 
-  // Q^T operand: lane l supplies head column l%16 and 16-byte run l/16 of
-  // each 64-byte step (the run the K rows use).
+  // Q^T operand: lane l supplies head column l%16 and the 16-byte run of dims
+  // that the same lane's K load holds.
   u32x4_t qop[kSteps];
   {
     const int qh = lane & 15;
@@ -215,25 +325,37 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
       qop[st] = (qh < gc) ? *reinterpret_cast<const u32x4_t*>(qrow + 64 * st) : u32x4_t{0, 0, 0, 0};
   }
 
-  float m_run = -INFINITY;  // running max (log2 units) of head column lane%16
-  float l_run = 0.0f;       // this lane's share of that head's exp-sum
-  float acc[GH][EPL];       // P.V partial: heads x this lane's dims
+  // Online softmax with a lazy reference: p = exp2(x - m_run) where m_run is
+  // raised (and the accumulators rescaled) only when a block's max exceeds it
+  // by more than kLazyLog2, so p <= 2^kLazyLog2 and rescaling is rare.  The
+  // result does not depend on the reference; m_true keeps the exact max.
+  float m_run = -INFINITY;   // reference max (log2 units) of head column lane%16
+  float m_true = -INFINITY;  // running max of that head's logits (log2 units)
+  float l_run = 0.0f;        // this lane's share of that head's exp-sum, relative to m_run
+  // P.V accumulator.  rows: acc[h][e] = head h, dim EPL*(lane%LPR)+e, summed
+  // over this lane's tokens.  tiled: accm[j][i] = head 4*(lane/16)+i, dim
+  // 16 j + lane%16.
+  float acc[kMfmaPV ? 1 : GH][EPL];
+  f32x4_t accm[kMfmaPV ? kSlices : 1];
 #pragma unroll
-  for (int h = 0; h < GH; ++h)
+  for (int h = 0; h < (kMfmaPV ? 1 : GH); ++h)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < (kMfmaPV ? kSlices : 1); ++j) accm[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   bool bad = false;
 
   float* ptile = lds + wave * kPTile;
   const int32_t* table_row = p.block_tables + (size_t)s * p.max_blocks;
   const size_t head_off = (size_t)g * G_::kTileBytes;
   const size_t block_stride = (size_t)p.num_kv_heads * G_::kTileBytes;
-  const int koff = (lane & 15) * G_::kRowBytes + 16 * (lane >> 4);
-  const int voff = 16 * lane;
+  const int koff = TM::k_off(lane);
+  const int voff = TM::v_off(lane);
+  const int rbase = 4 * (lane >> 4);  // first of the lane's 4 tokens in the logit tile
 
   struct Stage {
     u32x4_t k[kSteps];
-    u32x4_t v[kSteps];
+    VReg v[kVLoads];
   };
 
   for (int seg = blk_begin; seg < blk_end; seg += kWave * NW) {
@@ -256,68 +378,103 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
         rows = 0;
       }
       const size_t base = (size_t)phys * block_stride + head_off;
-      const int bytes = __builtin_amdgcn_readfirstlane(rows * G_::kRowBytes);
+      // rows layout: the bound drops the tail rows; tiled layout interleaves
+      // tokens, so the whole tile is read and the tail is masked by select
+      const int bytes = __builtin_amdgcn_readfirstlane(
+          LAYOUT == kLayoutTiled ? (rows > 0 ? G_::kTileBytes : 0) : rows * G_::kRowBytes);
       __amdgpu_buffer_rsrc_t rk =
           __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.key_cache + base), (short)0, bytes, kRsrcWord3);
       __amdgpu_buffer_rsrc_t rv =
           __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.value_cache + base), (short)0, bytes, kRsrcWord3);
 #pragma unroll
-      for (int j = 0; j < kSteps; ++j) st.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * j, 0, 0);
+      for (int j = 0; j < kSteps; ++j)
+        st.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + TM::kKStepBytes * j, 0, PAD_KV_LOAD_POLICY);
 #pragma unroll
-      for (int j = 0; j < kSteps; ++j) st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + 1024 * j, 0, 0);
+      for (int j = 0; j < kVLoads; ++j)
+        st.v[j] = buffer_load<0>(rv, voff + TM::kVLoadStride * j, static_cast<VReg*>(nullptr));
     };
 
     auto compute = [&](const Stage& st, int blk) {
-      // logits: lane l holds tokens 4*(l/16)+i of the block for head column l%16
+      // logits: lane l holds tokens rbase+i of the block for head column l%16
       f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int j = 0; j < kSteps; ++j) c = qk_step(DT{}, st.k[j], qop[j], c);
-      const int rbase = 4 * (lane >> 4);
-      const int t0 = blk * kBlockTokens + rbase;
+      const int rows = min(kBlockTokens, L - blk * kBlockTokens);
       float x[4];
       float bm = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = (t0 + i < L) ? c[i] * p.qscale : -INFINITY;
+        x[i] = (rbase + i < rows) ? c[i] * p.qscale : -INFINITY;
         bm = fmaxf(bm, x[i]);
       }
       // lanes l, l^16, l^32, l^48 share a head column
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float m_new = fmaxf(m_run, bm);
-      const float alpha = fast_exp2(m_run - m_new);
-      float psum = 0.0f;
+      m_true = fmaxf(m_true, bm);
+      if (__ballot(bm > m_run + kLazyLog2) != 0) {
+        // raise the reference of every head to its running max
+        const float m_new = fmaxf(m_run, bm);
+        const float alpha = fast_exp2(m_run - m_new);  // 0 on the first block
+        l_run *= alpha;
+        m_run = m_new;
+        if constexpr (kMfmaPV) {
+          // accumulator rows are heads rbase+i; their factors live in lanes rbase+i
+          float a[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pw = fast_exp2(x[i] - m_new);
-        psum += pw;
-        ptile[(rbase + i) * kMaxHeadsPerGroup + (lane & 15)] = pw;
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (__ballot(alpha != 1.0f)) {
+          for (int i = 0; i < 4; ++i) a[i] = __shfl(alpha, rbase + i);
 #pragma unroll
-        for (int h = 0; h < GH; ++h) {
-          const float a = readlane_f(alpha, h);
+          for (int j = 0; j < kSlices; ++j)
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] *= a;
+            for (int i = 0; i < 4; ++i) accm[j][i] *= a[i];
+        } else {
+#pragma unroll
+          for (int h = 0; h < GH; ++h) {
+            const float a = readlane_f(alpha, h);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] *= a;
+          }
         }
       }
-      __builtin_amdgcn_wave_barrier();
+      float pw[4];
 #pragma unroll
-      for (int j = 0; j < kSteps; ++j) {
-        const int r = RPL * j + lane / LPR;
-        float pr[GH];
-#pragma unroll
-        for (int h = 0; h < GH; ++h) pr[h] = ptile[r * kMaxHeadsPerGroup + h];
-        float vf[EPL];
-        widen(DT{}, st.v[j], vf);
-#pragma unroll
-        for (int h = 0; h < GH; ++h)
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
+      for (int i = 0; i < 4; ++i) {
+        pw[i] = fast_exp2(x[i] - m_run);
+        l_run += pw[i];
       }
-      __builtin_amdgcn_wave_barrier();
+      if constexpr (kMfmaPV) {
+        s16x4_t p_hi = {0, 0, 0, 0}, p_lo = {0, 0, 0, 0};
+        if constexpr (DT::kBytes == 2) {
+          uint32_t hi[4], lo[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hi[i] = bf16_rne(pw[i]);
+            lo[i] = bf16_rne(pw[i] - __builtin_bit_cast(float, hi[i] << 16));
+          }
+          p_hi = __builtin_bit_cast(s16x4_t, u32x2_t{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)});
+          p_lo = __builtin_bit_cast(s16x4_t, u32x2_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
+        }
+        // V of tail tokens (padding, possibly NaN) is zeroed: 0 * NaN would poison the sum
+#pragma unroll
+        for (int j = 0; j < kVLoads; ++j) accm[j] = pv_step(DT{}, p_hi, p_lo, pw, mask_tail(st.v[j], rbase, rows), accm[j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ptile[(rbase + i) * kMaxHeadsPerGroup + (lane & 15)] = pw[i];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) {
+          const int r = RPL * j + lane / LPR;
+          float pr[GH];
+#pragma unroll
+          for (int h = 0; h < GH; ++h) pr[h] = ptile[r * kMaxHeadsPerGroup + h];
+          float vf[EPL];
+          widen(DT{}, st.v[j], vf);
+#pragma unroll
+          for (int h = 0; h < GH; ++h)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
     };
 
     Stage ring[R];
@@ -333,87 +490,130 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
     }
   }
 
-  // ---- wave totals: fold the token groups of acc and the 4 lanes of l ----
+  // ---- wave totals: fold the token groups of acc (rows) and the 4 lanes of l ----
+  if constexpr (!kMfmaPV) {
 #pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1)
+    for (int off = LPR; off < kWave; off <<= 1)
 #pragma unroll
-    for (int h = 0; h < GH; ++h)
+      for (int h = 0; h < GH; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+        for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+  }
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
+  // (head, dim) -> accumulator element held by this lane, for the merge and
+  // the epilogue.  rows: lanes < LPR hold dims EPL*lane..+EPL-1 of heads 0..GH-1.
+  // tiled: every lane holds heads rbase..rbase+3 at dims 16 j + lane%16.
   if constexpr (NW > 1) {
     // common max per head, each wave rescales itself, then a fixed-order tree sum
     bad = __syncthreads_or(bad);
-    if (lane < kMaxHeadsPerGroup) m_lds[wave][lane] = m_run;
+    if (lane < kMaxHeadsPerGroup) {
+      m_lds[wave][lane] = m_run;
+      t_lds[wave][lane] = m_true;
+    }
     __syncthreads();
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, m_lds[w][lane & 15]);
+    for (int w = 0; w < NW; ++w) {
+      mx = fmaxf(mx, m_lds[w][lane & 15]);
+      m_true = fmaxf(m_true, t_lds[w][lane & 15]);
+    }
     const float sc = fast_exp2(m_run - mx);
     l_run *= sc;
+    if constexpr (kMfmaPV) {
+      float a[4];
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      const float a = readlane_f(sc, h);
+      for (int i = 0; i < 4; ++i) a[i] = __shfl(sc, rbase + i);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= a;
+      for (int j = 0; j < kSlices; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accm[j][i] *= a[i];
+    } else {
+#pragma unroll
+      for (int h = 0; h < GH; ++h) {
+        const float a = readlane_f(sc, h);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= a;
+      }
     }
     m_run = mx;
 #pragma unroll
     for (int half = NW / 2; half >= 1; half /= 2) {
       __syncthreads();
       if (wave >= half && wave < 2 * half) {
-        float* dst = lds + (wave - half) * GH * D;
-        if (lane < LPR)
+        float* dst = lds + (wave - half) * kRowsHeld * D;
+        if constexpr (kMfmaPV) {
+#pragma unroll
+          for (int j = 0; j < kSlices; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(rbase + i) * D + 16 * j + (lane & 15)] = accm[j][i];
+        } else if (lane < LPR) {
 #pragma unroll
           for (int h = 0; h < GH; ++h)
 #pragma unroll
             for (int e = 0; e < EPL; ++e) dst[h * D + EPL * lane + e] = acc[h][e];
+        }
         if (lane < kMaxHeadsPerGroup) l_lds[wave - half][lane] = l_run;
       }
       __syncthreads();
       if (wave < half) {
-        const float* src = lds + wave * GH * D;
-        if (lane < LPR)
+        const float* src = lds + wave * kRowsHeld * D;
+        if constexpr (kMfmaPV) {
+#pragma unroll
+          for (int j = 0; j < kSlices; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accm[j][i] += src[(rbase + i) * D + 16 * j + (lane & 15)];
+        } else if (lane < LPR) {
 #pragma unroll
           for (int h = 0; h < GH; ++h)
 #pragma unroll
             for (int e = 0; e < EPL; ++e) acc[h][e] += src[h * D + EPL * lane + e];
+        }
         l_run += l_lds[wave][lane & 15];
       }
     }
     if (wave != 0) return;
   }
 
-  // ---- epilogue (wave 0): lanes < LPR hold EPL dims of every head ----
+  // ---- epilogue (wave 0) ----
+  const float nan = __builtin_nanf("");
+  if constexpr (kMfmaPV) {
+    // lane l: heads rbase+i, dims 16 j + lane%16
+    float inv[4];
 #pragma unroll
-  for (int h = 0; h < GH; ++h) {
-    if (h >= gc) continue;
-    const float mh = readlane_f(m_run, h);
-    const float lh = readlane_f(l_run, h);
-    const float inv = bad ? __builtin_nanf("") : 1.0f / lh;
-    if constexpr (kSplit) {
-      const size_t row = ((size_t)s * H + h0 + h) * p.num_partitions + part;
+    for (int i = 0; i < 4; ++i) inv[i] = bad ? nan : 1.0f / __shfl(l_run, rbase + i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = rbase + i;
+      if (h < gc) {
+        float* dst = kSplit ? p.tmp_out + (((size_t)s * H + h0 + h) * p.num_partitions + part) * D
+                            : p.out + ((size_t)s * H + h0 + h) * D;
+#pragma unroll
+        for (int j = 0; j < kSlices; ++j) dst[16 * j + (lane & 15)] = accm[j][i] * inv[i];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+      if (h >= gc) continue;
+      const float inv = bad ? nan : 1.0f / readlane_f(l_run, h);
       if (lane < LPR) {
-        float* dst = p.tmp_out + row * D + EPL * lane;
+        float* dst = kSplit ? p.tmp_out + (((size_t)s * H + h0 + h) * p.num_partitions + part) * D + EPL * lane
+                            : p.out + ((size_t)s * H + h0 + h) * D + EPL * lane;
 #pragma unroll
         for (int e = 0; e < EPL; e += 4)
           *reinterpret_cast<f32x4_t*>(dst + e) =
               f32x4_t{acc[h][e] * inv, acc[h][e + 1] * inv, acc[h][e + 2] * inv, acc[h][e + 3] * inv};
       }
-      if (lane == 0) {
-        p.max_logits[row] = bad ? __builtin_nanf("") : mh * kLn2;
-        p.exp_sums[row] = lh;
-      }
-    } else {
-      if (lane < LPR) {
-        float* dst = p.out + ((size_t)s * H + h0 + h) * D + EPL * lane;
-#pragma unroll
-        for (int e = 0; e < EPL; e += 4)
-          *reinterpret_cast<f32x4_t*>(dst + e) =
-              f32x4_t{acc[h][e] * inv, acc[h][e + 1] * inv, acc[h][e + 2] * inv, acc[h][e + 3] * inv};
-      }
+    }
+  }
+  if constexpr (kSplit) {
+    // lane h holds head h's max and exp-sum
+    if (lane < gc) {
+      const size_t row = ((size_t)s * H + h0 + lane) * p.num_partitions + part;
+      p.max_logits[row] = bad ? nan : m_true * kLn2;
+      p.exp_sums[row] = l_run * fast_exp2(m_run - m_true);
     }
   }
 }
@@ -427,24 +627,34 @@ inline hipError_t launch_kernel(AttnKernelFn fn, dim3 grid, dim3 block, const At
   return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, args, 0, stream);
 }
 
-// Kernel for (D, GH, NW) within one (element type, form) family.
-template <class DT, bool kSplit, int NW>
+// Kernel for (D, GH) within one (element type, form, waves, layout) family.
+// The tiled layout's accumulator always spans 16 head rows, so it has a single
+// kernel per D.
+template <class DT, bool kSplit, int NW, int LAYOUT>
 AttnKernelFn select_attn(int d, int gh) {
-#define PAD_GH_CASES(DV)                                   \
-  switch (gh) {                                            \
-    case 1: return attn_kernel<DT, DV, 1, NW, kSplit>;     \
-    case 2: return attn_kernel<DT, DV, 2, NW, kSplit>;     \
-    case 4: return attn_kernel<DT, DV, 4, NW, kSplit>;     \
-    case 6: return attn_kernel<DT, DV, 6, NW, kSplit>;     \
-    case 8: return attn_kernel<DT, DV, 8, NW, kSplit>;     \
-    default: return attn_kernel<DT, DV, 16, NW, kSplit>;   \
+  if constexpr (LAYOUT == kLayoutTiled) {
+    switch (d) {
+      case 64: return attn_kernel<DT, 64, 16, NW, kSplit, LAYOUT>;
+      case 128: return attn_kernel<DT, 128, 16, NW, kSplit, LAYOUT>;
+      default: return attn_kernel<DT, 256, 16, NW, kSplit, LAYOUT>;
+    }
+  } else {
+#define PAD_GH_CASES(DV)                                           \
+  switch (gh) {                                                    \
+    case 1: return attn_kernel<DT, DV, 1, NW, kSplit, LAYOUT>;     \
+    case 2: return attn_kernel<DT, DV, 2, NW, kSplit, LAYOUT>;     \
+    case 4: return attn_kernel<DT, DV, 4, NW, kSplit, LAYOUT>;     \
+    case 6: return attn_kernel<DT, DV, 6, NW, kSplit, LAYOUT>;     \
+    case 8: return attn_kernel<DT, DV, 8, NW, kSplit, LAYOUT>;     \
+    default: return attn_kernel<DT, DV, 16, NW, kSplit, LAYOUT>;   \
   }
-  switch (d) {
-    case 64: PAD_GH_CASES(64)
-    case 128: PAD_GH_CASES(128)
-    default: PAD_GH_CASES(256)
-  }
+    switch (d) {
+      case 64: PAD_GH_CASES(64)
+      case 128: PAD_GH_CASES(128)
+      default: PAD_GH_CASES(256)
+    }
 #undef PAD_GH_CASES
+  }
 }
 
 }  // namespace pad

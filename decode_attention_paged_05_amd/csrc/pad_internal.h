@@ -16,6 +16,7 @@ constexpr int kMaxHeadsPerGroup = 16;
 // Everything the launchers need, validated and derived on the host.
 struct Plan {
   int dtype;          // PAD_DTYPE_*
+  int layout;         // PAD_KV_* (0 rows, 1 tiled)
   int num_seqs;       // S
   int num_heads;      // H
   int num_kv_heads;   // Hkv

@@ -12,16 +12,34 @@
 
 namespace pad {
 
-hipError_t launch_attn_bf16_split(const AttnParams& a, int d, int gh, dim3 grid, hipStream_t stream);
-hipError_t launch_attn_f32_split(const AttnParams& a, int d, int gh, dim3 grid, hipStream_t stream);
-hipError_t launch_attn_bf16_one_pass(const AttnParams& a, int d, int gh, int waves, dim3 grid, hipStream_t stream);
-hipError_t launch_attn_f32_one_pass(const AttnParams& a, int d, int gh, int waves, dim3 grid, hipStream_t stream);
+hipError_t launch_attn_bf16_rows_split(const AttnParams& a, int d, int gh, dim3 grid, hipStream_t stream);
+hipError_t launch_attn_f32_rows_split(const AttnParams& a, int d, int gh, dim3 grid, hipStream_t stream);
+hipError_t launch_attn_bf16_tiled_split(const AttnParams& a, int d, int gh, dim3 grid, hipStream_t stream);
+hipError_t launch_attn_f32_tiled_split(const AttnParams& a, int d, int gh, dim3 grid, hipStream_t stream);
+hipError_t launch_attn_bf16_rows_one_pass(const AttnParams& a, int d, int gh, int waves, dim3 grid,
+                                          hipStream_t stream);
+hipError_t launch_attn_f32_rows_one_pass(const AttnParams& a, int d, int gh, int waves, dim3 grid,
+                                         hipStream_t stream);
+hipError_t launch_attn_bf16_tiled_one_pass(const AttnParams& a, int d, int gh, int waves, dim3 grid,
+                                           hipStream_t stream);
+hipError_t launch_attn_f32_tiled_one_pass(const AttnParams& a, int d, int gh, int waves, dim3 grid,
+                                          hipStream_t stream);
 
 namespace {
 
 // ---------------------------------------------------------------------------
-// Phase 2: log-sum-exp merge.  Grid (ceil(D/64), H, S), 256 threads: 16 lanes
-// x float4 cover 64 dims, 16 lane groups stride over the partitions.
+// Phase 2: log-sum-exp merge.  Grid (D/64, H, S), 256 threads; the workgroup
+// owns 64 dims of one (sequence, head).  Its partitions are taken 256 at a
+// time; for each chunk every load is issued in one round before any
+// arithmetic (the merge is latency-bound, not bandwidth-bound):
+//   thread t     max_logits and exp_sums of partition t of the chunk;
+//   lanes        16 lanes x float4 cover the 64 dims, 16 lane groups take
+//                partitions g, g+16, ... of the chunk (16 float4 each).
+// Then: chunk max -> running max (earlier chunks rescaled), weights
+// w_p = exp_sum_p * exp(max_p - max) through LDS, weighted sums, and a final
+// LDS reduction over the 16 lane groups divided by the summed weights.
+// Slots past the sequence's partition count are read (they exist) but
+// discarded by select, so stale or NaN contents never enter the sums.
 // ---------------------------------------------------------------------------
 struct MergeParams {
   float* out;
@@ -36,6 +54,11 @@ struct MergeParams {
   int num_partitions;
 };
 
+constexpr int kMergeThreads = 256;
+constexpr int kMergeChunk = 256;  // partitions per round
+constexpr int kMergeGroups = 16;  // lane groups striding over a chunk
+constexpr int kMergePerThread = kMergeChunk / kMergeGroups;
+
 __device__ inline float block_reduce_256(float v, bool is_max, float* scratch) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -48,54 +71,79 @@ __device__ inline float block_reduce_256(float v, bool is_max, float* scratch) {
   __syncthreads();
   float r = scratch[0];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) r = is_max ? fmaxf(r, scratch[w]) : r + scratch[w];
+  for (int w = 1; w < kMergeThreads / kWave; ++w) r = is_max ? fmaxf(r, scratch[w]) : r + scratch[w];
   return r;
 }
 
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  __shared__ float scratch[4];
-  __shared__ f32x4_t part_acc[16][16];
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
+  __shared__ float scratch[kMergeThreads / kWave];
+  __shared__ float w_lds[kMergeChunk];
+  __shared__ f32x4_t part_acc[kMergeGroups][16];
   const int tid = threadIdx.x;
   const int s = blockIdx.z;
   const int h = blockIdx.y;
   const int D = p.head_size;
   const int d0 = blockIdx.x * 64;
-  const int L = p.seq_lens[s];
-  float* orow = p.out + ((size_t)s * p.num_heads + h) * D + d0;
-  if (L <= 0 || L > p.max_tokens) {
-    if (tid < 64) orow[tid] = (L == 0) ? 0.0f : __builtin_nanf("");
-    return;
-  }
-  const int np = (L + p.partition - 1) / p.partition;
-  const size_t row0 = ((size_t)s * p.num_heads + h) * p.num_partitions;
-  const float* ml = p.max_logits + row0;
-  const float* es = p.exp_sums + row0;
-  const float* tmp = p.tmp_out + row0 * D + d0;
-
-  float mx = -INFINITY;
-  for (int i = tid; i < np; i += 256) mx = fmaxf(mx, ml[i]);
-  mx = block_reduce_256(mx, true, scratch);
-  const float mx2 = mx * kLog2e;
-  float wsum = 0.0f;
-  for (int i = tid; i < np; i += 256) wsum += es[i] * fast_exp2(ml[i] * kLog2e - mx2);
-  wsum = block_reduce_256(wsum, false, scratch);
-
   const int dl = tid & 15;
   const int pg = tid >> 4;
+  const int NP = p.num_partitions;
+  const size_t row0 = ((size_t)s * p.num_heads + h) * NP;
+  const float* ml = p.max_logits + row0;
+  const float* es = p.exp_sums + row0;
+  const float* tmp = p.tmp_out + row0 * D + d0 + 4 * dl;
+  float* orow = p.out + ((size_t)s * p.num_heads + h) * D + d0;
+
   f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int i = pg; i < np; i += 16) {
-    const float w = es[i] * fast_exp2(ml[i] * kLog2e - mx2);
-    const f32x4_t t = *reinterpret_cast<const f32x4_t*>(tmp + (size_t)i * D + 4 * dl);
-    a += w * t;
+  float wsum = 0.0f;
+  float mrun = -INFINITY;  // running max, log2 units
+  int np = -1;             // partitions of this sequence (known after the first round's loads)
+  for (int c0 = 0; c0 < NP; c0 += kMergeChunk) {
+    // one round of loads: slots that exist, whatever the sequence length
+    const int ti = c0 + tid;
+    const float my_ml = ti < NP ? ml[ti] : -INFINITY;
+    const float my_es = ti < NP ? es[ti] : 0.0f;
+    f32x4_t t[kMergePerThread];
+#pragma unroll
+    for (int k = 0; k < kMergePerThread; ++k) {
+      const int i = c0 + pg + kMergeGroups * k;
+      t[k] = i < NP ? *reinterpret_cast<const f32x4_t*>(tmp + (size_t)i * D) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    if (np < 0) {
+      const int L = p.seq_lens[s];
+      if (L <= 0 || L > p.max_tokens) {
+        if (tid < 64) orow[tid] = (L == 0) ? 0.0f : __builtin_nanf("");
+        return;
+      }
+      np = (L + p.partition - 1) / p.partition;
+    }
+    if (c0 >= np) break;
+    const bool valid = ti < np;
+    const float m2 = valid ? my_ml * kLog2e : -INFINITY;
+    const float cmax = block_reduce_256(m2, true, scratch);
+    const float mnew = fmaxf(mrun, cmax);
+    const float resc = fast_exp2(mrun - mnew);  // 0 on the first chunk
+    a *= resc;
+    wsum *= resc;
+    mrun = mnew;
+    const float w = valid ? my_es * fast_exp2(m2 - mnew) : 0.0f;
+    wsum += w;
+    w_lds[tid] = w;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kMergePerThread; ++k) {
+      const int i = c0 + pg + kMergeGroups * k;
+      if (i < np) a += w_lds[pg + kMergeGroups * k] * t[k];
+    }
+    __syncthreads();  // w_lds is rewritten by the next chunk
   }
+  wsum = block_reduce_256(wsum, false, scratch);
   part_acc[pg][dl] = a;
   __syncthreads();
   if (tid < 16) {
     f32x4_t r = part_acc[0][tid];
 #pragma unroll
-    for (int g = 1; g < 16; ++g) r += part_acc[g][tid];
-    const float inv = 1.0f / wsum;
-    *reinterpret_cast<f32x4_t*>(orow + 4 * tid) = r * inv;
+    for (int g = 1; g < kMergeGroups; ++g) r += part_acc[g][tid];
+    *reinterpret_cast<f32x4_t*>(orow + 4 * tid) = r * (1.0f / wsum);
   }
 }
 
@@ -168,8 +216,11 @@ hipError_t launch_phase1(const Plan& plan, const void* query, const void* key_ca
   const AttnParams a = make_params(plan, query, key_cache, value_cache, block_tables, seq_lens);
   const dim3 grid(plan.num_partitions, plan.num_kv_heads * plan.head_chunks, plan.num_seqs);
   const int gh = heads_template(plan.heads_per_wg);
-  return plan.dtype == 0 ? launch_attn_f32_split(a, plan.head_size, gh, grid, stream)
-                         : launch_attn_bf16_split(a, plan.head_size, gh, grid, stream);
+  if (plan.layout == kLayoutTiled)
+    return plan.dtype == 0 ? launch_attn_f32_tiled_split(a, plan.head_size, gh, grid, stream)
+                           : launch_attn_bf16_tiled_split(a, plan.head_size, gh, grid, stream);
+  return plan.dtype == 0 ? launch_attn_f32_rows_split(a, plan.head_size, gh, grid, stream)
+                         : launch_attn_bf16_rows_split(a, plan.head_size, gh, grid, stream);
 }
 
 hipError_t launch_one_pass(const Plan& plan, float* out, const void* query, const void* key_cache,
@@ -183,8 +234,11 @@ hipError_t launch_one_pass(const Plan& plan, float* out, const void* query, cons
   // otherwise four waves share each workgroup's context
   const int64_t wgs = (int64_t)grid.y * grid.z;
   const int waves = wgs >= 4 * (int64_t)device_cus() ? 1 : 4;
-  return plan.dtype == 0 ? launch_attn_f32_one_pass(a, plan.head_size, gh, waves, grid, stream)
-                         : launch_attn_bf16_one_pass(a, plan.head_size, gh, waves, grid, stream);
+  if (plan.layout == kLayoutTiled)
+    return plan.dtype == 0 ? launch_attn_f32_tiled_one_pass(a, plan.head_size, gh, waves, grid, stream)
+                           : launch_attn_bf16_tiled_one_pass(a, plan.head_size, gh, waves, grid, stream);
+  return plan.dtype == 0 ? launch_attn_f32_rows_one_pass(a, plan.head_size, gh, waves, grid, stream)
+                         : launch_attn_bf16_rows_one_pass(a, plan.head_size, gh, waves, grid, stream);
 }
 
 hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens, hipStream_t stream) {

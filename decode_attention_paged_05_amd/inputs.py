@@ -298,6 +298,16 @@ def fill_pool(problem: Problem, sink: Callable[[np.ndarray, np.ndarray, np.ndarr
             sink(*_assemble(problem, s, rows))
 
 
+def to_tiled(k_blocks: np.ndarray, v_blocks: np.ndarray, dtype: str):
+    """Rows-layout blocks [n, Hkv, bs, D] -> the tiled layout: K [n, Hkv, D/x, bs, x]
+    with x = 16 bytes of elements, V [n, Hkv, D, bs].  A pure permutation."""
+    n, hkv, bs, d = k_blocks.shape
+    x = 16 // np.dtype(storage_dtype(dtype)).itemsize
+    kt = np.ascontiguousarray(k_blocks.reshape(n, hkv, bs, d // x, x).transpose(0, 1, 3, 2, 4))
+    vt = np.ascontiguousarray(v_blocks.transpose(0, 1, 3, 2))
+    return kt, vt
+
+
 def build_pool(problem: Problem, poison: bool = True, threads: Optional[int] = None):
     """Whole K and V pools on the host, unreferenced blocks filled with poison (NaN)."""
     shape = (problem.num_blocks, problem.num_kv_heads, problem.block_size, problem.head_size)

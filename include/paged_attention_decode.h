@@ -29,13 +29,19 @@
  * (row-major, innermost last):
  *   out          float32 [num_seqs, num_heads, head_size]
  *   query        dtype   [num_seqs, num_heads, head_size]
- *   key_cache    dtype   [num_blocks, num_kv_heads, block_size, head_size]
- *   value_cache  dtype   [num_blocks, num_kv_heads, block_size, head_size]
+ *   key_cache    dtype   PAD_KV_ROWS:  [num_blocks, num_kv_heads, block_size, head_size]
+ *                        PAD_KV_TILED: [num_blocks, num_kv_heads, head_size/x, block_size, x]
+ *                                      with x = 16 bytes of elements (8 bf16, 4 fp32)
+ *   value_cache  dtype   PAD_KV_ROWS:  [num_blocks, num_kv_heads, block_size, head_size]
+ *                        PAD_KV_TILED: [num_blocks, num_kv_heads, head_size, block_size]
  *   block_tables int32   [num_seqs, max_blocks_per_seq]
  *   seq_lens     int32   [num_seqs]
- * The second page's hardware-test message names this 4-D layout for both
- * caches of the split kernel; each (block, KV head) tile is block_size *
- * head_size contiguous elements.
+ * The second page's hardware-test message lists both layouts: the 4-D
+ * token-row layout for K and V of its split kernel, and the 5-D x-split K
+ * with the dims-by-tokens V of its one-pass kernel.  In both, each (block, KV
+ * head) tile is block_size * head_size contiguous elements.  PAD_KV_TILED is
+ * the faster one here: every K and V load feeds a matrix-core instruction
+ * directly, so P.V runs on the matrix cores as well as Q.K^T.
  *
  * Ownership: every buffer belongs to the caller.  The library allocates no
  * memory and keeps no per-call state; calls only enqueue kernels on `stream`
@@ -67,10 +73,14 @@ extern "C" {
 #define PAD_DTYPE_F32 0
 #define PAD_DTYPE_BF16 1
 
+/* KV cache layouts (see "Conventions") */
+#define PAD_KV_ROWS 0
+#define PAD_KV_TILED 1
+
 /* status codes */
 #define PAD_OK 0
 #define PAD_ERR_NULL (-1)        /* a required pointer is NULL */
-#define PAD_ERR_DTYPE (-2)       /* dtype is neither PAD_DTYPE_F32 nor PAD_DTYPE_BF16 */
+#define PAD_ERR_DTYPE (-2)       /* dtype is neither PAD_DTYPE_F32 nor PAD_DTYPE_BF16, or kv_layout unknown */
 #define PAD_ERR_SHAPE (-3)       /* a size is out of range or sizes disagree (e.g. num_heads % num_kv_heads != 0) */
 #define PAD_ERR_UNSUPPORTED (-4) /* head_size not 64/128/256, or block_size not 16 */
 #define PAD_ERR_PARTITION (-5)   /* partition_size negative or not a multiple of block_size */
@@ -85,6 +95,7 @@ extern "C" {
  *   head_size          D in {64, 128, 256}
  *   num_blocks         physical blocks in the KV pool, >= 1
  *   max_blocks_per_seq W >= 1, the block-table row width
+ *   kv_layout          PAD_KV_ROWS | PAD_KV_TILED (key_cache and value_cache)
  */
 typedef struct pad_dims {
   int32_t dtype;
@@ -93,6 +104,7 @@ typedef struct pad_dims {
   int32_t head_size;
   int64_t num_blocks;
   int32_t max_blocks_per_seq;
+  int32_t kv_layout;
 } pad_dims_t;
 
 /*

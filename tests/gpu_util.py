@@ -27,17 +27,34 @@ def torch_dtype(dtype: str):
     return torch.float32 if dtype == "f32" else torch.bfloat16
 
 
-class DeviceProblem:
-    """A problem's inputs on the GPU (pool poisoned with NaN outside referenced rows),
-    optionally with the host pool kept for the oracle."""
+LAYOUTS = ("rows", "tiled")
 
-    def __init__(self, problem: gen.Problem, keep_host: bool = True, device="cuda", pool_copies: int = 1):
+
+def tiled_shapes(problem: gen.Problem):
+    x = 16 // np.dtype(gen.storage_dtype(problem.dtype)).itemsize
+    NB, Hkv, bs, D = problem.num_blocks, problem.num_kv_heads, problem.block_size, problem.head_size
+    return (NB, Hkv, D // x, bs, x), (NB, Hkv, D, bs)
+
+
+class DeviceProblem:
+    """A problem's inputs on the GPU in one or both cache layouts (pool
+    poisoned with NaN outside referenced rows), optionally with the host pool
+    (rows layout) kept for the oracle."""
+
+    def __init__(self, problem: gen.Problem, keep_host: bool = True, device="cuda", layouts=LAYOUTS):
         require_gpu()
         self.p = problem
         shape = (problem.num_blocks, problem.num_kv_heads, problem.block_size, problem.head_size)
         td = torch_dtype(problem.dtype)
-        self.kc = torch.full(shape, float("nan"), dtype=td, device=device)
-        self.vc = torch.full(shape, float("nan"), dtype=td, device=device)
+        self.caches = {}
+        if "rows" in layouts:
+            self.caches["rows"] = (torch.full(shape, float("nan"), dtype=td, device=device),
+                                   torch.full(shape, float("nan"), dtype=td, device=device))
+        if "tiled" in layouts:
+            ks, vs = tiled_shapes(problem)
+            self.caches["tiled"] = (torch.full(ks, float("nan"), dtype=td, device=device),
+                                    torch.full(vs, float("nan"), dtype=td, device=device))
+        self.layout = layouts[0]
         self.kc_host = self.vc_host = None
         if keep_host:
             sd = gen.storage_dtype(problem.dtype)
@@ -47,8 +64,15 @@ class DeviceProblem:
 
         def sink(ids, kb, vb):
             idx = torch.from_numpy(ids.astype(np.int64)).to(device)
-            self.kc.index_copy_(0, idx, to_device(kb, problem.dtype, device))
-            self.vc.index_copy_(0, idx, to_device(vb, problem.dtype, device))
+            if "rows" in self.caches:
+                k, v = self.caches["rows"]
+                k.index_copy_(0, idx, to_device(kb, problem.dtype, device))
+                v.index_copy_(0, idx, to_device(vb, problem.dtype, device))
+            if "tiled" in self.caches:
+                kt, vt = gen.to_tiled(kb, vb, problem.dtype)
+                k, v = self.caches["tiled"]
+                k.index_copy_(0, idx, to_device(kt, problem.dtype, device))
+                v.index_copy_(0, idx, to_device(vt, problem.dtype, device))
             if keep_host:
                 self.kc_host[ids] = kb
                 self.vc_host[ids] = vb
@@ -58,6 +82,18 @@ class DeviceProblem:
         self.tables = torch.from_numpy(problem.block_tables).to(device)
         self.lens = torch.from_numpy(problem.seq_lens).to(device)
         torch.cuda.synchronize()
+
+    @property
+    def kc(self):
+        return self.caches[self.layout][0]
+
+    @property
+    def vc(self):
+        return self.caches[self.layout][1]
+
+    def use(self, layout: str) -> "DeviceProblem":
+        self.layout = layout
+        return self
 
     def workspace(self, partition_size: int, init: bool = True):
         p = self.p

@@ -50,6 +50,7 @@ def call(partition=512, scale=0.0625, kv=4, bs=16, ws=FAKE, ws_bytes=1 << 30, d=
 
 @pytest.mark.parametrize("kw,status", [
     (dict(d=dims(dtype=7)), -2),
+    (dict(d=dims(kv_layout=2)), -2),
     (dict(d=dims(num_heads=24), kv=5), -3),
     (dict(d=dims(num_seqs=-1)), -3),
     (dict(d=dims(num_blocks=0)), -3),

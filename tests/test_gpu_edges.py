@@ -34,10 +34,11 @@ def custom(lens, H=24, Hkv=4, D=256, dtype="bf16", W=None, P=512, seed=21, extra
 RAGGED = [0, 1, 15, 16, 17, 511, 512, 513, 1000]
 
 
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
 @pytest.mark.parametrize("P", [0, 16, 512, 1024])
-def test_ragged_and_empty(P):
-    dp = gu.DeviceProblem(custom(RAGGED, P=P))
-    log(f"[run] ragged P={P}")
+def test_ragged_and_empty(P, layout):
+    dp = gu.DeviceProblem(custom(RAGGED, P=P)).use(layout)
+    log(f"[run] ragged P={P} {layout}")
     out = dp.run()
     ref = dp.oracle()
     assert np.all(ref[0] == 0)
@@ -63,24 +64,29 @@ SHAPES = [
 @pytest.mark.parametrize("P", [0, 64])
 def test_head_groupings(shape, P):
     dp = gu.DeviceProblem(custom([37, 300, 1, 129], P=P, **shape))
-    log(f"[run] {shape} P={P}")
-    out = dp.run()
-    gu.assert_close(out, dp.oracle(), shape["dtype"], f"{shape} P={P}")
+    ref = dp.oracle()
+    for layout in gu.LAYOUTS:
+        log(f"[run] {shape} P={P} {layout}")
+        out = dp.use(layout).run()
+        gu.assert_close(out, ref, shape["dtype"], f"{shape} P={P} {layout}")
 
 
 def test_one_pass_one_wave_variant():
     # 256 sequences x 4 KV heads = 1024 workgroups: the one-wave one-pass kernel
     lens = np.random.default_rng(5).integers(1, 200, size=256).tolist()
     dp = gu.DeviceProblem(custom(lens, P=0))
-    log("[run] one-pass, 1024 workgroups")
-    out = dp.run()
-    gu.assert_close(out, dp.oracle(), "bf16", "one-pass one-wave")
-    split = dp.run(partition_size=64)
-    gu.assert_close(split, dp.oracle(), "bf16", "split P=64, 256 seqs")
+    ref = dp.oracle()
+    for layout in gu.LAYOUTS:
+        log(f"[run] one-pass, 1024 workgroups, {layout}")
+        out = dp.use(layout).run()
+        gu.assert_close(out, ref, "bf16", f"one-pass one-wave {layout}")
+        split = dp.run(partition_size=64)
+        gu.assert_close(split, ref, "bf16", f"split P=64, 256 seqs {layout}")
 
 
-def test_phase_entry_points_match_combined_call():
-    dp = gu.DeviceProblem(custom([700, 33, 1500], P=256))
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_phase_entry_points_match_combined_call(layout):
+    dp = gu.DeviceProblem(custom([700, 33, 1500], P=256)).use(layout)
     p = dp.p
     combined = dp.run()
     ws = dp.workspace(256)
@@ -106,12 +112,13 @@ def test_workspace_init_contents():
     assert torch.all(ws[tmp: tmp + 4 * n * D].view(torch.float32) == 0)
 
 
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
 @pytest.mark.parametrize("P", [0, 64])
-def test_out_of_contract_inputs_give_nan_rows(P):
+def test_out_of_contract_inputs_give_nan_rows(P, layout):
     """A length beyond the table width and a block id outside the pool are
     caught inside the kernels: those rows become NaN, the other rows stay
     exact, and no load leaves the pool (bounded buffer loads)."""
-    dp = gu.DeviceProblem(custom([100, 40, 50, 70], P=P, W=8))
+    dp = gu.DeviceProblem(custom([100, 40, 50, 70], P=P, W=8)).use(layout)
     good = dp.run()
     ref = dp.oracle()
     lens = dp.lens.clone()

@@ -36,8 +36,9 @@ def problem(name, **kw):
     return _CACHE[key]
 
 
-def test_tiny_split_and_workspace():
-    dp = problem("tiny")
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_tiny_split_and_workspace(layout):
+    dp = problem("tiny").use(layout)
     p = dp.p
     ws = dp.workspace(p.partition_size)
     log("[run] tiny P=32")
@@ -56,18 +57,20 @@ def test_tiny_split_and_workspace():
         assert np.max(np.abs(tmp[0, h, :n] - o)) < 1e-5
 
 
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
 @pytest.mark.parametrize("P", [0, 16, 48, 112, 1024])
-def test_tiny_every_path(P):
-    dp = problem("tiny")
-    log(f"[run] tiny P={P}")
+def test_tiny_every_path(P, layout):
+    dp = problem("tiny").use(layout)
+    log(f"[run] tiny P={P} {layout}")
     out = dp.run(partition_size=P)
     gu.assert_close(out, dp.oracle(), "f32", f"tiny P={P}")
 
 
-def test_short_one_pass_and_split():
-    dp = problem("short")
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_short_one_pass_and_split(layout):
+    dp = problem("short").use(layout)
     ref = dp.oracle()
-    log("[run] short P=0")
+    log(f"[run] short P=0 {layout}")
     one = dp.run(partition_size=0)
     gu.assert_close(one, ref, "bf16", "short one-pass")
     for P in (512, 8192):
@@ -77,11 +80,12 @@ def test_short_one_pass_and_split():
         assert float((sp - one).abs().max()) <= 2e-3
 
 
-def test_long_split():
-    dp = problem("long")
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_long_split(layout):
+    dp = problem("long").use(layout)
     p = dp.p
     ws = dp.workspace(512)
-    log("[run] long P=512")
+    log(f"[run] long P=512 {layout}")
     out = dp.run(workspace=ws)
     torch.cuda.synchronize()
     ref = dp.oracle()
@@ -100,18 +104,20 @@ def test_long_split():
         assert np.max(np.abs(tmp[0, h, :196] - o)) < 2e-3
 
 
-def test_mixed_split():
-    dp = problem("mixed")
-    log("[run] mixed P=512")
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_mixed_split(layout):
+    dp = problem("mixed").use(layout)
+    log(f"[run] mixed P=512 {layout}")
     out = dp.run()
     err = gu.assert_close(out, dp.oracle(), "bf16", "mixed")
     log(f"[mixed] max err {err:.2e}")
 
 
-def test_stress_sampled():
-    dp = problem("stress")
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_stress_sampled(layout):
+    dp = problem("stress").use(layout)
     p = dp.p
-    log("[run] stress P=1024")
+    log(f"[run] stress P=1024 {layout}")
     out = dp.run()
     torch.cuda.synchronize()
     o = out.cpu().numpy().astype(np.float64)
@@ -128,8 +134,9 @@ def test_stress_sampled():
     assert np.abs(o).max() < 8.0
 
 
-def test_workspace_garbage_is_never_read():
-    dp = problem("tiny")
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_workspace_garbage_is_never_read(layout):
+    dp = problem("tiny").use(layout)
     ws = dp.workspace(32, init=False)
     ws.fill_(0xFF)  # every float is NaN
     a = dp.run(partition_size=32, workspace=ws)
@@ -137,8 +144,9 @@ def test_workspace_garbage_is_never_read():
     assert torch.equal(a, b)
 
 
-def test_long_repeatable_and_block_permutation_invariant():
-    dp = problem("long")
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_long_repeatable_and_block_permutation_invariant(layout):
+    dp = problem("long").use(layout)
     a = dp.run()
     b = dp.run()
     assert torch.equal(a, b), "two runs differ"

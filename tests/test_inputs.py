@@ -95,3 +95,16 @@ def test_threads_do_not_change_bits():
 def test_bad_lengths_rejected():
     with pytest.raises(ValueError):
         gen.make_problem("tiny", seq_lens=[113])
+
+
+@pytest.mark.parametrize("dtype,x", [("bf16", 8), ("f32", 4)])
+def test_tiled_layout_is_the_documented_permutation(dtype, x):
+    rng = np.random.default_rng(3)
+    sd = gen.storage_dtype(dtype)
+    kb = rng.integers(0, 60000, size=(3, 2, 16, 64)).astype(sd)
+    vb = rng.integers(0, 60000, size=(3, 2, 16, 64)).astype(sd)
+    kt, vt = gen.to_tiled(kb, vb, dtype)
+    assert kt.shape == (3, 2, 64 // x, 16, x) and vt.shape == (3, 2, 64, 16)
+    for n, g, t, d in [(0, 0, 0, 0), (2, 1, 15, 63), (1, 0, 7, 9), (2, 1, 3, x)]:
+        assert kt[n, g, d // x, t, d % x] == kb[n, g, t, d]
+        assert vt[n, g, d, t] == vb[n, g, t, d]
