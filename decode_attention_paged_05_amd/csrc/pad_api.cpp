@@ -18,7 +18,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t ml, es, tmp, total;
+  size_t ml, es, tmp, counters, scratch, total;
   int64_t np;
   size_t n_stats, n_tmp;
 };
@@ -27,7 +27,7 @@ struct Layout {
 bool workspace_layout(int32_t S, int32_t H, int32_t D, int32_t W, int32_t bs, int32_t P, Layout* out) {
   if (S < 0 || H <= 0 || D <= 0 || W <= 0 || bs <= 0 || P < 0) return false;
   if (P == 0) {
-    *out = Layout{0, 0, 0, 0, 0, 0, 0};
+    *out = Layout{0, 0, 0, 0, 0, 0, 0, 0, 0};
     return true;
   }
   if (P % bs) return false;
@@ -42,7 +42,10 @@ bool workspace_layout(int32_t S, int32_t H, int32_t D, int32_t W, int32_t bs, in
   l.ml = 0;
   l.es = round_up(n_stats * sizeof(float), kAlign);
   l.tmp = l.es + round_up(n_stats * sizeof(float), kAlign);
-  l.total = l.tmp + round_up(n_tmp * sizeof(float), kAlign);
+  // bookkeeping of the phase-1 pool: counters, then the chunk scratch slots
+  l.counters = l.tmp + round_up(n_tmp * sizeof(float), kAlign);
+  l.scratch = l.counters + round_up(pad::kPoolCounters * sizeof(unsigned), kAlign);
+  l.total = l.scratch + round_up((size_t)pad::kMaxPoolTickets * pad::piece_floats(D) * sizeof(float), kAlign);
   *out = l;
   return true;
 }
@@ -105,6 +108,8 @@ bool attach_workspace(pad::Plan* p, void* workspace, size_t workspace_bytes) {
   p->max_logits = reinterpret_cast<float*>(base + l.ml);
   p->exp_sums = reinterpret_cast<float*>(base + l.es);
   p->tmp_out = reinterpret_cast<float*>(base + l.tmp);
+  p->counters = reinterpret_cast<unsigned*>(base + l.counters);
+  p->scratch = reinterpret_cast<float*>(base + l.scratch);
   return true;
 }
 
@@ -150,6 +155,7 @@ int32_t paged_attention_decode_workspace_init(void* workspace, size_t workspace_
   return status_of(pad::launch_workspace_fill(reinterpret_cast<float*>(base + l.ml),
                                               reinterpret_cast<float*>(base + l.es),
                                               reinterpret_cast<float*>(base + l.tmp), l.n_stats, l.n_tmp,
+                                              reinterpret_cast<unsigned*>(base + l.counters), pad::kPoolCounters,
                                               static_cast<hipStream_t>(stream)));
 }
 

@@ -113,6 +113,17 @@ struct AttnParams {
   int partition;       // tokens per partition (split)
   int num_partitions;  // NP (split)
   float qscale;        // scale * log2(e)
+  // phase-1 pool (pool_tickets == 0: none): partitions [main_parts, NP) of
+  // every (sequence, head group) are cut into chunks that workgroups take
+  // after their own partition
+  unsigned* counters;  // [0] tickets handed out, [1 + item] chunks done
+  float* scratch;      // [pool_tickets][piece_floats(D)]
+  int gy_count;        // head groups per sequence (num_kv_heads * head_chunks)
+  int main_parts;      // partitions per (sequence, head group) owned by a workgroup
+  int pool_parts;      // NP - main_parts
+  int pool_chunks;     // chunks per pooled partition
+  int pool_chunk_blocks;
+  int pool_tickets;    // S * gy_count * pool_parts * pool_chunks
 };
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -177,6 +188,19 @@ constexpr float kLazyLog2 = 8.0f;
 #define PAD_KV_LOAD_POLICY 2
 #endif
 constexpr int kLayoutTiled = 1;
+#ifndef PAD_TICKET_LEAD
+// blocks before the end of a walk at which the next pool ticket is requested,
+// so that the request's round trip overlaps the last loads
+#define PAD_TICKET_LEAD 3
+#endif
+// Atomics on the pool's ticket counter, performed at system scope: every
+// workgroup, on whichever XCD, sees one sequence of values.
+__device__ inline unsigned atomic_add_system(unsigned* ptr, unsigned v) {
+  return __hip_atomic_fetch_add(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ inline void atomic_store_system(unsigned* ptr, unsigned v) {
+  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
@@ -258,24 +282,414 @@ __device__ inline u32x4_t mask_tail(u32x4_t v, int t0, int rows) {
                  t0 + 3 < rows ? v[3] : 0u};
 }
 
-template <class DT, int D, int GH, int NW, bool kSplit, int LAYOUT>
-__global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
+// One wave's walk over a range of blocks for one (sequence, KV head, head
+// chunk): its running max, exp-sum and P.V accumulator, plus the flag of a
+// block id outside the pool.
+template <class DT, int D, int GH, int NW, int LAYOUT>
+struct Walker {
   using G_ = Geom<DT, D>;
   using TM = TileMap<DT, D, LAYOUT>;
   using VReg = typename TM::VReg;
-  constexpr bool kMfmaPV = TM::kMfmaPV;
-  constexpr int R = TM::template ring<GH>();
-  constexpr int kSteps = G_::kSteps;
-  constexpr int kVLoads = TM::kVLoads;
-  constexpr int LPR = G_::kLanesPerRow;
-  constexpr int RPL = G_::kRowsPerLoad;
-  constexpr int EPL = G_::kElemsPerLane;
-  constexpr int kSlices = D / 16;                               // tiled: 16-dim output slices
-  constexpr int kRowsHeld = kMfmaPV ? kMaxHeadsPerGroup : GH;   // head rows an accumulator covers
-  constexpr int kPTile = kMfmaPV ? 0 : kBlockTokens * kMaxHeadsPerGroup;  // floats per wave
-  constexpr int kTreeFloats = (NW / 2) * kRowsHeld * D;                  // tree-merge buffer
+  static constexpr bool kMfmaPV = TM::kMfmaPV;
+  static constexpr int R = TM::template ring<GH>();
+  static constexpr int kSteps = G_::kSteps;
+  static constexpr int kVLoads = TM::kVLoads;
+  static constexpr int LPR = G_::kLanesPerRow;
+  static constexpr int RPL = G_::kRowsPerLoad;
+  static constexpr int EPL = G_::kElemsPerLane;
+  static constexpr int kSlices = D / 16;                               // tiled: 16-dim output slices
+  static constexpr int kRowsHeld = kMfmaPV ? kMaxHeadsPerGroup : GH;   // head rows an accumulator covers
+  static constexpr int kPTile = kMfmaPV ? 0 : kBlockTokens * kMaxHeadsPerGroup;  // floats per wave
+
+  struct Stage {
+    u32x4_t k[kSteps];
+    VReg v[kVLoads];
+  };
+
+  int lane;
+  int rbase;  // first of the lane's 4 tokens in the logit tile
+  u32x4_t qop[kSteps];
+  // Online softmax with a lazy reference: p = exp2(x - m_run) where m_run is
+  // raised (and the accumulators rescaled) only when a block's max exceeds it
+  // by more than kLazyLog2, so p <= 2^kLazyLog2 and rescaling is rare.  The
+  // result does not depend on the reference; m_true keeps the exact max.
+  float m_run;   // reference max (log2 units) of head column lane%16
+  float m_true;  // running max of that head's logits (log2 units)
+  float l_run;   // this lane's share of that head's exp-sum, relative to m_run
+  // P.V accumulator.  rows: acc[h][e] = head h, dim EPL*(lane%LPR)+e, summed
+  // over this lane's tokens.  tiled: accm[j][i] = head rbase+i, dim 16 j + lane%16.
+  float acc[kMfmaPV ? 1 : GH][EPL];
+  f32x4_t accm[kMfmaPV ? kSlices : 1];
+  bool bad;
+  // Pool ticket requested during the walk (phase-1 pool): the counter to take
+  // it from (null: none), and the value (lane 0) once `asked`.
+  unsigned* ticket_ctr = nullptr;
+  unsigned next_ticket = 0;
+  bool asked = false;
+
+  __device__ explicit Walker(int lane_) : lane(lane_), rbase(4 * (lane_ >> 4)) {}
+
+  __device__ void ask_ticket() {
+    if (lane == 0) next_ticket = atomic_add_system(ticket_ctr, 1u);
+    asked = true;
+  }
+
+  // Q^T operand: lane l supplies head column l%16 and the 16-byte run of dims
+  // that the same lane's K load holds.
+  __device__ void load_q(const AttnParams& p, int s, int h0, int gc) {
+    const int qh = lane & 15;
+    const char* qrow = p.query + ((size_t)s * p.num_heads + h0 + qh) * G_::kRowBytes + 16 * (lane >> 4);
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st)
+      qop[st] = (qh < gc) ? *reinterpret_cast<const u32x4_t*>(qrow + 64 * st) : u32x4_t{0, 0, 0, 0};
+  }
+
+  __device__ void reset() {
+    m_run = -INFINITY;
+    m_true = -INFINITY;
+    l_run = 0.0f;
+#pragma unroll
+    for (int h = 0; h < (kMfmaPV ? 1 : GH); ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < (kMfmaPV ? kSlices : 1); ++j) accm[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    bad = false;
+    asked = false;
+  }
+
+  // Multiply the accumulator rows of head h by the factor lane h holds.
+  __device__ void scale_heads(float f) {
+    if constexpr (kMfmaPV) {
+      float a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = __shfl(f, rbase + i);
+#pragma unroll
+      for (int j = 0; j < kSlices; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accm[j][i] *= a[i];
+    } else {
+#pragma unroll
+      for (int h = 0; h < GH; ++h) {
+        const float a = readlane_f(f, h);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= a;
+      }
+    }
+  }
+
+  // Blocks [blk_begin, blk_end) of sequence s (L tokens), KV head g; wave
+  // `wave` of NW takes blocks blk_begin + wave, + NW, ...
+  __device__ void walk(const AttnParams& p, int s, int g, int L, int blk_begin, int blk_end, int wave,
+                       float* ptile) {
+    const int32_t* table_row = p.block_tables + (size_t)s * p.max_blocks;
+    const size_t head_off = (size_t)g * G_::kTileBytes;
+    const size_t block_stride = (size_t)p.num_kv_heads * G_::kTileBytes;
+    const int koff = TM::k_off(lane);
+    const int voff = TM::v_off(lane);
+
+    for (int seg = blk_begin; seg < blk_end; seg += kWave * NW) {
+      const int seg_end = min(seg + kWave * NW, blk_end);
+      const int first = seg + wave;
+      const int n = first < seg_end ? (seg_end - first + NW - 1) / NW : 0;
+      const int my_id = lane < n ? table_row[first + NW * lane] : -1;
+      // the pool ticket goes out PAD_TICKET_LEAD blocks before the walk ends
+      const int ask_at = (ticket_ctr != nullptr && seg_end == blk_end) ? max(0, n - PAD_TICKET_LEAD) : -1;
+
+      // Enqueue the loads of the wave's idx-th block (zero-length, no traffic,
+      // past the wave's last block).
+      auto issue = [&](Stage& st, int idx) {
+        const bool live = idx < n;
+        int phys = live ? __builtin_amdgcn_readlane(my_id, idx) : 0;
+        const int blk = first + NW * idx;
+        int rows = live ? min(kBlockTokens, L - blk * kBlockTokens) : 0;
+        const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
+        bad |= live && !ok;
+        if (!ok) {
+          phys = 0;
+          rows = 0;
+        }
+        const size_t base = (size_t)phys * block_stride + head_off;
+        // rows layout: the bound drops the tail rows; tiled layout interleaves
+        // tokens, so the whole tile is read and the tail is masked by select
+        const int bytes = __builtin_amdgcn_readfirstlane(
+            LAYOUT == kLayoutTiled ? (rows > 0 ? G_::kTileBytes : 0) : rows * G_::kRowBytes);
+        __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.key_cache + base), (short)0, bytes, kRsrcWord3);
+        __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.value_cache + base), (short)0, bytes, kRsrcWord3);
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j)
+          st.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + TM::kKStepBytes * j, 0, PAD_KV_LOAD_POLICY);
+#pragma unroll
+        for (int j = 0; j < kVLoads; ++j)
+          st.v[j] = buffer_load<0>(rv, voff + TM::kVLoadStride * j, static_cast<VReg*>(nullptr));
+      };
+
+      auto compute = [&](const Stage& st, int blk) {
+        // logits: lane l holds tokens rbase+i of the block for head column l%16
+        f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) c = qk_step(DT{}, st.k[j], qop[j], c);
+        const int rows = min(kBlockTokens, L - blk * kBlockTokens);
+        float x[4];
+        float bm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = (rbase + i < rows) ? c[i] * p.qscale : -INFINITY;
+          bm = fmaxf(bm, x[i]);
+        }
+        // lanes l, l^16, l^32, l^48 share a head column
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        m_true = fmaxf(m_true, bm);
+        if (__ballot(bm > m_run + kLazyLog2) != 0) {
+          // raise the reference of every head to its running max
+          const float m_new = fmaxf(m_run, bm);
+          const float alpha = fast_exp2(m_run - m_new);  // 0 on the first block
+          l_run *= alpha;
+          m_run = m_new;
+          scale_heads(alpha);
+        }
+        float pw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pw[i] = fast_exp2(x[i] - m_run);
+          l_run += pw[i];
+        }
+        if constexpr (kMfmaPV) {
+          s16x4_t p_hi = {0, 0, 0, 0}, p_lo = {0, 0, 0, 0};
+          if constexpr (DT::kBytes == 2) {
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              hi[i] = bf16_rne(pw[i]);
+              lo[i] = bf16_rne(pw[i] - __builtin_bit_cast(float, hi[i] << 16));
+            }
+            p_hi = __builtin_bit_cast(s16x4_t, u32x2_t{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)});
+            p_lo = __builtin_bit_cast(s16x4_t, u32x2_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
+          }
+          // V of tail tokens (padding, possibly NaN) is zeroed: 0 * NaN would poison the sum
+#pragma unroll
+          for (int j = 0; j < kVLoads; ++j)
+            accm[j] = pv_step(DT{}, p_hi, p_lo, pw, mask_tail(st.v[j], rbase, rows), accm[j]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ptile[(rbase + i) * kMaxHeadsPerGroup + (lane & 15)] = pw[i];
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int j = 0; j < kSteps; ++j) {
+            const int r = RPL * j + lane / LPR;
+            float pr[GH];
+#pragma unroll
+            for (int h = 0; h < GH; ++h) pr[h] = ptile[r * kMaxHeadsPerGroup + h];
+            float vf[EPL];
+            widen(DT{}, st.v[j], vf);
+#pragma unroll
+            for (int h = 0; h < GH; ++h)
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
+          }
+          __builtin_amdgcn_wave_barrier();
+        }
+      };
+
+      Stage ring[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) issue(ring[r], r);
+      for (int i = 0; i < n; i += R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int idx = i + r;
+          if (idx == ask_at) ask_ticket();
+          if (idx < n) compute(ring[r], first + NW * idx);
+          issue(ring[r], idx + R);
+        }
+      }
+    }
+  }
+
+  // Wave totals: fold the token groups of acc (rows) and the 4 lanes of l.
+  __device__ void fold() {
+    if constexpr (!kMfmaPV) {
+#pragma unroll
+      for (int off = LPR; off < kWave; off <<= 1)
+#pragma unroll
+        for (int h = 0; h < GH; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+    }
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+  }
+
+  // Rows of heads [0, gc), each scaled by the factor lane h holds, into a
+  // scratch slot starting at byte `slot`: float kPieceStats + h * D + d.  One
+  // per-lane offset register; the rest rides in the scalar offset (which
+  // changes with the slot, so no per-store offset registers are kept live).
+  __device__ void write_piece(__amdgpu_buffer_rsrc_t rs, int slot, int gc, float inv_of_lane) const {
+    if constexpr (kMfmaPV) {
+      float inv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) inv[i] = __shfl(inv_of_lane, rbase + i);
+      const int voff = 4 * (kPieceStats + rbase * D + (lane & 15));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (rbase + i < gc) {
+#pragma unroll
+          for (int j = 0; j < kSlices; ++j)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, accm[j][i] * inv[i]), rs, voff,
+                                                  slot + 4 * (i * D + 16 * j), 0);
+        }
+      }
+    } else {
+      const int voff = 4 * (kPieceStats + EPL * lane);
+#pragma unroll
+      for (int h = 0; h < GH; ++h) {
+        if (h >= gc) continue;
+        const float ih = readlane_f(inv_of_lane, h);
+        if (lane < LPR) {
+#pragma unroll
+          for (int e = 0; e < EPL; e += 4)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t, f32x4_t{acc[h][e] * ih, acc[h][e + 1] * ih, acc[h][e + 2] * ih,
+                                                    acc[h][e + 3] * ih}),
+                rs, voff, slot + 4 * (h * D + e), 0);
+        }
+      }
+    }
+  }
+
+  // Normalised rows of heads [0, gc): store(h, d, value) with value scaled by
+  // the factor lane h holds.
+  template <class Store>
+  __device__ void write_rows(int gc, float inv_of_lane, Store store) const {
+    if constexpr (kMfmaPV) {
+      // lane l: heads rbase+i, dims 16 j + lane%16
+      float inv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) inv[i] = __shfl(inv_of_lane, rbase + i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = rbase + i;
+        if (h < gc) {
+#pragma unroll
+          for (int j = 0; j < kSlices; ++j) store(h, 16 * j + (lane & 15), accm[j][i] * inv[i]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < GH; ++h) {
+        if (h >= gc) continue;
+        const float inv = readlane_f(inv_of_lane, h);
+        if (lane < LPR) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) store(h, EPL * lane + e, acc[h][e] * inv);
+        }
+      }
+    }
+  }
+};
+
+
+
+// One unit of phase-1 work for a workgroup: blocks [b0, b1) of sequence s,
+// KV head g, query heads [h0, h0 + gc), inside partition `part`.
+struct WorkItem {
+  int s, g, h0, gc, L, part, b0, b1;
+  bool len_ok;
+};
+
+__device__ inline WorkItem make_item(const AttnParams& p, int s, int gy, int part) {
+  WorkItem it;
+  it.s = s;
+  it.g = gy / p.head_chunks;
+  const int chunk = gy - it.g * p.head_chunks;
+  it.h0 = it.g * p.group + chunk * kMaxHeadsPerGroup;
+  it.gc = min(kMaxHeadsPerGroup, p.group - chunk * kMaxHeadsPerGroup);
+  it.L = p.seq_lens[s];
+  it.len_ok = it.L >= 0 && it.L <= p.max_blocks * kBlockTokens;
+  it.part = part;
+  it.b0 = 0;
+  it.b1 = 0;
+  return it;
+}
+
+// The pool of phase 1 (one-wave workgroups).  After its own partition every
+// workgroup takes tickets from p.counters[0] until the pool is empty.  Ticket
+// t is chunk t % pool_chunks (p.pool_chunk_blocks blocks) of pooled item
+// t / pool_chunks, that is partition main_parts + pp of one (sequence, head
+// group).  The chunk's partial result -- max, exp-sum and normalised rows, as
+// for a partition -- goes to scratch slot t, and phase 2 merges the chunk
+// entries together with the partition entries: the log-sum-exp merge is the
+// same whether a stretch of tokens arrives as one partition or as several
+// chunks.  The counter returns to zero by itself: every workgroup makes
+// exactly one failing request, and the one that receives the launch's last
+// value resets it.
+
+// Resolve the ticket the walk asked for (or ask now); false when the pool is
+// empty.
+template <class W_>
+__device__ inline bool take_ticket(const AttnParams& p, W_& w, unsigned* ticket) {
+  if (!w.asked) w.ask_ticket();
+  const unsigned t = __builtin_amdgcn_readfirstlane(w.next_ticket);
+  const unsigned total = (unsigned)p.pool_tickets;
+  if (t < total) {
+    *ticket = t;
+    return true;
+  }
+  const unsigned nwg = gridDim.x * gridDim.y * gridDim.z;
+  if (t == total + nwg - 1 && w.lane == 0) atomic_store_system(p.counters, 0u);
+  return false;
+}
+
+__device__ inline WorkItem ticket_item(const AttnParams& p, unsigned t) {
+  const int item = (int)t / p.pool_chunks;
+  const int c = (int)t - item * p.pool_chunks;
+  const int pp = item % p.pool_parts;
+  const int sg = item / p.pool_parts;
+  WorkItem it = make_item(p, sg / p.gy_count, sg % p.gy_count, p.main_parts + pp);
+  const int pblocks = p.partition / kBlockTokens;
+  const int lblocks = it.len_ok ? (it.L + kBlockTokens - 1) / kBlockTokens : 0;
+  const int pb0 = it.part * pblocks;
+  it.b0 = pb0 + c * p.pool_chunk_blocks;
+  it.b1 = min(min(it.b0 + p.pool_chunk_blocks, pb0 + pblocks), lblocks);
+  return it;
+}
+
+// The walker's partial result for ticket t -> scratch slot t (layout at
+// piece_floats).  A chunk without tokens stores max -inf, exp-sum 0, zero rows.
+template <class W_, int D>
+__device__ void store_chunk(const AttnParams& p, const W_& w, unsigned t, const WorkItem& it) {
+  const int lane = w.lane;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(reinterpret_cast<const char*>(p.scratch)), (short)0,
+      (int)((unsigned)p.pool_tickets * (unsigned)piece_floats(D) * 4u), kRsrcWord3);
+  const int slot = (int)t * piece_floats(D) * 4;
+  const bool empty = !(w.m_true > -INFINITY);
+  const float inv = (empty || w.bad) ? 0.0f : 1.0f / w.l_run;
+  w.write_piece(rs, slot, it.gc, inv);
+  if (lane < kMaxHeadsPerGroup) {
+    const float m = w.bad ? __builtin_nanf("") : w.m_true;
+    const float l = empty ? 0.0f : w.l_run * fast_exp2(w.m_run - w.m_true);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, m), rs, 4 * lane, slot, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, l), rs, 4 * (16 + lane), slot, 0);
+  }
+}
+
+template <class DT, int D, int GH, int NW, bool kSplit, int LAYOUT>
+__global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
+  using W_ = Walker<DT, D, GH, NW, LAYOUT>;
+  constexpr bool kMfmaPV = W_::kMfmaPV;
+  constexpr int kRowsHeld = W_::kRowsHeld;
+  constexpr int kPTile = W_::kPTile;
+  constexpr int kSlices = W_::kSlices;
+  constexpr int EPL = W_::EPL;
+  constexpr int LPR = W_::LPR;
+  constexpr int kTreeFloats = (NW / 2) * kRowsHeld * D;  // tree-merge buffer
   constexpr int kLdsFloats1 = (NW * kPTile > kTreeFloats) ? NW * kPTile : kTreeFloats;
   constexpr int kLdsFloats = kLdsFloats1 > 0 ? kLdsFloats1 : 1;
+  constexpr bool kPool = kSplit && NW == 1;
   static_assert((NW & (NW - 1)) == 0, "NW is a power of two");
 
   __shared__ float lds[kLdsFloats];  // rows layout: p tiles in the loop; then the tree-merge buffer
@@ -287,334 +701,144 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
   // wave index is uniform across the wave; say so, so that everything derived
   // from it (block ids, buffer resources) stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int part = blockIdx.x;
-  const int s = blockIdx.z;
-  const int g = blockIdx.y / p.head_chunks;
-  const int chunk = blockIdx.y - g * p.head_chunks;
-  const int h0 = g * p.group + chunk * kMaxHeadsPerGroup;
-  const int gc = min(kMaxHeadsPerGroup, p.group - chunk * kMaxHeadsPerGroup);
+  float* ptile = lds + wave * kPTile;
+  W_ w(lane);
+  const int rbase = w.rbase;
   const int H = p.num_heads;
-  const int L = p.seq_lens[s];
-  const bool len_ok = L >= 0 && L <= p.max_blocks * kBlockTokens;
 
-  int tok_begin = 0, tok_end = L;
+  // the workgroup's own item: its partition (split) or the whole context
+  WorkItem it = make_item(p, blockIdx.z, blockIdx.y, blockIdx.x);
+  bool live;
   if constexpr (kSplit) {
-    tok_begin = part * p.partition;
     // partitions past the sequence end write nothing; an invalid length is
     // reported by phase 2
-    if (!len_ok || tok_begin >= L) return;
-    tok_end = min(tok_begin + p.partition, L);
+    const int tok_begin = it.part * p.partition;
+    live = it.len_ok && tok_begin < it.L;
+    it.b0 = tok_begin / kBlockTokens;
+    it.b1 = live ? (min(tok_begin + p.partition, it.L) + kBlockTokens - 1) / kBlockTokens : it.b0;
   } else {
-    if (!len_ok || L == 0) {
-      const float fill = len_ok ? 0.0f : __builtin_nanf("");
-      for (int i = threadIdx.x; i < gc * D; i += NW * kWave) p.out[((size_t)s * H + h0 + i / D) * D + (i % D)] = fill;
+    if (!it.len_ok || it.L == 0) {
+      const float fill = it.len_ok ? 0.0f : __builtin_nanf("");
+      for (int i = threadIdx.x; i < it.gc * D; i += NW * kWave)
+        p.out[((size_t)it.s * H + it.h0 + i / D) * D + (i % D)] = fill;
       return;
     }
+    live = true;
+    it.b1 = (it.L + kBlockTokens - 1) / kBlockTokens;
   }
-  const int blk_begin = tok_begin / kBlockTokens;
-  const int blk_end = (tok_end + kBlockTokens - 1) / kBlockTokens;
+  bool pooled = false;  // the current item is a pool ticket
+  unsigned ticket = 0;
 
-  // Q^T operand: lane l supplies head column l%16 and the 16-byte run of dims
-  // that the same lane's K load holds.
-  u32x4_t qop[kSteps];
-  {
-    const int qh = lane & 15;
-    const char* qrow = p.query + ((size_t)s * H + h0 + qh) * G_::kRowBytes + 16 * (lane >> 4);
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st)
-      qop[st] = (qh < gc) ? *reinterpret_cast<const u32x4_t*>(qrow + 64 * st) : u32x4_t{0, 0, 0, 0};
-  }
-
-  // Online softmax with a lazy reference: p = exp2(x - m_run) where m_run is
-  // raised (and the accumulators rescaled) only when a block's max exceeds it
-  // by more than kLazyLog2, so p <= 2^kLazyLog2 and rescaling is rare.  The
-  // result does not depend on the reference; m_true keeps the exact max.
-  float m_run = -INFINITY;   // reference max (log2 units) of head column lane%16
-  float m_true = -INFINITY;  // running max of that head's logits (log2 units)
-  float l_run = 0.0f;        // this lane's share of that head's exp-sum, relative to m_run
-  // P.V accumulator.  rows: acc[h][e] = head h, dim EPL*(lane%LPR)+e, summed
-  // over this lane's tokens.  tiled: accm[j][i] = head 4*(lane/16)+i, dim
-  // 16 j + lane%16.
-  float acc[kMfmaPV ? 1 : GH][EPL];
-  f32x4_t accm[kMfmaPV ? kSlices : 1];
-#pragma unroll
-  for (int h = 0; h < (kMfmaPV ? 1 : GH); ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
-#pragma unroll
-  for (int j = 0; j < (kMfmaPV ? kSlices : 1); ++j) accm[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  bool bad = false;
-
-  float* ptile = lds + wave * kPTile;
-  const int32_t* table_row = p.block_tables + (size_t)s * p.max_blocks;
-  const size_t head_off = (size_t)g * G_::kTileBytes;
-  const size_t block_stride = (size_t)p.num_kv_heads * G_::kTileBytes;
-  const int koff = TM::k_off(lane);
-  const int voff = TM::v_off(lane);
-  const int rbase = 4 * (lane >> 4);  // first of the lane's 4 tokens in the logit tile
-
-  struct Stage {
-    u32x4_t k[kSteps];
-    VReg v[kVLoads];
-  };
-
-  for (int seg = blk_begin; seg < blk_end; seg += kWave * NW) {
-    const int seg_end = min(seg + kWave * NW, blk_end);
-    const int first = seg + wave;
-    const int n = first < seg_end ? (seg_end - first + NW - 1) / NW : 0;
-    const int my_id = lane < n ? table_row[first + NW * lane] : -1;
-
-    // Enqueue the loads of the wave's idx-th block (zero-length, no traffic,
-    // past the wave's last block).
-    auto issue = [&](Stage& st, int idx) {
-      const bool live = idx < n;
-      int phys = live ? __builtin_amdgcn_readlane(my_id, idx) : 0;
-      const int blk = first + NW * idx;
-      int rows = live ? min(kBlockTokens, L - blk * kBlockTokens) : 0;
-      const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
-      bad |= live && !ok;
-      if (!ok) {
-        phys = 0;
-        rows = 0;
-      }
-      const size_t base = (size_t)phys * block_stride + head_off;
-      // rows layout: the bound drops the tail rows; tiled layout interleaves
-      // tokens, so the whole tile is read and the tail is masked by select
-      const int bytes = __builtin_amdgcn_readfirstlane(
-          LAYOUT == kLayoutTiled ? (rows > 0 ? G_::kTileBytes : 0) : rows * G_::kRowBytes);
-      __amdgpu_buffer_rsrc_t rk =
-          __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.key_cache + base), (short)0, bytes, kRsrcWord3);
-      __amdgpu_buffer_rsrc_t rv =
-          __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.value_cache + base), (short)0, bytes, kRsrcWord3);
-#pragma unroll
-      for (int j = 0; j < kSteps; ++j)
-        st.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + TM::kKStepBytes * j, 0, PAD_KV_LOAD_POLICY);
-#pragma unroll
-      for (int j = 0; j < kVLoads; ++j)
-        st.v[j] = buffer_load<0>(rv, voff + TM::kVLoadStride * j, static_cast<VReg*>(nullptr));
-    };
-
-    auto compute = [&](const Stage& st, int blk) {
-      // logits: lane l holds tokens rbase+i of the block for head column l%16
-      f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int j = 0; j < kSteps; ++j) c = qk_step(DT{}, st.k[j], qop[j], c);
-      const int rows = min(kBlockTokens, L - blk * kBlockTokens);
-      float x[4];
-      float bm = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = (rbase + i < rows) ? c[i] * p.qscale : -INFINITY;
-        bm = fmaxf(bm, x[i]);
-      }
-      // lanes l, l^16, l^32, l^48 share a head column
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      m_true = fmaxf(m_true, bm);
-      if (__ballot(bm > m_run + kLazyLog2) != 0) {
-        // raise the reference of every head to its running max
-        const float m_new = fmaxf(m_run, bm);
-        const float alpha = fast_exp2(m_run - m_new);  // 0 on the first block
-        l_run *= alpha;
-        m_run = m_new;
-        if constexpr (kMfmaPV) {
-          // accumulator rows are heads rbase+i; their factors live in lanes rbase+i
-          float a[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) a[i] = __shfl(alpha, rbase + i);
-#pragma unroll
-          for (int j = 0; j < kSlices; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) accm[j][i] *= a[i];
-        } else {
-#pragma unroll
-          for (int h = 0; h < GH; ++h) {
-            const float a = readlane_f(alpha, h);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[h][e] *= a;
-          }
-        }
-      }
-      float pw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pw[i] = fast_exp2(x[i] - m_run);
-        l_run += pw[i];
-      }
-      if constexpr (kMfmaPV) {
-        s16x4_t p_hi = {0, 0, 0, 0}, p_lo = {0, 0, 0, 0};
-        if constexpr (DT::kBytes == 2) {
-          uint32_t hi[4], lo[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            hi[i] = bf16_rne(pw[i]);
-            lo[i] = bf16_rne(pw[i] - __builtin_bit_cast(float, hi[i] << 16));
-          }
-          p_hi = __builtin_bit_cast(s16x4_t, u32x2_t{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)});
-          p_lo = __builtin_bit_cast(s16x4_t, u32x2_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
-        }
-        // V of tail tokens (padding, possibly NaN) is zeroed: 0 * NaN would poison the sum
-#pragma unroll
-        for (int j = 0; j < kVLoads; ++j) accm[j] = pv_step(DT{}, p_hi, p_lo, pw, mask_tail(st.v[j], rbase, rows), accm[j]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ptile[(rbase + i) * kMaxHeadsPerGroup + (lane & 15)] = pw[i];
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int j = 0; j < kSteps; ++j) {
-          const int r = RPL * j + lane / LPR;
-          float pr[GH];
-#pragma unroll
-          for (int h = 0; h < GH; ++h) pr[h] = ptile[r * kMaxHeadsPerGroup + h];
-          float vf[EPL];
-          widen(DT{}, st.v[j], vf);
-#pragma unroll
-          for (int h = 0; h < GH; ++h)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
-    };
-
-    Stage ring[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) issue(ring[r], r);
-    for (int i = 0; i < n; i += R) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int idx = i + r;
-        if (idx < n) compute(ring[r], first + NW * idx);
-        issue(ring[r], idx + R);
-      }
+  for (;;) {
+    w.reset();
+    if constexpr (kPool) w.ticket_ctr = p.pool_tickets > 0 ? p.counters : nullptr;
+    if (it.b0 < it.b1) {
+      w.load_q(p, it.s, it.h0, it.gc);
+      w.walk(p, it.s, it.g, it.L, it.b0, it.b1, wave, ptile);
     }
-  }
+    w.fold();
 
-  // ---- wave totals: fold the token groups of acc (rows) and the 4 lanes of l ----
-  if constexpr (!kMfmaPV) {
-#pragma unroll
-    for (int off = LPR; off < kWave; off <<= 1)
-#pragma unroll
-      for (int h = 0; h < GH; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
-  }
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-
-  // (head, dim) -> accumulator element held by this lane, for the merge and
-  // the epilogue.  rows: lanes < LPR hold dims EPL*lane..+EPL-1 of heads 0..GH-1.
-  // tiled: every lane holds heads rbase..rbase+3 at dims 16 j + lane%16.
-  if constexpr (NW > 1) {
-    // common max per head, each wave rescales itself, then a fixed-order tree sum
-    bad = __syncthreads_or(bad);
-    if (lane < kMaxHeadsPerGroup) {
-      m_lds[wave][lane] = m_run;
-      t_lds[wave][lane] = m_true;
-    }
-    __syncthreads();
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      mx = fmaxf(mx, m_lds[w][lane & 15]);
-      m_true = fmaxf(m_true, t_lds[w][lane & 15]);
-    }
-    const float sc = fast_exp2(m_run - mx);
-    l_run *= sc;
-    if constexpr (kMfmaPV) {
-      float a[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = __shfl(sc, rbase + i);
-#pragma unroll
-      for (int j = 0; j < kSlices; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) accm[j][i] *= a[i];
+    if (kPool && pooled) {
+      store_chunk<W_, D>(p, w, ticket, it);
     } else {
-#pragma unroll
-      for (int h = 0; h < GH; ++h) {
-        const float a = readlane_f(sc, h);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] *= a;
-      }
-    }
-    m_run = mx;
-#pragma unroll
-    for (int half = NW / 2; half >= 1; half /= 2) {
-      __syncthreads();
-      if (wave >= half && wave < 2 * half) {
-        float* dst = lds + (wave - half) * kRowsHeld * D;
-        if constexpr (kMfmaPV) {
-#pragma unroll
-          for (int j = 0; j < kSlices; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(rbase + i) * D + 16 * j + (lane & 15)] = accm[j][i];
-        } else if (lane < LPR) {
-#pragma unroll
-          for (int h = 0; h < GH; ++h)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) dst[h * D + EPL * lane + e] = acc[h][e];
+      // (head, dim) -> accumulator element held by this lane, for the merge and
+      // the epilogue.  rows: lanes < LPR hold dims EPL*lane..+EPL-1 of heads 0..GH-1.
+      // tiled: every lane holds heads rbase..rbase+3 at dims 16 j + lane%16.
+      if constexpr (NW > 1) {
+        // common max per head, each wave rescales itself, then a fixed-order tree sum
+        w.bad = __syncthreads_or(w.bad);
+        if (lane < kMaxHeadsPerGroup) {
+          m_lds[wave][lane] = w.m_run;
+          t_lds[wave][lane] = w.m_true;
         }
-        if (lane < kMaxHeadsPerGroup) l_lds[wave - half][lane] = l_run;
-      }
-      __syncthreads();
-      if (wave < half) {
-        const float* src = lds + wave * kRowsHeld * D;
-        if constexpr (kMfmaPV) {
+        __syncthreads();
+        float mx = -INFINITY;
 #pragma unroll
-          for (int j = 0; j < kSlices; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) accm[j][i] += src[(rbase + i) * D + 16 * j + (lane & 15)];
-        } else if (lane < LPR) {
-#pragma unroll
-          for (int h = 0; h < GH; ++h)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[h][e] += src[h * D + EPL * lane + e];
+        for (int ww = 0; ww < NW; ++ww) {
+          mx = fmaxf(mx, m_lds[ww][lane & 15]);
+          w.m_true = fmaxf(w.m_true, t_lds[ww][lane & 15]);
         }
-        l_run += l_lds[wave][lane & 15];
+        const float sc = fast_exp2(w.m_run - mx);
+        w.l_run *= sc;
+        w.scale_heads(sc);
+        w.m_run = mx;
+#pragma unroll
+        for (int half = NW / 2; half >= 1; half /= 2) {
+          __syncthreads();
+          if (wave >= half && wave < 2 * half) {
+            float* dst = lds + (wave - half) * kRowsHeld * D;
+            if constexpr (kMfmaPV) {
+#pragma unroll
+              for (int j = 0; j < kSlices; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[(rbase + i) * D + 16 * j + (lane & 15)] = w.accm[j][i];
+            } else if (lane < LPR) {
+#pragma unroll
+              for (int h = 0; h < kRowsHeld; ++h)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) dst[h * D + EPL * lane + e] = w.acc[h][e];
+            }
+            if (lane < kMaxHeadsPerGroup) l_lds[wave - half][lane] = w.l_run;
+          }
+          __syncthreads();
+          if (wave < half) {
+            const float* src = lds + wave * kRowsHeld * D;
+            if constexpr (kMfmaPV) {
+#pragma unroll
+              for (int j = 0; j < kSlices; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w.accm[j][i] += src[(rbase + i) * D + 16 * j + (lane & 15)];
+            } else if (lane < LPR) {
+#pragma unroll
+              for (int h = 0; h < kRowsHeld; ++h)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) w.acc[h][e] += src[h * D + EPL * lane + e];
+            }
+            w.l_run += l_lds[wave][lane & 15];
+          }
+        }
+        if (wave != 0) return;
       }
-    }
-    if (wave != 0) return;
-  }
 
-  // ---- epilogue (wave 0) ----
-  const float nan = __builtin_nanf("");
-  if constexpr (kMfmaPV) {
-    // lane l: heads rbase+i, dims 16 j + lane%16
-    float inv[4];
+      // ---- epilogue (wave 0) ----
+      if (live) {
+        const float nan = __builtin_nanf("");
+        const float inv = w.bad ? nan : 1.0f / w.l_run;
+        const size_t hstride = kSplit ? (size_t)p.num_partitions * D : (size_t)D;
+        float* base = p.out + ((size_t)it.s * H + it.h0) * D;
+        if constexpr (kSplit) base = p.tmp_out + ((size_t)it.s * H + it.h0) * hstride + (size_t)it.part * D;
+        if constexpr (kMfmaPV) {
+          w.write_rows(it.gc, inv, [&](int h, int d, float v) { base[h * hstride + d] = v; });
+        } else {
+          // four consecutive dims per store
 #pragma unroll
-    for (int i = 0; i < 4; ++i) inv[i] = bad ? nan : 1.0f / __shfl(l_run, rbase + i);
+          for (int h = 0; h < kRowsHeld; ++h) {
+            if (h >= it.gc) continue;
+            const float ih = readlane_f(inv, h);
+            if (lane < LPR) {
+              float* dst = base + h * hstride + EPL * lane;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = rbase + i;
-      if (h < gc) {
-        float* dst = kSplit ? p.tmp_out + (((size_t)s * H + h0 + h) * p.num_partitions + part) * D
-                            : p.out + ((size_t)s * H + h0 + h) * D;
-#pragma unroll
-        for (int j = 0; j < kSlices; ++j) dst[16 * j + (lane & 15)] = accm[j][i] * inv[i];
+              for (int e = 0; e < EPL; e += 4)
+                *reinterpret_cast<f32x4_t*>(dst + e) =
+                    f32x4_t{w.acc[h][e] * ih, w.acc[h][e + 1] * ih, w.acc[h][e + 2] * ih, w.acc[h][e + 3] * ih};
+            }
+          }
+        }
+        if constexpr (kSplit) {
+          // lane h holds head h's max and exp-sum
+          if (lane < it.gc) {
+            const size_t row = ((size_t)it.s * H + it.h0 + lane) * p.num_partitions + it.part;
+            p.max_logits[row] = w.bad ? nan : w.m_true * kLn2;
+            p.exp_sums[row] = w.l_run * fast_exp2(w.m_run - w.m_true);
+          }
+        }
       }
     }
-  } else {
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      if (h >= gc) continue;
-      const float inv = bad ? nan : 1.0f / readlane_f(l_run, h);
-      if (lane < LPR) {
-        float* dst = kSplit ? p.tmp_out + (((size_t)s * H + h0 + h) * p.num_partitions + part) * D + EPL * lane
-                            : p.out + ((size_t)s * H + h0 + h) * D + EPL * lane;
-#pragma unroll
-        for (int e = 0; e < EPL; e += 4)
-          *reinterpret_cast<f32x4_t*>(dst + e) =
-              f32x4_t{acc[h][e] * inv, acc[h][e + 1] * inv, acc[h][e + 2] * inv, acc[h][e + 3] * inv};
-      }
-    }
-  }
-  if constexpr (kSplit) {
-    // lane h holds head h's max and exp-sum
-    if (lane < gc) {
-      const size_t row = ((size_t)s * H + h0 + lane) * p.num_partitions + part;
-      p.max_logits[row] = bad ? nan : m_true * kLn2;
-      p.exp_sums[row] = l_run * fast_exp2(m_run - m_true);
-    }
+
+    if constexpr (!kPool) break;
+    if (p.pool_tickets == 0 || !take_ticket(p, w, &ticket)) break;
+    it = ticket_item(p, ticket);
+    pooled = true;
   }
 }
 

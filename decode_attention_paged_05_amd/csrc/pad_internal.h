@@ -13,6 +13,22 @@ constexpr int kBlockTokens = 16;
 // Query heads one workgroup serves: the N width of the 16x16 matrix-core tile.
 constexpr int kMaxHeadsPerGroup = 16;
 
+// Phase-1 pool limits.  A launch of one-wave workgroups that fills the GPU
+// for one resident round, but not by a whole multiple of the compute units,
+// launches workgroups for the first partitions only and cuts the remaining
+// partitions into chunks that workgroups take when they finish their own
+// partition; phase 2 merges the chunk entries with the partition entries.
+// The workspace holds the ticket counter and one scratch slot per chunk.
+constexpr int kMaxPoolChunks = 32;   // chunks per pooled partition
+constexpr int kMaxPoolTickets = 512; // chunks per launch
+constexpr int kPoolCounters = 1;
+// One chunk entry in the scratch area (floats): per head h < 16 of the
+// group its max logit (log2 units; -inf when the chunk holds no token, NaN
+// after a block id outside the pool) at [h], its exp-sum relative to that max
+// at [16 + h], and its normalised partial output row at [kPieceStats + h * D].
+constexpr int kPieceStats = 64;
+__host__ __device__ constexpr int piece_floats(int d) { return kPieceStats + kMaxHeadsPerGroup * d; }
+
 // Everything the launchers need, validated and derived on the host.
 struct Plan {
   int dtype;          // PAD_DTYPE_*
@@ -33,6 +49,8 @@ struct Plan {
   float* max_logits;  // [S, H, NP]
   float* exp_sums;    // [S, H, NP]
   float* tmp_out;     // [S, H, NP, D]
+  unsigned* counters; // [kPoolCounters]: the pool's ticket counter, zero between calls
+  float* scratch;     // [kMaxPoolTickets][piece_floats(D)]: chunk entries
 };
 
 hipError_t launch_phase1(const Plan& plan, const void* query, const void* key_cache,
@@ -48,6 +66,7 @@ hipError_t launch_one_pass(const Plan& plan, float* out, const void* query,
                            hipStream_t stream);
 
 hipError_t launch_workspace_fill(float* max_logits, float* exp_sums, float* tmp_out,
-                                 size_t n_stats, size_t n_tmp, hipStream_t stream);
+                                 size_t n_stats, size_t n_tmp, unsigned* counters,
+                                 size_t n_counters, hipStream_t stream);
 
 }  // namespace pad

@@ -52,6 +52,15 @@ struct MergeParams {
   int max_tokens;  // W * block_size
   int partition;
   int num_partitions;
+  // phase-1 pool (pool_chunks == 0: none): partitions >= main_parts arrive as
+  // pool_chunks chunk entries each in `scratch`
+  const float* scratch;
+  int main_parts;
+  int pool_parts;
+  int pool_chunks;
+  int gy_count;
+  int head_chunks;
+  int group;
 };
 
 constexpr int kMergeThreads = 256;
@@ -93,46 +102,78 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
   const float* tmp = p.tmp_out + row0 * D + d0 + 4 * dl;
   float* orow = p.out + ((size_t)s * p.num_heads + h) * D + d0;
 
+  // Sources: partition entries [0, n_reg), then (with the pool) the chunk
+  // entries of pooled partition pp at n_reg + pp * C + c.
+  const bool pooled = p.pool_chunks > 0;
+  const int C = p.pool_chunks;
+  const int n_reg = pooled ? p.main_parts : NP;
+  const int n_src = pooled ? p.main_parts + p.pool_parts * C : NP;
+  // this head's place among the pooled items and inside a chunk entry
+  const int g = h / p.group;
+  const int within = h - g * p.group;
+  const int hc = within / kMaxHeadsPerGroup;
+  const int hh = within - hc * kMaxHeadsPerGroup;
+  const int item0 = (s * p.gy_count + g * p.head_chunks + hc) * p.pool_parts;
+  const int PF = piece_floats(D);
+  auto piece = [&](int i) { return p.scratch + (size_t)((item0 + (i - n_reg) / C) * C + (i - n_reg) % C) * PF; };
+  // max (log2 units) and exp-sum of source i
+  auto stats = [&](int i, float* m2, float* l) {
+    if (i < n_reg) {
+      *m2 = ml[i] * kLog2e;
+      *l = es[i];
+    } else {
+      const float* q = piece(i);
+      *m2 = q[hh];
+      *l = q[16 + hh];
+    }
+  };
+  auto row = [&](int i) -> const f32x4_t* {
+    if (i < n_reg) return reinterpret_cast<const f32x4_t*>(tmp + (size_t)i * D);
+    return reinterpret_cast<const f32x4_t*>(piece(i) + kPieceStats + hh * D + d0 + 4 * dl);
+  };
+
   f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
   float wsum = 0.0f;
   float mrun = -INFINITY;  // running max, log2 units
-  int np = -1;             // partitions of this sequence (known after the first round's loads)
-  for (int c0 = 0; c0 < NP; c0 += kMergeChunk) {
-    // one round of loads: slots that exist, whatever the sequence length
+  int nvalid = -1;         // sources of this sequence (known after the first round's loads)
+  for (int c0 = 0; c0 < n_src; c0 += kMergeChunk) {
+    // one round of loads: sources that exist, whatever the sequence length
     const int ti = c0 + tid;
-    const float my_ml = ti < NP ? ml[ti] : -INFINITY;
-    const float my_es = ti < NP ? es[ti] : 0.0f;
+    float my_m2 = -INFINITY, my_l = 0.0f;
+    if (ti < n_src) stats(ti, &my_m2, &my_l);
     f32x4_t t[kMergePerThread];
 #pragma unroll
     for (int k = 0; k < kMergePerThread; ++k) {
       const int i = c0 + pg + kMergeGroups * k;
-      t[k] = i < NP ? *reinterpret_cast<const f32x4_t*>(tmp + (size_t)i * D) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      t[k] = i < n_src ? *row(i) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    if (np < 0) {
+    if (nvalid < 0) {
       const int L = p.seq_lens[s];
       if (L <= 0 || L > p.max_tokens) {
         if (tid < 64) orow[tid] = (L == 0) ? 0.0f : __builtin_nanf("");
         return;
       }
-      np = (L + p.partition - 1) / p.partition;
+      const int np = (L + p.partition - 1) / p.partition;
+      nvalid = pooled ? (np <= n_reg ? np : n_reg + (np - n_reg) * C) : np;
     }
-    if (c0 >= np) break;
-    const bool valid = ti < np;
-    const float m2 = valid ? my_ml * kLog2e : -INFINITY;
+    if (c0 >= nvalid) break;
+    const bool valid = ti < nvalid;
+    const float m2 = valid ? my_m2 : -INFINITY;
     const float cmax = block_reduce_256(m2, true, scratch);
     const float mnew = fmaxf(mrun, cmax);
     const float resc = fast_exp2(mrun - mnew);  // 0 on the first chunk
     a *= resc;
     wsum *= resc;
     mrun = mnew;
-    const float w = valid ? my_es * fast_exp2(m2 - mnew) : 0.0f;
+    // a chunk without tokens (max -inf, exp-sum 0) weighs nothing
+    const float w = (valid && m2 > -INFINITY) ? my_l * fast_exp2(m2 - mnew) : (valid && m2 != m2 ? m2 : 0.0f);
     wsum += w;
     w_lds[tid] = w;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kMergePerThread; ++k) {
       const int i = c0 + pg + kMergeGroups * k;
-      if (i < np) a += w_lds[pg + kMergeGroups * k] * t[k];
+      if (i < nvalid) a += w_lds[pg + kMergeGroups * k] * t[k];
     }
     __syncthreads();  // w_lds is rewritten by the next chunk
   }
@@ -142,19 +183,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
   if (tid < 16) {
     f32x4_t r = part_acc[0][tid];
 #pragma unroll
-    for (int g = 1; g < kMergeGroups; ++g) r += part_acc[g][tid];
+    for (int g2 = 1; g2 < kMergeGroups; ++g2) r += part_acc[g2][tid];
     *reinterpret_cast<f32x4_t*>(orow + 4 * tid) = r * (1.0f / wsum);
   }
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(float* ml, float* es, float* tmp, size_t n_stats,
-                                                   size_t n_tmp) {
+                                                   size_t n_tmp, unsigned* counters, size_t n_counters) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_stats; i += stride) {
+  const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (size_t i = i0; i < n_stats; i += stride) {
     ml[i] = -INFINITY;
     es[i] = 0.0f;
   }
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_tmp; i += stride) tmp[i] = 0.0f;
+  for (size_t i = i0; i < n_tmp; i += stride) tmp[i] = 0.0f;
+  for (size_t i = i0; i < n_counters; i += stride) counters[i] = 0u;
 }
 
 // Smallest instantiated accumulator width that holds `heads` heads.
@@ -206,15 +249,66 @@ AttnParams make_params(const Plan& plan, const void* q, const void* k, const voi
   a.max_logits = plan.max_logits;
   a.exp_sums = plan.exp_sums;
   a.tmp_out = plan.tmp_out;
+  a.counters = plan.counters;
+  a.scratch = plan.scratch;
+  a.gy_count = plan.num_kv_heads * plan.head_chunks;
   return a;
+}
+
+#ifndef PAD_POOL_CHUNK_BLOCKS
+#define PAD_POOL_CHUNK_BLOCKS 4  // blocks per pooled chunk
+#endif
+
+// The pool rule.  With `items` one-wave partition workgroups, C compute units
+// and k = items / C whole workgroups per unit (1 <= k <= 4: one resident
+// round), the first k * C partition workgroups are launched as usual and the
+// remaining partitions of every (sequence, head group) are cut into chunks
+// for the pool.  Phase 1 and phase 2 derive the same plan from the same
+// sizes.
+struct PoolPlan {
+  int main_parts = 0;  // partitions per (sequence, head group) launched as workgroups
+  int pool_parts = 0;
+  int chunks = 0;      // per pooled partition; 0 = no pool
+  int chunk_blocks = 0;
+  int tickets = 0;
+};
+
+PoolPlan plan_pool(const Plan& plan) {
+  PoolPlan pp;
+  const int np = plan.num_partitions;
+  pp.main_parts = np;
+  if (PAD_SPLIT_WAVES != 1 || plan.counters == nullptr || plan.scratch == nullptr) return pp;
+  const int64_t per_col = (int64_t)plan.num_seqs * plan.num_kv_heads * plan.head_chunks;
+  const int64_t items = per_col * np;
+  const int64_t cus = device_cus();
+  if (items <= cus || items > 4 * cus || items % cus == 0) return pp;
+  const int64_t main_parts = (items / cus) * cus / per_col;
+  const int64_t pool_parts = np - main_parts;
+  const int pblocks = plan.partition / kBlockTokens;
+  const int cb = PAD_POOL_CHUNK_BLOCKS;
+  const int chunks = (pblocks + cb - 1) / cb;
+  const int64_t tickets = per_col * pool_parts * chunks;
+  if (main_parts < 1 || pool_parts < 1 || chunks > kMaxPoolChunks || tickets > kMaxPoolTickets) return pp;
+  pp.main_parts = (int)main_parts;
+  pp.pool_parts = (int)pool_parts;
+  pp.chunks = chunks;
+  pp.chunk_blocks = cb;
+  pp.tickets = (int)tickets;
+  return pp;
 }
 
 }  // namespace
 
 hipError_t launch_phase1(const Plan& plan, const void* query, const void* key_cache, const void* value_cache,
                          const int32_t* block_tables, const int32_t* seq_lens, hipStream_t stream) {
-  const AttnParams a = make_params(plan, query, key_cache, value_cache, block_tables, seq_lens);
-  const dim3 grid(plan.num_partitions, plan.num_kv_heads * plan.head_chunks, plan.num_seqs);
+  AttnParams a = make_params(plan, query, key_cache, value_cache, block_tables, seq_lens);
+  const PoolPlan pp = plan_pool(plan);
+  a.main_parts = pp.main_parts;
+  a.pool_parts = pp.pool_parts;
+  a.pool_chunks = pp.chunks;
+  a.pool_chunk_blocks = pp.chunk_blocks;
+  a.pool_tickets = pp.tickets;
+  const dim3 grid(pp.main_parts, plan.num_kv_heads * plan.head_chunks, plan.num_seqs);
   const int gh = heads_template(plan.heads_per_wg);
   if (plan.layout == kLayoutTiled)
     return plan.dtype == 0 ? launch_attn_f32_tiled_split(a, plan.head_size, gh, grid, stream)
@@ -253,18 +347,26 @@ hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens, 
   m.max_tokens = plan.max_blocks * kBlockTokens;
   m.partition = plan.partition;
   m.num_partitions = plan.num_partitions;
+  const PoolPlan pp = plan_pool(plan);
+  m.scratch = plan.scratch;
+  m.main_parts = pp.main_parts;
+  m.pool_parts = pp.pool_parts;
+  m.pool_chunks = pp.chunks;
+  m.gy_count = plan.num_kv_heads * plan.head_chunks;
+  m.head_chunks = plan.head_chunks;
+  m.group = plan.group;
   const dim3 grid(plan.head_size / 64, plan.num_heads, plan.num_seqs);
   void* args[] = {&m};
   return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel), grid, dim3(256), args, 0, stream);
 }
 
 hipError_t launch_workspace_fill(float* max_logits, float* exp_sums, float* tmp_out, size_t n_stats, size_t n_tmp,
-                                 hipStream_t stream) {
+                                 unsigned* counters, size_t n_counters, hipStream_t stream) {
   const size_t n = n_tmp > n_stats ? n_tmp : n_stats;
   size_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks == 0) blocks = 1;
-  void* args[] = {&max_logits, &exp_sums, &tmp_out, &n_stats, &n_tmp};
+  void* args[] = {&max_logits, &exp_sums, &tmp_out, &n_stats, &n_tmp, &counters, &n_counters};
   return hipLaunchKernel(reinterpret_cast<const void*>(&fill_kernel), dim3((unsigned)blocks), dim3(256), args, 0,
                          stream);
 }

@@ -44,7 +44,8 @@
  * directly, so P.V runs on the matrix cores as well as Q.K^T.
  *
  * Ownership: every buffer belongs to the caller.  The library allocates no
- * memory and keeps no per-call state; calls only enqueue kernels on `stream`
+ * memory and keeps no per-call state outside the workspace (it caches each
+ * device's compute-unit count); calls only enqueue kernels on `stream`
  * (a hipStream_t; NULL = the null stream) and return without synchronising.
  * Buffers must stay valid until that work completes.  One workspace must not
  * be used by two calls whose work may overlap.
@@ -116,9 +117,11 @@ typedef struct pad_dims {
  *   partition_size 0 = one-pass; else tokens per partition, a multiple of block_size
  *   workspace      device buffer of >= paged_attention_decode_workspace_size(...)
  *                  bytes, used only when partition_size > 0 (may be NULL otherwise).
- *                  It needs no initialisation: phase 1 writes every entry phase 2
- *                  reads.  paged_attention_decode_workspace_init gives it the
- *                  defined starting contents (-inf / 0 / 0) all the same.
+ *                  Initialise it once with paged_attention_decode_workspace_init
+ *                  after allocating it: the library keeps a counter there that must
+ *                  start at zero (every call leaves it at zero again).  The
+ *                  partition entries need no initialisation: phase 1 writes every
+ *                  entry phase 2 reads.
  * Sequences with seq_lens[s] == 0 get all-zero output rows.
  */
 int32_t paged_attention_decode(float* out, const void* query, const void* key_cache,
@@ -133,6 +136,17 @@ int32_t paged_attention_decode(float* out, const void* query, const void* key_ca
  * for each query head of the group, written into `workspace`.  Arguments as in
  * paged_attention_decode.  Partitions at or beyond ceil(seq_lens[s] /
  * partition_size) are left untouched.
+ *
+ * Load balance: when the launch's partition workgroups fill the GPU's compute
+ * units once to four times over but not by a whole multiple, workgroups are
+ * launched for the first k * num_cus partitions only; the remaining
+ * partitions of every (sequence, KV head) are cut into chunks of 64 tokens,
+ * which workgroups take from a counter in the workspace as they finish their
+ * own partition.  Such a pooled partition's result is then held as its chunks'
+ * entries (same three quantities, in the bookkeeping area), not in its
+ * max_logits / exp_sums / tmp_output slots; phase 2 merges chunk entries and
+ * partition entries alike.  Phase 2 must run on the same device, with the
+ * same sizes, to find them.
  */
 int32_t paged_attention_decode_phase1(const void* query, const void* key_cache,
                                       const void* value_cache, const int32_t* block_tables,
@@ -143,7 +157,8 @@ int32_t paged_attention_decode_phase1(const void* query, const void* key_cache,
 /*
  * Phase 2 alone: log-sum-exp merge of the first ceil(seq_lens[s] /
  * partition_size) partitions of each (sequence, head) in `workspace` into
- * `out`.  Reads only entries phase 1 wrote for the same seq_lens.
+ * `out` (pooled partitions through their chunk entries).  Reads only entries
+ * phase 1 wrote for the same seq_lens.
  */
 int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32_t block_size,
                                       int32_t partition_size, const void* workspace,
@@ -155,8 +170,10 @@ int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32
  *   max_logits [S, H, NP] | exp_sums [S, H, NP] | tmp_output [S, H, NP, D]
  * with NP = ceil(max_blocks_per_seq * block_size / partition_size), the most
  * partitions any sequence can have (the pages' tmp_output, exp_sums and
- * max_logits, second page, workspace-initialisation message).  Returns 0 when
- * partition_size == 0 and (size_t)-1 for invalid arguments.
+ * max_logits, second page, workspace-initialisation message), followed by the
+ * library's bookkeeping for phase 1's load balance: one uint32 counter (256
+ * bytes reserved) and 512 chunk entries of (64 + 16 * head_size) floats.
+ * Returns 0 when partition_size == 0 and (size_t)-1 for invalid arguments.
  */
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
                                              int32_t max_blocks_per_seq, int32_t block_size,
@@ -172,7 +189,8 @@ int32_t paged_attention_decode_workspace_layout(int32_t num_seqs, int32_t num_he
 /*
  * Enqueue the workspace's defined starting contents on `stream`: max_logits =
  * -inf, exp_sums = 0, tmp_output = 0 (second page, workspace-initialisation
- * message).  Done with a fill kernel, so the call may be captured in a HIP graph.
+ * message) and the bookkeeping counter = 0.  Done with a fill kernel, so the
+ * call may be captured in a HIP graph.
  */
 int32_t paged_attention_decode_workspace_init(void* workspace, size_t workspace_bytes,
                                               int32_t num_seqs, int32_t num_heads,

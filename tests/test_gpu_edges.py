@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import decode_attention_paged_05_amd as pad
+import oracle
 from decode_attention_paged_05_amd import inputs as gen
 from tests import gpu_util as gu
 
@@ -131,3 +132,88 @@ def test_out_of_contract_inputs_give_nan_rows(P, layout):
     assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all() and torch.isnan(o[3]).all()
     gu.assert_close(out[:1], ref[:1], "bf16", "untouched row")
     assert torch.equal(out[0], good[0])
+
+
+def long_like(L, W=6272, seed=31):
+    """1 sequence, 24 q / 4 KV heads, D 256, P 512 and a table 6272 blocks wide:
+    4 x 196 partition workgroups, as in the 100K-token workload.  On 256
+    compute units phase 1 launches partitions 0-191 and pools 192-195."""
+    spec = gen.ConfigSpec("long_like", num_seqs=1, num_heads=24, num_kv_heads=4, head_size=256, block_size=16,
+                          num_blocks=W + 5, max_blocks_per_seq=W, partition_size=512, dtype="bf16", seed=seed,
+                          seq_len=L)
+    return gen.make_problem(spec)
+
+
+def run_pooled(dp, P, what):
+    """Split run with the pool's scratch cleared first; checks against the
+    oracle, that the pool ran (scratch written) and left its counters at zero,
+    and that a second call is bitwise equal."""
+    ws = dp.workspace(P)
+    counters, scratch = gu.pool_views(ws, dp.p, P)
+    scratch.zero_()
+    out = dp.run(partition_size=P, workspace=ws)
+    torch.cuda.synchronize()
+    gu.assert_close(out, dp.oracle(), dp.p.dtype, what)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert torch.count_nonzero(scratch) > 0, f"{what}: the phase-1 pool did not run"
+    assert torch.count_nonzero(counters) == 0, f"{what}: pool counters not back at zero"
+    again = dp.run(partition_size=P, workspace=ws)
+    assert torch.equal(again, out), f"{what}: not repeatable"
+    return out
+
+
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+@pytest.mark.parametrize("L", [90000, 99000, 100352])
+def test_long_pool(L, layout):
+    # 90000: the pooled partitions are past the end; 99000: the context ends
+    # inside chunk 2 of pooled partition 193; 100352: every partition full
+    dp = gu.DeviceProblem(long_like(L)).use(layout)
+    log(f"[run] long-like L={L} {layout}")
+    run_pooled(dp, 512, f"long-like L={L} {layout}")
+
+
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_long_pool_phase1_entries(layout):
+    # partition and chunk entries equal the oracle's Phase 1 over their tokens
+    dp = gu.DeviceProblem(long_like(99000)).use(layout)
+    p = dp.p
+    ws = dp.workspace(512)
+    dp.run(workspace=ws)
+    torch.cuda.synchronize()
+    K = oracle.widen(oracle.gather_sequence(dp.kc_host, p.block_tables[0], 99000, 16), "bf16")
+    V = oracle.widen(oracle.gather_sequence(dp.vc_host, p.block_tables[0], 99000, 16), "bf16")
+    q = oracle.widen(p.query[0], "bf16")
+    for h in (0, 5, 11, 23):
+        entries = gu.phase1_entries(ws, p, 512, 0, h)
+        if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+            assert len(entries) == 192 + 2 * 8  # partitions 192 and 193 as 8 chunks each
+        gu.check_phase1_entries(entries, q[h], K[h // 6], V[h // 6], p.scale)
+
+
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_long_pool_bad_block_in_a_pooled_chunk(layout):
+    dp = gu.DeviceProblem(long_like(100352)).use(layout)
+    tables = dp.tables.clone()
+    tables[0, 6200] = dp.p.num_blocks + 11  # logical block 6200: pooled partition 193, chunk 6
+    out = dp.run(tables=tables)
+    assert torch.isnan(out).all()
+    good = dp.run()  # the counters are intact after the bad call
+    gu.assert_close(good, dp.oracle(), "bf16", "after the bad call")
+
+
+POOL_SHAPES = [
+    # (lens, H, Hkv, D, dtype, W, P): partition workgroups between 256 and 1024, not a multiple of 256
+    ([17900, 16500], 24, 4, 256, "bf16", 1120, 512),   # 2 seqs: pooled partitions 32-34
+    ([20380], 8, 8, 128, "bf16", 1280, 512),           # MHA: 64 pooled partitions, 512 chunks
+    ([76793], 8, 2, 64, "f32", 4800, 512),             # fp32: 44 pooled partitions
+    ([38397], 16, 2, 256, "bf16", 2400, 256),          # P 256: chunks of 4 blocks, 4 per partition
+]
+
+
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+@pytest.mark.parametrize("shape", POOL_SHAPES, ids=lambda s: f"S{len(s[0])}H{s[1]}kv{s[2]}D{s[3]}{s[4]}P{s[6]}")
+def test_pool_shapes(shape, layout):
+    lens, H, Hkv, D, dtype, W, P = shape
+    dp = gu.DeviceProblem(custom(lens, H=H, Hkv=Hkv, D=D, dtype=dtype, W=W, P=P)).use(layout)
+    log(f"[run] pool shape {shape} {layout}")
+    run_pooled(dp, P, f"pool {shape} {layout}")
