@@ -83,6 +83,11 @@ def main() -> int:
                     help="KV cache layout: tiled (K 16-byte chunks x tokens, V dims x tokens) or rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU work the oracle baseline repeats the step for (bounded sample)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the steps, one plain device copy of this many MiB (read + write), "
+                         "the reference kernel for calibrating HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -185,6 +190,17 @@ def main() -> int:
         if ev:
             ev[2].record()
 
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * 2**20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: {n} bytes read, {n} bytes written by one copy kernel", file=sys.stderr,
+              flush=True)
+        del src, dst
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -212,6 +228,8 @@ def main() -> int:
     ms_with_events = (time.perf_counter() - t_start) * 1e3 / K
     k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if n_ev == 3 else 0.0
+    step_us = np.array([e[0].elapsed_time(e[-1]) for e in evs]) * 1e3
+    pcts = [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)]
 
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     k1_gbs = kv_bytes / (k1_ms * 1e-3) / 1e9
@@ -228,16 +246,29 @@ def main() -> int:
             blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         except Exception:  # noqa: BLE001 - reporting only
             blas_threads = 1
+        def oracle_step():
+            return oracle.decode_attention(p.query, host_k, host_v, p.block_tables, p.seq_lens, p.scale,
+                                           p.num_kv_heads, p.block_size, p.dtype)
+
         t_or = time.perf_counter()
-        ref = oracle.decode_attention(p.query, host_k, host_v, p.block_tables, p.seq_lens, p.scale, p.num_kv_heads,
-                                      p.block_size, p.dtype)
+        ref = oracle_step()
         or_s = time.perf_counter() - t_or
         max_err = float(np.max(np.abs(result_gpu - ref)))
+        print(f"[bench] oracle {or_s:.2f}s per step, max |gpu - oracle| = {max_err:.3e}", file=sys.stderr,
+              flush=True)
         if not args.no_cpu_baseline:
-            cpu = {"value": round(kv_bytes / or_s / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
-                   "kind": "oracle", "sample": f"one full step of the same workload ({describe(p, args.layout)}), "
-                                               f"{or_s:.2f} s, fp64 NumPy"}
-        print(f"[bench] oracle {or_s:.1f}s, max |gpu - oracle| = {max_err:.3e}", file=sys.stderr, flush=True)
+            # a bounded sample: whole steps repeated until about --cpu-seconds of CPU work
+            reps, total = 1, or_s
+            while total < args.cpu_seconds and reps < 200:
+                t_or = time.perf_counter()
+                oracle_step()
+                total += time.perf_counter() - t_or
+                reps += 1
+            cpu = {"value": round(reps * kv_bytes / total / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+                   "kind": "oracle",
+                   "sample": f"{reps} full steps of the same workload ({describe(p, args.layout)}) in {total:.1f} s, "
+                             f"fp64 NumPy, {int(blas_threads)} BLAS threads; "
+                             f"{total / reps * 1e6:.0f} us per step"}
 
     line = {
         "metric": METRIC,
@@ -270,6 +301,7 @@ def main() -> int:
         },
         "kernels_ms": {"phase1" if P else "one_pass": round(k1_ms, 5), **({"phase2": round(k2_ms, 5)} if P else {})},
         "ms_per_step_with_kernel_events": round(ms_with_events, 5),
+        "event_step_us_p10_p50_p90": pcts,
         "roofline": {
             "bound": "hbm",
             "achieved": round(k1_gbs, 2),
