@@ -60,6 +60,57 @@ def load_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def record_traffic(workload: str, fetch_csv: str, write_csv: str, copy_mib: int) -> int:
+    """Write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs of this
+    script (FETCH_SIZE, then WRITE_SIZE, both with --copy-probe-mib): HBM bytes per
+    phase-1 launch, each counter scaled by what it reads for the copy probe, a
+    plain device copy of known size."""
+    import csv
+
+    def rows(path, counter):
+        with open(path) as f:
+            return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+
+    fetch, write = rows(fetch_csv, "FETCH_SIZE"), rows(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mib * 2**20
+    # the copy probe: the copy kernel whose WRITE_SIZE matches its size; the same dispatch in the fetch run
+    probe = min((r for r in write if "copy" in r["Kernel_Name"].lower()),
+                key=lambda r: abs(float(r["Counter_Value"]) * 1024 - copy_bytes))
+    probe_fetch = next(r for r in fetch if r["Dispatch_Id"] == probe["Dispatch_Id"])
+    assert probe_fetch["Kernel_Name"] == probe["Kernel_Name"], "the two runs dispatched different kernels"
+    read_scale = copy_bytes / (float(probe_fetch["Counter_Value"]) * 1024)
+    write_scale = copy_bytes / (float(probe["Counter_Value"]) * 1024)
+
+    def phase1(rs):
+        v = [float(r["Counter_Value"]) for r in rs if "attn_kernel" in r["Kernel_Name"]
+             and ", true," in r["Kernel_Name"]]
+        assert v, "no phase-1 dispatches in the counter file"
+        return sum(v) / len(v), len(v)
+
+    fk, nf = phase1(fetch)
+    wk, nw = phase1(write)
+    read_b, write_b = fk * 1024 * read_scale, wk * 1024 * write_scale
+    out = {
+        "workload": workload,
+        "kernel_source_hash": kernel_source_hash(),
+        "hbm_bytes_per_launch": round(read_b + write_b),
+        "read_bytes_per_launch": round(read_b),
+        "write_bytes_per_launch": round(write_b),
+        "fetch_size_kib_per_dispatch": fk,
+        "write_size_kib_per_dispatch": wk,
+        "dispatches": [nf, nw],
+        "calibration": {"copy_bytes": copy_bytes, "fetch_size_kib": float(probe_fetch["Counter_Value"]),
+                        "write_size_kib": float(probe["Counter_Value"]), "read_scale": read_scale,
+                        "write_scale": write_scale},
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+    return 0
+
+
 def describe(p, layout: str = "") -> str:
     lens = p.seq_lens
     L = f"{int(lens[0])} tokens" if (lens == lens[0]).all() else f"{int(lens.min())}-{int(lens.max())} tokens"
@@ -88,7 +139,12 @@ def main() -> int:
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, one plain device copy of this many MiB (read + write), "
                          "the reference kernel for calibrating HBM byte counters")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<config>.json from two rocprofv3 --pmc counter files of this "
+                         "script (FETCH_SIZE, WRITE_SIZE; both runs with --copy-probe-mib) and exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        return record_traffic(args.config, *args.record_traffic, args.copy_probe_mib or 1024)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -186,7 +242,7 @@ def main() -> int:
         pad.paged_attention_decode_phase1(q, k, v, tables, lens, p.scale, p.num_kv_heads, p.block_size, P, ws)
         if ev:
             ev[1].record()
-        pad.paged_attention_decode_phase2(out, lens, p.block_size, P, ws, dims)
+        pad.paged_attention_decode_phase2(out, lens, p.num_kv_heads, p.block_size, P, ws, dims)
         if ev:
             ev[2].record()
 

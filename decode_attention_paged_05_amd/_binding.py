@@ -76,7 +76,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode.restype = i32
     lib.paged_attention_decode_phase1.argtypes = [vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, sz, dims, vp]
     lib.paged_attention_decode_phase1.restype = i32
-    lib.paged_attention_decode_phase2.argtypes = [vp, vp, i32, i32, vp, sz, dims, vp]
+    lib.paged_attention_decode_phase2.argtypes = [vp, vp, i32, i32, i32, vp, sz, dims, vp]
     lib.paged_attention_decode_phase2.restype = i32
     lib.paged_attention_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.paged_attention_decode_workspace_size.restype = sz
@@ -214,9 +214,10 @@ def paged_attention_decode_phase1(query, key_cache, value_cache, block_tables, s
     _check(st, "paged_attention_decode_phase1")
 
 
-def paged_attention_decode_phase2(out, seq_lens, block_size: int, partition_size: int, workspace, dims: PadDims,
-                                  stream=None) -> None:
-    st = LIB.paged_attention_decode_phase2(_ptr(out), _ptr(seq_lens), int(block_size), int(partition_size),
+def paged_attention_decode_phase2(out, seq_lens, num_kv_heads: int, block_size: int, partition_size: int, workspace,
+                                  dims: PadDims, stream=None) -> None:
+    st = LIB.paged_attention_decode_phase2(_ptr(out), _ptr(seq_lens), int(num_kv_heads), int(block_size),
+                                           int(partition_size),
                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
                                            ctypes.byref(dims), _stream(stream))
     _check(st, "paged_attention_decode_phase2")

@@ -175,12 +175,14 @@ int32_t paged_attention_decode_phase1(const void* query, const void* key_cache, 
                                       static_cast<hipStream_t>(stream)));
 }
 
-int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32_t block_size,
-                                      int32_t partition_size, const void* workspace, size_t workspace_bytes,
-                                      const pad_dims_t* dims, void* stream) {
+int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32_t num_kv_heads,
+                                      int32_t block_size, int32_t partition_size, const void* workspace,
+                                      size_t workspace_bytes, const pad_dims_t* dims, void* stream) {
   if (!dims) return PAD_ERR_NULL;
   if (dims->dtype != PAD_DTYPE_F32 && dims->dtype != PAD_DTYPE_BF16) return PAD_ERR_DTYPE;
-  if (dims->num_seqs < 0 || dims->num_heads <= 0 || dims->max_blocks_per_seq <= 0) return PAD_ERR_SHAPE;
+  if (dims->num_seqs < 0 || dims->num_heads <= 0 || dims->max_blocks_per_seq <= 0 || num_kv_heads <= 0 ||
+      dims->num_heads % num_kv_heads != 0)
+    return PAD_ERR_SHAPE;
   if (dims->head_size != 64 && dims->head_size != 128 && dims->head_size != 256) return PAD_ERR_UNSUPPORTED;
   if (block_size != pad::kBlockTokens) return PAD_ERR_UNSUPPORTED;
   if (dims->num_seqs > 65535 || dims->num_heads > 65535) return PAD_ERR_UNSUPPORTED;
@@ -189,13 +191,8 @@ int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32
   if (dims->num_seqs == 0) return PAD_OK;
   if (!out || !seq_lens) return PAD_ERR_NULL;
   if (!aligned16(out) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u)) return PAD_ERR_ALIGN;
-  pad::Plan plan{};
-  plan.dtype = dims->dtype;
-  plan.num_seqs = dims->num_seqs;
-  plan.num_heads = dims->num_heads;
-  plan.head_size = dims->head_size;
-  plan.max_blocks = dims->max_blocks_per_seq;
-  plan.partition = partition_size;
+  // the same plan phase 1 made (it decides which partitions became chunk entries)
+  pad::Plan plan = make_plan(1.0f, num_kv_heads, partition_size, dims);
   if (!attach_workspace(&plan, const_cast<void*>(workspace), workspace_bytes)) return PAD_ERR_WORKSPACE;
   return status_of(pad::launch_phase2(plan, out, seq_lens, static_cast<hipStream_t>(stream)));
 }

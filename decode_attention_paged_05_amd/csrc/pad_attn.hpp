@@ -191,7 +191,7 @@ constexpr int kLayoutTiled = 1;
 #ifndef PAD_TICKET_LEAD
 // blocks before the end of a walk at which the next pool ticket is requested,
 // so that the request's round trip overlaps the last loads
-#define PAD_TICKET_LEAD 3
+#define PAD_TICKET_LEAD 8
 #endif
 // Atomics on the pool's ticket counter, performed at system scope: every
 // workgroup, on whichever XCD, sees one sequence of values.

@@ -158,11 +158,14 @@ int32_t paged_attention_decode_phase1(const void* query, const void* key_cache,
  * Phase 2 alone: log-sum-exp merge of the first ceil(seq_lens[s] /
  * partition_size) partitions of each (sequence, head) in `workspace` into
  * `out` (pooled partitions through their chunk entries).  Reads only entries
- * phase 1 wrote for the same seq_lens.
+ * phase 1 wrote for the same seq_lens.  num_kv_heads, block_size,
+ * partition_size and dims must be those of the phase-1 call: they determine
+ * where phase 1 put each partition's result.
  */
-int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32_t block_size,
-                                      int32_t partition_size, const void* workspace,
-                                      size_t workspace_bytes, const pad_dims_t* dims, void* stream);
+int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32_t num_kv_heads,
+                                      int32_t block_size, int32_t partition_size,
+                                      const void* workspace, size_t workspace_bytes,
+                                      const pad_dims_t* dims, void* stream);
 
 /*
  * Bytes of workspace a split call needs: three float32 arrays, each starting on

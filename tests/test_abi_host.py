@@ -82,9 +82,12 @@ def test_null_dims_and_phase_errors():
                                                ctypes.byref(d), None) == -5
     assert B.LIB.paged_attention_decode_phase1(FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 4, 16, 512, FAKE, 10,
                                                ctypes.byref(d), None) == -6
-    assert B.LIB.paged_attention_decode_phase2(FAKE, FAKE, 16, 0, FAKE, 1 << 30, ctypes.byref(d), None) == -5
-    assert B.LIB.paged_attention_decode_phase2(0, FAKE, 16, 512, FAKE, 1 << 30, ctypes.byref(d), None) == -1
-    assert B.LIB.paged_attention_decode_phase2(FAKE, FAKE, 16, 512, FAKE, 10, ctypes.byref(d), None) == -6
+    assert B.LIB.paged_attention_decode_phase2(FAKE, FAKE, 4, 16, 0, FAKE, 1 << 30, ctypes.byref(d), None) == -5
+    assert B.LIB.paged_attention_decode_phase2(0, FAKE, 4, 16, 512, FAKE, 1 << 30, ctypes.byref(d), None) == -1
+    assert B.LIB.paged_attention_decode_phase2(FAKE, FAKE, 4, 16, 512, FAKE, 10, ctypes.byref(d), None) == -6
+    # the KV-head count must be that of phase 1: positive and a divisor of num_heads
+    assert B.LIB.paged_attention_decode_phase2(FAKE, FAKE, 0, 16, 512, FAKE, 1 << 30, ctypes.byref(d), None) == -3
+    assert B.LIB.paged_attention_decode_phase2(FAKE, FAKE, 5, 16, 512, FAKE, 1 << 30, ctypes.byref(d), None) == -3
     assert B.LIB.paged_attention_decode_workspace_init(FAKE, 10, 1, 24, 256, 10, 16, 512, None) == -6
     assert B.LIB.paged_attention_decode_workspace_init(FAKE, 1 << 30, 1, 24, 256, 10, 16, 100, None) == -5
 

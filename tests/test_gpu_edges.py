@@ -95,7 +95,7 @@ def test_phase_entry_points_match_combined_call(layout):
     pad.paged_attention_decode_phase1(dp.query, dp.kc, dp.vc, dp.tables, dp.lens, p.scale, p.num_kv_heads, 16, 256,
                                       ws)
     dims = pad.make_dims(dp.query, dp.kc, dp.tables)
-    pad.paged_attention_decode_phase2(out, dp.lens, 16, 256, ws, dims)
+    pad.paged_attention_decode_phase2(out, dp.lens, p.num_kv_heads, 16, 256, ws, dims)
     assert torch.equal(out, combined)
 
 
@@ -188,6 +188,22 @@ def test_long_pool_phase1_entries(layout):
         if torch.cuda.get_device_properties(0).multi_processor_count == 256:
             assert len(entries) == 192 + 2 * 8  # partitions 192 and 193 as 8 chunks each
         gu.check_phase1_entries(entries, q[h], K[h // 6], V[h // 6], p.scale)
+
+
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_long_pool_phase_entry_points_match_combined_call(layout):
+    # phase 2 on its own must find the chunk entries phase 1 left for the pooled partitions
+    dp = gu.DeviceProblem(long_like(100000)).use(layout)
+    p = dp.p
+    combined = dp.run()
+    gu.assert_close(combined, dp.oracle(), "bf16", "long-like combined")
+    ws = dp.workspace(512)
+    out = torch.full_like(combined, float("nan"))
+    pad.paged_attention_decode_phase1(dp.query, dp.kc, dp.vc, dp.tables, dp.lens, p.scale, p.num_kv_heads, 16, 512,
+                                      ws)
+    dims = pad.make_dims(dp.query, dp.kc, dp.tables)
+    pad.paged_attention_decode_phase2(out, dp.lens, p.num_kv_heads, 16, 512, ws, dims)
+    assert torch.equal(out, combined)
 
 
 @pytest.mark.parametrize("layout", gu.LAYOUTS)
