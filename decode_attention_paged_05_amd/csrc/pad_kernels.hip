@@ -29,17 +29,16 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Phase 2: log-sum-exp merge.  Grid (D/64, H, S), 256 threads; the workgroup
-// owns 64 dims of one (sequence, head).  Its partitions are taken 256 at a
-// time; for each chunk every load is issued in one round before any
-// arithmetic (the merge is latency-bound, not bandwidth-bound):
-//   thread t     max_logits and exp_sums of partition t of the chunk;
-//   lanes        16 lanes x float4 cover the 64 dims, 16 lane groups take
-//                partitions g, g+16, ... of the chunk (16 float4 each).
-// Then: chunk max -> running max (earlier chunks rescaled), weights
-// w_p = exp_sum_p * exp(max_p - max) through LDS, weighted sums, and a final
-// LDS reduction over the 16 lane groups divided by the summed weights.
-// Slots past the sequence's partition count are read (they exist) but
-// discarded by select, so stale or NaN contents never enter the sums.
+// owns 64 dims of one (sequence, head).  Thread t = 16 g + l takes dims
+// 4 l .. 4 l + 3 of sources g, g + 16, g + 32, ... (a source is a partition
+// entry or, for pooled partitions, a chunk entry).  Sources are taken 256 at a
+// time and every load of a round -- each source's max and exp-sum and its four
+// dims -- is issued before any arithmetic (the merge is latency-bound, not
+// bandwidth-bound).  Each thread keeps a running max, exp-sum and weighted
+// row over its own sources; one barrier later, 16 threads combine the 16
+// source groups by the same log-sum-exp rule.  Slots past the sequence's
+// source count are read (they exist) but discarded by select, so stale or NaN
+// contents never enter the sums.
 // ---------------------------------------------------------------------------
 struct MergeParams {
   float* out;
@@ -64,30 +63,14 @@ struct MergeParams {
 };
 
 constexpr int kMergeThreads = 256;
-constexpr int kMergeChunk = 256;  // partitions per round
-constexpr int kMergeGroups = 16;  // lane groups striding over a chunk
+constexpr int kMergeChunk = 256;  // sources per round
+constexpr int kMergeGroups = 16;  // source groups (threads with the same dims)
 constexpr int kMergePerThread = kMergeChunk / kMergeGroups;
 
-__device__ inline float block_reduce_256(float v, bool is_max, float* scratch) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float o = __shfl_xor(v, off);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  const int wave = threadIdx.x / kWave;
-  __syncthreads();
-  if ((threadIdx.x & (kWave - 1)) == 0) scratch[wave] = v;
-  __syncthreads();
-  float r = scratch[0];
-#pragma unroll
-  for (int w = 1; w < kMergeThreads / kWave; ++w) r = is_max ? fmaxf(r, scratch[w]) : r + scratch[w];
-  return r;
-}
-
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
-  __shared__ float scratch[kMergeThreads / kWave];
-  __shared__ float w_lds[kMergeChunk];
-  __shared__ f32x4_t part_acc[kMergeGroups][16];
+  __shared__ float m_sh[kMergeGroups];
+  __shared__ float l_sh[kMergeGroups];
+  __shared__ f32x4_t a_sh[kMergeGroups][16];
   const int tid = threadIdx.x;
   const int s = blockIdx.z;
   const int h = blockIdx.y;
@@ -113,39 +96,32 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
   const int within = h - g * p.group;
   const int hc = within / kMaxHeadsPerGroup;
   const int hh = within - hc * kMaxHeadsPerGroup;
-  const int item0 = (s * p.gy_count + g * p.head_chunks + hc) * p.pool_parts;
+  // chunk entry of source i >= n_reg: slot (item0 + pp) * C + c = first_slot + (i - n_reg)
+  const int first_slot = (s * p.gy_count + g * p.head_chunks + hc) * p.pool_parts * C;
   const int PF = piece_floats(D);
-  auto piece = [&](int i) { return p.scratch + (size_t)((item0 + (i - n_reg) / C) * C + (i - n_reg) % C) * PF; };
-  // max (log2 units) and exp-sum of source i
-  auto stats = [&](int i, float* m2, float* l) {
-    if (i < n_reg) {
-      *m2 = ml[i] * kLog2e;
-      *l = es[i];
-    } else {
-      const float* q = piece(i);
-      *m2 = q[hh];
-      *l = q[16 + hh];
-    }
-  };
-  auto row = [&](int i) -> const f32x4_t* {
-    if (i < n_reg) return reinterpret_cast<const f32x4_t*>(tmp + (size_t)i * D);
-    return reinterpret_cast<const f32x4_t*>(piece(i) + kPieceStats + hh * D + d0 + 4 * dl);
-  };
 
   f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
-  float wsum = 0.0f;
-  float mrun = -INFINITY;  // running max, log2 units
+  float lrun = 0.0f;
+  float mrun = -INFINITY;  // running max of this thread's sources, log2 units
   int nvalid = -1;         // sources of this sequence (known after the first round's loads)
   for (int c0 = 0; c0 < n_src; c0 += kMergeChunk) {
     // one round of loads: sources that exist, whatever the sequence length
-    const int ti = c0 + tid;
-    float my_m2 = -INFINITY, my_l = 0.0f;
-    if (ti < n_src) stats(ti, &my_m2, &my_l);
+    float m2[kMergePerThread], l[kMergePerThread];
     f32x4_t t[kMergePerThread];
 #pragma unroll
     for (int k = 0; k < kMergePerThread; ++k) {
+      // branch-free: pick the three addresses, load unconditionally (a source
+      // past the list reads partition 0's entry, dropped below by select)
       const int i = c0 + pg + kMergeGroups * k;
-      t[k] = i < n_src ? *row(i) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      const bool reg = i < n_reg || i >= n_src;
+      const int ir = i < n_reg ? i : 0;
+      const float* q = p.scratch + (size_t)(reg ? 0 : first_slot + (i - n_reg)) * PF;
+      const float* pm = reg ? ml + ir : q + hh;
+      const float* pl = reg ? es + ir : q + 16 + hh;
+      const float* pr = reg ? tmp + (size_t)ir * D : q + kPieceStats + hh * D + d0 + 4 * dl;
+      m2[k] = *pm * (reg ? kLog2e : 1.0f);
+      l[k] = *pl;
+      t[k] = *reinterpret_cast<const f32x4_t*>(pr);
     }
     if (nvalid < 0) {
       const int L = p.seq_lens[s];
@@ -157,34 +133,46 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
       nvalid = pooled ? (np <= n_reg ? np : n_reg + (np - n_reg) * C) : np;
     }
     if (c0 >= nvalid) break;
-    const bool valid = ti < nvalid;
-    const float m2 = valid ? my_m2 : -INFINITY;
-    const float cmax = block_reduce_256(m2, true, scratch);
-    const float mnew = fmaxf(mrun, cmax);
-    const float resc = fast_exp2(mrun - mnew);  // 0 on the first chunk
-    a *= resc;
-    wsum *= resc;
-    mrun = mnew;
-    // a chunk without tokens (max -inf, exp-sum 0) weighs nothing
-    const float w = (valid && m2 > -INFINITY) ? my_l * fast_exp2(m2 - mnew) : (valid && m2 != m2 ? m2 : 0.0f);
-    wsum += w;
-    w_lds[tid] = w;
-    __syncthreads();
+    float cm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMergePerThread; ++k)
+      if (c0 + pg + kMergeGroups * k < nvalid) cm = fmaxf(cm, m2[k]);
+    if (cm > mrun) {
+      const float resc = fast_exp2(mrun - cm);  // 0 while nothing was summed
+      a *= resc;
+      lrun *= resc;
+      mrun = cm;
+    }
 #pragma unroll
     for (int k = 0; k < kMergePerThread; ++k) {
-      const int i = c0 + pg + kMergeGroups * k;
-      if (i < nvalid) a += w_lds[pg + kMergeGroups * k] * t[k];
+      if (c0 + pg + kMergeGroups * k >= nvalid) continue;
+      // a chunk without tokens (max -inf, exp-sum 0) weighs nothing; a NaN max
+      // (a bad block id in phase 1) poisons the row
+      const float w = m2[k] > -INFINITY ? l[k] * fast_exp2(m2[k] - mrun) : (m2[k] != m2[k] ? m2[k] : 0.0f);
+      lrun += w;
+      a += w * t[k];
     }
-    __syncthreads();  // w_lds is rewritten by the next chunk
   }
-  wsum = block_reduce_256(wsum, false, scratch);
-  part_acc[pg][dl] = a;
+  // combine the 16 source groups
+  if (dl == 0) {
+    m_sh[pg] = mrun;
+    l_sh[pg] = lrun;
+  }
+  a_sh[pg][dl] = a;
   __syncthreads();
   if (tid < 16) {
-    f32x4_t r = part_acc[0][tid];
+    float M = -INFINITY;
 #pragma unroll
-    for (int g2 = 1; g2 < kMergeGroups; ++g2) r += part_acc[g2][tid];
-    *reinterpret_cast<f32x4_t*>(orow + 4 * tid) = r * (1.0f / wsum);
+    for (int q = 0; q < kMergeGroups; ++q) M = fmaxf(M, m_sh[q]);
+    f32x4_t r = {0.0f, 0.0f, 0.0f, 0.0f};
+    float lsum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kMergeGroups; ++q) {
+      const float f = m_sh[q] > -INFINITY ? fast_exp2(m_sh[q] - M) : 0.0f;
+      lsum += f * l_sh[q];
+      r += f * a_sh[q][tid];
+    }
+    *reinterpret_cast<f32x4_t*>(orow + 4 * tid) = r * (1.0f / lsum);
   }
 }
 
