@@ -227,11 +227,14 @@ int32_t paged_attention_decode_choose_partition(int32_t num_seqs, int32_t num_he
   const int64_t group = num_heads / num_kv_heads;
   const int64_t chunks = (group + pad::kMaxHeadsPerGroup - 1) / pad::kMaxHeadsPerGroup;
   const int64_t wg_one_pass = (int64_t)num_seqs * num_kv_heads * chunks;
-  // Enough independent workgroups to keep every compute unit streaming: the
-  // one-pass form when the batch alone provides them or the context is too
-  // short to split; otherwise the largest partition that still provides them.
-  const int64_t target = 2 * (int64_t)num_cus;
-  if (wg_one_pass >= target || max_context_len <= 2 * 128) return 0;
+  // Fitted by a sweep on 256 compute units (24 q / 4 KV heads, head 256, bf16;
+  // batch 1-256, context 512-100K): the one-pass form wins once the batch
+  // alone gives every compute unit a workgroup (it also saves the workspace
+  // round trip), and for contexts of one partition or less; otherwise the
+  // largest partition that still yields about 1.5 workgroups per compute unit
+  // was the fastest or within a few percent of it.
+  if (wg_one_pass >= num_cus || max_context_len <= 512) return 0;
+  const int64_t target = 3 * (int64_t)num_cus / 2;
   static const int32_t kSizes[] = {2048, 1024, 512, 256, 128};
   for (int32_t p : kSizes) {
     if (p % block_size) continue;

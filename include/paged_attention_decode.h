@@ -204,11 +204,13 @@ int32_t paged_attention_decode_workspace_init(void* workspace, size_t workspace_
 /*
  * One-pass versus split choice for a batch, sized for a GPU with `num_cus`
  * compute units (256 on MI355X).  Returns 0 (one-pass) when the batch's
- * (sequence, KV head) workgroups already fill the GPU or the context is short,
- * otherwise the partition size (a multiple of block_size) that gives enough
- * workgroups.  The first page's two-pass message weighs partition count
- * against workgroups per compute unit for a 16-unit GPU; this rule redoes that
- * for num_cus units.  Negative status on invalid arguments.
+ * (sequence, KV head) workgroups already give every compute unit one, or the
+ * context is at most 512 tokens; otherwise the largest partition size in
+ * {2048, 1024, 512, 256, 128} whose partition workgroups number at least
+ * 1.5 x num_cus (else 128).  The first page's two-pass message weighs
+ * partition count against workgroups per compute unit for a 16-unit GPU;
+ * this rule redoes that for num_cus units, fitted by a timing sweep over batch
+ * 1-256 and context 512-100K.  Negative status on invalid arguments.
  */
 int32_t paged_attention_decode_choose_partition(int32_t num_seqs, int32_t num_heads,
                                                 int32_t num_kv_heads, int32_t max_context_len,

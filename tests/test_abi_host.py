@@ -140,12 +140,17 @@ def test_partition_counts_from_pages():
 
 
 @pytest.mark.parametrize("S,H,Hkv,ctx,expect", [
-    (1, 24, 4, 100000, 512),      # long context, one sequence: split into many partitions
-    (1, 24, 4, 8192, 128),        # 4 KV heads x 64 partitions of 128 still below 2 x 256 workgroups -> smallest
-    (256, 24, 4, 2048, 0),        # large batch: (seq, KV head) workgroups already fill 256 CUs
+    (1, 24, 4, 100000, 1024),     # one long sequence: 4 KV heads x 98 partitions >= 1.5 x 256 workgroups
+    (1, 24, 4, 32768, 256),       # 4 x 128 partitions
+    (1, 24, 4, 8192, 128),        # 4 x 64 partitions of 128 still below 384 workgroups -> smallest
+    (4, 24, 4, 100000, 2048),     # 16 x 49 partitions
+    (16, 24, 4, 2048, 256),       # 64 x 8 partitions
+    (64, 24, 4, 8192, 0),         # 256 (seq, KV head) workgroups: one per compute unit -> one-pass
+    (256, 24, 4, 2048, 0),        # large batch
     (8, 24, 24, 131072, 2048),    # MHA: 192 workgroups x 64 partitions
     (32, 24, 4, 32768, 2048),     # 128 workgroups x 16 partitions
-    (1, 24, 4, 200, 0),           # too short to split
+    (4, 24, 4, 512, 0),           # one partition's worth of context
+    (1, 24, 4, 200, 0),
     (0, 24, 4, 100, 0),
 ])
 def test_choose_partition(S, H, Hkv, ctx, expect):
