@@ -125,7 +125,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="long", help="tiny | short | long | mixed | stress")
+    ap.add_argument("--config", default="long", help="tiny | short | long | mixed | stress | batch256")
     ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
     ap.add_argument("--seq-len", type=int, default=None,
                     help="override every sequence's length (table width and pool follow)")

@@ -85,6 +85,12 @@ CONFIGS: Dict[str, ConfigSpec] = {
                          block_size=16, num_blocks=65536, max_blocks_per_seq=8192,
                          partition_size=1024, dtype="bf16", seed=5, seq_len=131072,
                          outlier_rate=0.01, outlier_scale=20.0),
+    # Large-batch, short-context serving decode: 256 concurrent sequences of 2048
+    # tokens (the serving configuration on the second page moves to 128-256
+    # concurrent sequences); one-pass, the form the dispatch rule picks here.
+    "batch256": ConfigSpec("batch256", num_seqs=256, num_heads=24, num_kv_heads=4, head_size=256,
+                           block_size=16, num_blocks=32768, max_blocks_per_seq=128,
+                           partition_size=0, dtype="bf16", seed=6, seq_len=2048),
 }
 
 

@@ -233,3 +233,37 @@ def test_pool_shapes(shape, layout):
     dp = gu.DeviceProblem(custom(lens, H=H, Hkv=Hkv, D=D, dtype=dtype, W=W, P=P)).use(layout)
     log(f"[run] pool shape {shape} {layout}")
     run_pooled(dp, P, f"pool {shape} {layout}")
+
+
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_graph_capture_replays(layout):
+    """The split call (with the phase-1 pool) and the one-pass call captured in
+    a HIP graph: every replay, with eager work and synchronisation in
+    between, equals the eager result bitwise (no memset nodes, no host state;
+    the pool's counter resets itself inside the launch)."""
+    dp = gu.DeviceProblem(long_like(100000)).use(layout)
+    p = dp.p
+    ws = dp.workspace(512)
+    out = torch.empty((1, 24, 256), dtype=torch.float32, device="cuda")
+    one = torch.empty_like(out)
+    eager = dp.run(workspace=ws)
+    eager_one = dp.run(partition_size=0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        dp.run(workspace=ws, out=out)  # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            dp.run(workspace=ws, out=out)
+            dp.run(partition_size=0, out=one)
+    for r in range(4):
+        out.fill_(float("nan"))
+        one.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r}: split result differs from eager"
+        assert torch.equal(one, eager_one), f"replay {r}: one-pass result differs from eager"
+        # eager work between replays, on the same workspace
+        assert torch.equal(dp.run(workspace=ws), eager)
+    gu.assert_close(out, dp.oracle(), "bf16", "graph replay vs oracle")

@@ -1,5 +1,6 @@
-"""GPU parity: the HIP library against the fp64 oracle on the five workloads,
-element by element (bf16 inputs: max abs error 2e-3; fp32 inputs: 1e-5).
+"""GPU parity: the HIP library against the fp64 oracle on the five workloads
+and the large-batch serving workload, element by element (bf16 inputs: max
+abs error 2e-3; fp32 inputs: 1e-5).
 
 Tiny, Short, Long and Mixed are compared in full; Stress (8 x 131072 tokens,
 MHA) on sampled (sequence, head) rows that the oracle computes one by one from
@@ -12,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import decode_attention_paged_05_amd as pad
 import oracle
 from decode_attention_paged_05_amd import inputs as gen
 from tests import gpu_util as gu
@@ -132,6 +134,20 @@ def test_stress_sampled(layout):
     assert worst <= 2e-3
     # each output row is a convex combination of V rows: |out| <= max |V| (< 6 for N(0,1) bf16 draws)
     assert np.abs(o).max() < 8.0
+
+
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_batch256_one_pass(layout):
+    # 256 sequences x 2048 tokens: 1024 one-wave workgroups, the dispatch rule's one-pass choice
+    dp = problem("batch256").use(layout)
+    p = dp.p
+    assert pad.paged_attention_decode_choose_partition(p.num_seqs, p.num_heads, p.num_kv_heads, 2048, 16, 256) == 0
+    log(f"[run] batch256 one-pass {layout}")
+    out = dp.run()
+    ref = dp.oracle()
+    err = gu.assert_close(out, ref, "bf16", "batch256 one-pass")
+    log(f"[batch256] max err {err:.2e}")
+    gu.assert_close(dp.run(partition_size=512), ref, "bf16", "batch256 split P=512")
 
 
 @pytest.mark.parametrize("layout", gu.LAYOUTS)
