@@ -62,6 +62,7 @@ namespace pad {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -105,6 +106,7 @@ struct AttnParams {
   float* exp_sums;
   float* tmp_out;
   int64_t num_blocks;
+  int num_seqs;
   int num_heads;
   int num_kv_heads;
   int group;
@@ -124,6 +126,11 @@ struct AttnParams {
   int pool_chunks;     // chunks per pooled partition
   int pool_chunk_blocks;
   int pool_tickets;    // S * gy_count * pool_parts * pool_chunks
+  // phase-1 queue (queue == 0: none): a resident 1-D grid takes the live
+  // items from counters[0]; up to queue_tail of the last are cut into
+  // pool_chunks chunks of pool_chunk_blocks blocks
+  int queue;
+  int queue_tail;
 };
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -543,6 +550,9 @@ struct Walker {
         }
       }
     } else {
+      // 8-byte stores: a buffer store of more than 8 bytes with a register
+      // scalar offset needs a wait state before its data registers are
+      // rewritten, which the compiler does not insert for that form
       const int voff = 4 * (kPieceStats + EPL * lane);
 #pragma unroll
       for (int h = 0; h < GH; ++h) {
@@ -550,11 +560,10 @@ struct Walker {
         const float ih = readlane_f(inv_of_lane, h);
         if (lane < LPR) {
 #pragma unroll
-          for (int e = 0; e < EPL; e += 4)
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(u32x4_t, f32x4_t{acc[h][e] * ih, acc[h][e + 1] * ih, acc[h][e + 2] * ih,
-                                                    acc[h][e + 3] * ih}),
-                rs, voff, slot + 4 * (h * D + e), 0);
+          for (int e = 0; e < EPL; e += 2)
+            __builtin_amdgcn_raw_buffer_store_b64(
+                __builtin_bit_cast(u32x2_t, f32x2_t{acc[h][e] * ih, acc[h][e + 1] * ih}), rs, voff,
+                slot + 4 * (h * D + e), 0);
         }
       }
     }
@@ -664,7 +673,7 @@ __device__ void store_chunk(const AttnParams& p, const W_& w, unsigned t, const 
   const int lane = w.lane;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       uniform_ptr(reinterpret_cast<const char*>(p.scratch)), (short)0,
-      (int)((unsigned)p.pool_tickets * (unsigned)piece_floats(D) * 4u), kRsrcWord3);
+      (int)((unsigned)kMaxPoolTickets * (unsigned)piece_floats(D) * 4u), kRsrcWord3);
   const int slot = (int)t * piece_floats(D) * 4;
   const bool empty = !(w.m_true > -INFINITY);
   const float inv = (empty || w.bad) ? 0.0f : 1.0f / w.l_run;
@@ -675,6 +684,145 @@ __device__ void store_chunk(const AttnParams& p, const W_& w, unsigned t, const 
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, m), rs, 4 * lane, slot, 0);
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, l), rs, 4 * (16 + lane), slot, 0);
   }
+}
+
+// ---- phase-1 queue ----
+// The live items of a launch: sequence s contributes n_s = ceil(L_s / P) x
+// (head groups) items (none for a length outside [1, W * 16]), enumerated
+// sequence by sequence, head group by head group, partition by partition.
+// pre[s] counts the items before sequence s; T = pre[S].  The last
+// K = min(T, queue_tail) items are cut into C chunks each, so a launch has
+// (T - K) + K * C tickets: ticket t < T - K is item t whole (its partition
+// entry), ticket T - K + j is chunk j % C of item T - K + j / C (scratch
+// slot j).  Workgroup w starts on ticket w; further tickets are
+// gridDim.x + the counter's value.
+struct QueueState {
+  unsigned* pre;  // LDS [S + 1]
+  int* len;       // LDS [S]
+  unsigned T, K, cut, total;
+};
+
+template <int kUnused = 0>
+__device__ inline QueueState queue_lds() {
+  __shared__ unsigned pre[kQueueMaxSeqs + 1];
+  __shared__ int len[kQueueMaxSeqs];
+  QueueState q;
+  q.pre = pre;
+  q.len = len;
+  q.T = q.K = q.cut = q.total = 0;
+  return q;
+}
+
+// The live-item prefix of the launch (one wave; every workgroup computes the
+// same).  Workgroup 0 also publishes T and pre[] for phase 2.
+__device__ inline void queue_prefix(const AttnParams& p, int lane, QueueState& q) {
+  constexpr int kRounds = kQueueMaxSeqs / kWave;
+  const int S = p.num_seqs;
+  const int maxtok = p.max_blocks * kBlockTokens;
+  int L[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int s = r * kWave + lane;
+    L[r] = s < S ? p.seq_lens[s] : 0;
+  }
+  unsigned run = 0;
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    if (r * kWave >= S) break;
+    const int s = r * kWave + lane;
+    const bool ok = s < S && L[r] > 0 && L[r] <= maxtok;
+    const unsigned n = ok ? (unsigned)((L[r] + p.partition - 1) / p.partition) * (unsigned)p.gy_count : 0u;
+    unsigned x = n;  // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const unsigned y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (s < S) {
+      q.pre[s] = run + x - n;
+      q.len[s] = L[r];
+    }
+    run += __shfl(x, kWave - 1);
+  }
+  if (lane == 0) q.pre[S] = run;
+  __builtin_amdgcn_wave_barrier();
+  q.T = __builtin_amdgcn_readfirstlane(run);
+  q.K = min(q.T, (unsigned)p.queue_tail);
+  q.cut = q.T - q.K;
+  q.total = q.cut + q.K * (unsigned)p.pool_chunks;
+  if (blockIdx.x == 0) {
+    unsigned* info = p.counters + kQueueInfoOffset;
+    if (lane == 0) info[0] = q.T;
+    for (int s = lane; s < S; s += kWave) info[1 + s] = q.pre[s];
+  }
+}
+
+// Ticket t -> its item; *chunk / *slot tell a chunk ticket from a whole one.
+__device__ inline WorkItem queue_item(const AttnParams& p, const QueueState& q, unsigned t, bool* chunk,
+                                      unsigned* slot) {
+  unsigned i;
+  int c = -1;
+  if (t < q.cut) {
+    i = t;
+  } else {
+    const unsigned j = t - q.cut;
+    i = q.cut + j / (unsigned)p.pool_chunks;
+    c = (int)(j % (unsigned)p.pool_chunks);
+    *slot = j;
+  }
+  *chunk = c >= 0;
+  // the sequence: the last s with pre[s] <= i (it has items, since pre[s + 1] > i)
+  int lo = 0, hi = p.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(q.pre[mid]) <= i) lo = mid;
+    else hi = mid - 1;
+  }
+  const int s = lo;
+  const unsigned pre_s = __builtin_amdgcn_readfirstlane(q.pre[s]);
+  const int L = __builtin_amdgcn_readfirstlane(q.len[s]);
+  const int np_s = (L + p.partition - 1) / p.partition;
+  const int within = (int)(i - pre_s);
+  const int gy = within / np_s;
+  const int part = within - gy * np_s;
+  WorkItem it;
+  it.s = s;
+  it.g = gy / p.head_chunks;
+  const int hc = gy - it.g * p.head_chunks;
+  it.h0 = it.g * p.group + hc * kMaxHeadsPerGroup;
+  it.gc = min(kMaxHeadsPerGroup, p.group - hc * kMaxHeadsPerGroup);
+  it.L = L;
+  it.len_ok = true;
+  it.part = part;
+  const int pblocks = p.partition / kBlockTokens;
+  const int lblocks = (L + kBlockTokens - 1) / kBlockTokens;
+  const int pb0 = part * pblocks;
+  if (c < 0) {
+    it.b0 = pb0;
+    it.b1 = min(pb0 + pblocks, lblocks);
+  } else {
+    it.b0 = pb0 + c * p.pool_chunk_blocks;
+    it.b1 = min(min(it.b0 + p.pool_chunk_blocks, pb0 + pblocks), lblocks);
+  }
+  return it;
+}
+
+// Resolve the next queue ticket (asked for during the walk, or now); false
+// when the queue is empty.  Every workgroup makes one failing request; the
+// counter's max(total, grid) - 1-th value resets it.
+template <class W_>
+__device__ inline bool take_queue_ticket(const AttnParams& p, W_& w, const QueueState& q, unsigned* ticket) {
+  if (!w.asked) w.ask_ticket();
+  const unsigned c = __builtin_amdgcn_readfirstlane(w.next_ticket);
+  const unsigned nwg = gridDim.x;
+  const unsigned t = nwg + c;
+  if (t < q.total) {
+    *ticket = t;
+    return true;
+  }
+  const unsigned requests = q.total > nwg ? q.total : nwg;
+  if (c == requests - 1 && w.lane == 0) atomic_store_system(p.counters, 0u);
+  return false;
 }
 
 template <class DT, int D, int GH, int NW, bool kSplit, int LAYOUT>
@@ -707,9 +855,26 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
   const int H = p.num_heads;
 
   // the workgroup's own item: its partition (split) or the whole context
-  WorkItem it = make_item(p, blockIdx.z, blockIdx.y, blockIdx.x);
+  WorkItem it = make_item(p, blockIdx.z, blockIdx.y, kSplit ? blockIdx.x : 0);
   bool live;
-  if constexpr (kSplit) {
+  bool pooled = false;  // the current item is a chunk (scratch slot `ticket`)
+  unsigned ticket = 0;
+  [[maybe_unused]] QueueState q{};
+  if constexpr (kPool) {
+    if (p.queue) {
+      q = queue_lds();
+      queue_prefix(p, lane, q);
+    }
+  }
+  if (kPool && p.queue) {
+    live = blockIdx.x < q.total;
+    if (live) {
+      it = queue_item(p, q, blockIdx.x, &pooled, &ticket);
+      live = !pooled;
+    } else {
+      it.b0 = it.b1 = 0;
+    }
+  } else if constexpr (kSplit) {
     // partitions past the sequence end write nothing; an invalid length is
     // reported by phase 2
     const int tok_begin = it.part * p.partition;
@@ -726,12 +891,10 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
     live = true;
     it.b1 = (it.L + kBlockTokens - 1) / kBlockTokens;
   }
-  bool pooled = false;  // the current item is a pool ticket
-  unsigned ticket = 0;
 
   for (;;) {
     w.reset();
-    if constexpr (kPool) w.ticket_ctr = p.pool_tickets > 0 ? p.counters : nullptr;
+    if constexpr (kPool) w.ticket_ctr = (p.pool_tickets > 0 || p.queue) ? p.counters : nullptr;
     if (it.b0 < it.b1) {
       w.load_q(p, it.s, it.h0, it.gc);
       w.walk(p, it.s, it.g, it.L, it.b0, it.b1, wave, ptile);
@@ -836,9 +999,16 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
     }
 
     if constexpr (!kPool) break;
-    if (p.pool_tickets == 0 || !take_ticket(p, w, &ticket)) break;
-    it = ticket_item(p, ticket);
-    pooled = true;
+    if (p.queue) {
+      unsigned t;
+      if (!take_queue_ticket(p, w, q, &t)) break;
+      it = queue_item(p, q, t, &pooled, &ticket);
+      live = !pooled;
+    } else {
+      if (p.pool_tickets == 0 || !take_ticket(p, w, &ticket)) break;
+      it = ticket_item(p, ticket);
+      pooled = true;
+    }
   }
 }
 

@@ -13,15 +13,25 @@ constexpr int kBlockTokens = 16;
 // Query heads one workgroup serves: the N width of the 16x16 matrix-core tile.
 constexpr int kMaxHeadsPerGroup = 16;
 
-// Phase-1 pool limits.  A launch of one-wave workgroups that fills the GPU
-// for one resident round, but not by a whole multiple of the compute units,
-// launches workgroups for the first partitions only and cuts the remaining
-// partitions into chunks that workgroups take when they finish their own
-// partition; phase 2 merges the chunk entries with the partition entries.
-// The workspace holds the ticket counter and one scratch slot per chunk.
-constexpr int kMaxPoolChunks = 32;   // chunks per pooled partition
-constexpr int kMaxPoolTickets = 512; // chunks per launch
-constexpr int kPoolCounters = 1;
+// Phase-1 load balance.  Two modes share the chunk machinery:
+//  * pool (a launch that fills the GPU once to four times over, but not by a
+//    whole multiple of the compute units): workgroups are launched for the
+//    first partitions only; the remaining partitions are cut into chunks that
+//    workgroups take when they finish their own partition;
+//  * queue (a launch of more than four workgroups per compute unit, at most
+//    kQueueMaxSeqs sequences): a resident grid of 4 workgroups per compute
+//    unit takes the live (sequence, head group, partition) items from a
+//    ticket counter, the last ones cut into chunks.
+// Phase 2 merges chunk entries with partition entries.  The workspace holds
+// the ticket counter, the queue's live-item prefix (for phase 2) and one
+// scratch slot per chunk.
+constexpr int kMaxPoolChunks = 32;    // chunks per pooled partition
+constexpr int kMaxPoolTickets = 512;  // chunks per launch
+constexpr int kQueueMaxSeqs = 1024;
+// counter area: the ticket counter alone in its first 256 bytes, then the
+// queue's live-item count T and the live items before each sequence
+constexpr int kQueueInfoOffset = 64;  // in uint32 (256 bytes)
+constexpr int kPoolCounters = kQueueInfoOffset + 1 + kQueueMaxSeqs;
 // One chunk entry in the scratch area (floats): per head h < 16 of the
 // group its max logit (log2 units; -inf when the chunk holds no token, NaN
 // after a block id outside the pool) at [h], its exp-sum relative to that max
@@ -49,7 +59,7 @@ struct Plan {
   float* max_logits;  // [S, H, NP]
   float* exp_sums;    // [S, H, NP]
   float* tmp_out;     // [S, H, NP, D]
-  unsigned* counters; // [kPoolCounters]: the pool's ticket counter, zero between calls
+  unsigned* counters; // [kPoolCounters]: [0] ticket counter (zero between calls); queue info
   float* scratch;     // [kMaxPoolTickets][piece_floats(D)]: chunk entries
 };
 

@@ -60,6 +60,12 @@ struct MergeParams {
   int gy_count;
   int head_chunks;
   int group;
+  // phase-1 queue (queue == 0: none): queue_info[0] = T live items,
+  // queue_info[1 + s] = items before sequence s; the last min(T, queue_tail)
+  // items arrive as pool_chunks chunk entries each
+  int queue;
+  int queue_tail;
+  const unsigned* queue_info;
 };
 
 constexpr int kMergeThreads = 256;
@@ -85,25 +91,52 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
   const float* tmp = p.tmp_out + row0 * D + d0 + 4 * dl;
   float* orow = p.out + ((size_t)s * p.num_heads + h) * D + d0;
 
-  // Sources: partition entries [0, n_reg), then (with the pool) the chunk
-  // entries of pooled partition pp at n_reg + pp * C + c.
-  const bool pooled = p.pool_chunks > 0;
+  // Sources: partition entries [0, n_reg), then the chunk entries of the
+  // partitions from n_reg on, C per partition, in scratch slots first_slot,
+  // first_slot + 1, ...
   const int C = p.pool_chunks;
-  const int n_reg = pooled ? p.main_parts : NP;
-  const int n_src = pooled ? p.main_parts + p.pool_parts * C : NP;
   // this head's place among the pooled items and inside a chunk entry
   const int g = h / p.group;
   const int within = h - g * p.group;
   const int hc = within / kMaxHeadsPerGroup;
   const int hh = within - hc * kMaxHeadsPerGroup;
-  // chunk entry of source i >= n_reg: slot (item0 + pp) * C + c = first_slot + (i - n_reg)
-  const int first_slot = (s * p.gy_count + g * p.head_chunks + hc) * p.pool_parts * C;
+  const int gy = g * p.head_chunks + hc;
+  int n_reg, n_src, first_slot;
+  int nvalid = -1;  // sources of this sequence (pool / plain: known after the first round's loads)
+  if (p.queue) {
+    // the sequence's live items are pre_s + gy * np + partition; items from
+    // cut = T - K on are chunked (slot = (item - cut) * C + chunk)
+    const int L = p.seq_lens[s];
+    if (L <= 0 || L > p.max_tokens) {
+      if (tid < 64) orow[tid] = (L == 0) ? 0.0f : __builtin_nanf("");
+      return;
+    }
+    const int np = (L + p.partition - 1) / p.partition;
+    const unsigned T = p.queue_info[0];
+    const unsigned K = T < (unsigned)p.queue_tail ? T : (unsigned)p.queue_tail;
+    const long long cut = (long long)(T - K);
+    const long long base = (long long)p.queue_info[1 + s] + (long long)gy * np;
+    const long long r = cut - base;
+    n_reg = r <= 0 ? 0 : (r >= np ? np : (int)r);
+    first_slot = (int)((base + n_reg - cut) * C);
+    n_src = n_reg + (np - n_reg) * C;
+    nvalid = n_src;
+  } else if (C > 0) {
+    // pool: partitions [main_parts, NP) of every (sequence, head group), item
+    // (s * gy_count + gy) * pool_parts + pp, slot item * C + chunk
+    n_reg = p.main_parts;
+    n_src = p.main_parts + p.pool_parts * C;
+    first_slot = (s * p.gy_count + gy) * p.pool_parts * C;
+  } else {
+    n_reg = NP;
+    n_src = NP;
+    first_slot = 0;
+  }
   const int PF = piece_floats(D);
 
   f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
   float lrun = 0.0f;
   float mrun = -INFINITY;  // running max of this thread's sources, log2 units
-  int nvalid = -1;         // sources of this sequence (known after the first round's loads)
   for (int c0 = 0; c0 < n_src; c0 += kMergeChunk) {
     // one round of loads: sources that exist, whatever the sequence length
     float m2[kMergePerThread], l[kMergePerThread];
@@ -130,7 +163,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
         return;
       }
       const int np = (L + p.partition - 1) / p.partition;
-      nvalid = pooled ? (np <= n_reg ? np : n_reg + (np - n_reg) * C) : np;
+      nvalid = C > 0 ? (np <= n_reg ? np : n_reg + (np - n_reg) * C) : np;
     }
     if (c0 >= nvalid) break;
     float cm = -INFINITY;
@@ -226,6 +259,7 @@ AttnParams make_params(const Plan& plan, const void* q, const void* k, const voi
   a.block_tables = tables;
   a.seq_lens = lens;
   a.num_blocks = plan.num_blocks;
+  a.num_seqs = plan.num_seqs;
   a.num_heads = plan.num_heads;
   a.num_kv_heads = plan.num_kv_heads;
   a.group = plan.group;
@@ -247,18 +281,23 @@ AttnParams make_params(const Plan& plan, const void* q, const void* k, const voi
 #define PAD_POOL_CHUNK_BLOCKS 4  // blocks per pooled chunk
 #endif
 
-// The pool rule.  With `items` one-wave partition workgroups, C compute units
-// and k = items / C whole workgroups per unit (1 <= k <= 4: one resident
-// round), the first k * C partition workgroups are launched as usual and the
-// remaining partitions of every (sequence, head group) are cut into chunks
-// for the pool.  Phase 1 and phase 2 derive the same plan from the same
-// sizes.
+// The load-balance rule (phase 1 and phase 2 derive the same plan from the
+// same sizes).  With `items` one-wave partition workgroups and C compute units:
+//  * C < items <= 4 C, not a multiple of C (one resident round): pool.  The
+//    first k * C partition workgroups (k = items / C) are launched; the other
+//    partitions of every (sequence, head group) are cut into chunks;
+//  * items > 4 C and at most kQueueMaxSeqs sequences: queue.  4 C resident
+//    workgroups take live items from the ticket counter; up to
+//    kMaxPoolTickets / chunks of the last live items are cut into chunks.
 struct PoolPlan {
-  int main_parts = 0;  // partitions per (sequence, head group) launched as workgroups
+  int main_parts = 0;  // pool: partitions per (sequence, head group) launched as workgroups
   int pool_parts = 0;
-  int chunks = 0;      // per pooled partition; 0 = no pool
+  int chunks = 0;      // chunks per pooled partition (or queue tail item); 0 = neither mode
   int chunk_blocks = 0;
-  int tickets = 0;
+  int tickets = 0;     // pool: chunk tickets
+  bool queue = false;
+  int queue_wgs = 0;   // queue: resident workgroups
+  int queue_tail = 0;  // queue: most tail items cut into chunks
 };
 
 PoolPlan plan_pool(const Plan& plan) {
@@ -269,14 +308,24 @@ PoolPlan plan_pool(const Plan& plan) {
   const int64_t per_col = (int64_t)plan.num_seqs * plan.num_kv_heads * plan.head_chunks;
   const int64_t items = per_col * np;
   const int64_t cus = device_cus();
-  if (items <= cus || items > 4 * cus || items % cus == 0) return pp;
-  const int64_t main_parts = (items / cus) * cus / per_col;
-  const int64_t pool_parts = np - main_parts;
   const int pblocks = plan.partition / kBlockTokens;
   const int cb = PAD_POOL_CHUNK_BLOCKS;
   const int chunks = (pblocks + cb - 1) / cb;
+  if (chunks > kMaxPoolChunks) return pp;
+  if (items > 4 * cus) {
+    if (plan.num_seqs > kQueueMaxSeqs) return pp;
+    pp.queue = true;
+    pp.queue_wgs = (int)(4 * cus);
+    pp.chunks = chunks;
+    pp.chunk_blocks = cb;
+    pp.queue_tail = kMaxPoolTickets / chunks;
+    return pp;
+  }
+  if (items <= cus || items % cus == 0) return pp;
+  const int64_t main_parts = (items / cus) * cus / per_col;
+  const int64_t pool_parts = np - main_parts;
   const int64_t tickets = per_col * pool_parts * chunks;
-  if (main_parts < 1 || pool_parts < 1 || chunks > kMaxPoolChunks || tickets > kMaxPoolTickets) return pp;
+  if (main_parts < 1 || pool_parts < 1 || tickets > kMaxPoolTickets) return pp;
   pp.main_parts = (int)main_parts;
   pp.pool_parts = (int)pool_parts;
   pp.chunks = chunks;
@@ -296,7 +345,10 @@ hipError_t launch_phase1(const Plan& plan, const void* query, const void* key_ca
   a.pool_chunks = pp.chunks;
   a.pool_chunk_blocks = pp.chunk_blocks;
   a.pool_tickets = pp.tickets;
-  const dim3 grid(pp.main_parts, plan.num_kv_heads * plan.head_chunks, plan.num_seqs);
+  a.queue = pp.queue ? 1 : 0;
+  a.queue_tail = pp.queue_tail;
+  const dim3 grid = pp.queue ? dim3((unsigned)pp.queue_wgs)
+                             : dim3(pp.main_parts, plan.num_kv_heads * plan.head_chunks, plan.num_seqs);
   const int gh = heads_template(plan.heads_per_wg);
   if (plan.layout == kLayoutTiled)
     return plan.dtype == 0 ? launch_attn_f32_tiled_split(a, plan.head_size, gh, grid, stream)
@@ -343,6 +395,9 @@ hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens, 
   m.gy_count = plan.num_kv_heads * plan.head_chunks;
   m.head_chunks = plan.head_chunks;
   m.group = plan.group;
+  m.queue = pp.queue ? 1 : 0;
+  m.queue_tail = pp.queue_tail;
+  m.queue_info = plan.counters + kQueueInfoOffset;
   const dim3 grid(plan.head_size / 64, plan.num_heads, plan.num_seqs);
   void* args[] = {&m};
   return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel), grid, dim3(256), args, 0, stream);

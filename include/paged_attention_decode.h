@@ -137,16 +137,23 @@ int32_t paged_attention_decode(float* out, const void* query, const void* key_ca
  * paged_attention_decode.  Partitions at or beyond ceil(seq_lens[s] /
  * partition_size) are left untouched.
  *
- * Load balance: when the launch's partition workgroups fill the GPU's compute
- * units once to four times over but not by a whole multiple, workgroups are
- * launched for the first k * num_cus partitions only; the remaining
- * partitions of every (sequence, KV head) are cut into chunks of 64 tokens,
- * which workgroups take from a counter in the workspace as they finish their
- * own partition.  Such a pooled partition's result is then held as its chunks'
- * entries (same three quantities, in the bookkeeping area), not in its
- * max_logits / exp_sums / tmp_output slots; phase 2 merges chunk entries and
- * partition entries alike.  Phase 2 must run on the same device, with the
- * same sizes, to find them.
+ * Load balance, two modes:
+ *  - pool: when the launch's partition workgroups fill the GPU's compute
+ *    units once to four times over but not by a whole multiple, workgroups
+ *    are launched for the first k * num_cus partitions only; the remaining
+ *    partitions of every (sequence, KV head) are cut into chunks of 64
+ *    tokens, which workgroups take from a counter in the workspace as they
+ *    finish their own partition;
+ *  - queue: when there are more than four partition workgroups per compute
+ *    unit and at most 1024 sequences, a resident grid of 4 workgroups per
+ *    compute unit takes the live (sequence, KV head, partition) items from
+ *    the counter -- partitions past a sequence's end are never visited --
+ *    and the last ones are cut into 64-token chunks.
+ * A chunked partition's result is held as its chunks' entries (same three
+ * quantities, in the bookkeeping area), not in its max_logits / exp_sums /
+ * tmp_output slots; phase 2 merges chunk entries and partition entries
+ * alike.  Phase 2 must run on the same device, with the same sizes, to find
+ * them.
  */
 int32_t paged_attention_decode_phase1(const void* query, const void* key_cache,
                                       const void* value_cache, const int32_t* block_tables,
@@ -174,8 +181,9 @@ int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32
  * with NP = ceil(max_blocks_per_seq * block_size / partition_size), the most
  * partitions any sequence can have (the pages' tmp_output, exp_sums and
  * max_logits, second page, workspace-initialisation message), followed by the
- * library's bookkeeping for phase 1's load balance: one uint32 counter (256
- * bytes reserved) and 512 chunk entries of (64 + 16 * head_size) floats.
+ * library's bookkeeping for phase 1's load balance: 4608 bytes of counters
+ * (a ticket counter and the live-item counts of the queue mode) and 512 chunk
+ * entries of (64 + 16 * head_size) floats.
  * Returns 0 when partition_size == 0 and (size_t)-1 for invalid arguments.
  */
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,

@@ -154,13 +154,13 @@ def workspace_views(ws: torch.Tensor, p: gen.Problem, partition_size: int):
     return (f(ml, n).view(S, H, NP), f(es, n).view(S, H, NP), f(tmp, n * D).view(S, H, NP, D))
 
 
-POOL_COUNTERS = 1       # phase-1 pool: the ticket counter
+COUNTER_BYTES = 4608    # bookkeeping counter area: ticket counter (256 B), then the queue's live-item prefix
 POOL_SLOTS = 512        # chunk entries in the scratch area
 POOL_CHUNK_BLOCKS = 4   # blocks per chunk
 
 
 def pool_views(ws: torch.Tensor, p: gen.Problem, partition_size: int):
-    """(counters int32 [1], scratch float32 [512, 64 + 16 D]) views of the
+    """(ticket counter int32 [1], scratch float32 [512, 64 + 16 D]) views of the
     workspace's bookkeeping area, which follows tmp_output (256-byte aligned)."""
     _, _, tmp = pad.paged_attention_decode_workspace_layout(p.num_seqs, p.num_heads, p.head_size,
                                                             p.max_blocks_per_seq, p.block_size, partition_size)
@@ -168,9 +168,9 @@ def pool_views(ws: torch.Tensor, p: gen.Problem, partition_size: int):
     n_tmp = p.num_seqs * p.num_heads * NP * p.head_size
     up = lambda x: -(-x // 256) * 256
     c_off = tmp + up(4 * n_tmp)
-    s_off = c_off + up(4 * POOL_COUNTERS)
+    s_off = c_off + COUNTER_BYTES
     piece = 64 + 16 * p.head_size
-    counters = ws[c_off: c_off + 4 * POOL_COUNTERS].view(torch.int32)
+    counters = ws[c_off: c_off + 4].view(torch.int32)
     scratch = ws[s_off: s_off + 4 * POOL_SLOTS * piece].view(torch.float32).view(POOL_SLOTS, piece)
     assert s_off + 4 * POOL_SLOTS * piece <= ws.numel()
     return counters, scratch
@@ -185,7 +185,7 @@ def pool_plan(p: gen.Problem, partition_size: int, cus: int):
     NP = -(-p.max_blocks_per_seq * p.block_size // partition_size)
     items = per_col * NP
     if items <= cus or items > 4 * cus or items % cus == 0:
-        return None
+        return None  # (a launch of more than 4 per unit uses the queue, not the pool)
     main = (items // cus) * cus // per_col
     pooled = NP - main
     chunks = -(-(partition_size // 16) // POOL_CHUNK_BLOCKS)

@@ -106,8 +106,8 @@ def test_workspace_size_and_layout():
     assert ml == 0 and es % 256 == 0 and tmp % 256 == 0
     assert es >= S * H * np_ * 4 and tmp - es >= S * H * np_ * 4
     size = pad.paged_attention_decode_workspace_size(S, H, D, W, bs, P)
-    # then the phase-1 pool's bookkeeping: its ticket counter and 512 chunk entries of 64 + 16 D floats
-    assert size >= tmp + S * H * np_ * D * 4 + 4 + 512 * (64 + 16 * D) * 4 and size % 256 == 0
+    # then phase 1's bookkeeping: 4608 bytes of counters and 512 chunk entries of 64 + 16 D floats
+    assert size >= tmp + S * H * np_ * D * 4 + 4608 + 512 * (64 + 16 * D) * 4 and size % 256 == 0
     assert pad.paged_attention_decode_workspace_size(S, H, D, W, bs, 0) == 0
     with pytest.raises(ValueError):
         pad.paged_attention_decode_workspace_size(S, H, D, W, bs, 100)
@@ -125,7 +125,7 @@ def test_workspace_matches_page_figures():
     f32 = 4
     assert es - ml == -(-g["max_logits"] * f32 // 256) * 256
     assert tmp - es == -(-g["exp_sums"] * f32 // 256) * 256
-    bookkeeping = 256 + 512 * (64 + 16 * g["head_size"]) * f32
+    bookkeeping = 4608 + 512 * (64 + 16 * g["head_size"]) * f32
     assert size - tmp == -(-g["tmp_output"] * f32 // 256) * 256 + bookkeeping
 
 

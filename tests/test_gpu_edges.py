@@ -267,3 +267,43 @@ def test_graph_capture_replays(layout):
         # eager work between replays, on the same workspace
         assert torch.equal(dp.run(workspace=ws), eager)
     gu.assert_close(out, dp.oracle(), "bf16", "graph replay vs oracle")
+
+
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_queue_mode_ragged_batch(layout):
+    """More than four partition workgroups per compute unit: phase 1 runs as a
+    resident queue over the live items only (its last items cut into chunks).
+    40 ragged sequences (some empty, one longer than its table), P 256."""
+    rng = np.random.default_rng(11)
+    lens = rng.integers(0, 5000, size=40)
+    lens[[3, 17]] = 0
+    lens[25] = 1
+    dp = gu.DeviceProblem(custom(lens.tolist(), H=24, Hkv=4, D=128, P=256, W=313)).use(layout)
+    p = dp.p
+    ref = dp.oracle()
+    ws = dp.workspace(256)
+    counters, scratch = gu.pool_views(ws, p, 256)
+    scratch.zero_()
+    log(f"[run] queue mode {layout}")
+    out = dp.run(workspace=ws)
+    torch.cuda.synchronize()
+    gu.assert_close(out, ref, "bf16", f"queue mode {layout}")
+    assert torch.all(out[3] == 0) and torch.all(out[17] == 0)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert torch.count_nonzero(scratch) > 0, "the queue's tail chunks were not used"
+    assert torch.count_nonzero(counters) == 0, "ticket counter not back at zero"
+    assert torch.equal(dp.run(workspace=ws), out), "not repeatable"
+    # the two phases called separately (phase 2 reads the live-item counts phase 1 left)
+    sep = torch.full_like(out, float("nan"))
+    pad.paged_attention_decode_phase1(dp.query, dp.kc, dp.vc, dp.tables, dp.lens, p.scale, p.num_kv_heads, 16, 256,
+                                      ws)
+    pad.paged_attention_decode_phase2(sep, dp.lens, p.num_kv_heads, 16, 256, ws, pad.make_dims(dp.query, dp.kc,
+                                                                                                dp.tables))
+    assert torch.equal(sep, out)
+    # a length past the table: that row NaN, the others unchanged
+    lens_bad = dp.lens.clone()
+    lens_bad[7] = 313 * 16 + 5
+    bad = dp.run(workspace=ws, lens=lens_bad)
+    assert torch.isnan(bad[7]).all()
+    keep = [i for i in range(40) if i != 7]
+    assert torch.equal(bad[keep], out[keep])
