@@ -307,3 +307,37 @@ def test_queue_mode_ragged_batch(layout):
     assert torch.isnan(bad[7]).all()
     keep = [i for i in range(40) if i != 7]
     assert torch.equal(bad[keep], out[keep])
+
+
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+@pytest.mark.parametrize("shape", [(16, 4, 64, "f32", 128), (8, 8, 256, "bf16", 512), (32, 2, 128, "f32", 64)],
+                         ids=lambda s: f"H{s[0]}kv{s[1]}D{s[2]}{s[3]}P{s[4]}")
+def test_queue_mode_shapes(shape, layout):
+    H, Hkv, D, dtype, P = shape
+    rng = np.random.default_rng(D + P)
+    lens = rng.integers(1, 3000, size=24).tolist()
+    W = -(-max(lens) // 16)
+    dp = gu.DeviceProblem(custom(lens, H=H, Hkv=Hkv, D=D, dtype=dtype, P=P, W=W)).use(layout)
+    log(f"[run] queue mode {shape} {layout}")
+    run_pooled(dp, P, f"queue {shape} {layout}")
+
+
+def test_two_streams_two_workspaces():
+    """Two split calls in flight at once on two streams, each with its own
+    workspace (the phase-1 ticket counter lives there): both exact."""
+    a = gu.DeviceProblem(long_like(100000)).use("tiled")
+    b = gu.DeviceProblem(custom(np.random.default_rng(3).integers(1, 6000, size=24).tolist(), P=512)).use("tiled")
+    ra, rb = a.oracle(), b.oracle()
+    wa, wb = a.workspace(512), b.workspace(512)
+    oa = torch.empty((1, 24, 256), dtype=torch.float32, device="cuda")
+    ob = torch.empty((24, 24, 256), dtype=torch.float32, device="cuda")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            a.run(workspace=wa, out=oa)
+        with torch.cuda.stream(sb):
+            b.run(workspace=wb, out=ob)
+    torch.cuda.synchronize()
+    gu.assert_close(oa, ra, "bf16", "stream a")
+    gu.assert_close(ob, rb, "bf16", "stream b")
