@@ -694,12 +694,14 @@ __device__ void store_chunk(const AttnParams& p, const W_& w, unsigned t, const 
 // K = min(T, queue_tail) items are cut into C chunks each, so a launch has
 // (T - K) + K * C tickets: ticket t < T - K is item t whole (its partition
 // entry), ticket T - K + j is chunk j % C of item T - K + j / C (scratch
-// slot j).  Workgroup w starts on ticket w; further tickets are
-// gridDim.x + the counter's value.
+// slot j).  Only the first G = ceil(T / rounds) workgroups take part
+// (rounds = ceil(T / gridDim.x)); workgroup w < G starts on ticket w,
+// further tickets are G + the counter's value.
 struct QueueState {
   unsigned* pre;  // LDS [S + 1]
   int* len;       // LDS [S]
   unsigned T, K, cut, total;
+  unsigned G;     // workgroups that take part: the fewest that still need no more rounds
 };
 
 template <int kUnused = 0>
@@ -709,7 +711,7 @@ __device__ inline QueueState queue_lds() {
   QueueState q;
   q.pre = pre;
   q.len = len;
-  q.T = q.K = q.cut = q.total = 0;
+  q.T = q.K = q.cut = q.total = q.G = 0;
   return q;
 }
 
@@ -750,6 +752,11 @@ __device__ inline void queue_prefix(const AttnParams& p, int lane, QueueState& q
   q.K = min(q.T, (unsigned)p.queue_tail);
   q.cut = q.T - q.K;
   q.total = q.cut + q.K * (unsigned)p.pool_chunks;
+  // T items over gridDim.x workgroups take ceil(T / gridDim.x) rounds; the
+  // fewest workgroups that need no more rounds share the items evenly, so
+  // no last round runs on a fraction of the workgroups
+  const unsigned rounds = (q.T + gridDim.x - 1) / gridDim.x;
+  q.G = rounds ? (q.T + rounds - 1) / rounds : 0u;
   if (blockIdx.x == 0) {
     unsigned* info = p.counters + kQueueInfoOffset;
     if (lane == 0) info[0] = q.T;
@@ -808,13 +815,13 @@ __device__ inline WorkItem queue_item(const AttnParams& p, const QueueState& q, 
 }
 
 // Resolve the next queue ticket (asked for during the walk, or now); false
-// when the queue is empty.  Every workgroup makes one failing request; the
-// counter's max(total, grid) - 1-th value resets it.
+// when the queue is empty.  Every taking-part workgroup makes one failing
+// request; the counter's max(total, G) - 1-th value resets it.
 template <class W_>
 __device__ inline bool take_queue_ticket(const AttnParams& p, W_& w, const QueueState& q, unsigned* ticket) {
   if (!w.asked) w.ask_ticket();
   const unsigned c = __builtin_amdgcn_readfirstlane(w.next_ticket);
-  const unsigned nwg = gridDim.x;
+  const unsigned nwg = q.G;  // the workgroups that take part
   const unsigned t = nwg + c;
   if (t < q.total) {
     *ticket = t;
@@ -867,6 +874,7 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
     }
   }
   if (kPool && p.queue) {
+    if (blockIdx.x >= q.G) return;  // not taking part (makes no ticket request)
     live = blockIdx.x < q.total;
     if (live) {
       it = queue_item(p, q, blockIdx.x, &pooled, &ticket);
