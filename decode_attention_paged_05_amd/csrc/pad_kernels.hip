@@ -28,15 +28,15 @@ hipError_t launch_attn_f32_tiled_one_pass(const AttnParams& a, int d, int gh, in
 namespace {
 
 // ---------------------------------------------------------------------------
-// Phase 2: log-sum-exp merge.  Grid (D/64, H, S), 256 threads; the workgroup
-// owns 64 dims of one (sequence, head).  Thread t = 16 g + l takes dims
-// 4 l .. 4 l + 3 of sources g, g + 16, g + 32, ... (a source is a partition
-// entry or, for pooled partitions, a chunk entry).  Sources are taken 256 at a
-// time and every load of a round -- each source's max and exp-sum and its four
-// dims -- is issued before any arithmetic (the merge is latency-bound, not
-// bandwidth-bound).  Each thread keeps a running max, exp-sum and weighted
-// row over its own sources; one barrier later, 16 threads combine the 16
-// source groups by the same log-sum-exp rule.  Slots past the sequence's
+// Phase 2: log-sum-exp merge.  Grid (D/64, H, S), 256 or 64 threads (G = 16
+// or 4 source groups); the workgroup owns 64 dims of one (sequence, head).
+// Thread t = 16 g + l takes dims 4 l .. 4 l + 3 of sources g, g + G,
+// g + 2 G, ... (a source is a partition entry or a chunk entry).  Sources are
+// taken 16 G at a time and every load of a round -- each source's max and
+// exp-sum and its four dims -- is issued before any arithmetic (the merge is
+// latency-bound, not bandwidth-bound).  Each thread keeps a running max,
+// exp-sum and weighted row over its own sources; one barrier later, 16
+// threads combine the G source groups by the same log-sum-exp rule.  Slots past the sequence's
 // source count are read (they exist) but discarded by select, so stale or NaN
 // contents never enter the sums.
 // ---------------------------------------------------------------------------
@@ -68,12 +68,15 @@ struct MergeParams {
   const unsigned* queue_info;
 };
 
-constexpr int kMergeThreads = 256;
-constexpr int kMergeChunk = 256;  // sources per round
-constexpr int kMergeGroups = 16;  // source groups (threads with the same dims)
-constexpr int kMergePerThread = kMergeChunk / kMergeGroups;
+constexpr int kMergePerThread = 16;  // sources a thread loads per round
 
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
+// kThreads = 256: 16 source groups, 256 sources per round (long contexts);
+// kThreads = 64: one wave, 4 source groups, 64 sources per round (batches of
+// shorter sequences: a quarter of the waves, all resident at once).
+template <int kThreads>
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
+  constexpr int kMergeGroups = kThreads / 16;  // source groups (threads with the same dims)
+  constexpr int kMergeChunk = kMergeGroups * kMergePerThread;  // sources per round
   __shared__ float m_sh[kMergeGroups];
   __shared__ float l_sh[kMergeGroups];
   __shared__ f32x4_t a_sh[kMergeGroups][16];
@@ -400,7 +403,9 @@ hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens, 
   m.queue_info = plan.counters + kQueueInfoOffset;
   const dim3 grid(plan.head_size / 64, plan.num_heads, plan.num_seqs);
   void* args[] = {&m};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel), grid, dim3(256), args, 0, stream);
+  if (plan.num_partitions <= 64)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<64>), grid, dim3(64), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<256>), grid, dim3(256), args, 0, stream);
 }
 
 hipError_t launch_workspace_fill(float* max_logits, float* exp_sums, float* tmp_out, size_t n_stats, size_t n_tmp,
