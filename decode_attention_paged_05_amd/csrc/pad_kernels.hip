@@ -68,32 +68,55 @@ struct MergeParams {
   const unsigned* queue_info;
 };
 
-constexpr int kMergePerThread = 16;  // sources a thread loads per round
+// Merge workgroup shapes: kThreads threads own kDims dims of one (sequence,
+// head); kDims / 4 "dim lanes" (4 dims each) x kThreads / (kDims / 4) source
+// groups.  Sources per round: 256 for 256 threads, 64 for one wave.
+template <int kThreads, int kDims>
+struct MergeShape {
+  static constexpr int kDL = kDims / 4;            // dim lanes
+  static constexpr int kG = kThreads / kDL;        // source groups
+  static constexpr int kPerThread = (kThreads == 64 ? 64 : 256) / kG;  // sources per thread per round
+  static constexpr int kChunk = kG * kPerThread;   // sources per round
+  static constexpr int kWaves = kThreads / kWave;
+  static_assert(kDL >= 1 && kDL <= 16 && (kWave % kDL) == 0, "dim lanes within a wave");
+};
 
-// kThreads = 256: 16 source groups, 256 sources per round (long contexts);
-// kThreads = 64: one wave, 4 source groups, 64 sources per round (batches of
-// shorter sequences: a quarter of the waves, all resident at once).
-template <int kThreads>
+// Log-sum-exp combine of (max m, exp-sum l, weighted row a) with another
+// partial; an empty partial has m = -inf, l = 0, a = 0; NaN propagates.
+__device__ inline void lse_combine(float& m, float& l, f32x4_t& a, float m2, float l2, f32x4_t a2) {
+  const float M = fmaxf(m, m2);
+  const float f1 = m > -INFINITY ? fast_exp2(m - M) : 0.0f;
+  const float f2 = m2 > -INFINITY ? fast_exp2(m2 - M) : 0.0f;
+  l = l * f1 + l2 * f2;
+  a = a * f1 + a2 * f2;
+  m = M;
+}
+
+template <int kThreads, int kDims>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
-  constexpr int kMergeGroups = kThreads / 16;  // source groups (threads with the same dims)
-  constexpr int kMergeChunk = kMergeGroups * kMergePerThread;  // sources per round
-  __shared__ float m_sh[kMergeGroups];
-  __shared__ float l_sh[kMergeGroups];
-  __shared__ f32x4_t a_sh[kMergeGroups][16];
+  using SH = MergeShape<kThreads, kDims>;
+  constexpr int kDL = SH::kDL;
+  constexpr int kMergeGroups = SH::kG;
+  constexpr int kMergePerThread = SH::kPerThread;
+  constexpr int kMergeChunk = SH::kChunk;
+  __shared__ float m_sh[SH::kWaves][kDL];
+  __shared__ float l_sh[SH::kWaves][kDL];
+  __shared__ f32x4_t a_sh[SH::kWaves][kDL];
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int s = blockIdx.z;
   const int h = blockIdx.y;
   const int D = p.head_size;
-  const int d0 = blockIdx.x * 64;
-  const int dl = tid & 15;
-  const int pg = tid >> 4;
+  const int d0 = blockIdx.x * kDims;
+  const int dl = tid % kDL;
+  const int pg = tid / kDL;
   const int NP = p.num_partitions;
   const size_t row0 = ((size_t)s * p.num_heads + h) * NP;
   const float* ml = p.max_logits + row0;
   const float* es = p.exp_sums + row0;
   const float* tmp = p.tmp_out + row0 * D + d0 + 4 * dl;
   float* orow = p.out + ((size_t)s * p.num_heads + h) * D + d0;
-
   // Sources: partition entries [0, n_reg), then the chunk entries of the
   // partitions from n_reg on, C per partition, in scratch slots first_slot,
   // first_slot + 1, ...
@@ -111,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
     // cut = T - K on are chunked (slot = (item - cut) * C + chunk)
     const int L = p.seq_lens[s];
     if (L <= 0 || L > p.max_tokens) {
-      if (tid < 64) orow[tid] = (L == 0) ? 0.0f : __builtin_nanf("");
+      if (tid < kDims) orow[tid] = (L == 0) ? 0.0f : __builtin_nanf("");
       return;
     }
     const int np = (L + p.partition - 1) / p.partition;
@@ -162,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
     if (nvalid < 0) {
       const int L = p.seq_lens[s];
       if (L <= 0 || L > p.max_tokens) {
-        if (tid < 64) orow[tid] = (L == 0) ? 0.0f : __builtin_nanf("");
+        if (tid < kDims) orow[tid] = (L == 0) ? 0.0f : __builtin_nanf("");
         return;
       }
       const int np = (L + p.partition - 1) / p.partition;
@@ -189,27 +212,30 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
       a += w * t[k];
     }
   }
-  // combine the 16 source groups
-  if (dl == 0) {
-    m_sh[pg] = mrun;
-    l_sh[pg] = lrun;
+  // combine the source groups: within each wave by shuffles over the lanes
+  // that hold the same dims, then across the waves through LDS
+#pragma unroll
+  for (int off = kDL; off < kWave; off <<= 1) {
+    const float m2 = __shfl_xor(mrun, off);
+    const float l2 = __shfl_xor(lrun, off);
+    f32x4_t a2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a2[e] = __shfl_xor(a[e], off);
+    lse_combine(mrun, lrun, a, m2, l2, a2);
   }
-  a_sh[pg][dl] = a;
-  __syncthreads();
-  if (tid < 16) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < kMergeGroups; ++q) M = fmaxf(M, m_sh[q]);
-    f32x4_t r = {0.0f, 0.0f, 0.0f, 0.0f};
-    float lsum = 0.0f;
-#pragma unroll
-    for (int q = 0; q < kMergeGroups; ++q) {
-      const float f = m_sh[q] > -INFINITY ? fast_exp2(m_sh[q] - M) : 0.0f;
-      lsum += f * l_sh[q];
-      r += f * a_sh[q][tid];
+  if constexpr (SH::kWaves > 1) {
+    if (lane < kDL) {
+      m_sh[wave][lane] = mrun;
+      l_sh[wave][lane] = lrun;
+      a_sh[wave][lane] = a;
     }
-    *reinterpret_cast<f32x4_t*>(orow + 4 * tid) = r * (1.0f / lsum);
+    __syncthreads();
+    if (tid < kDL) {
+#pragma unroll
+      for (int w = 1; w < SH::kWaves; ++w) lse_combine(mrun, lrun, a, m_sh[w][tid], l_sh[w][tid], a_sh[w][tid]);
+    }
   }
+  if (tid < kDL) *reinterpret_cast<f32x4_t*>(orow + 4 * tid) = a * (1.0f / lrun);
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(float* ml, float* es, float* tmp, size_t n_stats,
@@ -403,9 +429,20 @@ hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens, 
   m.queue_info = plan.counters + kQueueInfoOffset;
   const dim3 grid(plan.head_size / 64, plan.num_heads, plan.num_seqs);
   void* args[] = {&m};
+  // one wave of 64 dims for tables of at most 64 partitions; otherwise 256
+  // threads on the narrowest dim slice that keeps the grid to about three
+  // workgroups per compute unit (more, smaller workgroups share the latency)
   if (plan.num_partitions <= 64)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<64>), grid, dim3(64), args, 0, stream);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<256>), grid, dim3(256), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<64, 64>), grid, dim3(64), args, 0, stream);
+  const int64_t rows = (int64_t)plan.num_heads * plan.num_seqs;
+  const int64_t budget = 3 * (int64_t)device_cus();
+  if (rows * (plan.head_size / 16) <= budget)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<256, 16>),
+                           dim3(plan.head_size / 16, plan.num_heads, plan.num_seqs), dim3(256), args, 0, stream);
+  if (rows * (plan.head_size / 32) <= budget)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<256, 32>),
+                           dim3(plan.head_size / 32, plan.num_heads, plan.num_seqs), dim3(256), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<256, 64>), grid, dim3(256), args, 0, stream);
 }
 
 hipError_t launch_workspace_fill(float* max_logits, float* exp_sums, float* tmp_out, size_t n_stats, size_t n_tmp,
