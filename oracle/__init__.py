@@ -1,12 +1,13 @@
-"""CPU oracle for paged single-token decode attention (fp64, NumPy).
+"""CPU oracles for paged decode attention and paged prefix (prefill) attention (fp64, NumPy).
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
 and by the ``cpu_baseline`` leg of ``bench.py``, and by nothing else.  The GPU
 library never imports, links or calls it, and it imports nothing from the GPU
 library.  Every function is pinned by the ``-m "not gpu"`` tests in
-``tests/test_oracle.py`` (brute force, closed forms, invariants, the
-log-sum-exp merge identity, a float64 library special case and hand-worked
-fixtures); there is no "parity unpinned" function.
+``tests/test_oracle.py`` and ``tests/test_oracle_prefill.py`` (brute force,
+closed forms, invariants, the log-sum-exp merge identity, the pages' two-phase
+prefill form, float64 library special cases and hand-worked fixtures); there
+is no "parity unpinned" function.
 """
 
 from .attention import (  # noqa: F401
@@ -19,4 +20,11 @@ from .attention import (  # noqa: F401
     merge_partitions,
     partition_stats,
     widen,
+)
+from .prefill import (  # noqa: F401
+    chunk_bounds,
+    prefill_attention,
+    prefill_rows,
+    prefix_attention_two_phase,
+    write_chunk,
 )
