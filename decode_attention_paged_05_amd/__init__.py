@@ -1,7 +1,8 @@
-"""MI355X (gfx950) paged single-token decode attention.
+"""MI355X (gfx950) paged single-token decode attention, and paged prefix (chunked
+prefill) attention.
 
 The compute lives in ``libpad.so`` (hand-written HIP kernels behind a C ABI,
-``include/paged_attention_decode.h``).  This package exposes the same entry
+``include/paged_attention_decode.h`` and ``include/paged_attention_prefill.h``).  This package exposes the same entry
 points for torch tensors (:mod:`._binding`) and the seeded synthetic input
 generator (:mod:`.inputs`).  Importing the binding raises if the library has
 not been built: there is no fallback path.
@@ -14,8 +15,10 @@ from ._binding import (  # noqa: F401
     PAD_DTYPE_F32,
     PadDims,
     PadError,
+    PadPrefillDims,
     alloc_workspace,
     make_dims,
+    make_prefill_dims,
     paged_attention_decode,
     paged_attention_decode_choose_partition,
     paged_attention_decode_phase1,
@@ -24,4 +27,6 @@ from ._binding import (  # noqa: F401
     paged_attention_decode_workspace_init,
     paged_attention_decode_workspace_layout,
     paged_attention_decode_workspace_size,
+    paged_attention_prefill,
+    paged_attention_prefill_write_kv,
 )

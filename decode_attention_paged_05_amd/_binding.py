@@ -1,7 +1,7 @@
 """ctypes binding of ``libpad.so``: argument marshalling only.
 
-Every entry point of ``include/paged_attention_decode.h`` has a Python function
-of the same name.  Tensors are torch tensors on the current CUDA (HIP) device;
+Every entry point of ``include/paged_attention_decode.h`` and
+``include/paged_attention_prefill.h`` has a Python function of the same name.  Tensors are torch tensors on the current CUDA (HIP) device;
 torch supplies device memory and the stream, all arithmetic runs in the
 library's HIP kernels.  A missing library raises at import of this module, and
 a non-zero status raises ``RuntimeError`` with the library's message.
@@ -35,6 +35,8 @@ EXPORTED = [
     "paged_attention_decode_workspace_init",
     "paged_attention_decode_choose_partition",
     "paged_attention_decode_strerror",
+    "paged_attention_prefill",
+    "paged_attention_prefill_write_kv",
 ]
 
 
@@ -44,6 +46,20 @@ class PadDims(ctypes.Structure):
         ("num_seqs", ctypes.c_int32),
         ("num_heads", ctypes.c_int32),
         ("head_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("kv_layout", ctypes.c_int32),
+    ]
+
+
+class PadPrefillDims(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("num_tokens", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("max_query_len", ctypes.c_int32),
         ("num_blocks", ctypes.c_int64),
         ("max_blocks_per_seq", ctypes.c_int32),
         ("kv_layout", ctypes.c_int32),
@@ -90,6 +106,11 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode_choose_partition.restype = i32
     lib.paged_attention_decode_strerror.argtypes = [i32]
     lib.paged_attention_decode_strerror.restype = ctypes.c_char_p
+    pdims = ctypes.POINTER(PadPrefillDims)
+    lib.paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, pdims, vp]
+    lib.paged_attention_prefill.restype = i32
+    lib.paged_attention_prefill_write_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, pdims, vp]
+    lib.paged_attention_prefill_write_kv.restype = i32
     del i64
     return lib
 
@@ -275,3 +296,75 @@ def alloc_workspace(num_seqs, num_heads, head_size, max_blocks_per_seq, block_si
         paged_attention_decode_workspace_init(ws, num_seqs, num_heads, head_size, max_blocks_per_seq, block_size,
                                               partition_size, stream)
     return ws
+
+
+# ---------------------------------------------------------------------------
+# prefix (chunked prefill) attention
+# ---------------------------------------------------------------------------
+
+def make_prefill_dims(query, key_cache, block_tables, max_query_len: int, num_tokens=None) -> PadPrefillDims:
+    """Sizes of a prefill call; ``query`` is [T, H, D] (or the chunk keys [T, Hkv, D] for the write)."""
+    if query.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("expected rows [T, heads, D] and block_tables [S, W]")
+    T, H, D = query.shape
+    layout = PAD_KV_TILED if key_cache.dim() == 5 else PAD_KV_ROWS
+    return PadPrefillDims(_dtype_code(query), block_tables.shape[0], T if num_tokens is None else num_tokens, H, D,
+                          int(max_query_len), key_cache.shape[0], block_tables.shape[1], layout)
+
+
+def _check_prefill(query, key_cache, value_cache, block_tables, query_start, context_lens, num_kv_heads,
+                   block_size, heads_of_rows):
+    torch = _torch()
+    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+        raise TypeError("rows and caches must share a dtype")
+    T, _, D = query.shape
+    layout = cache_layout(key_cache, value_cache)
+    NB = key_cache.shape[0]
+    if layout == PAD_KV_ROWS:
+        want_k = want_v = (NB, num_kv_heads, block_size, D)
+    else:
+        x = 16 // query.element_size()
+        want_k = (NB, num_kv_heads, D // x, block_size, x)
+        want_v = (NB, num_kv_heads, D, block_size)
+    if tuple(key_cache.shape) != want_k or tuple(value_cache.shape) != want_v:
+        raise ValueError(f"caches must be K {want_k} and V {want_v}, got {tuple(key_cache.shape)} and "
+                         f"{tuple(value_cache.shape)}")
+    S = block_tables.shape[0]
+    for name, t in (("block_tables", block_tables), ("query_start", query_start), ("context_lens", context_lens)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if tuple(query_start.shape) != (S + 1,) or tuple(context_lens.shape) != (S,):
+        raise ValueError("query_start must be [num_seqs + 1] and context_lens [num_seqs]")
+    if heads_of_rows is not None and query.shape[1] != heads_of_rows:
+        raise ValueError(f"rows must have {heads_of_rows} heads")
+
+
+def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, query_start, context_lens,
+                            scale: float, num_kv_heads: int, block_size: int, max_query_len: int,
+                            stream=None) -> None:
+    """Prefix attention of the chunk rows ``query`` [T, H, D] into ``out`` (float32 [T, H, D])."""
+    torch = _torch()
+    _check_prefill(query, key_cache, value_cache, block_tables, query_start, context_lens, num_kv_heads,
+                   block_size, None)
+    if out.dtype != torch.float32 or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must be float32 with the shape of query")
+    dims = make_prefill_dims(query, key_cache, block_tables, max_query_len)
+    st = LIB.paged_attention_prefill(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                     _ptr(block_tables), _ptr(query_start), _ptr(context_lens), float(scale),
+                                     int(num_kv_heads), int(block_size), ctypes.byref(dims), _stream(stream))
+    _check(st, "paged_attention_prefill")
+
+
+def paged_attention_prefill_write_kv(key_cache, value_cache, key, value, block_tables, query_start, context_lens,
+                                     num_kv_heads: int, block_size: int, max_query_len: int, stream=None) -> None:
+    """Store the chunk rows ``key`` / ``value`` [T, Hkv, D] in the cache at their positions."""
+    _check_prefill(key, key_cache, value_cache, block_tables, query_start, context_lens, num_kv_heads,
+                   block_size, num_kv_heads)
+    if value.shape != key.shape or value.dtype != key.dtype:
+        raise ValueError("key and value must have one shape and dtype")
+    dims = make_prefill_dims(key, key_cache, block_tables, max_query_len)
+    st = LIB.paged_attention_prefill_write_kv(_ptr(key_cache), _ptr(value_cache), _ptr(key), _ptr(value),
+                                              _ptr(block_tables), _ptr(query_start), _ptr(context_lens),
+                                              int(num_kv_heads), int(block_size), ctypes.byref(dims),
+                                              _stream(stream))
+    _check(st, "paged_attention_prefill_write_kv")

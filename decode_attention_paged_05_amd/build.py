@@ -45,8 +45,13 @@ def _run(cmd, verbose):
         print("\n".join(lines), flush=True)
 
 
-DEVICE_SOURCES = ["pad_kernels.hip"] + [f"pad_attn_{dt}_{lay}_{form}.hip" for dt in ("bf16", "f32")
-                                         for lay in ("rows", "tiled") for form in ("split", "one_pass")]
+DEVICE_SOURCES = ["pad_kernels.hip", "pad_prefill.hip"] + [f"pad_attn_{dt}_{lay}_{form}.hip" for dt in ("bf16", "f32")
+                                                             for lay in ("rows", "tiled") for form in ("split", "one_pass")]
+# Per-source device flags.  The prefill kernel accumulates in ordinary vector
+# registers rather than accumulation registers: its lazy softmax rescale
+# multiplies the accumulators on the vector ALU, and the accumulation-register
+# form made the compiler copy all of them across on every key step.
+SOURCE_FLAGS = {"pad_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HOST_SOURCES = ["pad_api.cpp"]
 
 
@@ -57,8 +62,8 @@ def build(verbose: bool = False, extra_flags=(), out: str = None) -> str:
         jobs, objs = [], []
         for src in DEVICE_SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            jobs.append([cc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, *extra_flags, "-c",
-                         os.path.join(CSRC, src), "-o", obj])
+            jobs.append([cc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []),
+                         *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
         for src in HOST_SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")

@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "paged_attention_decode.h"
+#include "paged_attention_prefill.h"
 #include "pad_internal.h"
 
 namespace {
@@ -115,6 +116,34 @@ bool attach_workspace(pad::Plan* p, void* workspace, size_t workspace_bytes) {
 
 int32_t status_of(hipError_t e) { return e == hipSuccess ? PAD_OK : (int32_t)e; }
 
+// Validation shared by the prefill entry points (sizes first, then pointers).
+int32_t validate_prefill(const pad_prefill_dims_t* d, int32_t num_kv_heads, int32_t block_size, bool attention) {
+  if (!d) return PAD_ERR_NULL;
+  if (d->dtype != PAD_DTYPE_F32 && d->dtype != PAD_DTYPE_BF16) return PAD_ERR_DTYPE;
+  if (d->kv_layout != PAD_KV_ROWS && d->kv_layout != PAD_KV_TILED) return PAD_ERR_DTYPE;
+  if (d->num_seqs < 0 || d->num_tokens < 0 || d->max_query_len < 0 || d->num_heads <= 0 || num_kv_heads <= 0 ||
+      d->num_blocks <= 0 || d->max_blocks_per_seq <= 0 || d->head_size <= 0)
+    return PAD_ERR_SHAPE;
+  if (attention && d->num_heads % num_kv_heads != 0) return PAD_ERR_SHAPE;
+  if (d->head_size != 64 && d->head_size != 128 && d->head_size != 256) return PAD_ERR_UNSUPPORTED;
+  if (block_size != pad::kBlockTokens) return PAD_ERR_UNSUPPORTED;
+  // the attention kernels are bf16, tiled layout
+  if (attention && (d->dtype != PAD_DTYPE_BF16 || d->kv_layout != PAD_KV_TILED)) return PAD_ERR_UNSUPPORTED;
+  // offsets inside the kernels are 32-bit: query / out bytes, positions
+  const int64_t heads = attention ? d->num_heads : num_kv_heads;
+  if ((int64_t)d->num_tokens * heads * d->head_size * 4 > INT32_MAX) return PAD_ERR_UNSUPPORTED;
+  if ((int64_t)d->max_blocks_per_seq * block_size > INT32_MAX / 2) return PAD_ERR_UNSUPPORTED;
+  if (d->num_seqs > 65535) return PAD_ERR_UNSUPPORTED;
+  if (attention) {
+    const int group = d->num_heads / num_kv_heads;
+    const int64_t y = (int64_t)num_kv_heads * (group / pad::prefill_heads_per_wg(group));
+    if (y > 65535) return PAD_ERR_UNSUPPORTED;
+  }
+  return PAD_OK;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -217,6 +246,68 @@ int32_t paged_attention_decode(float* out, const void* query, const void* key_ca
   return status_of(pad::launch_phase2(plan, out, seq_lens, s));
 }
 
+int32_t paged_attention_prefill(float* out, const void* query, const void* key_cache, const void* value_cache,
+                                const int32_t* block_tables, const int32_t* query_start,
+                                const int32_t* context_lens, float scale, int32_t num_kv_heads,
+                                int32_t block_size, const pad_prefill_dims_t* dims, void* stream) {
+  int32_t st = validate_prefill(dims, num_kv_heads, block_size, true);
+  if (st != PAD_OK) return st;
+  if (!std::isfinite(scale)) return PAD_ERR_SHAPE;
+  if (dims->num_seqs == 0 || dims->num_tokens == 0 || dims->max_query_len == 0) return PAD_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !query_start || !context_lens)
+    return PAD_ERR_NULL;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned4(block_tables) || !aligned4(query_start) || !aligned4(context_lens))
+    return PAD_ERR_ALIGN;
+  pad::PrefillArgs a{};
+  a.out = out;
+  a.query = static_cast<const char*>(query);
+  a.key_cache = static_cast<const char*>(key_cache);
+  a.value_cache = static_cast<const char*>(value_cache);
+  a.block_tables = block_tables;
+  a.query_start = query_start;
+  a.context_lens = context_lens;
+  a.qscale = scale;
+  a.num_tokens = dims->num_tokens;
+  a.num_heads = dims->num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = dims->num_heads / num_kv_heads;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.num_blocks = dims->num_blocks;
+  return status_of(pad::launch_prefill(a, dims->num_seqs, dims->max_query_len, dims->head_size,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int32_t paged_attention_prefill_write_kv(void* key_cache, void* value_cache, const void* key, const void* value,
+                                         const int32_t* block_tables, const int32_t* query_start,
+                                         const int32_t* context_lens, int32_t num_kv_heads,
+                                         int32_t block_size, const pad_prefill_dims_t* dims, void* stream) {
+  int32_t st = validate_prefill(dims, num_kv_heads, block_size, false);
+  if (st != PAD_OK) return st;
+  if (dims->num_seqs == 0 || dims->num_tokens == 0 || dims->max_query_len == 0) return PAD_OK;
+  if (!key_cache || !value_cache || !key || !value || !block_tables || !query_start || !context_lens)
+    return PAD_ERR_NULL;
+  if (!aligned16(key_cache) || !aligned16(value_cache) || !aligned16(key) || !aligned16(value) ||
+      !aligned4(block_tables) || !aligned4(query_start) || !aligned4(context_lens))
+    return PAD_ERR_ALIGN;
+  pad::WriteKvArgs a{};
+  a.key_cache = static_cast<char*>(key_cache);
+  a.value_cache = static_cast<char*>(value_cache);
+  a.key = static_cast<const char*>(key);
+  a.value = static_cast<const char*>(value);
+  a.block_tables = block_tables;
+  a.query_start = query_start;
+  a.context_lens = context_lens;
+  a.num_tokens = dims->num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = dims->head_size;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.num_blocks = dims->num_blocks;
+  const int eb = dims->dtype == PAD_DTYPE_BF16 ? 2 : 4;
+  return status_of(pad::launch_write_kv(a, dims->num_seqs, dims->max_query_len, eb, dims->kv_layout,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int32_t paged_attention_decode_choose_partition(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                                 int32_t max_context_len, int32_t block_size, int32_t num_cus) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || max_context_len < 0 ||
@@ -250,7 +341,7 @@ const char* paged_attention_decode_strerror(int32_t status) {
     case PAD_ERR_NULL: return "a required pointer is NULL";
     case PAD_ERR_DTYPE: return "dtype must be PAD_DTYPE_F32 or PAD_DTYPE_BF16 and kv_layout PAD_KV_ROWS or PAD_KV_TILED";
     case PAD_ERR_SHAPE: return "invalid sizes: need num_seqs >= 0, num_heads, num_kv_heads, num_blocks, max_blocks_per_seq >= 1, num_heads % num_kv_heads == 0, finite scale";
-    case PAD_ERR_UNSUPPORTED: return "unsupported shape: head_size must be 64, 128 or 256 and block_size 16 (or a grid limit is exceeded)";
+    case PAD_ERR_UNSUPPORTED: return "unsupported shape: head_size must be 64, 128 or 256 and block_size 16 (the prefill attention also needs bf16 and the tiled layout), or a size limit is exceeded";
     case PAD_ERR_PARTITION: return "partition_size must be >= 0 and a multiple of block_size (> 0 for phase calls)";
     case PAD_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than paged_attention_decode_workspace_size()";
     case PAD_ERR_ALIGN: return "a device pointer is not 16-byte aligned";

@@ -1,0 +1,479 @@
+// Prefix (chunked prefill) attention over the paged KV cache, and the chunk
+// write that stores the chunk's keys and values in the cache, on CDNA4
+// (gfx950).
+//
+// Operation (first page, prefill note; second page, prefix-attention
+// messages): a sequence holds ctx tokens in the paged cache and receives a
+// chunk of n new tokens; chunk token i sits at absolute position ctx + i and
+// takes softmax attention over the sequence's positions 0 .. ctx + i.  The
+// chunk's own keys and values are stored in the cache first (write_kv_kernel),
+// so the attention reads every key through the block table and the causal rule
+// is a comparison of absolute positions.  The pages' form walks the context
+// tiles and then the chunk tiles with an online softmax; this kernel walks the
+// same keys as one range, in 32-key steps, with the same running max / sum.
+//
+// Work decomposition.  A workgroup of 4 waves serves one (sequence, KV head,
+// HC query heads of its group, 32 * 4 / HC chunk tokens); each wave owns 32
+// query rows: 32 consecutive chunk tokens of one head, as two 16-row column
+// tiles.  The workgroup walks the keys its last row can see in 32-key steps
+// (two 16-token blocks).  Each step's K and V tiles are copied from the pool
+// into LDS by direct-to-LDS buffer loads (one tile per wave, 16 bytes per lane
+// per load, double-buffered so the next step's copies overlap this step's
+// arithmetic; one barrier per step).  Each wave then:
+//   * forms S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = K (rows = keys; lane
+//     l reads key l%16 and 8 consecutive dims, one 16-byte LDS read of the
+//     tiled K layout), B = Q^T (columns = query rows: registers, or for D = 256
+//     the wave's own LDS slice), contracting over D;
+//   * masks keys beyond each row's position (logit -inf by select) and updates
+//     each row's running max (in-lane over 8 keys, then two xor shuffles),
+//     exp2-domain with a lazy reference: the accumulator is rescaled only when
+//     a row's max grows by more than 2^8;
+//   * accumulates O^T += V^T P^T on the same MFMA: A = V^T (rows = dims; lane
+//     l reads dim l%16 and 4 consecutive tokens of each block, two 8-byte LDS
+//     reads of the tiled V layout), B = P^T (exactly the lane layout the
+//     logits came out in).  p is split into bf16 hi + lo (two MFMAs), ~2^-16
+//     relative precision.  Lane l holds output dims of row l%16, so the
+//     softmax state and the rescale stay in the lane.
+// V elements at positions the sequence does not hold are zeroed before the
+// MFMA, so NaN padding never reaches a row.  Masking runs only on the steps
+// that need it (the diagonal, the end of the sequence), in separate code.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "pad_internal.h"
+
+namespace pad {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;          // waves per workgroup
+constexpr int kRowsPerWave = 32;   // two 16-row column tiles
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyLog2 = 8.0f;  // headroom of the lazy softmax reference
+// cache-policy bits of the K/V loads: default (every workgroup of a sequence
+// re-reads its keys, so they should stay in the caches)
+constexpr int kKvPolicy = 0;
+
+__device__ inline void* uniform_ptr(const void* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ inline f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+template <int D, int HC>
+__global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) {
+  constexpr int TW = kWaves / HC;        // 32-token groups per workgroup
+  constexpr int KS = D / 32;             // QK steps (32 dims each)
+  constexpr int DT = D / 16;             // 16-dim output tiles
+  constexpr int kTileBytes = kBlockTokens * D * 2;
+  constexpr int kStepBytes = 4 * kTileBytes;  // K and V of two blocks
+  constexpr bool kQInLds = D == 256;     // Q operand re-read from LDS each step
+  __shared__ __attribute__((aligned(16))) char kv_lds[2 * kStepBytes];
+  __shared__ u32x4_t q_lds[kQInLds ? kWaves * 2 * KS * kWave : 1];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lg = lane >> 4;              // lane group: keys / dims 4*lg .. 4*lg+3
+  const int s = blockIdx.z;
+  const int g = blockIdx.y / a.head_groups;
+  const int h = g * a.group + (blockIdx.y % a.head_groups) * HC + wave % HC;
+  const int qt = gridDim.x - 1 - blockIdx.x;  // longest walks first
+  const int q_lo = a.query_start[s];
+  const int q_hi = a.query_start[s + 1];
+  const int n = q_hi - q_lo;
+  const int ctx = a.context_lens[s];
+  const int wg_tok0 = qt * (kRowsPerWave * TW);
+  const int tok0 = wg_tok0 + (wave / HC) * kRowsPerWave;
+  const bool bad_seq = ctx < 0 || n < 0 || q_lo < 0 || q_hi > a.num_tokens ||
+                       (int64_t)ctx + n > (int64_t)a.max_blocks * kBlockTokens;
+  // the whole workgroup leaves together (it shares barriers below)
+  if (wg_tok0 >= max(n, 0)) return;
+
+  // rows of this wave: column tile ct, lane -> chunk token tok0 + 16 ct + lane%16
+  int rpos[2];
+  bool row_ok[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int tok = tok0 + 16 * ct + (lane & 15);
+    row_ok[ct] = tok < n;
+    rpos[ct] = ctx + tok;
+  }
+  auto store_rows = [&](const f32x4_t (*o)[DT], const float* inv) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int row = q_lo + tok0 + 16 * ct + (lane & 15);
+      if (!row_ok[ct] || row < 0 || row >= a.num_tokens) continue;
+      float* dst = a.out + ((size_t)row * a.num_heads + h) * D + 4 * lg;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4_t v = o[ct][dt] * inv[ct];
+        *reinterpret_cast<f32x4_t*>(dst + 16 * dt) = v;
+      }
+    }
+  };
+  if (bad_seq) {
+    // out-of-contract sizes: NaN rows, within the output's bounds
+    f32x4_t o[2][DT];
+    const float nan[2] = {NAN, NAN};
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4_t{1.0f, 1.0f, 1.0f, 1.0f};
+    store_rows(o, nan);
+    return;
+  }
+
+  // Q^T operand: column tile ct, step ks -> row's dims 32 ks + 8 lg .. + 8.
+  // Held in registers, or (kQInLds) in this wave's own LDS slice and re-read
+  // every step, which keeps the largest head size within the register file.
+  u32x4_t qop[kQInLds ? 1 : 2][KS];
+  {
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(a.query), (short)0, (int)((size_t)a.num_tokens * a.num_heads * D * 2), kRsrcWord3);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int row = q_lo + tok0 + 16 * ct + (lane & 15);
+      const int off = ((row * a.num_heads + h) * D + 8 * lg) * 2;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * ks, 0, 0);
+        v = row_ok[ct] ? v : u32x4_t{0u, 0u, 0u, 0u};
+        if constexpr (kQInLds)
+          q_lds[((wave * 2 + ct) * KS + ks) * kWave + lane] = v;
+        else
+          qop[ct][ks] = v;
+      }
+    }
+  }
+  // per-step LDS index, opaque to the compiler so the reads stay in the loop
+  int q_base = wave * 2 * KS * kWave + lane;
+  auto q_operand = [&](int ct, int ks) -> u32x4_t {
+    if constexpr (kQInLds)
+      return q_lds[q_base + (ct * KS + ks) * kWave];
+    else
+      return qop[ct][ks];
+  };
+
+  // keys the workgroup walks: up to its last row's position; each wave masks
+  // to its own rows
+  const int kend = ctx + min(wg_tok0 + kRowsPerWave * TW, n);
+  const int nblk = (kend + kBlockTokens - 1) / kBlockTokens;
+  const int nsteps = (nblk + 1) / 2;
+  // keys below a wave's first row position are visible to all its rows
+  const int diag_from = ctx + tok0;
+  // V is zeroed from here on: the tail slots of the sequence's last block, and
+  // a step's second block when the walk has an odd number of blocks (its LDS
+  // tile is not written)
+  const int v_end = min(ctx + n, nblk * kBlockTokens);
+  const int32_t* table_row = a.block_tables + (size_t)s * a.max_blocks;
+  const size_t head_off = (size_t)g * kTileBytes;
+  const size_t block_stride = (size_t)a.num_kv_heads * kTileBytes;
+  bool bad = false;
+
+  // Wave w copies tile w of each step into LDS: K of the step's first block,
+  // K of its second, V of the first, V of the second.  Block ids come 64 at a
+  // time (lane j holds block seg + j).
+  const char* pool = (wave < 2) ? a.key_cache : a.value_cache;
+  const int my_b = wave & 1;
+  auto load_ids = [&](int base) { return base + lane < nblk ? table_row[base + lane] : 0; };
+  int seg = 0;
+  int id_cur = load_ids(0);
+  int id_next = load_ids(kWave);
+  auto issue = [&](int step) {
+    const int blk = 2 * step + my_b;
+    int phys = __builtin_amdgcn_readlane(id_cur, blk - seg);
+    const bool live = blk < nblk;
+    const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
+    bad |= live && !ok;
+    const int bytes = (live && ok) ? kTileBytes : 0;
+    if (!ok) phys = 0;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(pool + (size_t)phys * block_stride + head_off), (short)0, bytes, kRsrcWord3);
+    char* dst = kv_lds + (step & 1) * kStepBytes + wave * kTileBytes;
+#pragma unroll
+    for (int j = 0; j < kTileBytes / 1024; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16,
+                                              1024 * j + 16 * lane, 0, 0, 0);
+  };
+
+  f32x4_t o[2][DT];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_ref[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.0f, 0.0f};
+
+  issue(0);
+  for (int st = 0; st < nsteps; ++st) {
+    const int b0 = 2 * st;  // first block of this step
+    // this step's tiles are in LDS once every wave's copies have landed; the
+    // barrier also retires every wave's reads of the buffer the next copies
+    // overwrite (that of step st - 1)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (st + 1 < nsteps) {
+      const int nb0 = b0 + 2;
+      if ((nb0 & (kWave - 1)) == 0) {
+        id_cur = id_next;
+        seg = nb0;
+        id_next = load_ids(seg + kWave);
+      }
+      issue(st + 1);
+    }
+    if constexpr (kQInLds) asm volatile("" : "+v"(q_base));
+    const char* kv = kv_lds + (st & 1) * kStepBytes;
+
+    // ---- logits S^T for two blocks x two column tiles
+    f32x4_t sc[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) sc[b][ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t kf[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        kf[b] = *reinterpret_cast<const u32x4_t*>(kv + b * kTileBytes + 1024 * ks + 16 * lane);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const u32x4_t qf = q_operand(ct, ks);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) sc[b][ct] = mfma_bf16(kf[b], qf, sc[b][ct]);
+      }
+    }
+
+    // ---- mask, running max, weights.  Only steps that reach the wave's first
+    // row position (the diagonal) or the end of the keys need the mask.
+    const bool diag = (b0 + 2) * kBlockTokens > diag_from;
+    float x[2][2][4];
+    float bm[2];
+    // separate code for the masked steps, so the common step carries no selects
+    auto logits = [&](auto masked) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        bm[ct] = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = sc[b][ct][i] * a.qscale;
+            if constexpr (decltype(masked)::value) {
+              const int jpos = (b0 + b) * kBlockTokens + 4 * lg + i;
+              x[b][ct][i] = (jpos <= rpos[ct] && jpos < kend) ? v : -INFINITY;
+            } else {
+              x[b][ct][i] = v;
+            }
+            bm[ct] = fmaxf(bm[ct], x[b][ct][i]);
+          }
+        bm[ct] = fmaxf(bm[ct], __shfl_xor(bm[ct], 16));
+        bm[ct] = fmaxf(bm[ct], __shfl_xor(bm[ct], 32));
+      }
+    };
+    if (diag)
+      logits(std::true_type{});
+    else
+      logits(std::false_type{});
+    if (__builtin_expect(__ballot(bm[0] > m_ref[0] + kLazyLog2 || bm[1] > m_ref[1] + kLazyLog2) != 0, 0)) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const float m_new = bm[ct] > m_ref[ct] + kLazyLog2 ? bm[ct] : m_ref[ct];
+        const float alpha = __builtin_amdgcn_exp2f(m_ref[ct] - m_new);  // 0 on a row's first keys
+        l_run[ct] *= alpha;
+        m_ref[ct] = m_new;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
+      }
+    }
+    // p = hi + lo in bf16: hi keeps the top 16 bits of p (truncation, so p - hi
+    // is exact), lo the top 16 bits of the remainder; packed by byte permutes
+    u32x4_t p_hi[2], p_lo[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int b = k >> 1, i = 2 * (k & 1);
+        const float p0 = __builtin_amdgcn_exp2f(x[b][ct][i] - m_ref[ct]);
+        const float p1 = __builtin_amdgcn_exp2f(x[b][ct][i + 1] - m_ref[ct]);
+        l_run[ct] += p0 + p1;
+        const uint32_t u0 = __builtin_bit_cast(uint32_t, p0), u1 = __builtin_bit_cast(uint32_t, p1);
+        const float r0 = p0 - __builtin_bit_cast(float, u0 & 0xffff0000u);
+        const float r1 = p1 - __builtin_bit_cast(float, u1 & 0xffff0000u);
+        hi[k] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+        lo[k] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, r1), __builtin_bit_cast(uint32_t, r0), 0x07060302u);
+      }
+      p_hi[ct] = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+      p_lo[ct] = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+    }
+
+    // ---- O^T += V^T P^T.  V elements at positions the walk does not hold are
+    // zeroed: p is 0 there, but 0 * NaN would poison the row.
+    auto pv = [&](auto masked) {
+      uint32_t vm[2][2];
+      if constexpr (decltype(masked)::value) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int pos = (b0 + b) * kBlockTokens + 4 * lg;
+          vm[b][0] = (pos < v_end ? 0xffffu : 0u) | (pos + 1 < v_end ? 0xffff0000u : 0u);
+          vm[b][1] = (pos + 2 < v_end ? 0xffffu : 0u) | (pos + 3 < v_end ? 0xffff0000u : 0u);
+        }
+      }
+      const char* vt = kv + 2 * kTileBytes + (lane & 15) * 32 + 8 * lg;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vt + 512 * dt);
+        const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vt + kTileBytes + 512 * dt);
+        u32x4_t va = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
+        if constexpr (decltype(masked)::value)
+          va = u32x4_t{va[0] & vm[0][0], va[1] & vm[0][1], va[2] & vm[1][0], va[3] & vm[1][1]};
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          o[ct][dt] = mfma_bf16(va, p_hi[ct], o[ct][dt]);
+          o[ct][dt] = mfma_bf16(va, p_lo[ct], o[ct][dt]);
+        }
+      }
+    };
+    if ((b0 + 2) * kBlockTokens > v_end)
+      pv(std::true_type{});
+    else
+      pv(std::false_type{});
+  }
+
+  // every wave's block-id checks count for the whole workgroup's tiles
+  bad = __syncthreads_or(bad);
+  float inv[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    float l = l_run[ct];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    inv[ct] = bad ? NAN : 1.0f / l;
+  }
+  store_rows(o, inv);
+}
+
+// Chunk write: key/value rows [T, Hkv, D] of the chunk tokens go to the cache
+// slots of their positions.  One thread per 16 bytes of one (token, KV head)
+// row.
+template <int EB, int LAYOUT>
+__global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
+  constexpr int X = 16 / EB;  // elements per 16 bytes
+  const int s = blockIdx.y;
+  const int q_lo = a.query_start[s];
+  const int n = a.query_start[s + 1] - q_lo;
+  const int ctx = a.context_lens[s];
+  const int chunks = a.head_size / X;
+  const int per_token = a.num_kv_heads * chunks;
+  const int flat = blockIdx.x * 256 + threadIdx.x;
+  const int i = flat / per_token;
+  if (i >= n || ctx < 0 || q_lo < 0) return;
+  const int rem = flat - i * per_token;
+  const int g = rem / chunks;
+  const int c = rem - g * chunks;
+  const int t = q_lo + i;
+  const int64_t pos = (int64_t)ctx + i;
+  if (t >= a.num_tokens || pos >= (int64_t)a.max_blocks * kBlockTokens) return;
+  const int blk = a.block_tables[(size_t)s * a.max_blocks + (int)(pos / kBlockTokens)];
+  if (blk < 0 || (int64_t)blk >= a.num_blocks) return;
+  const int slot = (int)(pos % kBlockTokens);
+  const size_t src = ((size_t)t * a.num_kv_heads + g) * a.head_size + (size_t)c * X;  // elements
+  const size_t tile = ((size_t)blk * a.num_kv_heads + g) * (size_t)kBlockTokens * a.head_size;
+  const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(a.key + src * EB);
+  const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(a.value + src * EB);
+  if (LAYOUT == kKvRows) {
+    const size_t dst = tile + (size_t)slot * a.head_size + (size_t)c * X;
+    *reinterpret_cast<u32x4_t*>(a.key_cache + dst * EB) = kv;
+    *reinterpret_cast<u32x4_t*>(a.value_cache + dst * EB) = vv;
+  } else {
+    // K [D/X][16][X]: the 16 bytes stay together; V [D][16]: one element per dim
+    const size_t kdst = tile + ((size_t)c * kBlockTokens + slot) * X;
+    *reinterpret_cast<u32x4_t*>(a.key_cache + kdst * EB) = kv;
+    const size_t vdst = tile + (size_t)c * X * kBlockTokens + slot;
+    if (EB == 2) {
+#pragma unroll
+      for (int e = 0; e < X; ++e) {
+        const uint32_t w = vv[e / 2];
+        reinterpret_cast<uint16_t*>(a.value_cache)[vdst + (size_t)e * kBlockTokens] =
+            (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < X; ++e) reinterpret_cast<uint32_t*>(a.value_cache)[vdst + (size_t)e * kBlockTokens] = vv[e];
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_prefill_d(const PrefillArgs& a, int hc, dim3 grid, hipStream_t stream) {
+  switch (hc) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, dim3(kWaves * kWave), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, dim3(kWaves * kWave), 0, stream, a); break;
+    default: hipLaunchKernelGGL((prefill_kernel<D, 4>), grid, dim3(kWaves * kWave), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_heads_per_wg(int group) {
+  // the largest of 4, 2, 1 that divides the group: the workgroup's waves are
+  // (head, 32-token group) pairs of one KV head
+  return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+}
+
+int prefill_tokens_per_wg(int group) { return kRowsPerWave * kWaves / prefill_heads_per_wg(group); }
+
+hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
+                          hipStream_t stream) {
+  PrefillArgs a = args;
+  const int hc = prefill_heads_per_wg(a.group);
+  a.head_groups = a.group / hc;
+  a.qscale = args.qscale * kLog2e;
+  const int tiles = (max_query_len + prefill_tokens_per_wg(a.group) - 1) / prefill_tokens_per_wg(a.group);
+  if (num_seqs == 0 || tiles == 0) return hipSuccess;
+  const dim3 grid(tiles, a.num_kv_heads * a.head_groups, num_seqs);
+  switch (head_size) {
+    case 64: return launch_prefill_d<64>(a, hc, grid, stream);
+    case 128: return launch_prefill_d<128>(a, hc, grid, stream);
+    default: return launch_prefill_d<256>(a, hc, grid, stream);
+  }
+}
+
+hipError_t launch_write_kv(const WriteKvArgs& a, int num_seqs, int max_query_len, int elem_bytes, int layout,
+                           hipStream_t stream) {
+  const int per_token = a.num_kv_heads * (a.head_size * elem_bytes / 16);
+  const int64_t threads = (int64_t)max_query_len * per_token;
+  if (num_seqs == 0 || threads == 0) return hipSuccess;
+  const dim3 grid((unsigned)((threads + 255) / 256), num_seqs);
+  if (elem_bytes == 2) {
+    if (layout == kKvRows)
+      hipLaunchKernelGGL((write_kv_kernel<2, kKvRows>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((write_kv_kernel<2, kKvTiled>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (layout == kKvRows)
+      hipLaunchKernelGGL((write_kv_kernel<4, kKvRows>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((write_kv_kernel<4, kKvTiled>), grid, dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pad

@@ -333,3 +333,124 @@ def build_pool(problem: Problem, poison: bool = True, threads: Optional[int] = N
 def logical_kv(problem: Problem, s: int) -> List[tuple]:
     """[(K_g, V_g) for each KV head] of sequence s in storage format."""
     return [sequence_kv(problem, s, g) for g in range(problem.num_kv_heads)]
+
+
+# ---------------------------------------------------------------------------
+# Prefix (chunked prefill) attention inputs
+# ---------------------------------------------------------------------------
+
+_S_PREFILL_QUERY = 6
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillSpec:
+    """Shape and value recipe of one prefill workload: per sequence, a cached
+    context of ``context_lens[s]`` tokens and a chunk of ``query_lens[s]`` new
+    tokens (whose keys and values also go into the cache)."""
+
+    name: str
+    context_lens: tuple
+    query_lens: tuple
+    num_heads: int
+    num_kv_heads: int
+    head_size: int
+    dtype: str
+    seed: int
+    block_size: int = 16
+    num_blocks: Optional[int] = None  # default: twice the blocks the sequences need
+    scale: Optional[float] = None     # default 1/sqrt(head_size)
+
+    @property
+    def softmax_scale(self) -> float:
+        return float(np.float32(self.scale if self.scale is not None
+                                else 1.0 / math.sqrt(self.head_size)))
+
+
+# Shapes are the pages' model attention shape (24 query / 4 KV heads, head
+# 256).  "prefill" is one chunk of 8192 new tokens (the serving
+# configuration's batched-token budget on the second page) over a 32768-token
+# cached prefix; the others are ragged batches that span several query tiles,
+# empty chunks and empty contexts.
+PREFILL_CONFIGS: Dict[str, PrefillSpec] = {
+    "prefill_small": PrefillSpec("prefill_small", context_lens=(0, 37, 200, 16, 5), query_lens=(50, 1, 77, 128, 0),
+                                 num_heads=24, num_kv_heads=4, head_size=256, dtype="bf16", seed=11),
+    "prefill": PrefillSpec("prefill", context_lens=(32768,), query_lens=(8192,), num_heads=24, num_kv_heads=4,
+                           head_size=256, dtype="bf16", seed=12),
+    "prefill_batch": PrefillSpec("prefill_batch", context_lens=(0, 5000, 12345, 30000),
+                                 query_lens=(2048, 1000, 777, 3000), num_heads=24, num_kv_heads=4, head_size=256,
+                                 dtype="bf16", seed=13),
+}
+
+
+@dataclasses.dataclass
+class PrefillProblem:
+    """A prefill step: the packed chunk queries and the paged cache holding, per
+    sequence, its context followed by its chunk (an inner decode
+    :class:`Problem` whose sequence lengths are context + chunk supplies the
+    block tables and the K/V generator)."""
+
+    spec: PrefillSpec
+    pool: Problem                # seq_lens = context + chunk; block tables, K/V streams
+    context_lens: np.ndarray     # int32 [S]
+    query_lens: np.ndarray       # int32 [S]
+    query_start: np.ndarray      # int32 [S + 1]
+    query: np.ndarray            # [T, H, D] storage format
+
+    @property
+    def num_seqs(self): return len(self.context_lens)
+    @property
+    def num_tokens(self): return int(self.query_start[-1])
+    @property
+    def max_query_len(self): return int(self.query_lens.max()) if len(self.query_lens) else 0
+    @property
+    def scale(self): return self.spec.softmax_scale
+
+    def chunk_kv(self):
+        """The chunk's own key and value rows [T, Hkv, D] (storage format): positions
+        context .. context + n - 1 of each sequence."""
+        T, Hkv, D = self.num_tokens, self.spec.num_kv_heads, self.spec.head_size
+        sd = storage_dtype(self.spec.dtype)
+        key = np.empty((T, Hkv, D), dtype=sd)
+        value = np.empty((T, Hkv, D), dtype=sd)
+        for s in range(self.num_seqs):
+            lo, hi = int(self.query_start[s]), int(self.query_start[s + 1])
+            c = int(self.context_lens[s])
+            for g in range(Hkv):
+                k, v = sequence_kv(self.pool, s, g)
+                key[lo:hi, g] = k[c:c + hi - lo]
+                value[lo:hi, g] = v[c:c + hi - lo]
+        return key, value
+
+    def flops(self) -> int:
+        """Algorithmic flops: 4 H D per (query row, visible key) pair."""
+        per_row = 0
+        for s in range(self.num_seqs):
+            c, n = int(self.context_lens[s]), int(self.query_lens[s])
+            per_row += n * c + n * (n + 1) // 2
+        return 4 * self.spec.num_heads * self.spec.head_size * per_row
+
+
+def make_prefill_problem(spec: PrefillSpec | str, **overrides) -> PrefillProblem:
+    if isinstance(spec, str):
+        spec = PREFILL_CONFIGS[spec]
+    if overrides:
+        spec = dataclasses.replace(spec, **overrides)
+    ctx = np.asarray(spec.context_lens, dtype=np.int64)
+    qn = np.asarray(spec.query_lens, dtype=np.int64)
+    if ctx.shape != qn.shape or (ctx < 0).any() or (qn < 0).any():
+        raise ValueError("context_lens and query_lens must be non-negative and of one length")
+    S, bs = len(ctx), spec.block_size
+    total = ctx + qn
+    W = max(1, int(((total + bs - 1) // bs).max()) if S else 1)
+    need = int(((total + bs - 1) // bs).sum())
+    NB = spec.num_blocks or max(2 * need, 1)
+    inner = ConfigSpec(spec.name, num_seqs=S, num_heads=spec.num_heads, num_kv_heads=spec.num_kv_heads,
+                       head_size=spec.head_size, block_size=bs, num_blocks=NB, max_blocks_per_seq=W,
+                       partition_size=0, dtype=spec.dtype, seed=spec.seed, scale=spec.scale)
+    pool = make_problem(inner, seq_lens=total)
+    qs = np.zeros(S + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(qn)
+    q = _rng(spec.seed, _S_PREFILL_QUERY).standard_normal((int(qs[-1]), spec.num_heads, spec.head_size),
+                                                          dtype=np.float32)
+    return PrefillProblem(spec=spec, pool=pool, context_lens=ctx.astype(np.int32), query_lens=qn.astype(np.int32),
+                          query_start=qs, query=to_storage(q, spec.dtype))

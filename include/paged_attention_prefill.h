@@ -1,0 +1,121 @@
+/*
+ * paged_attention_prefill.h - C ABI of the MI355X (gfx950) paged prefix
+ * (chunked prefill) attention, the step on the other side of decode.
+ *
+ * Operation (first page, prefill note; second page, the prefix-attention
+ * allocator-reuse message and the "pre-gather all context K/V" rewrite): a
+ * sequence s already holds context_lens[s] tokens in the paged KV cache and
+ * receives a chunk of n_s = query_start[s+1] - query_start[s] new tokens.
+ * Chunk token i sits at absolute position p = context_lens[s] + i and takes
+ * softmax attention over the sequence's positions 0 .. p:
+ *
+ *     x_j      = scale * <query[t,h,:], K_s[g(h), j, :]>        j = 0 .. p
+ *     out[t,h] = sum_j exp(x_j - max x) V_s[g(h), j, :] / sum_j exp(x_j - max x)
+ *
+ * with t = query_start[s] + i, g(h) = h / (num_heads / num_kv_heads), and
+ * K_s[g, j, :] = key_cache[block_tables[s, j / block_size], g, j % block_size, :]
+ * (likewise V).  The pages compute it as a K-tiled online softmax, the
+ * context's tiles first and then the chunk's own tiles under the causal
+ * mask.  Here the chunk's keys and values are first stored in the cache at
+ * their positions (paged_attention_prefill_write_kv), after which the
+ * attention reads every key through the block table in one walk with the same
+ * running max and sum.
+ *
+ * Conventions are those of paged_attention_decode.h (device pointers of the
+ * current HIP device, contiguous, 16-byte aligned; row-major; every buffer
+ * belongs to the caller; calls only enqueue work on `stream`; 0 = success, a
+ * negative status is an argument error found on the host before any HIP call,
+ * a positive status the hipError_t of a failed launch).  Layouts:
+ *   out          float32 [num_tokens, num_heads, head_size]
+ *   query        dtype   [num_tokens, num_heads, head_size]: the chunk rows of
+ *                        all sequences, sequence after sequence
+ *   key, value   dtype   [num_tokens, num_kv_heads, head_size]: the chunk's own
+ *                        keys and values (write_kv only)
+ *   key_cache,   dtype   as in paged_attention_decode.h, PAD_KV_ROWS or PAD_KV_TILED
+ *   value_cache
+ *   block_tables int32   [num_seqs, max_blocks_per_seq]
+ *   query_start  int32   [num_seqs + 1]: query_start[0] = 0, non-decreasing,
+ *                        query_start[num_seqs] = num_tokens
+ *   context_lens int32   [num_seqs]
+ *
+ * Device-side contract (not checkable without a synchronisation): the
+ * query_start bounds above; n_s <= max_query_len; 0 <= context_lens[s] and
+ * context_lens[s] + n_s <= max_blocks_per_seq * block_size; block_tables[s, j]
+ * lies in [0, num_blocks) for j < ceil((context_lens[s] + n_s) / block_size).
+ * A violation never faults: the attention writes NaN rows for that sequence
+ * (only rows inside [0, num_tokens)), and the chunk write skips tokens whose
+ * slot would fall outside the table or the pool.
+ */
+#ifndef PAGED_ATTENTION_PREFILL_H
+#define PAGED_ATTENTION_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "paged_attention_decode.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Problem sizes of a prefill call.
+ *   dtype              PAD_DTYPE_BF16 for the attention; PAD_DTYPE_F32 or
+ *                      PAD_DTYPE_BF16 for the chunk write
+ *   num_seqs           S >= 0 (0 makes every call a no-op)
+ *   num_tokens         T >= 0, the packed chunk rows of all sequences
+ *   num_heads          H >= 1, a multiple of num_kv_heads
+ *   head_size          D in {64, 128, 256}
+ *   max_query_len      >= every n_s (sizes the launch grid), >= 0
+ *   num_blocks         physical blocks in the KV pool, >= 1
+ *   max_blocks_per_seq W >= 1, the block-table row width
+ *   kv_layout          PAD_KV_TILED for the attention; PAD_KV_ROWS or
+ *                      PAD_KV_TILED for the chunk write
+ */
+typedef struct pad_prefill_dims {
+  int32_t dtype;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t num_heads;
+  int32_t head_size;
+  int32_t max_query_len;
+  int64_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t kv_layout;
+} pad_prefill_dims_t;
+
+/*
+ * Prefix attention of every chunk token over its sequence's cached positions
+ * up to and including its own (the chunk's keys and values must already be
+ * in the cache), written to `out` (float32).
+ *   scale          multiplies every query-key dot product; finite
+ *   num_kv_heads   KV heads in the pool (>= 1, divides num_heads)
+ *   block_size     tokens per block; must be 16
+ * Supported: bf16 query and cache in the PAD_KV_TILED layout (else
+ * PAD_ERR_UNSUPPORTED).  Sequences with n_s == 0 produce no rows.
+ * Accumulation is fp32; the attention weights enter the P.V product as a
+ * bf16 hi + lo pair (about 2^-16 relative precision).
+ */
+int32_t paged_attention_prefill(float* out, const void* query, const void* key_cache, const void* value_cache,
+                                const int32_t* block_tables, const int32_t* query_start,
+                                const int32_t* context_lens, float scale, int32_t num_kv_heads,
+                                int32_t block_size, const pad_prefill_dims_t* dims, void* stream);
+
+/*
+ * Store the chunk's keys and values in the cache: row query_start[s] + i of
+ * `key` / `value` goes to position context_lens[s] + i of sequence s, that
+ * is to block block_tables[s, p / block_size], slot p % block_size, in the
+ * cache layout dims->kv_layout.  Nothing else in the cache changes.
+ *   num_kv_heads   KV heads (>= 1); block_size must be 16
+ * dims->num_heads is not used (any value >= 1).
+ */
+int32_t paged_attention_prefill_write_kv(void* key_cache, void* value_cache, const void* key, const void* value,
+                                         const int32_t* block_tables, const int32_t* query_start,
+                                         const int32_t* context_lens, int32_t num_kv_heads,
+                                         int32_t block_size, const pad_prefill_dims_t* dims, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTENTION_PREFILL_H */

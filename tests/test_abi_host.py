@@ -14,16 +14,22 @@ import decode_attention_paged_05_amd as pad
 from decode_attention_paged_05_amd import _binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "paged_attention_decode.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("paged_attention_decode.h", "paged_attention_prefill.h")]
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(paged_attention_decode\w*)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(paged_attention_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_every_header_is_checked():
+    assert sorted(os.path.basename(h) for h in HEADERS) == sorted(os.listdir(os.path.join(ROOT, "include")))
 
 
 def test_header_symbols_exported():
@@ -175,3 +181,68 @@ def test_one_hip_runtime_in_process():
     maps = open("/proc/self/maps").read().splitlines()
     runtimes = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
     assert len(runtimes) == 1, runtimes
+
+
+def pdims(**kw):
+    d = dict(dtype=1, num_seqs=2, num_tokens=100, num_heads=24, head_size=256, max_query_len=64, num_blocks=100,
+             max_blocks_per_seq=10, kv_layout=1)
+    d.update(kw)
+    return B.PadPrefillDims(**d)
+
+
+def prefill_call(d=None, kv=4, bs=16, scale=0.0625, ptrs=None):
+    p = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, t=FAKE, qs=FAKE, c=FAKE)
+    if ptrs:
+        p.update(ptrs)
+    return B.LIB.paged_attention_prefill(p["out"], p["q"], p["k"], p["v"], p["t"], p["qs"], p["c"], scale, kv, bs,
+                                         ctypes.byref(d or pdims()), None)
+
+
+def write_call(d=None, kv=4, bs=16, ptrs=None):
+    p = dict(kc=FAKE, vc=FAKE, k=FAKE, v=FAKE, t=FAKE, qs=FAKE, c=FAKE)
+    if ptrs:
+        p.update(ptrs)
+    return B.LIB.paged_attention_prefill_write_kv(p["kc"], p["vc"], p["k"], p["v"], p["t"], p["qs"], p["c"], kv, bs,
+                                                  ctypes.byref(d or pdims()), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=pdims(dtype=0)), -4),            # the attention kernels are bf16
+    (dict(d=pdims(kv_layout=0)), -4),        # and tiled
+    (dict(d=pdims(dtype=3)), -2),
+    (dict(d=pdims(kv_layout=2)), -2),
+    (dict(kv=5), -3),
+    (dict(d=pdims(num_tokens=-1)), -3),
+    (dict(d=pdims(max_query_len=-1)), -3),
+    (dict(d=pdims(num_blocks=0)), -3),
+    (dict(d=pdims(head_size=96)), -4),
+    (dict(bs=32), -4),
+    (dict(scale=float("nan")), -3),
+    (dict(d=pdims(num_tokens=1 << 20)), -4),  # 32-bit offsets inside the kernel
+    (dict(ptrs=dict(qs=0)), -1),
+    (dict(ptrs=dict(out=0)), -1),
+    (dict(ptrs=dict(k=FAKE + 8)), -7),
+    (dict(ptrs=dict(c=FAKE + 2)), -7),
+])
+def test_prefill_argument_errors(kw, status):
+    assert prefill_call(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=pdims(dtype=3)), -2),
+    (dict(d=pdims(head_size=48)), -4),
+    (dict(kv=0), -3),
+    (dict(ptrs=dict(kc=0)), -1),
+    (dict(ptrs=dict(v=FAKE + 4)), -7),
+])
+def test_prefill_write_argument_errors(kw, status):
+    assert write_call(**kw) == status
+
+
+def test_prefill_empty_is_a_noop():
+    assert B.LIB.paged_attention_prefill(None, None, None, None, None, None, None, 1.0, 4, 16,
+                                         ctypes.byref(pdims(num_seqs=0)), None) == 0
+    assert B.LIB.paged_attention_prefill(None, None, None, None, None, None, None, 1.0, 4, 16,
+                                         ctypes.byref(pdims(num_tokens=0)), None) == 0
+    assert B.LIB.paged_attention_prefill_write_kv(None, None, None, None, None, None, None, 4, 16,
+                                                  ctypes.byref(pdims(max_query_len=0)), None) == 0

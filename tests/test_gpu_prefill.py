@@ -1,0 +1,227 @@
+"""Prefix (chunked prefill) attention and the chunk write on the GPU, against the oracle.
+
+Every call goes through the C ABI (``paged_attention_prefill``,
+``paged_attention_prefill_write_kv``).  Small problems are compared row by
+row with the full oracle; the 8192-token chunk over a 32768-token prefix (the
+workload the benchmark times) and a ragged batch are compared on sampled
+rows that the oracle computes one by one, plus properties of every row.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_paged_05_amd as pad
+import oracle
+from decode_attention_paged_05_amd import inputs as gen
+from tests.gpu_util import TOL, DeviceProblem, require_gpu, to_device, torch_dtype, tiled_shapes
+
+pytestmark = pytest.mark.gpu
+
+
+class DevicePrefill:
+    """A prefill problem on the GPU: packed queries, the cache holding every
+    sequence's context and chunk (tiled layout unless asked otherwise)."""
+
+    def __init__(self, pp: gen.PrefillProblem, keep_host=True, layouts=("tiled",)):
+        require_gpu()
+        self.pp = pp
+        self.dp = DeviceProblem(pp.pool, keep_host=keep_host, layouts=layouts)
+        self.query = to_device(pp.query, pp.spec.dtype)
+        self.qs = torch.from_numpy(pp.query_start).cuda()
+        self.ctx = torch.from_numpy(pp.context_lens).cuda()
+        torch.cuda.synchronize()
+
+    def run(self, kc=None, vc=None, tables=None, qs=None, ctx=None, out=None):
+        pp = self.pp
+        if out is None:
+            out = torch.full(tuple(pp.query.shape), float("nan"), dtype=torch.float32, device="cuda")
+        pad.paged_attention_prefill(out, self.query, self.dp.kc if kc is None else kc,
+                                    self.dp.vc if vc is None else vc, self.dp.tables if tables is None else tables,
+                                    self.qs if qs is None else qs, self.ctx if ctx is None else ctx, pp.scale,
+                                    pp.spec.num_kv_heads, 16, pp.max_query_len)
+        torch.cuda.synchronize()
+        return out
+
+    def oracle(self):
+        pp = self.pp
+        return oracle.prefill_attention(pp.query, self.dp.kc_host, self.dp.vc_host, pp.pool.block_tables,
+                                        pp.query_start, pp.context_lens, pp.scale, pp.spec.num_kv_heads, 16,
+                                        pp.spec.dtype)
+
+
+def max_err(got: torch.Tensor, want: np.ndarray) -> float:
+    g = got.double().cpu().numpy()
+    assert np.all(np.isfinite(g)), "non-finite output"
+    return float(np.max(np.abs(g - want))) if want.size else 0.0
+
+
+def test_prefill_small_ragged():
+    """Five sequences: no context, a one-token chunk, several query tiles, an empty chunk."""
+    dp = DevicePrefill(gen.make_prefill_problem("prefill_small"))
+    got = dp.run()
+    assert max_err(got, dp.oracle()) <= TOL["bf16"]
+
+
+PREFILL_SHAPES = [
+    # (H, Hkv, D, context_lens, query_lens): every head grouping the workgroup
+    # shape distinguishes (1, 2 or 4 heads per workgroup) and every head size
+    (4, 1, 64, (3, 100, 0), (70, 33, 129)),
+    (8, 4, 128, (0, 64), (200, 17)),
+    (6, 2, 256, (31, 5), (40, 96)),
+    (8, 1, 128, (16, 250), (65, 31)),
+    (32, 8, 64, (500,), (130,)),
+    (24, 24, 128, (7, 0), (33, 64)),
+    (24, 4, 256, (1000, 0, 1), (1, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("H,Hkv,D,ctx,qn", PREFILL_SHAPES, ids=lambda v: str(v))
+def test_prefill_shapes(H, Hkv, D, ctx, qn):
+    spec = gen.PrefillSpec("shape", context_lens=ctx, query_lens=qn, num_heads=H, num_kv_heads=Hkv, head_size=D,
+                           dtype="bf16", seed=hash((H, Hkv, D, ctx, qn)) % 1000)
+    dp = DevicePrefill(gen.make_prefill_problem(spec))
+    assert max_err(dp.run(), dp.oracle()) <= TOL["bf16"]
+
+
+def test_prefill_one_token_chunks_match_decode():
+    """Chunks of one token are decode over the context plus that token: the
+    prefill kernel agrees with the oracle and with the library's decode path."""
+    spec = gen.PrefillSpec("one", context_lens=(1000, 0, 4097), query_lens=(1, 1, 1), num_heads=24, num_kv_heads=4,
+                           head_size=256, dtype="bf16", seed=21)
+    pp = gen.make_prefill_problem(spec)
+    dp = DevicePrefill(pp)
+    got = dp.run()
+    assert max_err(got, dp.oracle()) <= TOL["bf16"]
+    dec = torch.full((3, 24, 256), float("nan"), dtype=torch.float32, device="cuda")
+    pad.paged_attention_decode(dec, dp.query, dp.dp.kc, dp.dp.vc, dp.dp.tables, dp.dp.lens, pp.scale, 4, 16, 0)
+    torch.cuda.synchronize()
+    assert float((got - dec).abs().max()) <= 2 * TOL["bf16"]
+
+
+def _poison_chunk_slots(host_cache: np.ndarray, pp: gen.PrefillProblem) -> np.ndarray:
+    c = host_cache.copy()
+    nan = gen.poison_value(pp.spec.dtype)
+    for s in range(pp.num_seqs):
+        for i in range(int(pp.query_lens[s])):
+            p = int(pp.context_lens[s]) + i
+            c[int(pp.pool.block_tables[s, p // 16]), :, p % 16] = nan
+    return c
+
+
+def _upload(host_rows: np.ndarray, layout: str, dtype: str, kv: str):
+    if layout == "rows":
+        return to_device(host_rows, dtype)
+    kt, vt = gen.to_tiled(host_rows, host_rows, dtype)
+    return to_device(kt if kv == "k" else vt, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+def test_write_kv_bitwise(dtype, layout):
+    """The chunk write stores exactly the chunk's rows in their slots and changes nothing else."""
+    spec = gen.PrefillSpec("write", context_lens=(0, 37, 16, 5), query_lens=(50, 1, 77, 0), num_heads=8,
+                           num_kv_heads=2, head_size=128, dtype=dtype, seed=31)
+    pp = gen.make_prefill_problem(spec)
+    dp = DevicePrefill(pp, layouts=(layout,))
+    key, value = pp.chunk_kv()
+    kc = _upload(_poison_chunk_slots(dp.dp.kc_host, pp), layout, dtype, "k")
+    vc = _upload(_poison_chunk_slots(dp.dp.vc_host, pp), layout, dtype, "v")
+    pad.paged_attention_prefill_write_kv(kc, vc, to_device(key, dtype), to_device(value, dtype), dp.dp.tables,
+                                         dp.qs, dp.ctx, 2, 16, pp.max_query_len)
+    torch.cuda.synchronize()
+    iv = torch.int32 if dtype == "f32" else torch.int16
+    assert torch.equal(kc.view(iv), dp.dp.kc.view(iv)), "keys"
+    assert torch.equal(vc.view(iv), dp.dp.vc.view(iv)), "values"
+
+
+def test_write_then_prefill_matches_two_phase_form():
+    """The whole step from the chunk's own rows (write, then attention) against
+    the pages' two-phase form, which reads the chunk from those rows directly."""
+    pp = gen.make_prefill_problem("prefill_small")
+    dp = DevicePrefill(pp)
+    key, value = pp.chunk_kv()
+    kc_ctx = _poison_chunk_slots(dp.dp.kc_host, pp)
+    vc_ctx = _poison_chunk_slots(dp.dp.vc_host, pp)
+    kc = _upload(kc_ctx, "tiled", "bf16", "k")
+    vc = _upload(vc_ctx, "tiled", "bf16", "v")
+    pad.paged_attention_prefill_write_kv(kc, vc, to_device(key, "bf16"), to_device(value, "bf16"), dp.dp.tables,
+                                         dp.qs, dp.ctx, 4, 16, pp.max_query_len)
+    got = dp.run(kc=kc, vc=vc)
+    want = oracle.prefix_attention_two_phase(pp.query, key, value, kc_ctx, vc_ctx, pp.pool.block_tables,
+                                             pp.query_start, pp.context_lens, pp.scale, 4, 16, "bf16", 64)
+    assert max_err(got, want) <= TOL["bf16"]
+
+
+def _sampled_check(pp: gen.PrefillProblem, got: torch.Tensor, rows_per_seq, heads):
+    """Oracle rows computed one by one from the logical K/V of each sequence."""
+    Hkv, H = pp.spec.num_kv_heads, pp.spec.num_heads
+    G = H // Hkv
+    worst = 0.0
+    for s in range(pp.num_seqs):
+        n, c, lo = int(pp.query_lens[s]), int(pp.context_lens[s]), int(pp.query_start[s])
+        toks = sorted({t for t in rows_per_seq(n) if 0 <= t < n})
+        if not toks:
+            continue
+        for g in sorted({h // G for h in heads}):
+            K, V = gen.sequence_kv(pp.pool, s, g)
+            for h in [h for h in heads if h // G == g]:
+                for t in toks:
+                    want = oracle.prefill_rows(pp.query[lo + t:lo + t + 1, h], K, V, c, t, pp.scale,
+                                               pp.spec.dtype)[0]
+                    worst = max(worst, float(np.max(np.abs(got[lo + t, h].double().cpu().numpy() - want))))
+    return worst
+
+
+def _edge_rows(n):
+    return [0, 1, 15, 16, 31, 32, 33, 63, 64, 65, 127, 128, n // 2, n - 65, n - 64, n - 33, n - 32, n - 2, n - 1]
+
+
+def test_prefill_full_size_sampled():
+    """8192 new tokens over a 32768-token prefix (the timed workload, same launch):
+    every row finite, sampled rows against the oracle."""
+    pp = gen.make_prefill_problem("prefill")
+    dp = DevicePrefill(pp, keep_host=False)
+    got = dp.run()
+    assert bool(torch.isfinite(got).all())
+    assert _sampled_check(pp, got, _edge_rows, heads=(0, 5, 6, 13, 23)) <= TOL["bf16"]
+
+
+def test_prefill_ragged_batch_sampled():
+    pp = gen.make_prefill_problem("prefill_batch")
+    dp = DevicePrefill(pp, keep_host=False)
+    got = dp.run()
+    assert bool(torch.isfinite(got).all())
+    assert _sampled_check(pp, got, _edge_rows, heads=(0, 7, 17, 23)) <= TOL["bf16"]
+
+
+def test_prefill_repeatable():
+    dp = DevicePrefill(gen.make_prefill_problem("prefill_small"), keep_host=False)
+    a = dp.run()
+    b = dp.run()
+    assert torch.equal(a, b)
+
+
+def test_prefill_block_outside_pool_gives_nan_rows():
+    """A block id outside the pool (out of contract) makes that sequence's rows
+    NaN and leaves the other sequences exact; nothing faults."""
+    pp = gen.make_prefill_problem("prefill_small")
+    dp = DevicePrefill(pp)
+    tables = dp.dp.tables.clone()
+    tables[2, 3] = pp.pool.num_blocks + 5
+    got = dp.run(tables=tables)
+    want = dp.oracle()
+    lo, hi = int(pp.query_start[2]), int(pp.query_start[3])
+    assert bool(torch.isnan(got[lo:hi]).all())
+    keep = np.r_[0:lo, hi:pp.num_tokens]
+    g = got[keep].double().cpu().numpy()
+    assert np.max(np.abs(g - want[keep])) <= TOL["bf16"]
+
+
+def test_prefill_rejects_unsupported():
+    pp = gen.make_prefill_problem("prefill_small")
+    dp = DevicePrefill(pp, layouts=("rows",), keep_host=False)
+    out = torch.empty(tuple(pp.query.shape), dtype=torch.float32, device="cuda")
+    with pytest.raises(pad.PadError):
+        pad.paged_attention_prefill(out, dp.query, dp.dp.kc, dp.dp.vc, dp.dp.tables, dp.qs, dp.ctx, pp.scale, 4, 16,
+                                    pp.max_query_len)
