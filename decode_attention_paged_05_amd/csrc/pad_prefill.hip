@@ -54,7 +54,8 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;          // waves per workgroup
+constexpr int kWaves = 8;          // waves per workgroup: 4 row groups x 2 halves of D
+constexpr int kRowGroups = 4;      // 32-row groups per workgroup
 constexpr int kRowsPerWave = 32;   // two 16-row column tiles
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -62,6 +63,38 @@ constexpr float kLazyLog2 = 8.0f;  // headroom of the lazy softmax reference
 // cache-policy bits of the K/V loads: default (every workgroup of a sequence
 // re-reads its keys, so they should stay in the caches)
 constexpr int kKvPolicy = 0;
+#ifndef PAD_PREFILL_Q_LDS_MIN_D
+// head sizes from which the Q operand lives in LDS rather than registers
+#define PAD_PREFILL_Q_LDS_MIN_D 512
+#endif
+
+// s_waitcnt immediate: at most n vector-memory loads outstanding and every
+// LDS access done (export counter left at its maximum)
+constexpr int kWaitVmLds(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
+
+// 16 bytes per lane from a buffer into LDS (lane i's bytes land at lds + 16 i),
+// issued so that the compiler does not track it: it would otherwise wait for
+// every copy in flight before each LDS read.  The caller waits on the
+// vector-memory counter itself.  M0 (the LDS address) is restored.
+// The LDS destination is passed as a pointer so that the compiler knows the
+// statement writes there.
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ inline void lds_copy16(lds_char* lds, int voffset, u32x4_t rsrc) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voffset), "s"(rsrc)
+      : "memory");
+}
+
+// s_barrier without the memory fences of __syncthreads (those would wait for
+// the copies in flight); the "memory" clobber keeps the compiler from moving
+// LDS accesses across it.  Callers wait for their own copies and LDS reads first.
+__device__ inline void workgroup_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ inline void* uniform_ptr(const void* ptr) {
   const uint64_t a = reinterpret_cast<uint64_t>(ptr);
@@ -77,28 +110,32 @@ __device__ inline f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
 
 template <int D, int HC>
 __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) {
-  constexpr int TW = kWaves / HC;        // 32-token groups per workgroup
+  constexpr int TW = kRowGroups / HC;    // 32-token groups per workgroup
   constexpr int KS = D / 32;             // QK steps (32 dims each)
-  constexpr int DT = D / 16;             // 16-dim output tiles
+  constexpr int DT = D / 32;             // 16-dim output tiles of this wave's half of D
   constexpr int kTileBytes = kBlockTokens * D * 2;
   constexpr int kStepBytes = 4 * kTileBytes;  // K and V of two blocks
-  constexpr bool kQInLds = D == 256;     // Q operand re-read from LDS each step
-  __shared__ __attribute__((aligned(16))) char kv_lds[2 * kStepBytes];
+  constexpr bool kQInLds = D >= PAD_PREFILL_Q_LDS_MIN_D;  // Q operand re-read from LDS each step
+  constexpr int CH = kTileBytes / 1024;  // 1 KB copies per tile (one per load instruction)
+  constexpr int kBufs = 4;               // step buffers: copies run kBufs - 1 steps ahead
+  __shared__ __attribute__((aligned(16))) char kv_lds[kBufs * kStepBytes];
   __shared__ u32x4_t q_lds[kQInLds ? kWaves * 2 * KS * kWave : 1];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int rg = wave >> 1;              // row group
+  const int dh = wave & 1;               // half of D this wave accumulates
   const int lg = lane >> 4;              // lane group: keys / dims 4*lg .. 4*lg+3
   const int s = blockIdx.z;
   const int g = blockIdx.y / a.head_groups;
-  const int h = g * a.group + (blockIdx.y % a.head_groups) * HC + wave % HC;
+  const int h = g * a.group + (blockIdx.y % a.head_groups) * HC + rg % HC;
   const int qt = gridDim.x - 1 - blockIdx.x;  // longest walks first
   const int q_lo = a.query_start[s];
   const int q_hi = a.query_start[s + 1];
   const int n = q_hi - q_lo;
   const int ctx = a.context_lens[s];
   const int wg_tok0 = qt * (kRowsPerWave * TW);
-  const int tok0 = wg_tok0 + (wave / HC) * kRowsPerWave;
+  const int tok0 = wg_tok0 + (rg / HC) * kRowsPerWave;
   const bool bad_seq = ctx < 0 || n < 0 || q_lo < 0 || q_hi > a.num_tokens ||
                        (int64_t)ctx + n > (int64_t)a.max_blocks * kBlockTokens;
   // the whole workgroup leaves together (it shares barriers below)
@@ -118,7 +155,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     for (int ct = 0; ct < 2; ++ct) {
       const int row = q_lo + tok0 + 16 * ct + (lane & 15);
       if (!row_ok[ct] || row < 0 || row >= a.num_tokens) continue;
-      float* dst = a.out + ((size_t)row * a.num_heads + h) * D + 4 * lg;
+      float* dst = a.out + ((size_t)row * a.num_heads + h) * D + (D / 2) * dh + 4 * lg;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const f32x4_t v = o[ct][dt] * inv[ct];
@@ -188,27 +225,35 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   // Wave w copies tile w of each step into LDS: K of the step's first block,
   // K of its second, V of the first, V of the second.  Block ids come 64 at a
   // time (lane j holds block seg + j).
-  const char* pool = (wave < 2) ? a.key_cache : a.value_cache;
-  const int my_b = wave & 1;
+  const int my_tile = wave >> 1;         // 0, 1: K of the two blocks; 2, 3: V
+  const char* pool = (my_tile < 2) ? a.key_cache : a.value_cache;
+  const int my_b = my_tile & 1;
+  constexpr int CHW = (CH + 1) / 2;       // 1 KB copies per wave (its half of the tile)
   auto load_ids = [&](int base) { return base + lane < nblk ? table_row[base + lane] : 0; };
   int seg = 0;
   int id_cur = load_ids(0);
   int id_next = load_ids(kWave);
-  auto issue = [&](int step) {
+  // V tiles are stored with the two 16-byte halves of every other group of 8
+  // dims swapped (16-byte chunk c of the tile lands at c ^ ((c >> 4) & 1)), so
+  // that the V operand reads of a half-wave hit distinct banks
+  const int k_src = 16 * lane;
+  const int v_src = 16 * (lane ^ ((lane >> 4) & 1));
+  const int src_off = (my_tile < 2 ? k_src : v_src) + 1024 * CHW * dh;
+  auto issue = [&](int step, char* buf) {
     const int blk = 2 * step + my_b;
     int phys = __builtin_amdgcn_readlane(id_cur, blk - seg);
     const bool live = blk < nblk;
     const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
     bad |= live && !ok;
-    const int bytes = (live && ok) ? kTileBytes : 0;
+    const uint32_t bytes = (live && ok) ? kTileBytes : 0u;
     if (!ok) phys = 0;
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(pool + (size_t)phys * block_stride + head_off), (short)0, bytes, kRsrcWord3);
-    char* dst = kv_lds + (step & 1) * kStepBytes + wave * kTileBytes;
+    const uint64_t base = reinterpret_cast<uint64_t>(pool + (size_t)phys * block_stride + head_off);
+    const u32x4_t rs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base),
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) & 0xffffu,
+                        (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kRsrcWord3};
+    lds_char* lds = (lds_char*)(buf + my_tile * kTileBytes + 1024 * CHW * dh);
 #pragma unroll
-    for (int j = 0; j < kTileBytes / 1024; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16,
-                                              1024 * j + 16 * lane, 0, 0, 0);
+    for (int j = 0; j < CHW; ++j) lds_copy16(lds + 1024 * j, src_off + 1024 * j, rs);
   };
 
   f32x4_t o[2][DT];
@@ -219,25 +264,41 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   float m_ref[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.0f, 0.0f};
 
-  issue(0);
-  for (int st = 0; st < nsteps; ++st) {
-    const int b0 = 2 * st;  // first block of this step
-    // this step's tiles are in LDS once every wave's copies have landed; the
-    // barrier also retires every wave's reads of the buffer the next copies
-    // overwrite (that of step st - 1)
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    if (st + 1 < nsteps) {
-      const int nb0 = b0 + 2;
-      if ((nb0 & (kWave - 1)) == 0) {
-        id_cur = id_next;
-        seg = nb0;
-        id_next = load_ids(seg + kWave);
-      }
-      issue(st + 1);
+  // ids for blocks [seg, seg + 64) are in id_cur; the copies of a step's two
+  // blocks never straddle a segment
+  auto advance_ids = [&](int step) {
+    const int b = 2 * step;
+    if (b >= seg + kWave) {
+      id_cur = id_next;
+      seg += kWave;
+      id_next = load_ids(seg + kWave);
     }
+  };
+  constexpr int kAhead = kBufs - 1;  // steps whose copies are in flight
+  for (int k = 0; k < kAhead && k < nsteps; ++k) {
+    advance_ids(k);
+    issue(k, kv_lds + k * kStepBytes);
+  }
+
+  // One step: wait for its copies (this wave's; the barrier makes every
+  // wave's visible and retires all reads of the buffer the next copies reuse),
+  // start the copies kAhead steps ahead, then the arithmetic.
+  for (int st = 0; st < nsteps; ++st) {
+    const int later = min(kAhead - 1, nsteps - 1 - st);  // steps issued after st
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(kWaitVmLds(2 * CHW));
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(kWaitVmLds(CHW));
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
+    workgroup_barrier();
+    if (st + kAhead < nsteps) {
+      advance_ids(st + kAhead);
+      issue(st + kAhead, kv_lds + ((st + kAhead) % kBufs) * kStepBytes);
+    }
+    const int b0 = 2 * st;  // first block of this step
+    const char* kv = kv_lds + (st % kBufs) * kStepBytes;
     if constexpr (kQInLds) asm volatile("" : "+v"(q_base));
-    const char* kv = kv_lds + (st & 1) * kStepBytes;
 
     // ---- logits S^T for two blocks x two column tiles
     f32x4_t sc[2][2];
@@ -335,7 +396,9 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
           vm[b][1] = (pos + 2 < v_end ? 0xffffu : 0u) | (pos + 3 < v_end ? 0xffff0000u : 0u);
         }
       }
-      const char* vt = kv + 2 * kTileBytes + (lane & 15) * 32 + 8 * lg;
+      // dim d = 16 dt + lane%16, tokens 4 lg ..: chunk 2 d + lg / 2, stored swizzled
+      const char* vt = kv + 2 * kTileBytes + 512 * DT * dh + (lane & 15) * 32 + 16 * ((lg >> 1) ^ ((lane >> 3) & 1)) +
+                       8 * (lg & 1);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vt + 512 * dt);
@@ -354,7 +417,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
       pv(std::true_type{});
     else
       pv(std::false_type{});
-  }
+    }
 
   // every wave's block-id checks count for the whole workgroup's tiles
   bad = __syncthreads_or(bad);
@@ -438,7 +501,7 @@ int prefill_heads_per_wg(int group) {
   return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
 }
 
-int prefill_tokens_per_wg(int group) { return kRowsPerWave * kWaves / prefill_heads_per_wg(group); }
+int prefill_tokens_per_wg(int group) { return kRowsPerWave * kRowGroups / prefill_heads_per_wg(group); }
 
 hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
                           hipStream_t stream) {
