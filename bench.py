@@ -33,7 +33,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn µs/step + achieved KV-read HBM GB/s (% roofline) at 100K ctx"
+PREFILL_METRIC = "prefix (chunked prefill) attention TFLOP/s over a paged KV cache"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 
 
 def kernel_source_hash() -> str:
@@ -111,6 +113,143 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str, copy_mib: int)
     return 0
 
 
+def run_prefill(args) -> int:
+    """One step = the chunk write into the cache plus the prefix attention of
+    every chunk token, for one prefill workload (``--config prefill`` is one
+    8192-token chunk over a 32768-token cached prefix, 24 query / 4 KV heads,
+    head 256, bf16).  The roofline is the bf16 matrix-core peak against the
+    algorithmic flops (4 H D per visible query-key pair)."""
+    import numpy as np
+    import torch
+
+    import decode_attention_paged_05_amd as pad
+    from decode_attention_paged_05_amd import inputs as gen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    pp = gen.make_prefill_problem(args.config)
+    spec, pool = pp.spec, pp.pool
+    t0 = time.perf_counter()
+    x = 16 // 2
+    kc = torch.full((pool.num_blocks, spec.num_kv_heads, spec.head_size // x, 16, x), float("nan"),
+                    dtype=torch.bfloat16, device=dev)
+    vc = torch.full((pool.num_blocks, spec.num_kv_heads, spec.head_size, 16), float("nan"), dtype=torch.bfloat16,
+                    device=dev)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def sink(ids, kb, vb):
+        idx = torch.from_numpy(ids.astype(np.int64)).to(dev)
+        kt, vt = gen.to_tiled(kb, vb, "bf16")
+        kc.index_copy_(0, idx, up(kt))
+        vc.index_copy_(0, idx, up(vt))
+
+    gen.fill_pool(pool, sink)
+    key, value = pp.chunk_kv()
+    q, kd, vd = up(pp.query), up(key), up(value)
+    tables = torch.from_numpy(pool.block_tables).to(dev)
+    qs = torch.from_numpy(pp.query_start).to(dev)
+    ctx = torch.from_numpy(pp.context_lens).to(dev)
+    out = torch.empty(tuple(pp.query.shape), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    flops = pp.flops()
+    desc = (f"{args.config}: {pp.num_seqs} seq, context {list(map(int, pp.context_lens))}, chunk "
+            f"{list(map(int, pp.query_lens))} tokens, {spec.num_heads} q / {spec.num_kv_heads} KV heads, head "
+            f"{spec.head_size}, bf16, block 16, tiled layout")
+    print(f"[bench] {desc}; inputs ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def step(ev=None):
+        pad.paged_attention_prefill_write_kv(kc, vc, kd, vd, tables, qs, ctx, spec.num_kv_heads, 16,
+                                             pp.max_query_len)
+        if ev:
+            ev[0].record()
+        pad.paged_attention_prefill(out, q, kc, vc, tables, qs, ctx, pp.scale, spec.num_kv_heads, 16,
+                                    pp.max_query_len)
+        if ev:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t_start = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / K
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    k_tflops = flops / (k_ms * 1e-3) / 1e12
+
+    max_err, cpu = None, None
+    if not (args.no_parity and args.no_cpu_baseline):
+        import oracle
+
+        got = out.double().cpu().numpy()
+        H, G = spec.num_heads, spec.num_heads // spec.num_kv_heads
+        s0, n0, c0, lo0 = 0, int(pp.query_lens[0]), int(pp.context_lens[0]), int(pp.query_start[0])
+        K0 = [gen.sequence_kv(pool, s0, g) for g in range(spec.num_kv_heads)]
+        rows = sorted({0, 1, 31, 32, n0 // 2, n0 - 33, n0 - 1} & set(range(n0)))
+        heads = (0, G - 1, G, H - 1)
+        t_or = time.perf_counter()
+        done_flops, worst = 0, 0.0
+        first = True
+        while first or (not args.no_cpu_baseline and time.perf_counter() - t_or < args.cpu_seconds):
+            for t in rows:
+                for h in heads:
+                    k_rows, v_rows = K0[h // G]
+                    ref = oracle.prefill_rows(pp.query[lo0 + t:lo0 + t + 1, h], k_rows, v_rows, c0, t, pp.scale,
+                                              "bf16")[0]
+                    if first:
+                        worst = max(worst, float(np.max(np.abs(got[lo0 + t, h] - ref))))
+                    done_flops += 4 * spec.head_size * (c0 + t + 1)
+            first = False
+        total = time.perf_counter() - t_or
+        max_err = worst
+        if not args.no_cpu_baseline:
+            cpu = {"value": round(done_flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{len(rows) * len(heads)} (token, head) output rows of sequence 0 computed one by one "
+                             f"by the fp64 oracle, repeated for {total:.1f} s"}
+    line = {
+        "metric": PREFILL_METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "num_tokens": pp.num_tokens, "algorithmic_flops_per_step": flops,
+                   "accumulate": "fp32", "seed": spec.seed},
+        "kernels_ms": {"prefill": round(k_ms, 4)},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(k_tflops, 2),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(k_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "prefill",
+            "algorithmic_flops_per_launch": flops,
+        },
+        "cpu_baseline": cpu,
+        "max_abs_err_vs_oracle_sampled_rows": max_err,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def describe(p, layout: str = "") -> str:
     lens = p.seq_lens
     L = f"{int(lens[0])} tokens" if (lens == lens[0]).all() else f"{int(lens.min())}-{int(lens.max())} tokens"
@@ -125,7 +264,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="long", help="tiny | short | long | mixed | stress | batch256")
+    ap.add_argument("--config", default="long",
+                    help="decode: tiny | short | long | mixed | stress | batch256; prefill: prefill | prefill_batch")
     ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
     ap.add_argument("--seq-len", type=int, default=None,
                     help="override every sequence's length (table width and pool follow)")
@@ -152,6 +292,9 @@ def main() -> int:
               "the decode path is sharded by sequence or KV head with no exchange, so N GPUs run N "
               "independent copies of this step", file=sys.stderr)
         return 2
+
+    if args.config.startswith("prefill"):
+        return run_prefill(args)
 
     import numpy as np
     import torch

@@ -25,7 +25,7 @@
 //     tiled K layout), B = Q^T (columns = query rows: registers, or for D = 256
 //     the wave's own LDS slice), contracting over D;
 //   * masks keys beyond each row's position (logit -inf by select) and updates
-//     each row's running max (in-lane over 8 keys, then two xor shuffles),
+//     each row's running max (in-lane over 8 keys, then two lane swaps),
 //     exp2-domain with a lazy reference: the accumulator is rescaled only when
 //     a row's max grows by more than 2^8;
 //   * accumulates O^T += V^T P^T on the same MFMA: A = V^T (rows = dims; lane
@@ -67,6 +67,36 @@ constexpr int kKvPolicy = 0;
 // head sizes from which the Q operand lives in LDS rather than registers
 #define PAD_PREFILL_Q_LDS_MIN_D 512
 #endif
+
+// Reductions over the lanes l, l^16, l^32, l^48 (the four lane groups that
+// hold one row), on the vector ALU: v_permlane16_swap / v_permlane32_swap
+// given the same values in both registers leave (rows of 16 lanes) the even
+// and the odd rows, resp. the low and the high half, in both halves.  Issued
+// as inline assembly with both registers as explicit in-out operands (this
+// compiler's lowering of the two-result builtin reads the first result twice),
+// after the two wait states a vector-ALU write of an operand needs.
+__device__ inline void swap16(float v, float& lo_rows, float& hi_rows) {
+  lo_rows = v;
+  hi_rows = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(lo_rows), "+v"(hi_rows));
+}
+__device__ inline void swap32(float v, float& lo_half, float& hi_half) {
+  lo_half = v;
+  hi_half = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo_half), "+v"(hi_half));
+}
+__device__ inline float group_max(float v) {
+  float a, b;
+  swap16(v, a, b);
+  swap32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ inline float group_sum(float v) {
+  float a, b;
+  swap16(v, a, b);
+  swap32(a + b, a, b);
+  return a + b;
+}
 
 // s_waitcnt immediate: at most n vector-memory loads outstanding and every
 // LDS access done (export counter left at its maximum)
@@ -343,8 +373,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
             }
             bm[ct] = fmaxf(bm[ct], x[b][ct][i]);
           }
-        bm[ct] = fmaxf(bm[ct], __shfl_xor(bm[ct], 16));
-        bm[ct] = fmaxf(bm[ct], __shfl_xor(bm[ct], 32));
+        bm[ct] = group_max(bm[ct]);
       }
     };
     if (diag)
@@ -424,9 +453,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   float inv[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
-    float l = l_run[ct];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = group_sum(l_run[ct]);
     inv[ct] = bad ? NAN : 1.0f / l;
   }
   store_rows(o, inv);
