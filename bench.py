@@ -39,9 +39,12 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources that determine the decode kernels' code (phase 1, the
+    merge, their launchers and shared definitions)."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "decode_attention_paged_05_amd", "csrc", "*"))
-                   + glob.glob(os.path.join(ROOT, "include", "*.h")))
+    csrc = os.path.join(ROOT, "decode_attention_paged_05_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "pad_attn*")) +
+                   [os.path.join(csrc, n) for n in ("pad_kernels.hip", "pad_internal.h")])
     for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())

@@ -9,6 +9,7 @@
 #include "paged_attention_decode.h"
 #include "paged_attention_prefill.h"
 #include "pad_internal.h"
+#include "pad_prefill_internal.h"
 
 namespace {
 

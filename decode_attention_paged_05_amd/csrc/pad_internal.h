@@ -75,53 +75,6 @@ hipError_t launch_one_pass(const Plan& plan, float* out, const void* query,
                            const int32_t* block_tables, const int32_t* seq_lens,
                            hipStream_t stream);
 
-// Prefix (chunked prefill) attention and the chunk write (pad_prefill.hip).
-constexpr int kKvRows = 0;   // PAD_KV_ROWS
-constexpr int kKvTiled = 1;  // PAD_KV_TILED
-
-struct PrefillArgs {
-  float* out;                  // [T, H, D]
-  const char* query;           // bf16 [T, H, D]
-  const char* key_cache;       // bf16, tiled layout
-  const char* value_cache;
-  const int32_t* block_tables; // [S, W]
-  const int32_t* query_start;  // [S + 1]
-  const int32_t* context_lens; // [S]
-  float qscale;                // softmax scale (the launcher folds in log2(e))
-  int num_tokens;              // T
-  int num_heads;               // H
-  int num_kv_heads;            // Hkv
-  int group;                   // H / Hkv
-  int head_groups;             // workgroups per KV head along the heads (set by the launcher)
-  int max_blocks;              // W
-  int64_t num_blocks;          // NB
-};
-
-struct WriteKvArgs {
-  char* key_cache;             // [NB, Hkv, ...] in the cache layout
-  char* value_cache;
-  const char* key;             // [T, Hkv, D]
-  const char* value;
-  const int32_t* block_tables;
-  const int32_t* query_start;
-  const int32_t* context_lens;
-  int num_tokens;
-  int num_kv_heads;
-  int head_size;
-  int max_blocks;
-  int64_t num_blocks;
-};
-
-// Query heads and chunk tokens one prefill workgroup serves.
-int prefill_heads_per_wg(int group);
-int prefill_tokens_per_wg(int group);
-
-hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
-                          hipStream_t stream);
-
-hipError_t launch_write_kv(const WriteKvArgs& args, int num_seqs, int max_query_len, int elem_bytes, int layout,
-                           hipStream_t stream);
-
 hipError_t launch_workspace_fill(float* max_logits, float* exp_sums, float* tmp_out,
                                  size_t n_stats, size_t n_tmp, unsigned* counters,
                                  size_t n_counters, hipStream_t stream);

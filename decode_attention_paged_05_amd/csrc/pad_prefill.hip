@@ -43,7 +43,7 @@
 
 #include <type_traits>
 
-#include "pad_internal.h"
+#include "pad_prefill_internal.h"
 
 namespace pad {
 namespace {
@@ -60,9 +60,6 @@ constexpr int kRowsPerWave = 32;   // two 16-row column tiles
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.0f;  // headroom of the lazy softmax reference
-// cache-policy bits of the K/V loads: default (every workgroup of a sequence
-// re-reads its keys, so they should stay in the caches)
-constexpr int kKvPolicy = 0;
 #ifndef PAD_PREFILL_Q_LDS_MIN_D
 // head sizes from which the Q operand lives in LDS rather than registers
 #define PAD_PREFILL_Q_LDS_MIN_D 512
