@@ -14,7 +14,7 @@ import torch
 import decode_attention_paged_05_amd as pad
 import oracle
 from decode_attention_paged_05_amd import inputs as gen
-from tests.gpu_util import TOL, DeviceProblem, require_gpu, to_device, torch_dtype, tiled_shapes
+from tests.gpu_util import TOL, DeviceProblem, require_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -225,3 +225,71 @@ def test_prefill_rejects_unsupported():
     with pytest.raises(pad.PadError):
         pad.paged_attention_prefill(out, dp.query, dp.dp.kc, dp.dp.vc, dp.dp.tables, dp.qs, dp.ctx, pp.scale, 4, 16,
                                     pp.max_query_len)
+
+
+def test_prefill_graph_capture_replays():
+    """The chunk write and the prefix attention captured in a HIP graph: every
+    replay, with eager work and synchronisation in between, equals the eager
+    result bitwise (no memset nodes, no host-side state)."""
+    pp = gen.make_prefill_problem("prefill_small")
+    dp = DevicePrefill(pp)
+    key, value = pp.chunk_kv()
+    kd, vd = to_device(key, "bf16"), to_device(value, "bf16")
+    eager = dp.run()
+    out = torch.empty_like(eager)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+
+    def step():
+        pad.paged_attention_prefill_write_kv(dp.dp.kc, dp.dp.vc, kd, vd, dp.dp.tables, dp.qs, dp.ctx, 4, 16,
+                                             pp.max_query_len)
+        pad.paged_attention_prefill(out, dp.query, dp.dp.kc, dp.dp.vc, dp.dp.tables, dp.qs, dp.ctx, pp.scale, 4,
+                                    16, pp.max_query_len)
+
+    with torch.cuda.stream(stream):
+        step()  # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+    for r in range(4):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs from the eager result"
+        assert torch.equal(dp.run(), eager)
+    assert max_err(out, dp.oracle()) <= TOL["bf16"]
+
+
+def test_prefill_two_streams():
+    """Two prefill calls in flight at once on two streams: both exact."""
+    a = DevicePrefill(gen.make_prefill_problem("prefill_small"))
+    b = DevicePrefill(gen.make_prefill_problem(gen.PrefillSpec(
+        "b", context_lens=(300, 0, 77), query_lens=(200, 333, 64), num_heads=24, num_kv_heads=4, head_size=256,
+        dtype="bf16", seed=41)))
+    ra, rb = a.oracle(), b.oracle()
+    oa = torch.empty(tuple(a.pp.query.shape), dtype=torch.float32, device="cuda")
+    ob = torch.empty(tuple(b.pp.query.shape), dtype=torch.float32, device="cuda")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for dp, o, st in ((a, oa, sa), (b, ob, sb)):
+            with torch.cuda.stream(st):
+                pp = dp.pp
+                pad.paged_attention_prefill(o, dp.query, dp.dp.kc, dp.dp.vc, dp.dp.tables, dp.qs, dp.ctx, pp.scale,
+                                            4, 16, pp.max_query_len)
+    torch.cuda.synchronize()
+    assert max_err(oa, ra) <= TOL["bf16"]
+    assert max_err(ob, rb) <= TOL["bf16"]
+
+
+def test_prefill_long_chunk_no_context_sampled():
+    """A 16384-token chunk with no cached context (the raised batched-token
+    budget of the serving configuration): plain causal attention, the largest
+    launch grid; sampled rows against the oracle."""
+    spec = gen.PrefillSpec("chunk16k", context_lens=(0,), query_lens=(16384,), num_heads=24, num_kv_heads=4,
+                           head_size=256, dtype="bf16", seed=42)
+    pp = gen.make_prefill_problem(spec)
+    dp = DevicePrefill(pp, keep_host=False)
+    got = dp.run()
+    assert bool(torch.isfinite(got).all())
+    assert _sampled_check(pp, got, _edge_rows, heads=(0, 11, 23)) <= TOL["bf16"]
