@@ -12,31 +12,34 @@
 // tiles and then the chunk tiles with an online softmax; this kernel walks the
 // same keys as one range, in 32-key steps, with the same running max / sum.
 //
-// Work decomposition.  A workgroup of 4 waves serves one (sequence, KV head,
-// HC query heads of its group, 32 * 4 / HC chunk tokens); each wave owns 32
-// query rows: 32 consecutive chunk tokens of one head, as two 16-row column
-// tiles.  The workgroup walks the keys its last row can see in 32-key steps
-// (two 16-token blocks).  Each step's K and V tiles are copied from the pool
-// into LDS by direct-to-LDS buffer loads (one tile per wave, 16 bytes per lane
-// per load, double-buffered so the next step's copies overlap this step's
-// arithmetic; one barrier per step).  Each wave then:
+// Work decomposition.  A workgroup of 8 waves serves one (sequence, KV head,
+// HC query heads of its group, 128 / HC chunk tokens): four row groups of 32
+// query rows (32 consecutive chunk tokens of one head, as two 16-row column
+// tiles), each owned by a pair of waves; both waves of a pair form the
+// logits over all of D, and each accumulates the output for one half of D.
+// The workgroup walks the keys its last row can see in 32-key steps (two
+// 16-token blocks).  Each step's two K and two V tiles are copied from the
+// pool into LDS by direct-to-LDS buffer loads (each wave half a tile, 16 bytes
+// per lane per load) into a ring of four step buffers, three steps ahead of
+// the arithmetic; one barrier per step.  Each wave then:
 //   * forms S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = K (rows = keys; lane
 //     l reads key l%16 and 8 consecutive dims, one 16-byte LDS read of the
-//     tiled K layout), B = Q^T (columns = query rows: registers, or for D = 256
-//     the wave's own LDS slice), contracting over D;
+//     tiled K layout), B = Q^T (columns = query rows, in registers),
+//     contracting over D;
 //   * masks keys beyond each row's position (logit -inf by select) and updates
 //     each row's running max (in-lane over 8 keys, then two lane swaps),
 //     exp2-domain with a lazy reference: the accumulator is rescaled only when
 //     a row's max grows by more than 2^8;
-//   * accumulates O^T += V^T P^T on the same MFMA: A = V^T (rows = dims; lane
-//     l reads dim l%16 and 4 consecutive tokens of each block, two 8-byte LDS
-//     reads of the tiled V layout), B = P^T (exactly the lane layout the
-//     logits came out in).  p is split into bf16 hi + lo (two MFMAs), ~2^-16
-//     relative precision.  Lane l holds output dims of row l%16, so the
-//     softmax state and the rescale stay in the lane.
-// V elements at positions the sequence does not hold are zeroed before the
-// MFMA, so NaN padding never reaches a row.  Masking runs only on the steps
-// that need it (the diagonal, the end of the sequence), in separate code.
+//   * accumulates O^T += V^T P^T for its half of D on the same MFMA: A = V^T
+//     (rows = dims; lane l reads dim l%16 and 4 consecutive tokens of each
+//     block, two 8-byte LDS reads of the tiled V layout, stored swizzled so
+//     that a half-wave's reads hit distinct banks), B = P^T (exactly the lane
+//     layout the logits came out in).  p is split into bf16 hi + lo (two
+//     MFMAs), ~2^-16 relative precision.  Lane l holds output dims of row
+//     l%16, so the softmax state and the rescale stay in the lane.
+// V elements at positions the walk does not hold are zeroed before the MFMA,
+// so NaN padding never reaches a row.  Masking runs only on the steps that
+// need it (the diagonal, the end of the walk), in separate code.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -60,10 +63,6 @@ constexpr int kRowsPerWave = 32;   // two 16-row column tiles
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.0f;  // headroom of the lazy softmax reference
-#ifndef PAD_PREFILL_Q_LDS_MIN_D
-// head sizes from which the Q operand lives in LDS rather than registers
-#define PAD_PREFILL_Q_LDS_MIN_D 512
-#endif
 
 // Reductions over the lanes l, l^16, l^32, l^48 (the four lane groups that
 // hold one row), on the vector ALU: v_permlane16_swap / v_permlane32_swap
@@ -142,11 +141,9 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   constexpr int DT = D / 32;             // 16-dim output tiles of this wave's half of D
   constexpr int kTileBytes = kBlockTokens * D * 2;
   constexpr int kStepBytes = 4 * kTileBytes;  // K and V of two blocks
-  constexpr bool kQInLds = D >= PAD_PREFILL_Q_LDS_MIN_D;  // Q operand re-read from LDS each step
   constexpr int CH = kTileBytes / 1024;  // 1 KB copies per tile (one per load instruction)
   constexpr int kBufs = 4;               // step buffers: copies run kBufs - 1 steps ahead
   __shared__ __attribute__((aligned(16))) char kv_lds[kBufs * kStepBytes];
-  __shared__ u32x4_t q_lds[kQInLds ? kWaves * 2 * KS * kWave : 1];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -202,10 +199,9 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     return;
   }
 
-  // Q^T operand: column tile ct, step ks -> row's dims 32 ks + 8 lg .. + 8.
-  // Held in registers, or (kQInLds) in this wave's own LDS slice and re-read
-  // every step, which keeps the largest head size within the register file.
-  u32x4_t qop[kQInLds ? 1 : 2][KS];
+  // Q^T operand, held in registers for the whole walk: column tile ct, step
+  // ks -> the row's dims 32 ks + 8 lg .. + 8
+  u32x4_t qop[2][KS];
   {
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(a.query), (short)0, (int)((size_t)a.num_tokens * a.num_heads * D * 2), kRsrcWord3);
@@ -215,23 +211,11 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
       const int off = ((row * a.num_heads + h) * D + 8 * lg) * 2;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * ks, 0, 0);
-        v = row_ok[ct] ? v : u32x4_t{0u, 0u, 0u, 0u};
-        if constexpr (kQInLds)
-          q_lds[((wave * 2 + ct) * KS + ks) * kWave + lane] = v;
-        else
-          qop[ct][ks] = v;
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * ks, 0, 0);
+        qop[ct][ks] = row_ok[ct] ? v : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
   }
-  // per-step LDS index, opaque to the compiler so the reads stay in the loop
-  int q_base = wave * 2 * KS * kWave + lane;
-  auto q_operand = [&](int ct, int ks) -> u32x4_t {
-    if constexpr (kQInLds)
-      return q_lds[q_base + (ct * KS + ks) * kWave];
-    else
-      return qop[ct][ks];
-  };
 
   // keys the workgroup walks: up to its last row's position; each wave masks
   // to its own rows
@@ -325,7 +309,6 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     }
     const int b0 = 2 * st;  // first block of this step
     const char* kv = kv_lds + (st % kBufs) * kStepBytes;
-    if constexpr (kQInLds) asm volatile("" : "+v"(q_base));
 
     // ---- logits S^T for two blocks x two column tiles
     f32x4_t sc[2][2];
@@ -341,7 +324,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
         kf[b] = *reinterpret_cast<const u32x4_t*>(kv + b * kTileBytes + 1024 * ks + 16 * lane);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const u32x4_t qf = q_operand(ct, ks);
+        const u32x4_t qf = qop[ct][ks];
 #pragma unroll
         for (int b = 0; b < 2; ++b) sc[b][ct] = mfma_bf16(kf[b], qf, sc[b][ct]);
       }
