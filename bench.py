@@ -218,6 +218,7 @@ def run_prefill(args) -> int:
         max_err = worst
         if not args.no_cpu_baseline:
             cpu = {"value": round(done_flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                   "cpu_model": cpu_model(),
                    "sample": f"{len(rows) * len(heads)} (token, head) output rows of sequence 0 computed one by one "
                              f"by the fp64 oracle, repeated for {total:.1f} s"}
     line = {
@@ -251,6 +252,17 @@ def run_prefill(args) -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def describe(p, layout: str = "") -> str:
@@ -437,6 +449,31 @@ def main() -> int:
     k1_gbs = kv_bytes / (k1_ms * 1e-3) / 1e9
     traffic = load_traffic(args.config)
 
+    # ---- warm figure: the same steps on one pool copy only (labelled warm; the
+    # pool still exceeds the 256 MB memory-side cache when it is larger) ----
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(K):
+        step(0)
+    torch.cuda.synchronize()
+    ms_warm = (time.perf_counter() - t_start) * 1e3 / K
+
+    # ---- a measured HBM reference: one 1 GiB device-to-device copy (read plus
+    # write bytes over its time), next to the published 8 TB/s ----
+    n_copy = 1 << 30
+    src = torch.empty(n_copy, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    c1.record()
+    c1.synchronize()
+    copy_gbs = 3 * 2 * n_copy / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
     # ---- oracle: parity of the timed output and the CPU baseline ---------------
     max_err = None
     cpu = None
@@ -467,7 +504,7 @@ def main() -> int:
                 total += time.perf_counter() - t_or
                 reps += 1
             cpu = {"value": round(reps * kv_bytes / total / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
-                   "kind": "oracle",
+                   "kind": "oracle", "cpu_model": cpu_model(),
                    "sample": f"{reps} full steps of the same workload ({describe(p, args.layout)}) in {total:.1f} s, "
                              f"fp64 NumPy, {int(blas_threads)} BLAS threads; "
                              f"{total / reps * 1e6:.0f} us per step"}
@@ -504,6 +541,8 @@ def main() -> int:
         "kernels_ms": {"phase1" if P else "one_pass": round(k1_ms, 5), **({"phase2": round(k2_ms, 5)} if P else {})},
         "ms_per_step_with_kernel_events": round(ms_with_events, 5),
         "event_step_us_p10_p50_p90": pcts,
+        "us_per_step_warm_one_pool_copy": round(ms_warm * 1e3, 2),
+        "measured_copy_gbs_read_plus_write": round(copy_gbs, 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(k1_gbs, 2),
