@@ -28,17 +28,18 @@ hipError_t launch_attn_f32_tiled_one_pass(const AttnParams& a, int d, int gh, in
 namespace {
 
 // ---------------------------------------------------------------------------
-// Phase 2: log-sum-exp merge.  Grid (D/64, H, S), 256 or 64 threads (G = 16
-// or 4 source groups); the workgroup owns 64 dims of one (sequence, head).
-// Thread t = 16 g + l takes dims 4 l .. 4 l + 3 of sources g, g + G,
-// g + 2 G, ... (a source is a partition entry or a chunk entry).  Sources are
-// taken 16 G at a time and every load of a round -- each source's max and
-// exp-sum and its four dims -- is issued before any arithmetic (the merge is
-// latency-bound, not bandwidth-bound).  Each thread keeps a running max,
-// exp-sum and weighted row over its own sources; one barrier later, 16
-// threads combine the G source groups by the same log-sum-exp rule.  Slots past the sequence's
-// source count are read (they exist) but discarded by select, so stale or NaN
-// contents never enter the sums.
+// Phase 2: log-sum-exp merge.  Grid (D / kDims, H, S), kThreads threads (one
+// wave or four); the workgroup owns kDims dims of one (sequence, head), as
+// kDims / 4 dim lanes (4 dims each) x G source groups.  Thread t = kDims/4 g + l
+// takes dims 4 l .. 4 l + 3 of sources g, g + G, g + 2 G, ... (a source is a
+// partition entry or a chunk entry).  Every load of a round -- each source's
+// max and exp-sum and its four dims -- is issued before any arithmetic (the
+// merge is latency-bound, not bandwidth-bound).  Each thread keeps a running
+// max, exp-sum and weighted row over its own sources; the source groups are
+// then combined by the same log-sum-exp rule, by shuffles within a wave and
+// through LDS across waves.  Slots past the sequence's source count are read
+// (they exist) but discarded by select, so stale or NaN contents never enter
+// the sums.
 // ---------------------------------------------------------------------------
 struct MergeParams {
   float* out;
@@ -404,6 +405,10 @@ hipError_t launch_one_pass(const Plan& plan, float* out, const void* query, cons
                          : launch_attn_bf16_rows_one_pass(a, plan.head_size, gh, waves, grid, stream);
 }
 
+#ifndef PAD_MERGE_SHAPE
+#define PAD_MERGE_SHAPE 0  // 0: chosen per launch below
+#endif
+
 hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens, hipStream_t stream) {
   MergeParams m{};
   m.out = out;
@@ -429,17 +434,36 @@ hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens, 
   m.queue_info = plan.counters + kQueueInfoOffset;
   const dim3 grid(plan.head_size / 64, plan.num_heads, plan.num_seqs);
   void* args[] = {&m};
-  // one wave of 64 dims for tables of at most 64 partitions; otherwise 256
-  // threads on the narrowest dim slice that keeps the grid to about three
-  // workgroups per compute unit (more, smaller workgroups share the latency)
-  if (plan.num_partitions <= 64)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<64, 64>), grid, dim3(64), args, 0, stream);
+#if PAD_MERGE_SHAPE
+  // fixed shape (tuning builds): 1 <64,64>, 2 <256,16>, 3 <256,32>, 4 <256,64>, 5 <64,16>, 6 <64,32>
+  {
+    const void* k = PAD_MERGE_SHAPE == 1 ? reinterpret_cast<const void*>(&merge_kernel<64, 64>)
+                  : PAD_MERGE_SHAPE == 2 ? reinterpret_cast<const void*>(&merge_kernel<256, 16>)
+                  : PAD_MERGE_SHAPE == 3 ? reinterpret_cast<const void*>(&merge_kernel<256, 32>)
+                  : PAD_MERGE_SHAPE == 4 ? reinterpret_cast<const void*>(&merge_kernel<256, 64>)
+                  : PAD_MERGE_SHAPE == 5 ? reinterpret_cast<const void*>(&merge_kernel<64, 16>)
+                                         : reinterpret_cast<const void*>(&merge_kernel<64, 32>);
+    const int dims = (PAD_MERGE_SHAPE == 2 || PAD_MERGE_SHAPE == 5) ? 16 : (PAD_MERGE_SHAPE == 3 || PAD_MERGE_SHAPE == 6) ? 32 : 64;
+    const int threads = (PAD_MERGE_SHAPE == 1 || PAD_MERGE_SHAPE >= 5) ? 64 : 256;
+    return hipLaunchKernel(k, dim3(plan.head_size / dims, plan.num_heads, plan.num_seqs), dim3(threads), args, 0,
+                           stream);
+  }
+#endif
+  // Measured on 256 compute units (phase 2 alone): one wave on 32 dims for
+  // tables of at most 64 partitions (a batch of 32 sequences up to 32K tokens:
+  // 22 us against 27 us with 64 dims); otherwise 256 threads on 16 dims while
+  // the grid stays within about three workgroups per compute unit (one 100K
+  // sequence), on 32 dims up to about eight (8 x 131072 tokens, MHA: 17.5 us
+  // against 19 us with 64 dims), else on 64 dims.
   const int64_t rows = (int64_t)plan.num_heads * plan.num_seqs;
-  const int64_t budget = 3 * (int64_t)device_cus();
-  if (rows * (plan.head_size / 16) <= budget)
+  const int64_t cus = device_cus();
+  if (plan.num_partitions <= 64)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<64, 32>),
+                           dim3(plan.head_size / 32, plan.num_heads, plan.num_seqs), dim3(64), args, 0, stream);
+  if (rows * (plan.head_size / 16) <= 3 * cus)
     return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<256, 16>),
                            dim3(plan.head_size / 16, plan.num_heads, plan.num_seqs), dim3(256), args, 0, stream);
-  if (rows * (plan.head_size / 32) <= budget)
+  if (rows * (plan.head_size / 32) <= 8 * cus)
     return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<256, 32>),
                            dim3(plan.head_size / 32, plan.num_heads, plan.num_seqs), dim3(256), args, 0, stream);
   return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<256, 64>), grid, dim3(256), args, 0, stream);
