@@ -15,17 +15,20 @@
 // Work decomposition.  A workgroup of 8 waves serves one (sequence, KV head,
 // HC query heads of its group, 128 / HC chunk tokens): four row groups of 32
 // query rows (32 consecutive chunk tokens of one head, as two 16-row column
-// tiles), each owned by a pair of waves; both waves of a pair form the
-// logits over all of D, and each accumulates the output for one half of D.
-// The workgroup walks the keys its last row can see in 32-key steps (two
-// 16-token blocks).  Each step's two K and two V tiles are copied from the
-// pool into LDS by direct-to-LDS buffer loads (each wave half a tile, 16 bytes
-// per lane per load) into a ring of four step buffers, three steps ahead of
-// the arithmetic; one barrier per step.  Each wave then:
-//   * forms S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = K (rows = keys; lane
-//     l reads key l%16 and 8 consecutive dims, one 16-byte LDS read of the
-//     tiled K layout), B = Q^T (columns = query rows, in registers),
-//     contracting over D;
+// tiles), each owned by a pair of waves.  The workgroup walks the keys its
+// last row can see in 32-key steps (two 16-token blocks).  Each wave of a
+// pair forms the logits of one of the step's two blocks, over all of D, and
+// leaves them in LDS for its partner; both then run the softmax over the whole
+// step, and each accumulates the output for one half of D.  The logits are
+// formed one step ahead, so the step barrier that every workgroup needs
+// anyway also orders the exchange.  Each step's two K and two V tiles are
+// copied from the pool into LDS by direct-to-LDS buffer loads (each wave half
+// a tile, 16 bytes per lane per load) into a ring of three step buffers; one
+// barrier per step.  Each wave:
+//   * forms S^T = K Q^T for its block of step st + 1 on
+//     v_mfma_f32_16x16x32_bf16: A = K (rows = keys; lane l reads key l%16 and
+//     8 consecutive dims, one 16-byte LDS read of the tiled K layout), B = Q^T
+//     (columns = query rows, in registers), contracting over D;
 //   * masks keys beyond each row's position (logit -inf by select) and updates
 //     each row's running max (in-lane over 8 keys, then two lane swaps),
 //     exp2-domain with a lazy reference: the accumulator is rescaled only when
@@ -142,8 +145,12 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   constexpr int kTileBytes = kBlockTokens * D * 2;
   constexpr int kStepBytes = 4 * kTileBytes;  // K and V of two blocks
   constexpr int CH = kTileBytes / 1024;  // 1 KB copies per tile (one per load instruction)
-  constexpr int kBufs = 4;               // step buffers: copies run kBufs - 1 steps ahead
+  // step buffers: in iteration st the arithmetic reads V of step st and K of
+  // step st + 1, and the copies of step st + 2 are in flight
+  constexpr int kBufs = 3;
   __shared__ __attribute__((aligned(16))) char kv_lds[kBufs * kStepBytes];
+  // the logits a wave leaves for its partner: [step parity][row group][block][column tile][lane]
+  __shared__ f32x4_t xs_lds[2][kRowGroups][2][2][kWave];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -285,50 +292,59 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
       id_next = load_ids(seg + kWave);
     }
   };
-  constexpr int kAhead = kBufs - 1;  // steps whose copies are in flight
-  for (int k = 0; k < kAhead && k < nsteps; ++k) {
+  // S^T of block `kb` of a step (its 16 keys x the wave's 32 rows, over all
+  // of D): the A operand comes straight from the step's K tile in LDS
+  const int kb = dh;  // the block of every step whose logits this wave forms
+  auto qk_block = [&](const char* kv, f32x4_t* r) {
+    r[0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    r[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kv + kb * kTileBytes + 1024 * ks + 16 * lane);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) r[ct] = mfma_bf16(kf, qop[ct][ks], r[ct]);
+    }
+  };
+  constexpr int kLead = kBufs - 1;  // iteration st issues the copies of step st + kLead
+  for (int k = 0; k < kLead && k < nsteps; ++k) {
     advance_ids(k);
     issue(k, kv_lds + k * kStepBytes);
   }
+  // step 0's logits
+  if (nsteps > 1)
+    __builtin_amdgcn_s_waitcnt(kWaitVmLds(CHW));
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
+  workgroup_barrier();
+  {
+    f32x4_t first[2];
+    qk_block(kv_lds, first);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) xs_lds[0][rg][kb][ct][lane] = first[ct];
+  }
 
-  // One step: wait for its copies (this wave's; the barrier makes every
-  // wave's visible and retires all reads of the buffer the next copies reuse),
-  // start the copies kAhead steps ahead, then the arithmetic.
+  // Iteration st: wait for the copies of step st + 1 (this wave's; the
+  // barrier makes every wave's visible, publishes every wave's logits of step
+  // st, and retires all reads of the buffer the next copies reuse), start the
+  // copies of step st + 2, then the softmax of step st, this wave's logits of
+  // step st + 1 and the P.V of step st.
   for (int st = 0; st < nsteps; ++st) {
-    const int later = min(kAhead - 1, nsteps - 1 - st);  // steps issued after st
-    if (later >= 2)
-      __builtin_amdgcn_s_waitcnt(kWaitVmLds(2 * CHW));
-    else if (later == 1)
-      __builtin_amdgcn_s_waitcnt(kWaitVmLds(CHW));
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
+    __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
     workgroup_barrier();
-    if (st + kAhead < nsteps) {
-      advance_ids(st + kAhead);
-      issue(st + kAhead, kv_lds + ((st + kAhead) % kBufs) * kStepBytes);
+    if (st + kLead < nsteps) {
+      advance_ids(st + kLead);
+      issue(st + kLead, kv_lds + ((st + kLead) % kBufs) * kStepBytes);
     }
     const int b0 = 2 * st;  // first block of this step
     const char* kv = kv_lds + (st % kBufs) * kStepBytes;
 
-    // ---- logits S^T for two blocks x two column tiles
+    // ---- logits S^T of the step: two blocks x two column tiles, one block
+    // formed by each wave of the pair
     f32x4_t sc[2][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) sc[b][ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t kf[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        kf[b] = *reinterpret_cast<const u32x4_t*>(kv + b * kTileBytes + 1024 * ks + 16 * lane);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const u32x4_t qf = qop[ct][ks];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) sc[b][ct] = mfma_bf16(kf[b], qf, sc[b][ct]);
-      }
-    }
+      for (int ct = 0; ct < 2; ++ct) sc[b][ct] = xs_lds[st & 1][rg][b][ct][lane];
 
     // ---- mask, running max, weights.  Only steps that reach the wave's first
     // row position (the diagonal) or the end of the keys need the mask.
@@ -393,6 +409,16 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
       p_lo[ct] = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
     }
 
+    // ---- this wave's logits of the next step, for the pair (issued after
+    // the softmax, so that the matrix cores work through them while P.V's
+    // operands are read)
+    if (st + 1 < nsteps) {
+      f32x4_t next[2];
+      qk_block(kv_lds + ((st + 1) % kBufs) * kStepBytes, next);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) xs_lds[(st + 1) & 1][rg][kb][ct][lane] = next[ct];
+    }
+
     // ---- O^T += V^T P^T.  V elements at positions the walk does not hold are
     // zeroed: p is 0 there, but 0 * NaN would poison the row.
     auto pv = [&](auto masked) {
@@ -426,7 +452,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
       pv(std::true_type{});
     else
       pv(std::false_type{});
-    }
+  }
 
   // every wave's block-id checks count for the whole workgroup's tiles
   bad = __syncthreads_or(bad);
