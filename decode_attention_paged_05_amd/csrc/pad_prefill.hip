@@ -17,7 +17,7 @@
 // query rows (32 consecutive chunk tokens of one head, as two 16-row column
 // tiles), each owned by a pair of waves.  The workgroup walks the keys its
 // last row can see in 32-key steps (two 16-token blocks).  Each wave of a
-// pair forms the logits of one of the step's two blocks, over all of D, and
+// pair forms the logits of half of the step's keys, over all of D, and
 // leaves them in LDS for its partner; both then run the softmax over the whole
 // step, and each accumulates the output for one half of D.  The logits are
 // formed one step ahead, so the step barrier that every workgroup needs
@@ -25,21 +25,24 @@
 // copied from the pool into LDS by direct-to-LDS buffer loads (each wave half
 // a tile, 16 bytes per lane per load) into a ring of three step buffers; one
 // barrier per step.  Each wave:
-//   * forms S^T = K Q^T for its block of step st + 1 on
-//     v_mfma_f32_16x16x32_bf16: A = K (rows = keys; lane l reads key l%16 and
-//     8 consecutive dims, one 16-byte LDS read of the tiled K layout), B = Q^T
-//     (columns = query rows, in registers), contracting over D;
+//   * forms its 16 x 32 tile of S^T = K Q^T for step st + 1 on
+//     v_mfma_f32_16x16x32_bf16: A = K (rows = keys; lane l reads one key and 8
+//     consecutive dims, one 16-byte LDS read of the tiled K layout), B = Q^T
+//     (columns = query rows, in registers), contracting over D.  The keys are
+//     dealt to tile rows so that lane group g ends up holding, over the two
+//     tiles, the 8 consecutive keys 8 (g & 1) .. of block g >> 1;
 //   * masks keys beyond each row's position (logit -inf by select) and updates
 //     each row's running max (in-lane over 8 keys, then two lane swaps),
 //     exp2-domain with a lazy reference: the accumulator is rescaled only when
-//     a row's max grows by more than 2^8;
+//     a row's max grows by more than 2^8.  The scale enters through the exp2
+//     argument (one FMA per logit); the launcher makes it positive;
 //   * accumulates O^T += V^T P^T for its half of D on the same MFMA: A = V^T
-//     (rows = dims; lane l reads dim l%16 and 4 consecutive tokens of each
-//     block, two 8-byte LDS reads of the tiled V layout, stored swizzled so
-//     that a half-wave's reads hit distinct banks), B = P^T (exactly the lane
-//     layout the logits came out in).  p is split into bf16 hi + lo (two
-//     MFMAs), ~2^-16 relative precision.  Lane l holds output dims of row
-//     l%16, so the softmax state and the rescale stay in the lane.
+//     (rows = dims; lane l reads dim l%16 and the same 8 keys, one 16-byte
+//     LDS read of the tiled V layout, stored swizzled so that a lane group's
+//     reads hit distinct banks), B = P^T (exactly the lane layout the logits
+//     came out in).  p is split into bf16 hi + lo (two MFMAs), ~2^-16
+//     relative precision.  Lane l holds output dims of row l%16, so the
+//     softmax state and the rescale stay in the lane.
 // V elements at positions the walk does not hold are zeroed before the MFMA,
 // so NaN padding never reaches a row.  Masking runs only on the steps that
 // need it (the diagonal, the end of the walk), in separate code.
@@ -57,7 +60,6 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
-typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 
 constexpr int kWave = 64;
 constexpr int kWaves = 8;          // waves per workgroup: 4 row groups x 2 halves of D
@@ -143,7 +145,10 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   constexpr int KS = D / 32;             // QK steps (32 dims each)
   constexpr int DT = D / 32;             // 16-dim output tiles of this wave's half of D
   constexpr int kTileBytes = kBlockTokens * D * 2;
-  constexpr int kStepBytes = 4 * kTileBytes;  // K and V of two blocks
+  // tiles sit 64 bytes apart in the LDS bank space, so that the K reads of the
+  // two blocks' keys in one lane group hit distinct banks
+  constexpr int kTileStride = kTileBytes + 64;
+  constexpr int kStepBytes = 4 * kTileStride;  // K and V of two blocks
   constexpr int CH = kTileBytes / 1024;  // 1 KB copies per tile (one per load instruction)
   // step buffers: in iteration st the arithmetic reads V of step st and K of
   // step st + 1, and the copies of step st + 2 are in flight
@@ -218,7 +223,8 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
       const int off = ((row * a.num_heads + h) * D + 8 * lg) * 2;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * ks, 0, 0);
+        u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * ks, 0, 0);
+        if (a.negate_q) v ^= u32x4_t{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
         qop[ct][ks] = row_ok[ct] ? v : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     const u32x4_t rs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base),
                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) & 0xffffu,
                         (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kRsrcWord3};
-    lds_char* lds = (lds_char*)(buf + my_tile * kTileBytes + 1024 * CHW * dh);
+    lds_char* lds = (lds_char*)(buf + my_tile * kTileStride + 1024 * CHW * dh);
 #pragma unroll
     for (int j = 0; j < CHW; ++j) lds_copy16(lds + 1024 * j, src_off + 1024 * j, rs);
   };
@@ -292,15 +298,20 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
       id_next = load_ids(seg + kWave);
     }
   };
-  // S^T of block `kb` of a step (its 16 keys x the wave's 32 rows, over all
-  // of D): the A operand comes straight from the step's K tile in LDS
-  const int kb = dh;  // the block of every step whose logits this wave forms
+  // Tile kb of a step's S^T (16 of its 32 keys x the wave's 32 rows, over all
+  // of D): the A operand comes straight from the step's K tiles in LDS
+  const int kb = dh;  // the tile of every step that this wave forms
+  // tile kb's row r (lane r % 16) is key 8 ((r >> 2) & 1) + 4 kb + (r & 3) of
+  // the step's block r >> 3, so that the rows a lane holds in the two tiles are
+  // 8 consecutive keys of one block: its P.V operand is one 16-byte V read
+  const int k_lane = ((lane & 15) >> 3) * kTileStride + 256 * lg +
+                     16 * (8 * (((lane & 15) >> 2) & 1) + 4 * kb + (lane & 3));
   auto qk_block = [&](const char* kv, f32x4_t* r) {
     r[0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     r[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kv + kb * kTileBytes + 1024 * ks + 16 * lane);
+      const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kv + k_lane + 1024 * ks);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) r[ct] = mfma_bf16(kf, qop[ct][ks], r[ct]);
     }
@@ -360,9 +371,9 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float v = sc[b][ct][i] * a.qscale;
+            const float v = sc[b][ct][i];
             if constexpr (decltype(masked)::value) {
-              const int jpos = (b0 + b) * kBlockTokens + 4 * lg + i;
+              const int jpos = (b0 + (lg >> 1)) * kBlockTokens + 8 * (lg & 1) + 4 * b + i;
               x[b][ct][i] = (jpos <= rpos[ct] && jpos < kend) ? v : -INFINITY;
             } else {
               x[b][ct][i] = v;
@@ -370,6 +381,8 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
             bm[ct] = fmaxf(bm[ct], x[b][ct][i]);
           }
         bm[ct] = group_max(bm[ct]);
+        // the scale is positive: the max of the scaled logits is the scaled max
+        bm[ct] = bm[ct] > -INFINITY ? bm[ct] * a.qscale : -INFINITY;
       }
     };
     if (diag)
@@ -396,8 +409,8 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int b = k >> 1, i = 2 * (k & 1);
-        const float p0 = __builtin_amdgcn_exp2f(x[b][ct][i] - m_ref[ct]);
-        const float p1 = __builtin_amdgcn_exp2f(x[b][ct][i + 1] - m_ref[ct]);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[b][ct][i], a.qscale, -m_ref[ct]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[b][ct][i + 1], a.qscale, -m_ref[ct]));
         l_run[ct] += p0 + p1;
         const uint32_t u0 = __builtin_bit_cast(uint32_t, p0), u1 = __builtin_bit_cast(uint32_t, p1);
         const float r0 = p0 - __builtin_bit_cast(float, u0 & 0xffff0000u);
@@ -422,25 +435,21 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     // ---- O^T += V^T P^T.  V elements at positions the walk does not hold are
     // zeroed: p is 0 there, but 0 * NaN would poison the row.
     auto pv = [&](auto masked) {
-      uint32_t vm[2][2];
+      uint32_t vm[4];
       if constexpr (decltype(masked)::value) {
+        const int pos = (b0 + (lg >> 1)) * kBlockTokens + 8 * (lg & 1);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int pos = (b0 + b) * kBlockTokens + 4 * lg;
-          vm[b][0] = (pos < v_end ? 0xffffu : 0u) | (pos + 1 < v_end ? 0xffff0000u : 0u);
-          vm[b][1] = (pos + 2 < v_end ? 0xffffu : 0u) | (pos + 3 < v_end ? 0xffff0000u : 0u);
-        }
+        for (int w = 0; w < 4; ++w)
+          vm[w] = (pos + 2 * w < v_end ? 0xffffu : 0u) | (pos + 2 * w + 1 < v_end ? 0xffff0000u : 0u);
       }
-      // dim d = 16 dt + lane%16, tokens 4 lg ..: chunk 2 d + lg / 2, stored swizzled
-      const char* vt = kv + 2 * kTileBytes + 512 * DT * dh + (lane & 15) * 32 + 16 * ((lg >> 1) ^ ((lane >> 3) & 1)) +
-                       8 * (lg & 1);
+      // dim d = 16 dt + lane%16, tokens 8 (lg & 1) .. + 8 of block lg >> 1:
+      // 16-byte chunk 2 d + (lg & 1) of that block's tile, stored swizzled
+      const char* vt = kv + (2 + (lg >> 1)) * kTileStride + 512 * DT * dh + (lane & 15) * 32 +
+                       16 * ((lg & 1) ^ ((lane >> 3) & 1));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vt + 512 * dt);
-        const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vt + kTileBytes + 512 * dt);
-        u32x4_t va = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
-        if constexpr (decltype(masked)::value)
-          va = u32x4_t{va[0] & vm[0][0], va[1] & vm[0][1], va[2] & vm[1][0], va[3] & vm[1][1]};
+        u32x4_t va = *reinterpret_cast<const u32x4_t*>(vt + 512 * dt);
+        if constexpr (decltype(masked)::value) va = u32x4_t{va[0] & vm[0], va[1] & vm[1], va[2] & vm[2], va[3] & vm[3]};
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           o[ct][dt] = mfma_bf16(va, p_hi[ct], o[ct][dt]);
@@ -541,7 +550,14 @@ hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_l
   PrefillArgs a = args;
   const int hc = prefill_heads_per_wg(a.group);
   a.head_groups = a.group / hc;
-  a.qscale = args.qscale * kLog2e;
+  // The kernel applies the scale in the exp2 argument and takes maxima over the
+  // raw logits, which needs a positive scale: a negative one moves onto the
+  // query's sign, and 0 becomes the smallest normal float (for logits below
+  // 2^100 in magnitude every weight is then exp2 of less than 2^-26, which
+  // rounds to 1, as with 0)
+  const float qs = args.qscale * kLog2e;
+  a.negate_q = qs < 0.0f ? 1 : 0;
+  a.qscale = qs < 0.0f ? -qs : (qs > 0.0f ? qs : 1.17549435e-38f);
   const int tiles = (max_query_len + prefill_tokens_per_wg(a.group) - 1) / prefill_tokens_per_wg(a.group);
   if (num_seqs == 0 || tiles == 0) return hipSuccess;
   const dim3 grid(tiles, a.num_kv_heads * a.head_groups, num_seqs);

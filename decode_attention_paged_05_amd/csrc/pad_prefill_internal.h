@@ -23,7 +23,8 @@ struct PrefillArgs {
   const int32_t* block_tables; // [S, W]
   const int32_t* query_start;  // [S + 1]
   const int32_t* context_lens; // [S]
-  float qscale;                // softmax scale (the launcher folds in log2(e))
+  float qscale;                // softmax scale (the launcher folds in log2(e) and takes |.|)
+  int negate_q;                // the scale was negative: the kernel flips the query's sign
   int num_tokens;              // T
   int num_heads;               // H
   int num_kv_heads;            // Hkv

@@ -32,22 +32,22 @@ class DevicePrefill:
         self.ctx = torch.from_numpy(pp.context_lens).cuda()
         torch.cuda.synchronize()
 
-    def run(self, kc=None, vc=None, tables=None, qs=None, ctx=None, out=None):
+    def run(self, kc=None, vc=None, tables=None, qs=None, ctx=None, out=None, scale=None):
         pp = self.pp
         if out is None:
             out = torch.full(tuple(pp.query.shape), float("nan"), dtype=torch.float32, device="cuda")
         pad.paged_attention_prefill(out, self.query, self.dp.kc if kc is None else kc,
                                     self.dp.vc if vc is None else vc, self.dp.tables if tables is None else tables,
-                                    self.qs if qs is None else qs, self.ctx if ctx is None else ctx, pp.scale,
-                                    pp.spec.num_kv_heads, 16, pp.max_query_len)
+                                    self.qs if qs is None else qs, self.ctx if ctx is None else ctx,
+                                    pp.scale if scale is None else scale, pp.spec.num_kv_heads, 16, pp.max_query_len)
         torch.cuda.synchronize()
         return out
 
-    def oracle(self):
+    def oracle(self, scale=None):
         pp = self.pp
         return oracle.prefill_attention(pp.query, self.dp.kc_host, self.dp.vc_host, pp.pool.block_tables,
-                                        pp.query_start, pp.context_lens, pp.scale, pp.spec.num_kv_heads, 16,
-                                        pp.spec.dtype)
+                                        pp.query_start, pp.context_lens, pp.scale if scale is None else scale,
+                                        pp.spec.num_kv_heads, 16, pp.spec.dtype)
 
 
 def max_err(got: torch.Tensor, want: np.ndarray) -> float:
@@ -61,6 +61,17 @@ def test_prefill_small_ragged():
     dp = DevicePrefill(gen.make_prefill_problem("prefill_small"))
     got = dp.run()
     assert max_err(got, dp.oracle()) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.7])
+def test_prefill_scale_sign_and_zero(scale):
+    """The kernel applies the scale inside the exp2 argument and takes maxima over
+    the raw logits, so the launcher turns a negative scale into a flipped query
+    and 0 into a tiny positive one: each must still match the oracle (0 gives the
+    mean of the visible values)."""
+    dp = DevicePrefill(gen.make_prefill_problem("prefill_small"))
+    got = dp.run(scale=scale)
+    assert max_err(got, dp.oracle(scale=scale)) <= TOL["bf16"]
 
 
 PREFILL_SHAPES = [
