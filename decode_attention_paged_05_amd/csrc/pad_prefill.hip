@@ -139,6 +139,53 @@ __device__ inline f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  c, 0, 0, 0);
 }
 
+// Workgroup order.  The dispatcher deals linear workgroup ids to the 8 XCDs
+// in turn, and each XCD has its own L2; workgroups of one (sequence, KV head)
+// read the same K/V tiles.  The grid is (token tiles, KV heads x head_groups,
+// sequences); this returns the (x, y, z) a workgroup serves.
+//  * One sequence whose KV heads divide 8 (or are a multiple of 8): each XCD
+//    serves the token tiles of one KV head (of one residue class of them, when
+//    there are fewer than 8 heads; of every 8th head, when there are more), so
+//    the L2 of an XCD holds one K/V stream at a time.
+//  * Otherwise (a batch, whose sequences may differ in length and must stay
+//    spread over all XCDs): the head_groups workgroups that share a (sequence,
+//    KV head, token tile) get linear ids 8 apart -- same XCD, back to back.
+// Token tiles keep their order within an XCD (x ascending = longest first).
+__device__ inline void remap_workgroup(int HG, int* bx, int* by, int* bz) {
+  const int NX = gridDim.x, NY = gridDim.y, NZ = gridDim.z;
+  const int NG = NY / HG;  // KV heads
+  const int L = blockIdx.x + NX * (blockIdx.y + NY * blockIdx.z);
+  const int c = L & 7, k = L >> 3;  // XCD, and place in its dispatch order
+  if (NZ == 1 && 8 % NG == 0 && NX % (8 / NG) == 0) {
+    const int R = 8 / NG;  // XCDs per KV head
+    const int j = k / HG;
+    *bx = j * R + c % R;
+    *by = (c / R) * HG + k % HG;
+    *bz = 0;
+    return;
+  }
+  if (NZ == 1 && NG % 8 == 0) {
+    const int j = k / HG;
+    *bx = j % NX;
+    *by = ((j / NX) * 8 + c) * HG + k % HG;
+    *bz = 0;
+    return;
+  }
+  const int N = NX * NY * NZ;
+  const int M = N / (8 * HG) * (8 * HG);
+  int U, hp;  // unit = (token tile, KV head, sequence); head group within it
+  if (L < M) {
+    U = (k / HG) * 8 + c;
+    hp = k % HG;
+  } else {
+    U = M / HG + (L - M) / HG;
+    hp = (L - M) % HG;
+  }
+  *bx = U % NX;
+  *by = ((U / NX) % NG) * HG + hp;
+  *bz = U / NX / NG;
+}
+
 template <int D, int HC>
 __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) {
   constexpr int TW = kRowGroups / HC;    // 32-token groups per workgroup
@@ -161,11 +208,13 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int rg = wave >> 1;              // row group
   const int dh = wave & 1;               // half of D this wave accumulates
-  const int lg = lane >> 4;              // lane group: keys / dims 4*lg .. 4*lg+3
-  const int s = blockIdx.z;
-  const int g = blockIdx.y / a.head_groups;
-  const int h = g * a.group + (blockIdx.y % a.head_groups) * HC + rg % HC;
-  const int qt = gridDim.x - 1 - blockIdx.x;  // longest walks first
+  const int lg = lane >> 4;              // lane group
+  int bx, by, bz;
+  remap_workgroup(a.head_groups, &bx, &by, &bz);
+  const int s = bz;
+  const int g = by / a.head_groups;
+  const int h = g * a.group + (by % a.head_groups) * HC + rg % HC;
+  const int qt = gridDim.x - 1 - bx;  // longest walks first
   const int q_lo = a.query_start[s];
   const int q_hi = a.query_start[s + 1];
   const int n = q_hi - q_lo;

@@ -84,6 +84,11 @@ PREFILL_SHAPES = [
     (32, 8, 64, (500,), (130,)),
     (24, 24, 128, (7, 0), (33, 64)),
     (24, 4, 256, (1000, 0, 1), (1, 1, 1)),
+    # one sequence: the workgroup order that gives each XCD one KV head (or a
+    # residue class of its token tiles, or every 8th head)
+    (8, 1, 64, (0,), (512,)),
+    (16, 2, 64, (50,), (256,)),
+    (24, 24, 128, (300,), (200,)),
 ]
 
 
