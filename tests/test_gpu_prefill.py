@@ -89,6 +89,10 @@ PREFILL_SHAPES = [
     (8, 1, 64, (0,), (512,)),
     (16, 2, 64, (50,), (256,)),
     (24, 24, 128, (300,), (200,)),
+    # KV-head counts that neither divide 8 nor are a multiple of it: the
+    # other workgroup order
+    (12, 3, 128, (40, 7), (100, 64)),
+    (10, 5, 64, (0,), (90,)),
 ]
 
 
