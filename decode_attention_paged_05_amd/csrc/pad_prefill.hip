@@ -45,7 +45,9 @@
 //     softmax state and the rescale stay in the lane.
 // V elements at positions the walk does not hold are zeroed before the MFMA,
 // so NaN padding never reaches a row.  Masking runs only on the steps that
-// need it (the diagonal, the end of the walk), in separate code.
+// need it (the diagonal, the end of the walk), in separate code.  Workgroups
+// are ordered so that those sharing K/V tiles share an XCD's L2
+// (remap_workgroup).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
