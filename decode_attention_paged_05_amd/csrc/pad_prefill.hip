@@ -22,9 +22,9 @@
 // step, and each accumulates the output for one half of D.  The logits are
 // formed one step ahead, so the step barrier that every workgroup needs
 // anyway also orders the exchange.  Each step's two K and two V tiles are
-// copied from the pool into LDS by direct-to-LDS buffer loads (each wave half
-// a tile, 16 bytes per lane per load) into a ring of three step buffers; one
-// barrier per step.  Each wave:
+// copied from the pool into LDS by direct-to-LDS buffer loads (one wave of
+// each pair a tile, 16 bytes per lane per load) into a ring of three step
+// buffers; one barrier per step.  Each wave:
 //   * forms its 16 x 32 tile of S^T = K Q^T for step st + 1 on
 //     v_mfma_f32_16x16x32_bf16: A = K (rows = keys; lane l reads one key and 8
 //     consecutive dims, one 16-byte LDS read of the tiled K layout), B = Q^T
@@ -297,13 +297,16 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   const size_t block_stride = (size_t)a.num_kv_heads * kTileBytes;
   bool bad = false;
 
-  // Wave w copies tile w of each step into LDS: K of the step's first block,
-  // K of its second, V of the first, V of the second.  Block ids come 64 at a
+  // The first wave of pair t copies tile t of each step into LDS: K of the
+  // step's first block, K of its second, V of the first, V of the second; the
+  // second wave of each pair copies nothing.  (Measured: copies issued by four
+  // waves, one per SIMD pair, beat the same copies spread over all eight by
+  // 2.5 %; by one or two waves, they were slower.)  Block ids come 64 at a
   // time (lane j holds block seg + j).
   const int my_tile = wave >> 1;         // 0, 1: K of the two blocks; 2, 3: V
+  const bool copier = dh == 0;
   const char* pool = (my_tile < 2) ? a.key_cache : a.value_cache;
   const int my_b = my_tile & 1;
-  constexpr int CHW = (CH + 1) / 2;       // 1 KB copies per wave (its half of the tile)
   auto load_ids = [&](int base) { return base + lane < nblk ? table_row[base + lane] : 0; };
   int seg = 0;
   int id_cur = load_ids(0);
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   // that the V operand reads of a half-wave hit distinct banks
   const int k_src = 16 * lane;
   const int v_src = 16 * (lane ^ ((lane >> 4) & 1));
-  const int src_off = (my_tile < 2 ? k_src : v_src) + 1024 * CHW * dh;
+  const int src_off = my_tile < 2 ? k_src : v_src;
   auto issue = [&](int step, char* buf) {
     const int blk = 2 * step + my_b;
     int phys = __builtin_amdgcn_readlane(id_cur, blk - seg);
@@ -326,9 +329,11 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     const u32x4_t rs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base),
                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) & 0xffffu,
                         (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kRsrcWord3};
-    lds_char* lds = (lds_char*)(buf + my_tile * kTileStride + 1024 * CHW * dh);
+    lds_char* lds = (lds_char*)(buf + my_tile * kTileStride);
+    if (copier) {
 #pragma unroll
-    for (int j = 0; j < CHW; ++j) lds_copy16(lds + 1024 * j, src_off + 1024 * j, rs);
+      for (int j = 0; j < CH; ++j) lds_copy16(lds + 1024 * j, src_off + 1024 * j, rs);
+    }
   };
 
   f32x4_t o[2][DT];
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   }
   // step 0's logits
   if (nsteps > 1)
-    __builtin_amdgcn_s_waitcnt(kWaitVmLds(CHW));
+    __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
   else
     __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
   workgroup_barrier();
