@@ -15,7 +15,10 @@
 // Work decomposition.  A workgroup of 8 waves serves one (sequence, KV head,
 // HC query heads of its group, 128 / HC chunk tokens): four row groups of 32
 // query rows (32 consecutive chunk tokens of one head, as two 16-row column
-// tiles), each owned by a pair of waves.  The workgroup walks the keys its
+// tiles), each owned by a pair of waves.  (Up to D = 128 a wave holds its rows
+// over all of D: 8 row groups of one wave, 256 / HC tokens, each wave forming
+// both logit tiles itself -- the "solo" layout; the rest of this note
+// describes the paired one.)  The workgroup walks the keys its
 // last row can see in 32-key steps (two 16-token blocks).  Each wave of a
 // pair forms the logits of half of the step's keys, over all of D, and
 // leaves them in LDS for its partner; both then run the softmax over the whole
@@ -112,15 +115,17 @@ constexpr int kWaitVmLds(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 
 // The LDS destination is passed as a pointer so that the compiler knows the
 // statement writes there.
 typedef __attribute__((address_space(3))) char lds_char;
-__device__ inline void lds_copy16(lds_char* lds, int voffset, u32x4_t rsrc) {
+// The byte offset is voffset (per lane) + soffset (uniform), so that the
+// copies of one tile share a single address register.
+__device__ inline void lds_copy16(lds_char* lds, int voffset, int soffset, u32x4_t rsrc) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "v"(voffset), "s"(rsrc)
+      : "s"(lds), "v"(voffset), "s"(rsrc), "s"(soffset)
       : "memory");
 }
 
@@ -190,9 +195,14 @@ __device__ inline void remap_workgroup(int HG, int* bx, int* by, int* bz) {
 
 template <int D, int HC>
 __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) {
-  constexpr int TW = kRowGroups / HC;    // 32-token groups per workgroup
+  // Up to D = 128 the registers hold a wave's output rows over all of D: each
+  // wave then owns its 32 rows alone (8 row groups, 256 rows per workgroup),
+  // forms both logit tiles of a step itself, and nothing is exchanged.
+  constexpr bool kSolo = D <= 128;
+  constexpr int RG = kSolo ? 2 * kRowGroups : kRowGroups;  // 32-row groups per workgroup
+  constexpr int TW = RG / HC;            // 32-token groups per workgroup
   constexpr int KS = D / 32;             // QK steps (32 dims each)
-  constexpr int DT = D / 32;             // 16-dim output tiles of this wave's half of D
+  constexpr int DT = kSolo ? D / 16 : D / 32;  // 16-dim output tiles of this wave's part of D
   constexpr int kTileBytes = kBlockTokens * D * 2;
   // tiles sit 64 bytes apart in the LDS bank space, so that the K reads of the
   // two blocks' keys in one lane group hit distinct banks
@@ -204,12 +214,12 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   constexpr int kBufs = 3;
   __shared__ __attribute__((aligned(16))) char kv_lds[kBufs * kStepBytes];
   // the logits a wave leaves for its partner: [step parity][row group][block][column tile][lane]
-  __shared__ f32x4_t xs_lds[2][kRowGroups][2][2][kWave];
+  __shared__ f32x4_t xs_lds[kSolo ? 1 : 2][kSolo ? 1 : kRowGroups][2][2][kWave];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int rg = wave >> 1;              // row group
-  const int dh = wave & 1;               // half of D this wave accumulates
+  const int rg = kSolo ? wave : wave >> 1;   // row group
+  const int dh = kSolo ? 0 : wave & 1;       // half of D this wave accumulates
   const int lg = lane >> 4;              // lane group
   int bx, by, bz;
   remap_workgroup(a.head_groups, &bx, &by, &bz);
@@ -242,7 +252,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     for (int ct = 0; ct < 2; ++ct) {
       const int row = q_lo + tok0 + 16 * ct + (lane & 15);
       if (!row_ok[ct] || row < 0 || row >= a.num_tokens) continue;
-      float* dst = a.out + ((size_t)row * a.num_heads + h) * D + (D / 2) * dh + 4 * lg;
+      float* dst = a.out + ((size_t)row * a.num_heads + h) * D + 16 * DT * dh + 4 * lg;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const f32x4_t v = o[ct][dt] * inv[ct];
@@ -303,8 +313,8 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   // waves, one per SIMD pair, beat the same copies spread over all eight by
   // 2.5 %; by one or two waves, they were slower.)  Block ids come 64 at a
   // time (lane j holds block seg + j).
-  const int my_tile = wave >> 1;         // 0, 1: K of the two blocks; 2, 3: V
-  const bool copier = dh == 0;
+  const int my_tile = kSolo ? wave & 3 : wave >> 1;  // 0, 1: K of the two blocks; 2, 3: V
+  const bool copier = kSolo ? wave < 4 : dh == 0;
   const char* pool = (my_tile < 2) ? a.key_cache : a.value_cache;
   const int my_b = my_tile & 1;
   auto load_ids = [&](int base) { return base + lane < nblk ? table_row[base + lane] : 0; };
@@ -332,7 +342,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     lds_char* lds = (lds_char*)(buf + my_tile * kTileStride);
     if (copier) {
 #pragma unroll
-      for (int j = 0; j < CH; ++j) lds_copy16(lds + 1024 * j, src_off + 1024 * j, rs);
+      for (int j = 0; j < CH; ++j) lds_copy16(lds + 1024 * j, src_off, 1024 * j, rs);
     }
   };
 
@@ -356,7 +366,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   };
   // Tile kb of a step's S^T (16 of its 32 keys x the wave's 32 rows, over all
   // of D): the A operand comes straight from the step's K tiles in LDS
-  const int kb = dh;  // the tile of every step that this wave forms
+  const int kb = dh;  // the tile of every step that this wave forms (paired waves)
   // tile kb's row r (lane r % 16) is key 8 ((r >> 2) & 1) + 4 kb + (r & 3) of
   // the step's block r >> 3, so that the rows a lane holds in the two tiles are
   // 8 consecutive keys of one block: its P.V operand is one 16-byte V read
@@ -377,13 +387,13 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     advance_ids(k);
     issue(k, kv_lds + k * kStepBytes);
   }
-  // step 0's logits
-  if (nsteps > 1)
-    __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
-  else
-    __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
-  workgroup_barrier();
-  {
+  // step 0's logits (paired waves: formed ahead, for the exchange)
+  if constexpr (!kSolo) {
+    if (nsteps > 1)
+      __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
+    workgroup_barrier();
     f32x4_t first[2];
     qk_block(kv_lds, first);
 #pragma unroll
@@ -396,7 +406,11 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   // copies of step st + 2, then the softmax of step st, this wave's logits of
   // step st + 1 and the P.V of step st.
   for (int st = 0; st < nsteps; ++st) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
+    // paired waves need K of step st + 1 now; solo waves only step st
+    if (kSolo && st + 1 < nsteps)
+      __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
     workgroup_barrier();
     if (st + kLead < nsteps) {
       advance_ids(st + kLead);
@@ -408,10 +422,16 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     // ---- logits S^T of the step: two blocks x two column tiles, one block
     // formed by each wave of the pair
     f32x4_t sc[2][2];
+    if constexpr (kSolo) {
+      // solo waves: kb = 0, so k_lane is tile 0's offset; tile 1's is 64 bytes on
+      qk_block(kv, sc[0]);
+      qk_block(kv + 64, sc[1]);
+    } else {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) sc[b][ct] = xs_lds[st & 1][rg][b][ct][lane];
+        for (int ct = 0; ct < 2; ++ct) sc[b][ct] = xs_lds[st & 1][rg][b][ct][lane];
+    }
 
     // ---- mask, running max, weights.  Only steps that reach the wave's first
     // row position (the diagonal) or the end of the keys need the mask.
@@ -481,7 +501,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     // ---- this wave's logits of the next step, for the pair (issued after
     // the softmax, so that the matrix cores work through them while P.V's
     // operands are read)
-    if (st + 1 < nsteps) {
+    if (!kSolo && st + 1 < nsteps) {
       f32x4_t next[2];
       qk_block(kv_lds + ((st + 1) % kBufs) * kStepBytes, next);
 #pragma unroll
@@ -599,7 +619,10 @@ int prefill_heads_per_wg(int group) {
   return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
 }
 
-int prefill_tokens_per_wg(int group) { return kRowsPerWave * kRowGroups / prefill_heads_per_wg(group); }
+int prefill_tokens_per_wg(int group, int head_size) {
+  const int row_groups = head_size <= 128 ? 2 * kRowGroups : kRowGroups;
+  return kRowsPerWave * row_groups / prefill_heads_per_wg(group);
+}
 
 hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
                           hipStream_t stream) {
@@ -614,7 +637,8 @@ hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_l
   const float qs = args.qscale * kLog2e;
   a.negate_q = qs < 0.0f ? 1 : 0;
   a.qscale = qs < 0.0f ? -qs : (qs > 0.0f ? qs : 1.17549435e-38f);
-  const int tiles = (max_query_len + prefill_tokens_per_wg(a.group) - 1) / prefill_tokens_per_wg(a.group);
+  const int tpw = prefill_tokens_per_wg(a.group, head_size);
+  const int tiles = (max_query_len + tpw - 1) / tpw;
   if (num_seqs == 0 || tiles == 0) return hipSuccess;
   const dim3 grid(tiles, a.num_kv_heads * a.head_groups, num_seqs);
   switch (head_size) {

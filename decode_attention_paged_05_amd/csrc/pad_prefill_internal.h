@@ -51,7 +51,7 @@ struct WriteKvArgs {
 
 // Query heads and chunk tokens one prefill workgroup serves.
 int prefill_heads_per_wg(int group);
-int prefill_tokens_per_wg(int group);
+int prefill_tokens_per_wg(int group, int head_size);
 
 hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
                           hipStream_t stream);
