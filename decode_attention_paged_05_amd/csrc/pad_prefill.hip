@@ -108,25 +108,54 @@ __device__ inline float group_sum(float v) {
 // LDS access done (export counter left at its maximum)
 constexpr int kWaitVmLds(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
 
-// 16 bytes per lane from a buffer into LDS (lane i's bytes land at lds + 16 i),
-// issued so that the compiler does not track it: it would otherwise wait for
-// every copy in flight before each LDS read.  The caller waits on the
-// vector-memory counter itself.  M0 (the LDS address) is restored.
-// The LDS destination is passed as a pointer so that the compiler knows the
-// statement writes there.
+// N (1 to 4) copies of 16 bytes per lane from a buffer into LDS, 1 KB apart:
+// copy j takes the bytes at voffset + 1024 j of the buffer and leaves lane i's
+// at lds + 1024 j + 16 i.  One M0 (the LDS address) serves the whole run, as
+// the instruction offset moves the LDS address along with the buffer one; M0
+// is restored afterwards.  The copies are issued so that the compiler does not
+// track them: it would otherwise wait for every copy in flight before each LDS
+// read.  The caller waits on the vector-memory counter itself (one count per
+// copy).  The LDS destination is passed as a pointer so that the compiler
+// knows the statement writes there.
 typedef __attribute__((address_space(3))) char lds_char;
-// The byte offset is voffset (per lane) + soffset (uniform), so that the
-// copies of one tile share a single address register.
-__device__ inline void lds_copy16(lds_char* lds, int voffset, int soffset, u32x4_t rsrc) {
+template <int N>
+__device__ inline void lds_copy16_run(lds_char* lds, int voffset, u32x4_t rsrc) {
+  static_assert(N >= 1 && N <= 4, "1 to 4 copies per run");
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voffset), "s"(rsrc), "s"(soffset)
-      : "memory");
+  if constexpr (N == 1)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved) : "s"(lds), "v"(voffset), "s"(rsrc) : "memory");
+  else if constexpr (N == 2)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved) : "s"(lds), "v"(voffset), "s"(rsrc) : "memory");
+  else if constexpr (N == 3)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen offset:2048 lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved) : "s"(lds), "v"(voffset), "s"(rsrc) : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen offset:3072 lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved) : "s"(lds), "v"(voffset), "s"(rsrc) : "memory");
 }
 
 // s_barrier without the memory fences of __syncthreads (those would wait for
@@ -341,8 +370,13 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
                         (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kRsrcWord3};
     lds_char* lds = (lds_char*)(buf + my_tile * kTileStride);
     if (copier) {
-#pragma unroll
-      for (int j = 0; j < CH; ++j) lds_copy16(lds + 1024 * j, src_off, 1024 * j, rs);
+      static_assert(CH <= 8, "at most two runs of copies per tile");
+      if constexpr (CH <= 4) {
+        lds_copy16_run<CH>(lds, src_off, rs);
+      } else {
+        lds_copy16_run<4>(lds, src_off, rs);
+        lds_copy16_run<CH - 4>(lds + 4096, src_off + 4096, rs);
+      }
     }
   };
 
