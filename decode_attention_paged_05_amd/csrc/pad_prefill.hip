@@ -27,7 +27,9 @@
 // anyway also orders the exchange.  Each step's two K and two V tiles are
 // copied from the pool into LDS by direct-to-LDS buffer loads (one wave of
 // each pair a tile, 16 bytes per lane per load) into a ring of three step
-// buffers; one barrier per step.  Each wave:
+// buffers, two steps ahead (issued after the wave's next-step logits, away
+// from the waits the compiler places on its own loads); one barrier per
+// step.  Each wave:
 //   * forms its 16 x 32 tile of S^T = K Q^T for step st + 1 on
 //     v_mfma_f32_16x16x32_bf16: A = K (rows = keys; lane l reads one key and 8
 //     consecutive dims, one 16-byte LDS read of the tiled K layout), B = Q^T
@@ -241,6 +243,15 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   // step buffers: in iteration st the arithmetic reads V of step st and K of
   // step st + 1, and the copies of step st + 2 are in flight
   constexpr int kBufs = 3;
+  // Where in a step the copies of step st + 2 are issued.  The compiler
+  // guards each load it issues itself (the block ids; at D = 256 also the
+  // reload of a spilled register, once per step) with a wait for the whole
+  // vector-memory counter, which counts these copies too: issued at the top
+  // of the step, they were waited for inside the step they were issued in.
+  // Issued after this wave's logits of step st + 1 instead, the prefix
+  // attention ran 8 % faster at D = 256 and 7 % at D = 128; at D = 64, whose
+  // steps are short, 2 % slower, so there they stay at the top.
+  constexpr bool kEarlyCopies = D < 128;
   __shared__ __attribute__((aligned(16))) char kv_lds[kBufs * kStepBytes];
   // the logits a wave leaves for its partner: [step parity][row group][block][column tile][lane]
   __shared__ f32x4_t xs_lds[kSolo ? 1 : 2][kSolo ? 1 : kRowGroups][2][2][kWave];
@@ -436,9 +447,10 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
 
   // Iteration st: wait for the copies of step st + 1 (this wave's; the
   // barrier makes every wave's visible, publishes every wave's logits of step
-  // st, and retires all reads of the buffer the next copies reuse), start the
-  // copies of step st + 2, then the softmax of step st, this wave's logits of
-  // step st + 1 and the P.V of step st.
+  // st, and retires all reads of the buffer the next copies reuse); then the
+  // softmax of step st, this wave's logits of step st + 1, the copies of step
+  // st + 2 (at D = 64 they come first, right after the barrier) and the P.V
+  // of step st.
   for (int st = 0; st < nsteps; ++st) {
     // paired waves need K of step st + 1 now; solo waves only step st
     if (kSolo && st + 1 < nsteps)
@@ -446,7 +458,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     else
       __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
     workgroup_barrier();
-    if (st + kLead < nsteps) {
+    if (kEarlyCopies && st + kLead < nsteps) {
       advance_ids(st + kLead);
       issue(st + kLead, kv_lds + ((st + kLead) % kBufs) * kStepBytes);
     }
@@ -540,6 +552,13 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
       qk_block(kv_lds + ((st + 1) % kBufs) * kStepBytes, next);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) xs_lds[(st + 1) & 1][rg][kb][ct][lane] = next[ct];
+    }
+
+    // ---- the copies of step st + 2 (head sizes from 128: here, after the
+    // logits of step st + 1, see kEarlyCopies)
+    if (!kEarlyCopies && st + kLead < nsteps) {
+      advance_ids(st + kLead);
+      issue(st + kLead, kv_lds + ((st + kLead) % kBufs) * kStepBytes);
     }
 
     // ---- O^T += V^T P^T.  V elements at positions the walk does not hold are
