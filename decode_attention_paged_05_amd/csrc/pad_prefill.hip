@@ -244,17 +244,23 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   // step st + 1, and the copies of step st + 2 are in flight
   constexpr int kBufs = 3;
   // Where in a step the copies of step st + 2 are issued.  The compiler
-  // guards each load it issues itself (the block ids; at D = 256 also the
-  // reload of a spilled register, once per step) with a wait for the whole
-  // vector-memory counter, which counts these copies too: issued at the top
-  // of the step, they were waited for inside the step they were issued in.
-  // Issued after this wave's logits of step st + 1 instead, the prefix
-  // attention ran 8 % faster at D = 256 and 7 % at D = 128; at D = 64, whose
-  // steps are short, 2 % slower, so there they stay at the top.
+  // guards each load it issues itself (the block ids, the reload of a spilled
+  // register) with a wait for the whole vector-memory counter, which counts
+  // these copies too: issued at the top of the step, they can be waited for
+  // inside the step they were issued in.  Issued after this wave's logits of
+  // step st + 1 instead, the prefix attention ran 8 % faster at D = 256 (with
+  // a spilled register then reloaded in every step) and 7 % at D = 128; at
+  // D = 64, whose steps are short, 2 % slower, so there they stay at the top.
   constexpr bool kEarlyCopies = D < 128;
   __shared__ __attribute__((aligned(16))) char kv_lds[kBufs * kStepBytes];
   // the logits a wave leaves for its partner: [step parity][row group][block][column tile][lane]
   __shared__ f32x4_t xs_lds[kSolo ? 1 : 2][kSolo ? 1 : kRowGroups][2][2][kWave];
+  // Paired waves (D = 256) keep one of their Q^T operands -- column tile 1,
+  // last 32 dims -- in LDS instead of registers, 16 bytes per lane.  In
+  // registers it was the one value the allocator spilled, and its reload in
+  // every step cost a scratch round trip (8 % of the kernel); two operands
+  // in LDS measured slower than one.
+  __shared__ u32x4_t q_lds[kSolo ? 1 : kWaves][kWave];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -312,8 +318,8 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     return;
   }
 
-  // Q^T operand, held in registers for the whole walk: column tile ct, step
-  // ks -> the row's dims 32 ks + 8 lg .. + 8
+  // Q^T operand, held in registers for the whole walk (one of them in LDS at
+  // D = 256, q_lds): column tile ct, step ks -> the row's dims 32 ks + 8 lg .. + 8
   u32x4_t qop[2][KS];
   {
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
@@ -328,6 +334,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
         if (a.negate_q) v ^= u32x4_t{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
         qop[ct][ks] = row_ok[ct] ? v : u32x4_t{0u, 0u, 0u, 0u};
       }
+      if (!kSolo && ct == 1) q_lds[wave][lane] = qop[1][KS - 1];
     }
   }
 
@@ -424,7 +431,10 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     for (int ks = 0; ks < KS; ++ks) {
       const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kv + k_lane + 1024 * ks);
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) r[ct] = mfma_bf16(kf, qop[ct][ks], r[ct]);
+      for (int ct = 0; ct < 2; ++ct) {
+        const u32x4_t qb = (!kSolo && ct == 1 && ks == KS - 1) ? q_lds[wave][lane] : qop[ct][ks];
+        r[ct] = mfma_bf16(kf, qb, r[ct]);
+      }
     }
   };
   constexpr int kLead = kBufs - 1;  // iteration st issues the copies of step st + kLead
