@@ -243,15 +243,14 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   // step buffers: in iteration st the arithmetic reads V of step st and K of
   // step st + 1, and the copies of step st + 2 are in flight
   constexpr int kBufs = 3;
-  // Where in a step the copies of step st + 2 are issued.  The compiler
-  // guards each load it issues itself (the block ids, the reload of a spilled
-  // register) with a wait for the whole vector-memory counter, which counts
-  // these copies too: issued at the top of the step, they can be waited for
-  // inside the step they were issued in.  Issued after this wave's logits of
-  // step st + 1 instead, the prefix attention ran 8 % faster at D = 256 (with
-  // a spilled register then reloaded in every step) and 7 % at D = 128; at
-  // D = 64, whose steps are short, 2 % slower, so there they stay at the top.
-  constexpr bool kEarlyCopies = D < 128;
+  // The copies of step st + 2 are issued after this wave's logits of step
+  // st + 1, not at the top of the step.  The compiler guards each vector load
+  // it issues itself (the reload of a spilled register, for one) with a wait
+  // for the whole vector-memory counter, which counts these copies too;
+  // issued at the top, they could be waited for inside the step they were
+  // issued in.  Issued late, the prefix attention measured 8 % faster at
+  // D = 256 (where a spilled register was then reloaded in every step), 7 %
+  // at D = 128 and, once the block ids came by scalar loads, 6 % at D = 64.
   __shared__ __attribute__((aligned(16))) char kv_lds[kBufs * kStepBytes];
   // the logits a wave leaves for its partner: [step parity][row group][block][column tile][lane]
   __shared__ f32x4_t xs_lds[kSolo ? 1 : 2][kSolo ? 1 : kRowGroups][2][2][kWave];
@@ -358,16 +357,23 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   // step's first block, K of its second, V of the first, V of the second; the
   // second wave of each pair copies nothing.  (Measured: copies issued by four
   // waves, one per SIMD pair, beat the same copies spread over all eight by
-  // 2.5 %; by one or two waves, they were slower.)  Block ids come 64 at a
-  // time (lane j holds block seg + j).
+  // 2.5 %; by one or two waves, they were slower.)
   const int my_tile = kSolo ? wave & 3 : wave >> 1;  // 0, 1: K of the two blocks; 2, 3: V
   const bool copier = kSolo ? wave < 4 : dh == 0;
   const char* pool = (my_tile < 2) ? a.key_cache : a.value_cache;
   const int my_b = my_tile & 1;
-  auto load_ids = [&](int base) { return base + lane < nblk ? table_row[base + lane] : 0; };
-  int seg = 0;
-  int id_cur = load_ids(0);
-  int id_next = load_ids(kWave);
+  // The block table is read-only for the launch: each wave fetches the id of
+  // the block it copies next by a scalar load, one issue ahead.  (Loaded 64 at
+  // a time into a vector register instead, the id load left the loop with a
+  // wait for the whole vector-memory counter at its back edge, which drained
+  // the step's own copies: 3 to 5 % slower.)
+  const int32_t __attribute__((address_space(4)))* table_c =
+      (const int32_t __attribute__((address_space(4)))*)table_row;
+  auto fetch_id = [&](int step) {
+    const int blk = 2 * step + my_b;
+    return blk < nblk ? table_c[blk] : 0;
+  };
+  int next_id = fetch_id(0);
   // V tiles are stored with the two 16-byte halves of every other group of 8
   // dims swapped (16-byte chunk c of the tile lands at c ^ ((c >> 4) & 1)), so
   // that the V operand reads of a half-wave hit distinct banks
@@ -376,7 +382,8 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   const int src_off = my_tile < 2 ? k_src : v_src;
   auto issue = [&](int step, char* buf) {
     const int blk = 2 * step + my_b;
-    int phys = __builtin_amdgcn_readlane(id_cur, blk - seg);
+    int phys = next_id;
+    next_id = fetch_id(step + 1);
     const bool live = blk < nblk;
     const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
     bad |= live && !ok;
@@ -406,16 +413,6 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   float m_ref[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.0f, 0.0f};
 
-  // ids for blocks [seg, seg + 64) are in id_cur; the copies of a step's two
-  // blocks never straddle a segment
-  auto advance_ids = [&](int step) {
-    const int b = 2 * step;
-    if (b >= seg + kWave) {
-      id_cur = id_next;
-      seg += kWave;
-      id_next = load_ids(seg + kWave);
-    }
-  };
   // Tile kb of a step's S^T (16 of its 32 keys x the wave's 32 rows, over all
   // of D): the A operand comes straight from the step's K tiles in LDS
   const int kb = dh;  // the tile of every step that this wave forms (paired waves)
@@ -439,7 +436,6 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   };
   constexpr int kLead = kBufs - 1;  // iteration st issues the copies of step st + kLead
   for (int k = 0; k < kLead && k < nsteps; ++k) {
-    advance_ids(k);
     issue(k, kv_lds + k * kStepBytes);
   }
   // step 0's logits (paired waves: formed ahead, for the exchange)
@@ -459,8 +455,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   // barrier makes every wave's visible, publishes every wave's logits of step
   // st, and retires all reads of the buffer the next copies reuse); then the
   // softmax of step st, this wave's logits of step st + 1, the copies of step
-  // st + 2 (at D = 64 they come first, right after the barrier) and the P.V
-  // of step st.
+  // st + 2 and the P.V of step st.
   for (int st = 0; st < nsteps; ++st) {
     // paired waves need K of step st + 1 now; solo waves only step st
     if (kSolo && st + 1 < nsteps)
@@ -468,10 +463,6 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     else
       __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
     workgroup_barrier();
-    if (kEarlyCopies && st + kLead < nsteps) {
-      advance_ids(st + kLead);
-      issue(st + kLead, kv_lds + ((st + kLead) % kBufs) * kStepBytes);
-    }
     const int b0 = 2 * st;  // first block of this step
     const char* kv = kv_lds + (st % kBufs) * kStepBytes;
 
@@ -564,10 +555,8 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
       for (int ct = 0; ct < 2; ++ct) xs_lds[(st + 1) & 1][rg][kb][ct][lane] = next[ct];
     }
 
-    // ---- the copies of step st + 2 (head sizes from 128: here, after the
-    // logits of step st + 1, see kEarlyCopies)
-    if (!kEarlyCopies && st + kLead < nsteps) {
-      advance_ids(st + kLead);
+    // ---- the copies of step st + 2 (here, after the logits of step st + 1)
+    if (st + kLead < nsteps) {
       issue(st + kLead, kv_lds + ((st + kLead) % kBufs) * kStepBytes);
     }
 
