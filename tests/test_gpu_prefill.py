@@ -313,3 +313,20 @@ def test_prefill_long_chunk_no_context_sampled():
     got = dp.run()
     assert bool(torch.isfinite(got).all())
     assert _sampled_check(pp, got, _edge_rows, heads=(0, 11, 23)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("H,Hkv,D", [(64, 8, 64), (32, 8, 128), (16, 16, 128)])
+def test_prefill_long_walks_small_heads_sampled(H, Hkv, D):
+    """Head sizes 64 and 128 (the one-wave-per-row-group layout) over walks of
+    hundreds of blocks: a 5000-token context with a 700-token chunk, and a
+    second sequence with a 2000-token chunk over 1000 cached.  Sampled rows
+    against the oracle, every row finite."""
+    spec = gen.PrefillSpec(f"long_d{D}", context_lens=(5000, 1000), query_lens=(700, 2000), num_heads=H,
+                           num_kv_heads=Hkv, head_size=D, dtype="bf16", seed=44)
+    pp = gen.make_prefill_problem(spec)
+    dp = DevicePrefill(pp, keep_host=False)
+    got = dp.run()
+    assert bool(torch.isfinite(got).all())
+    G = H // Hkv
+    heads = sorted({0, G - 1, G, H // 2, H - 1})
+    assert _sampled_check(pp, got, _edge_rows, heads=heads) <= TOL["bf16"]
