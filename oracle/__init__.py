@@ -6,8 +6,11 @@ library never imports, links or calls it, and it imports nothing from the GPU
 library.  Every function is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle.py`` and ``tests/test_oracle_prefill.py`` (brute force,
 closed forms, invariants, the log-sum-exp merge identity, the pages' two-phase
-prefill form, float64 library special cases and hand-worked fixtures); there
-is no "parity unpinned" function.
+prefill form, float64 library special cases and hand-worked fixtures).  The
+two helpers that serve sampled checks at full size, ``attend_logical`` and
+``prefill_rows``, are pinned row for row against pure-Python brute force and
+against ``decode_attention`` / ``prefill_attention``; there is no "parity
+unpinned" function.
 """
 
 from .attention import (  # noqa: F401

@@ -329,8 +329,39 @@ def pin_library_sdpa(orc):
         assert np.max(np.abs(got - ref)) <= 1e-12, "float64 SDPA special case"
 
 
+def pin_attend_logical(orc):
+    """The one-row helper used for sampled checks equals pure-Python brute force
+    and the paged oracle, row for row, in both storage formats, with ordinary
+    keys and with large-logit outliers (keys x 20 at a few positions)."""
+    rng = np.random.default_rng(16)
+    scale = 0.1  # not a float32 value: whether the scale is rounded to float32 shows at ~1e-9
+    for dtype in ("f32", "bf16"):
+        for outliers in (False, True):
+            H, Hkv, D, bs = 6, 2, 8, 4
+            lens = (13, 1, 6)
+            S = len(lens)
+            q = store(rng.standard_normal((S, H, D)) * 2.0, dtype)
+            lk, lv = [], []
+            for L in lens:
+                k = rng.standard_normal((Hkv, L, D))
+                if outliers:
+                    k[:, rng.random(L) < 0.3] *= 20.0
+                lk.append(store(k, dtype))
+                lv.append(store(rng.standard_normal((Hkv, L, D)), dtype))
+            kc, vc, tables, L = paged(lk, lv, bs, dtype, rng)
+            want = brute_force(q, lk, lv, float(np.float32(scale)), Hkv, dtype)
+            full = run(orc, q, kc, vc, tables, L, scale, Hkv, bs, dtype)
+            for s in range(S):
+                for h in range(H):
+                    g = h // (H // Hkv)
+                    got = orc.attend_logical(q[s, h], lk[s][g], lv[s][g], scale, dtype)
+                    assert got.shape == (D,)
+                    assert np.max(np.abs(got - want[s, h])) <= 1e-12, ("attend_logical vs brute force", s, h)
+                    assert np.max(np.abs(got - full[s, h])) <= 1e-12, ("attend_logical vs decode_attention", s, h)
+
+
 ALL_PINS = [pin_brute_force, pin_hand_cases, pin_closed_forms, pin_invariants,
-            pin_lse_identity, pin_partition_counts, pin_library_sdpa]
+            pin_lse_identity, pin_partition_counts, pin_library_sdpa, pin_attend_logical]
 
 
 def failing_pins(orc):

@@ -242,8 +242,34 @@ def pin_write_chunk(orc):
         assert np.max(np.abs(a - b)) <= 1e-12, "written cache vs chunk rows"
 
 
+def pin_prefill_rows(orc):
+    """The sampled-row helper equals the plain prefix attention and pure-Python
+    brute force, row for row, for windows of chunk rows that start past the
+    chunk's first token and end before its last (so a causal bound that is off
+    by one either way changes the answer), with and without context."""
+    rng = np.random.default_rng(28)
+    scale = 0.1  # not a float32 value: whether the scale is rounded to float32 shows at ~1e-9
+    for sh in (dict(dtype="f32", ctx=(5, 0), n=(9, 8), H=4, Hkv=2, D=6, bs=4),
+               dict(dtype="bf16", ctx=(17, 3), n=(7, 10), H=6, Hkv=3, D=4, bs=4)):
+        c = make_case(rng, sh["dtype"], sh["ctx"], sh["n"], sh["H"], sh["Hkv"], sh["D"], sh["bs"], spread=2.0)
+        full = run(orc, c, scale)
+        want = brute_force(c, float(np.float32(scale)))
+        group = sh["H"] // sh["Hkv"]
+        for s in range(len(sh["ctx"])):
+            lo, n, ctx = int(c["qs"][s]), sh["n"][s], sh["ctx"][s]
+            for first, m in ((0, 1), (1, 3), (2, n - 3), (n - 1, 1)):
+                rows = slice(lo + first, lo + first + m)
+                for h in range(sh["H"]):
+                    g = h // group
+                    got = orc.prefill_rows(c["q"][rows, h], c["lk"][s][g], c["lv"][s][g], ctx, first, scale,
+                                           sh["dtype"])
+                    assert got.shape == (m, sh["D"])
+                    assert np.max(np.abs(got - full[rows, h])) <= 1e-12, ("prefill_rows vs plain", s, first, h)
+                    assert np.max(np.abs(got - want[rows, h])) <= 1e-12, ("prefill_rows vs brute force", s, h)
+
+
 ALL_PINS = [pin_prefill_brute_force, pin_prefill_two_phase, pin_prefill_decode_reduction, pin_prefill_sdpa,
-            pin_prefill_closed_forms, pin_prefill_invariants, pin_write_chunk]
+            pin_prefill_closed_forms, pin_prefill_invariants, pin_write_chunk, pin_prefill_rows]
 
 
 def failing_pins(orc):

@@ -109,6 +109,22 @@ def _mut_widen_shift(values, dtype):
     return orc_widen(values, dtype)
 
 
+def _mut_logical_kv_swapped(q_row, K_rows, V_rows, scale, dtype):
+    return orc_attend(orc_widen(q_row, dtype), orc_widen(V_rows, dtype), orc_widen(K_rows, dtype),
+                      float(np.float32(scale)))
+
+
+def _mut_logical_scale_unrounded(q_row, K_rows, V_rows, scale, dtype):
+    return orc_attend(orc_widen(q_row, dtype), orc_widen(K_rows, dtype), orc_widen(V_rows, dtype), float(scale))
+
+
+def _mut_logical_one_token_short(q_row, K_rows, V_rows, scale, dtype):
+    n = max(K_rows.shape[0] - 1, 1)
+    return orc_attend(orc_widen(q_row, dtype), orc_widen(K_rows[:n], dtype), orc_widen(V_rows[:n], dtype),
+                      float(np.float32(scale)))
+
+
+orc_attend = orc.attend
 orc_gather = orc.gather_sequence
 orc_partition_stats = orc.partition_stats
 orc_widen = orc.widen
@@ -129,6 +145,9 @@ MUTANTS = [
     ("merge_partitions", _mut_merge_sign),
     ("partition_stats", _mut_partition_unnormalised),
     ("widen", _mut_widen_shift),
+    ("attend_logical", _mut_logical_kv_swapped),
+    ("attend_logical", _mut_logical_scale_unrounded),
+    ("attend_logical", _mut_logical_one_token_short),
 ]
 
 

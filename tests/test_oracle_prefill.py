@@ -95,6 +95,22 @@ def _write_ignoring_context(key_cache, value_cache, key, value, block_tables, qu
     return kc, vc
 
 
+def _rows_with(visible_of=None, swap=False, unrounded=False):
+    """prefill_rows with a planted mistake: the causal bound, K/V swapped, or
+    the scale used without its float32 rounding."""
+    def f(query_rows, K_rows, V_rows, ctx, first, scale, dtype):
+        q = dec.widen(query_rows, dtype)
+        K = dec.widen(V_rows if swap else K_rows, dtype)
+        V = dec.widen(K_rows if swap else V_rows, dtype)
+        sc = float(scale) if unrounded else float(np.float32(scale))
+        out = np.empty((q.shape[0], K.shape[1]))
+        for r in range(q.shape[0]):
+            visible = visible_of(ctx, first, r) if visible_of else ctx + first + r + 1
+            out[r] = dec.attend(q[r], K[:visible], V[:visible], sc)
+        return out
+    return f
+
+
 MUTANTS = [
     ("prefill_attention", _prefill_with(lambda ctx, i: (0, ctx + i)), "excludes its own token"),
     ("prefill_attention", _prefill_with(lambda ctx, i: (0, i + 1)), "causal rule without the context offset"),
@@ -106,6 +122,11 @@ MUTANTS = [
     ("prefix_attention_two_phase", _two_phase_with(skip_context=True), "context phase skipped"),
     ("write_chunk", _write_off_by_one, "chunk written one slot late"),
     ("write_chunk", _write_ignoring_context, "chunk written from position 0"),
+    ("prefill_rows", _rows_with(lambda ctx, first, r: ctx + first + r + 2), "rows: one token into the future"),
+    ("prefill_rows", _rows_with(lambda ctx, first, r: ctx + first + r), "rows: own token excluded"),
+    ("prefill_rows", _rows_with(lambda ctx, first, r: ctx + r + 1), "rows: window start ignored"),
+    ("prefill_rows", _rows_with(swap=True), "rows: keys and values swapped"),
+    ("prefill_rows", _rows_with(unrounded=True), "rows: scale not rounded to float32"),
 ]
 
 
