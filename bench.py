@@ -218,7 +218,7 @@ def run_prefill(args) -> int:
         max_err = worst
         if not args.no_cpu_baseline:
             cpu = {"value": round(done_flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-                   "cpu_model": cpu_model(),
+                   "host_cores": host_cores(), "cpu_model": cpu_model(),
                    "sample": f"{len(rows) * len(heads)} (token, head) output rows of sequence 0 computed one by one "
                              f"by the fp64 oracle, repeated for {total:.1f} s"}
     line = {
@@ -252,6 +252,14 @@ def run_prefill(args) -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def host_cores() -> int:
+    """Cores this process may run on (its CPU affinity set)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
 
 
 def cpu_model() -> str:
@@ -504,9 +512,10 @@ def main() -> int:
                 total += time.perf_counter() - t_or
                 reps += 1
             cpu = {"value": round(reps * kv_bytes / total / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
-                   "kind": "oracle", "cpu_model": cpu_model(),
+                   "kind": "oracle", "host_cores": host_cores(), "cpu_model": cpu_model(),
                    "sample": f"{reps} full steps of the same workload ({describe(p, args.layout)}) in {total:.1f} s, "
-                             f"fp64 NumPy, {int(blas_threads)} BLAS threads; "
+                             f"fp64 NumPy on a host with {host_cores()} usable cores: matrix products on "
+                             f"{int(blas_threads)} BLAS threads, the rest on one thread; "
                              f"{total / reps * 1e6:.0f} us per step"}
 
     line = {
@@ -551,6 +560,7 @@ def main() -> int:
             "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel": "phase1" if P else "one_pass",
+            "step_frac": round(gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_launch": kv_bytes,
         },
         "cpu_baseline": cpu,

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     make_prefill_dims,
     paged_attention_decode,
     paged_attention_decode_choose_partition,
+    paged_attention_decode_entry_ranges,
     paged_attention_decode_phase1,
     paged_attention_decode_phase2,
     paged_attention_decode_strerror,

@@ -35,6 +35,7 @@ EXPORTED = [
     "paged_attention_decode_workspace_init",
     "paged_attention_decode_choose_partition",
     "paged_attention_decode_strerror",
+    "paged_attention_decode_entry_ranges",
     "paged_attention_prefill",
     "paged_attention_prefill_write_kv",
 ]
@@ -83,7 +84,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         pass
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is missing: build it with `python -m decode_attention_paged_05_amd.build` "
+            f"{path} is missing: build it with `python decode_attention_paged_05_amd/build.py` "
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(path)
     vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -104,6 +105,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode_workspace_init.restype = i32
     lib.paged_attention_decode_choose_partition.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.paged_attention_decode_choose_partition.restype = i32
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.paged_attention_decode_entry_ranges.argtypes = [ip, i32, i32, i32, i32, i32, i32, i32, ip, ip, ip]
+    lib.paged_attention_decode_entry_ranges.restype = i32
     lib.paged_attention_decode_strerror.argtypes = [i32]
     lib.paged_attention_decode_strerror.restype = ctypes.c_char_p
     pdims = ctypes.POINTER(PadPrefillDims)
@@ -283,6 +287,35 @@ def paged_attention_decode_choose_partition(num_seqs, num_heads, num_kv_heads, m
 
 def paged_attention_decode_strerror(status: int) -> str:
     return strerror(status)
+
+
+def paged_attention_decode_entry_ranges(seq_lens, num_heads: int, num_kv_heads: int, max_blocks_per_seq: int,
+                                        block_size: int, partition_size: int, num_cus: int = 256):
+    """Where phase 1 puts each (sequence, head)'s results, for host lengths.
+
+    Returns ``(balanced, count [S, H], begin [S, H, NP], end [S, H, NP])`` as
+    NumPy int32 arrays: slot e < count[s, h] of (s, h) holds tokens
+    [begin, end); count is 0 for an empty sequence and -1 for a length outside
+    the table.
+    """
+    import numpy as np
+
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    S = int(lens.shape[0])
+    if partition_size <= 0 or partition_size % block_size:
+        raise PadError(-5, "paged_attention_decode_entry_ranges")
+    NP = -(-max_blocks_per_seq * block_size // partition_size)
+    count = np.zeros((S, num_heads), dtype=np.int32)
+    begin = np.zeros((S, num_heads, NP), dtype=np.int32)
+    end = np.zeros((S, num_heads, NP), dtype=np.int32)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    r = LIB.paged_attention_decode_entry_ranges(lens.ctypes.data_as(ip), S, int(num_heads), int(num_kv_heads),
+                                                int(max_blocks_per_seq), int(block_size), int(partition_size),
+                                                int(num_cus), count.ctypes.data_as(ip), begin.ctypes.data_as(ip),
+                                                end.ctypes.data_as(ip))
+    if r < 0:
+        raise PadError(r, "paged_attention_decode_entry_ranges")
+    return bool(r), count, begin, end
 
 
 def alloc_workspace(num_seqs, num_heads, head_size, max_blocks_per_seq, block_size, partition_size, device=None,

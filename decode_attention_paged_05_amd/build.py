@@ -1,6 +1,7 @@
 """Build ``libpad.so`` (the C-ABI library) in-tree with hipcc for gfx950.
 
-Usage: ``python -m decode_attention_paged_05_amd.build [-v]``.  Always
+Usage: ``python decode_attention_paged_05_amd/build.py [-v]`` (run as a file:
+importing the package loads the library, which may not exist yet).  Always
 recompiles.  The shared library lands next to this file, where the Python
 binding loads it.
 """

@@ -5,6 +5,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <algorithm>
+#include <vector>
 
 #include "paged_attention_decode.h"
 #include "paged_attention_prefill.h"
@@ -20,7 +22,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t ml, es, tmp, counters, scratch, total;
+  size_t ml, es, tmp, info, total;
   int64_t np;
   size_t n_stats, n_tmp;
 };
@@ -29,7 +31,7 @@ struct Layout {
 bool workspace_layout(int32_t S, int32_t H, int32_t D, int32_t W, int32_t bs, int32_t P, Layout* out) {
   if (S < 0 || H <= 0 || D <= 0 || W <= 0 || bs <= 0 || P < 0) return false;
   if (P == 0) {
-    *out = Layout{0, 0, 0, 0, 0, 0, 0, 0, 0};
+    *out = Layout{0, 0, 0, 0, 0, 0, 0, 0};
     return true;
   }
   if (P % bs) return false;
@@ -44,10 +46,9 @@ bool workspace_layout(int32_t S, int32_t H, int32_t D, int32_t W, int32_t bs, in
   l.ml = 0;
   l.es = round_up(n_stats * sizeof(float), kAlign);
   l.tmp = l.es + round_up(n_stats * sizeof(float), kAlign);
-  // bookkeeping of the phase-1 pool: counters, then the chunk scratch slots
-  l.counters = l.tmp + round_up(n_tmp * sizeof(float), kAlign);
-  l.scratch = l.counters + round_up(pad::kPoolCounters * sizeof(unsigned), kAlign);
-  l.total = l.scratch + round_up((size_t)pad::kMaxPoolTickets * pad::piece_floats(D) * sizeof(float), kAlign);
+  // the balanced split's launch info
+  l.info = l.tmp + round_up(n_tmp * sizeof(float), kAlign);
+  l.total = l.info + round_up(pad::kInfoWords * sizeof(unsigned), kAlign);
   *out = l;
   return true;
 }
@@ -110,8 +111,7 @@ bool attach_workspace(pad::Plan* p, void* workspace, size_t workspace_bytes) {
   p->max_logits = reinterpret_cast<float*>(base + l.ml);
   p->exp_sums = reinterpret_cast<float*>(base + l.es);
   p->tmp_out = reinterpret_cast<float*>(base + l.tmp);
-  p->counters = reinterpret_cast<unsigned*>(base + l.counters);
-  p->scratch = reinterpret_cast<float*>(base + l.scratch);
+  p->info = reinterpret_cast<unsigned*>(base + l.info);
   return true;
 }
 
@@ -185,7 +185,7 @@ int32_t paged_attention_decode_workspace_init(void* workspace, size_t workspace_
   return status_of(pad::launch_workspace_fill(reinterpret_cast<float*>(base + l.ml),
                                               reinterpret_cast<float*>(base + l.es),
                                               reinterpret_cast<float*>(base + l.tmp), l.n_stats, l.n_tmp,
-                                              reinterpret_cast<unsigned*>(base + l.counters), pad::kPoolCounters,
+                                              reinterpret_cast<unsigned*>(base + l.info), pad::kInfoWords,
                                               static_cast<hipStream_t>(stream)));
 }
 
@@ -334,6 +334,74 @@ int32_t paged_attention_decode_choose_partition(int32_t num_seqs, int32_t num_he
     if (parts >= 2 && wg_one_pass * parts >= target) return p;
   }
   return 128;
+}
+
+int32_t paged_attention_decode_entry_ranges(const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                                            int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t block_size,
+                                            int32_t partition_size, int32_t num_cus, int32_t* entry_count,
+                                            int32_t* entry_begin, int32_t* entry_end) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || max_blocks_per_seq <= 0 ||
+      num_cus <= 0)
+    return PAD_ERR_SHAPE;
+  if (block_size != pad::kBlockTokens) return PAD_ERR_UNSUPPORTED;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PAD_ERR_UNSUPPORTED;
+  if (partition_size <= 0 || partition_size % block_size) return PAD_ERR_PARTITION;
+  if (num_seqs == 0) return 0;
+  if (!seq_lens || !entry_count || !entry_begin || !entry_end) return PAD_ERR_NULL;
+  const int64_t S = num_seqs, H = num_heads;
+  const int group = num_heads / num_kv_heads;
+  const int chunks = (group + pad::kMaxHeadsPerGroup - 1) / pad::kMaxHeadsPerGroup;
+  const int64_t gyc = (int64_t)num_kv_heads * chunks;
+  const int64_t maxtok = (int64_t)max_blocks_per_seq * block_size;
+  const int64_t np = (maxtok + partition_size - 1) / partition_size;
+  const bool bal = pad::balanced_split(S, gyc, np, max_blocks_per_seq, num_cus);
+  // live blocks per sequence and their prefix, as phase 1 derives them
+  std::vector<uint64_t> pre(S + 1, 0);
+  uint64_t nb_max = 0;
+  for (int64_t s = 0; s < S; ++s) {
+    const int64_t L = seq_lens[s];
+    const uint64_t nb = (L > 0 && L <= maxtok) ? (uint64_t)((L + block_size - 1) / block_size) : 0;
+    nb_max = nb > nb_max ? nb : nb_max;
+    pre[s + 1] = pre[s] + nb;
+  }
+  const uint64_t B = pre[S] * (uint64_t)gyc;
+  const uint64_t N = bal ? pad::balanced_ranges(B, nb_max, (unsigned)(pad::kBalancedWgsPerCu * num_cus),
+                                                (unsigned)np, (unsigned)num_cus)
+                         : 0;
+  for (int64_t s = 0; s < S; ++s) {
+    const int64_t L = seq_lens[s];
+    for (int64_t h = 0; h < H; ++h) {
+      int32_t* cnt = entry_count + s * H + h;
+      int32_t* lo = entry_begin + (s * H + h) * np;
+      int32_t* hi = entry_end + (s * H + h) * np;
+      if (L == 0 || L < 0 || L > maxtok) {
+        *cnt = L == 0 ? 0 : -1;
+        continue;
+      }
+      if (!bal) {
+        const int64_t n = (L + partition_size - 1) / partition_size;
+        *cnt = (int32_t)n;
+        for (int64_t e = 0; e < n; ++e) {
+          lo[e] = (int32_t)(e * partition_size);
+          hi[e] = (int32_t)std::min<int64_t>((e + 1) * partition_size, L);
+        }
+        continue;
+      }
+      const int64_t g = h / group;
+      const int64_t gy = g * chunks + (h - g * group) / pad::kMaxHeadsPerGroup;
+      const uint64_t nb = pre[s + 1] - pre[s];
+      const uint64_t g0 = (uint64_t)gyc * pre[s] + (uint64_t)gy * nb;
+      const uint64_t j0 = pad::range_owner(g0, N, B), j1 = pad::range_owner(g0 + nb - 1, N, B);
+      *cnt = (int32_t)(j1 - j0 + 1);
+      for (uint64_t j = j0; j <= j1; ++j) {
+        const uint64_t a = std::max<uint64_t>(j * B / N, g0) - g0;
+        const uint64_t b = std::min<uint64_t>((j + 1) * B / N, g0 + nb) - g0;
+        lo[j - j0] = (int32_t)(a * block_size);
+        hi[j - j0] = (int32_t)std::min<int64_t>((int64_t)b * block_size, L);
+      }
+    }
+  }
+  return bal ? 1 : 0;
 }
 
 const char* paged_attention_decode_strerror(int32_t status) {

@@ -115,22 +115,11 @@ struct AttnParams {
   int partition;       // tokens per partition (split)
   int num_partitions;  // NP (split)
   float qscale;        // scale * log2(e)
-  // phase-1 pool (pool_tickets == 0: none): partitions [main_parts, NP) of
-  // every (sequence, head group) are cut into chunks that workgroups take
-  // after their own partition
-  unsigned* counters;  // [0] tickets handed out, [1 + item] chunks done
-  float* scratch;      // [pool_tickets][piece_floats(D)]
+  // balanced split (balanced == 0: one workgroup per partition)
+  unsigned* info;      // launch info (N, B, block prefix) published by workgroup 0
   int gy_count;        // head groups per sequence (num_kv_heads * head_chunks)
-  int main_parts;      // partitions per (sequence, head group) owned by a workgroup
-  int pool_parts;      // NP - main_parts
-  int pool_chunks;     // chunks per pooled partition
-  int pool_chunk_blocks;
-  int pool_tickets;    // S * gy_count * pool_parts * pool_chunks
-  // phase-1 queue (queue == 0: none): a resident 1-D grid takes the live
-  // items from counters[0]; up to queue_tail of the last are cut into
-  // pool_chunks chunks of pool_chunk_blocks blocks
-  int queue;
-  int queue_tail;
+  int balanced;
+  int num_cus;         // compute units of the device
 };
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -195,20 +184,6 @@ constexpr float kLazyLog2 = 8.0f;
 #define PAD_KV_LOAD_POLICY 2
 #endif
 constexpr int kLayoutTiled = 1;
-#ifndef PAD_TICKET_LEAD
-// blocks before the end of a walk at which the next pool ticket is requested,
-// so that the request's round trip overlaps the last loads
-#define PAD_TICKET_LEAD 8
-#endif
-// Atomics on the pool's ticket counter, performed at system scope: every
-// workgroup, on whichever XCD, sees one sequence of values.
-__device__ inline unsigned atomic_add_system(unsigned* ptr, unsigned v) {
-  return __hip_atomic_fetch_add(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ inline void atomic_store_system(unsigned* ptr, unsigned v) {
-  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 
@@ -328,18 +303,8 @@ struct Walker {
   float acc[kMfmaPV ? 1 : GH][EPL];
   f32x4_t accm[kMfmaPV ? kSlices : 1];
   bool bad;
-  // Pool ticket requested during the walk (phase-1 pool): the counter to take
-  // it from (null: none), and the value (lane 0) once `asked`.
-  unsigned* ticket_ctr = nullptr;
-  unsigned next_ticket = 0;
-  bool asked = false;
 
   __device__ explicit Walker(int lane_) : lane(lane_), rbase(4 * (lane_ >> 4)) {}
-
-  __device__ void ask_ticket() {
-    if (lane == 0) next_ticket = atomic_add_system(ticket_ctr, 1u);
-    asked = true;
-  }
 
   // Q^T operand: lane l supplies head column l%16 and the 16-byte run of dims
   // that the same lane's K load holds.
@@ -362,7 +327,6 @@ struct Walker {
 #pragma unroll
     for (int j = 0; j < (kMfmaPV ? kSlices : 1); ++j) accm[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     bad = false;
-    asked = false;
   }
 
   // Multiply the accumulator rows of head h by the factor lane h holds.
@@ -400,8 +364,6 @@ struct Walker {
       const int first = seg + wave;
       const int n = first < seg_end ? (seg_end - first + NW - 1) / NW : 0;
       const int my_id = lane < n ? table_row[first + NW * lane] : -1;
-      // the pool ticket goes out PAD_TICKET_LEAD blocks before the walk ends
-      const int ask_at = (ticket_ctr != nullptr && seg_end == blk_end) ? max(0, n - PAD_TICKET_LEAD) : -1;
 
       // Enqueue the loads of the wave's idx-th block (zero-length, no traffic,
       // past the wave's last block).
@@ -508,7 +470,6 @@ struct Walker {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int idx = i + r;
-          if (idx == ask_at) ask_ticket();
           if (idx < n) compute(ring[r], first + NW * idx);
           issue(ring[r], idx + R);
         }
@@ -528,45 +489,6 @@ struct Walker {
     }
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
-  }
-
-  // Rows of heads [0, gc), each scaled by the factor lane h holds, into a
-  // scratch slot starting at byte `slot`: float kPieceStats + h * D + d.  One
-  // per-lane offset register; the rest rides in the scalar offset (which
-  // changes with the slot, so no per-store offset registers are kept live).
-  __device__ void write_piece(__amdgpu_buffer_rsrc_t rs, int slot, int gc, float inv_of_lane) const {
-    if constexpr (kMfmaPV) {
-      float inv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) inv[i] = __shfl(inv_of_lane, rbase + i);
-      const int voff = 4 * (kPieceStats + rbase * D + (lane & 15));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (rbase + i < gc) {
-#pragma unroll
-          for (int j = 0; j < kSlices; ++j)
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, accm[j][i] * inv[i]), rs, voff,
-                                                  slot + 4 * (i * D + 16 * j), 0);
-        }
-      }
-    } else {
-      // 8-byte stores: a buffer store of more than 8 bytes with a register
-      // scalar offset needs a wait state before its data registers are
-      // rewritten, which the compiler does not insert for that form
-      const int voff = 4 * (kPieceStats + EPL * lane);
-#pragma unroll
-      for (int h = 0; h < GH; ++h) {
-        if (h >= gc) continue;
-        const float ih = readlane_f(inv_of_lane, h);
-        if (lane < LPR) {
-#pragma unroll
-          for (int e = 0; e < EPL; e += 2)
-            __builtin_amdgcn_raw_buffer_store_b64(
-                __builtin_bit_cast(u32x2_t, f32x2_t{acc[h][e] * ih, acc[h][e + 1] * ih}), rs, voff,
-                slot + 4 * (h * D + e), 0);
-        }
-      }
-    }
   }
 
   // Normalised rows of heads [0, gc): store(h, d, value) with value scaled by
@@ -603,7 +525,8 @@ struct Walker {
 
 
 // One unit of phase-1 work for a workgroup: blocks [b0, b1) of sequence s,
-// KV head g, query heads [h0, h0 + gc), inside partition `part`.
+// KV head g, query heads [h0, h0 + gc); its entry goes to partition slot
+// `part` (split) or to the output (one-pass).
 struct WorkItem {
   int s, g, h0, gc, L, part, b0, b1;
   bool len_ok;
@@ -624,101 +547,74 @@ __device__ inline WorkItem make_item(const AttnParams& p, int s, int gy, int par
   return it;
 }
 
-// The pool of phase 1 (one-wave workgroups).  After its own partition every
-// workgroup takes tickets from p.counters[0] until the pool is empty.  Ticket
-// t is chunk t % pool_chunks (p.pool_chunk_blocks blocks) of pooled item
-// t / pool_chunks, that is partition main_parts + pp of one (sequence, head
-// group).  The chunk's partial result -- max, exp-sum and normalised rows, as
-// for a partition -- goes to scratch slot t, and phase 2 merges the chunk
-// entries together with the partition entries: the log-sum-exp merge is the
-// same whether a stretch of tokens arrives as one partition or as several
-// chunks.  The counter returns to zero by itself: every workgroup makes
-// exactly one failing request, and the one that receives the launch's last
-// value resets it.
-
-// Resolve the ticket the walk asked for (or ask now); false when the pool is
-// empty.
-template <class W_>
-__device__ inline bool take_ticket(const AttnParams& p, W_& w, unsigned* ticket) {
-  if (!w.asked) w.ask_ticket();
-  const unsigned t = __builtin_amdgcn_readfirstlane(w.next_ticket);
-  const unsigned total = (unsigned)p.pool_tickets;
-  if (t < total) {
-    *ticket = t;
-    return true;
-  }
-  const unsigned nwg = gridDim.x * gridDim.y * gridDim.z;
-  if (t == total + nwg - 1 && w.lane == 0) atomic_store_system(p.counters, 0u);
-  return false;
-}
-
-__device__ inline WorkItem ticket_item(const AttnParams& p, unsigned t) {
-  const int item = (int)t / p.pool_chunks;
-  const int c = (int)t - item * p.pool_chunks;
-  const int pp = item % p.pool_parts;
-  const int sg = item / p.pool_parts;
-  WorkItem it = make_item(p, sg / p.gy_count, sg % p.gy_count, p.main_parts + pp);
-  const int pblocks = p.partition / kBlockTokens;
-  const int lblocks = it.len_ok ? (it.L + kBlockTokens - 1) / kBlockTokens : 0;
-  const int pb0 = it.part * pblocks;
-  it.b0 = pb0 + c * p.pool_chunk_blocks;
-  it.b1 = min(min(it.b0 + p.pool_chunk_blocks, pb0 + pblocks), lblocks);
-  return it;
-}
-
-// The walker's partial result for ticket t -> scratch slot t (layout at
-// piece_floats).  A chunk without tokens stores max -inf, exp-sum 0, zero rows.
-template <class W_, int D>
-__device__ void store_chunk(const AttnParams& p, const W_& w, unsigned t, const WorkItem& it) {
+// The result of one wave's walk (after fold), written where the item says:
+// split, the entry (max logit in natural-log units, exp-sum relative to it,
+// normalised row per query head) in partition slot it.part; one-pass, the
+// output rows.  A block id outside the pool (w.bad) makes the rows and the
+// max NaN.
+template <class W_, int D, bool kSplit>
+__device__ inline void write_result(const AttnParams& p, const W_& w, const WorkItem& it) {
+  constexpr bool kMfmaPV = W_::kMfmaPV;
+  constexpr int EPL = W_::EPL;
+  constexpr int LPR = W_::LPR;
   const int lane = w.lane;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(reinterpret_cast<const char*>(p.scratch)), (short)0,
-      (int)((unsigned)kMaxPoolTickets * (unsigned)piece_floats(D) * 4u), kRsrcWord3);
-  const int slot = (int)t * piece_floats(D) * 4;
-  const bool empty = !(w.m_true > -INFINITY);
-  const float inv = (empty || w.bad) ? 0.0f : 1.0f / w.l_run;
-  w.write_piece(rs, slot, it.gc, inv);
-  if (lane < kMaxHeadsPerGroup) {
-    const float m = w.bad ? __builtin_nanf("") : w.m_true;
-    const float l = empty ? 0.0f : w.l_run * fast_exp2(w.m_run - w.m_true);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, m), rs, 4 * lane, slot, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, l), rs, 4 * (16 + lane), slot, 0);
+  const int H = p.num_heads;
+  const float nan = __builtin_nanf("");
+  const float inv = w.bad ? nan : 1.0f / w.l_run;
+  const size_t hstride = kSplit ? (size_t)p.num_partitions * D : (size_t)D;
+  float* base = p.out + ((size_t)it.s * H + it.h0) * D;
+  if constexpr (kSplit) base = p.tmp_out + ((size_t)it.s * H + it.h0) * hstride + (size_t)it.part * D;
+  if constexpr (kMfmaPV) {
+    w.write_rows(it.gc, inv, [&](int h, int d, float v) { base[h * hstride + d] = v; });
+  } else {
+    // four consecutive dims per store
+#pragma unroll
+    for (int h = 0; h < W_::kRowsHeld; ++h) {
+      if (h >= it.gc) continue;
+      const float ih = readlane_f(inv, h);
+      if (lane < LPR) {
+        float* dst = base + h * hstride + EPL * lane;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4)
+          *reinterpret_cast<f32x4_t*>(dst + e) =
+              f32x4_t{w.acc[h][e] * ih, w.acc[h][e + 1] * ih, w.acc[h][e + 2] * ih, w.acc[h][e + 3] * ih};
+      }
+    }
+  }
+  if constexpr (kSplit) {
+    // lane h holds head h's max and exp-sum
+    if (lane < it.gc) {
+      const size_t row = ((size_t)it.s * H + it.h0 + lane) * p.num_partitions + it.part;
+      p.max_logits[row] = w.bad ? nan : w.m_true * kLn2;
+      p.exp_sums[row] = w.l_run * fast_exp2(w.m_run - w.m_true);
+    }
   }
 }
 
-// ---- phase-1 queue ----
-// The live items of a launch: sequence s contributes n_s = ceil(L_s / P) x
-// (head groups) items (none for a length outside [1, W * 16]), enumerated
-// sequence by sequence, head group by head group, partition by partition.
-// pre[s] counts the items before sequence s; T = pre[S].  The last
-// K = min(T, queue_tail) items are cut into C chunks each, so a launch has
-// (T - K) + K * C tickets: ticket t < T - K is item t whole (its partition
-// entry), ticket T - K + j is chunk j % C of item T - K + j / C (scratch
-// slot j).  Only the first G = ceil(T / rounds) workgroups take part
-// (rounds = ceil(T / gridDim.x)); workgroup w < G starts on ticket w,
-// further tickets are G + the counter's value.
-struct QueueState {
+// ---- phase-1 balanced split ----
+// The launch's live units are the (block, head group) pairs of every
+// sequence with a valid, non-empty length, laid end to end: sequence s
+// occupies [gy_count * pre[s], gy_count * pre[s + 1]), head group gy of it
+// [gy_count * pre[s] + gy * nb_s, + nb_s), nb_s = ceil(L_s / 16), pre[s] the
+// live blocks of the sequences before s.  B = gy_count * pre[S] units are cut
+// into N ranges: workgroup j takes [floor(j B / N), floor((j + 1) B / N)).
+// The entry of the part of range j that lies in (sequence s, head group gy)
+// goes to partition slot j - owner(first unit of that head group), where
+// owner(x) = floor(((x + 1) N - 1) / B) is the range that holds unit x.
+struct Balance {
   unsigned* pre;  // LDS [S + 1]
   int* len;       // LDS [S]
-  unsigned T, K, cut, total;
-  unsigned G;     // workgroups that take part: the fewest that still need no more rounds
+  uint64_t B;
+  unsigned N;
 };
 
+// The live-block prefix (one wave; every workgroup computes the same), B and
+// N.  Workgroup 0 publishes them for phase 2.
 template <int kUnused = 0>
-__device__ inline QueueState queue_lds() {
-  __shared__ unsigned pre[kQueueMaxSeqs + 1];
-  __shared__ int len[kQueueMaxSeqs];
-  QueueState q;
-  q.pre = pre;
-  q.len = len;
-  q.T = q.K = q.cut = q.total = q.G = 0;
-  return q;
-}
-
-// The live-item prefix of the launch (one wave; every workgroup computes the
-// same).  Workgroup 0 also publishes T and pre[] for phase 2.
-__device__ inline void queue_prefix(const AttnParams& p, int lane, QueueState& q) {
-  constexpr int kRounds = kQueueMaxSeqs / kWave;
+__device__ inline Balance balance_plan(const AttnParams& p, int lane) {
+  __shared__ unsigned pre[kBalancedMaxSeqs + 1];
+  __shared__ int len[kBalancedMaxSeqs];
+  constexpr int kRounds = kBalancedMaxSeqs / kWave;
   const int S = p.num_seqs;
   const int maxtok = p.max_blocks * kBlockTokens;
   int L[kRounds];
@@ -727,109 +623,94 @@ __device__ inline void queue_prefix(const AttnParams& p, int lane, QueueState& q
     const int s = r * kWave + lane;
     L[r] = s < S ? p.seq_lens[s] : 0;
   }
-  unsigned run = 0;
+  unsigned run = 0, nb_max = 0;
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     if (r * kWave >= S) break;
     const int s = r * kWave + lane;
     const bool ok = s < S && L[r] > 0 && L[r] <= maxtok;
-    const unsigned n = ok ? (unsigned)((L[r] + p.partition - 1) / p.partition) * (unsigned)p.gy_count : 0u;
-    unsigned x = n;  // inclusive scan over the wave
+    const unsigned nb = ok ? (unsigned)((L[r] + kBlockTokens - 1) / kBlockTokens) : 0u;
+    nb_max = max(nb_max, nb);
+    unsigned x = nb;  // inclusive scan over the wave
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
       const unsigned y = __shfl_up(x, off);
       if (lane >= off) x += y;
     }
     if (s < S) {
-      q.pre[s] = run + x - n;
-      q.len[s] = L[r];
+      pre[s] = run + x - nb;
+      len[s] = L[r];
     }
     run += __shfl(x, kWave - 1);
   }
-  if (lane == 0) q.pre[S] = run;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) nb_max = max(nb_max, (unsigned)__shfl_xor(nb_max, off));
+  if (lane == 0) pre[S] = run;
   __builtin_amdgcn_wave_barrier();
-  q.T = __builtin_amdgcn_readfirstlane(run);
-  q.K = min(q.T, (unsigned)p.queue_tail);
-  q.cut = q.T - q.K;
-  q.total = q.cut + q.K * (unsigned)p.pool_chunks;
-  // T items over gridDim.x workgroups take ceil(T / gridDim.x) rounds; the
-  // fewest workgroups that need no more rounds share the items evenly, so
-  // no last round runs on a fraction of the workgroups
-  const unsigned rounds = (q.T + gridDim.x - 1) / gridDim.x;
-  q.G = rounds ? (q.T + rounds - 1) / rounds : 0u;
+  Balance b;
+  b.pre = pre;
+  b.len = len;
+  b.B = (uint64_t)__builtin_amdgcn_readfirstlane(run) * (uint64_t)p.gy_count;
+  b.N = __builtin_amdgcn_readfirstlane(
+      balanced_ranges(b.B, __builtin_amdgcn_readfirstlane(nb_max), gridDim.x, p.num_partitions, p.num_cus));
   if (blockIdx.x == 0) {
-    unsigned* info = p.counters + kQueueInfoOffset;
-    if (lane == 0) info[0] = q.T;
-    for (int s = lane; s < S; s += kWave) info[1 + s] = q.pre[s];
+    if (lane == 0) {
+      p.info[0] = b.N;
+      p.info[1] = (unsigned)b.B;
+      p.info[2] = (unsigned)(b.B >> 32);
+      p.info[3] = 0u;
+    }
+    for (int s = lane; s <= S; s += kWave) p.info[kInfoPrefix + s] = pre[s];
   }
+  return b;
 }
 
-// Ticket t -> its item; *chunk / *slot tell a chunk ticket from a whole one.
-__device__ inline WorkItem queue_item(const AttnParams& p, const QueueState& q, unsigned t, bool* chunk,
-                                      unsigned* slot) {
-  unsigned i;
-  int c = -1;
-  if (t < q.cut) {
-    i = t;
-  } else {
-    const unsigned j = t - q.cut;
-    i = q.cut + j / (unsigned)p.pool_chunks;
-    c = (int)(j % (unsigned)p.pool_chunks);
-    *slot = j;
+// Workgroup j of the balanced split: its range, one entry per head group it
+// meets.
+template <class W_, int D>
+__device__ inline void run_balanced(const AttnParams& p, W_& w, float* ptile) {
+  const Balance bal = balance_plan(p, w.lane);
+  const unsigned j = blockIdx.x;
+  if (j >= bal.N) return;
+  const uint64_t B = bal.B, N = bal.N;
+  const uint64_t gyc = (uint64_t)p.gy_count;
+  uint64_t a = (uint64_t)j * B / N;
+  const uint64_t end = ((uint64_t)j + 1) * B / N;
+  while (a < end) {
+    // the sequence: the last s with gy_count * pre[s] <= a (it has live blocks)
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (gyc * __builtin_amdgcn_readfirstlane(bal.pre[mid]) <= a) lo = mid;
+      else hi = mid - 1;
+    }
+    const int s = lo;
+    const uint64_t s0 = gyc * __builtin_amdgcn_readfirstlane(bal.pre[s]);
+    const int nb = (int)(__builtin_amdgcn_readfirstlane(bal.pre[s + 1]) - __builtin_amdgcn_readfirstlane(bal.pre[s]));
+    if (nb <= 0) break;  // cannot happen (the unit lies in sequence s); keeps every access in bounds regardless
+    const int gy = (int)((a - s0) / (uint64_t)nb);
+    const uint64_t g0 = s0 + (uint64_t)gy * (uint64_t)nb;  // first unit of (s, gy)
+    const uint64_t stop = min(end, g0 + (uint64_t)nb);
+    WorkItem it;
+    it.s = s;
+    it.g = gy / p.head_chunks;
+    const int hc = gy - it.g * p.head_chunks;
+    it.h0 = it.g * p.group + hc * kMaxHeadsPerGroup;
+    it.gc = min(kMaxHeadsPerGroup, p.group - hc * kMaxHeadsPerGroup);
+    it.L = __builtin_amdgcn_readfirstlane(bal.len[s]);
+    it.len_ok = true;
+    it.part = (int)(j - range_owner(g0, N, B));
+    it.b0 = (int)(a - g0);
+    it.b1 = (int)(stop - g0);
+    // the slot is below num_partitions by the choice of N; checked so that no store can leave the table
+    if (gy >= p.gy_count || it.part >= p.num_partitions) break;
+    w.reset();
+    w.load_q(p, it.s, it.h0, it.gc);
+    w.walk(p, it.s, it.g, it.L, it.b0, it.b1, 0, ptile);
+    w.fold();
+    write_result<W_, D, true>(p, w, it);
+    a = stop;
   }
-  *chunk = c >= 0;
-  // the sequence: the last s with pre[s] <= i (it has items, since pre[s + 1] > i)
-  int lo = 0, hi = p.num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (__builtin_amdgcn_readfirstlane(q.pre[mid]) <= i) lo = mid;
-    else hi = mid - 1;
-  }
-  const int s = lo;
-  const unsigned pre_s = __builtin_amdgcn_readfirstlane(q.pre[s]);
-  const int L = __builtin_amdgcn_readfirstlane(q.len[s]);
-  const int np_s = (L + p.partition - 1) / p.partition;
-  const int within = (int)(i - pre_s);
-  const int gy = within / np_s;
-  const int part = within - gy * np_s;
-  WorkItem it;
-  it.s = s;
-  it.g = gy / p.head_chunks;
-  const int hc = gy - it.g * p.head_chunks;
-  it.h0 = it.g * p.group + hc * kMaxHeadsPerGroup;
-  it.gc = min(kMaxHeadsPerGroup, p.group - hc * kMaxHeadsPerGroup);
-  it.L = L;
-  it.len_ok = true;
-  it.part = part;
-  const int pblocks = p.partition / kBlockTokens;
-  const int lblocks = (L + kBlockTokens - 1) / kBlockTokens;
-  const int pb0 = part * pblocks;
-  if (c < 0) {
-    it.b0 = pb0;
-    it.b1 = min(pb0 + pblocks, lblocks);
-  } else {
-    it.b0 = pb0 + c * p.pool_chunk_blocks;
-    it.b1 = min(min(it.b0 + p.pool_chunk_blocks, pb0 + pblocks), lblocks);
-  }
-  return it;
-}
-
-// Resolve the next queue ticket (asked for during the walk, or now); false
-// when the queue is empty.  Every taking-part workgroup makes one failing
-// request; the counter's max(total, G) - 1-th value resets it.
-template <class W_>
-__device__ inline bool take_queue_ticket(const AttnParams& p, W_& w, const QueueState& q, unsigned* ticket) {
-  if (!w.asked) w.ask_ticket();
-  const unsigned c = __builtin_amdgcn_readfirstlane(w.next_ticket);
-  const unsigned nwg = q.G;  // the workgroups that take part
-  const unsigned t = nwg + c;
-  if (t < q.total) {
-    *ticket = t;
-    return true;
-  }
-  const unsigned requests = q.total > nwg ? q.total : nwg;
-  if (c == requests - 1 && w.lane == 0) atomic_store_system(p.counters, 0u);
-  return false;
 }
 
 template <class DT, int D, int GH, int NW, bool kSplit, int LAYOUT>
@@ -844,7 +725,6 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
   constexpr int kTreeFloats = (NW / 2) * kRowsHeld * D;  // tree-merge buffer
   constexpr int kLdsFloats1 = (NW * kPTile > kTreeFloats) ? NW * kPTile : kTreeFloats;
   constexpr int kLdsFloats = kLdsFloats1 > 0 ? kLdsFloats1 : 1;
-  constexpr bool kPool = kSplit && NW == 1;
   static_assert((NW & (NW - 1)) == 0, "NW is a power of two");
 
   __shared__ float lds[kLdsFloats];  // rows layout: p tiles in the loop; then the tree-merge buffer
@@ -859,30 +739,18 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
   float* ptile = lds + wave * kPTile;
   W_ w(lane);
   const int rbase = w.rbase;
-  const int H = p.num_heads;
+
+  if constexpr (kSplit && NW == 1) {
+    if (p.balanced) {
+      run_balanced<W_, D>(p, w, ptile);
+      return;
+    }
+  }
 
   // the workgroup's own item: its partition (split) or the whole context
   WorkItem it = make_item(p, blockIdx.z, blockIdx.y, kSplit ? blockIdx.x : 0);
   bool live;
-  bool pooled = false;  // the current item is a chunk (scratch slot `ticket`)
-  unsigned ticket = 0;
-  [[maybe_unused]] QueueState q{};
-  if constexpr (kPool) {
-    if (p.queue) {
-      q = queue_lds();
-      queue_prefix(p, lane, q);
-    }
-  }
-  if (kPool && p.queue) {
-    if (blockIdx.x >= q.G) return;  // not taking part (makes no ticket request)
-    live = blockIdx.x < q.total;
-    if (live) {
-      it = queue_item(p, q, blockIdx.x, &pooled, &ticket);
-      live = !pooled;
-    } else {
-      it.b0 = it.b1 = 0;
-    }
-  } else if constexpr (kSplit) {
+  if constexpr (kSplit) {
     // partitions past the sequence end write nothing; an invalid length is
     // reported by phase 2
     const int tok_begin = it.part * p.partition;
@@ -893,131 +761,81 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
     if (!it.len_ok || it.L == 0) {
       const float fill = it.len_ok ? 0.0f : __builtin_nanf("");
       for (int i = threadIdx.x; i < it.gc * D; i += NW * kWave)
-        p.out[((size_t)it.s * H + it.h0 + i / D) * D + (i % D)] = fill;
+        p.out[((size_t)it.s * p.num_heads + it.h0 + i / D) * D + (i % D)] = fill;
       return;
     }
     live = true;
     it.b1 = (it.L + kBlockTokens - 1) / kBlockTokens;
   }
 
-  for (;;) {
-    w.reset();
-    if constexpr (kPool) w.ticket_ctr = (p.pool_tickets > 0 || p.queue) ? p.counters : nullptr;
-    if (it.b0 < it.b1) {
-      w.load_q(p, it.s, it.h0, it.gc);
-      w.walk(p, it.s, it.g, it.L, it.b0, it.b1, wave, ptile);
-    }
-    w.fold();
-
-    if (kPool && pooled) {
-      store_chunk<W_, D>(p, w, ticket, it);
-    } else {
-      // (head, dim) -> accumulator element held by this lane, for the merge and
-      // the epilogue.  rows: lanes < LPR hold dims EPL*lane..+EPL-1 of heads 0..GH-1.
-      // tiled: every lane holds heads rbase..rbase+3 at dims 16 j + lane%16.
-      if constexpr (NW > 1) {
-        // common max per head, each wave rescales itself, then a fixed-order tree sum
-        w.bad = __syncthreads_or(w.bad);
-        if (lane < kMaxHeadsPerGroup) {
-          m_lds[wave][lane] = w.m_run;
-          t_lds[wave][lane] = w.m_true;
-        }
-        __syncthreads();
-        float mx = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-          mx = fmaxf(mx, m_lds[ww][lane & 15]);
-          w.m_true = fmaxf(w.m_true, t_lds[ww][lane & 15]);
-        }
-        const float sc = fast_exp2(w.m_run - mx);
-        w.l_run *= sc;
-        w.scale_heads(sc);
-        w.m_run = mx;
-#pragma unroll
-        for (int half = NW / 2; half >= 1; half /= 2) {
-          __syncthreads();
-          if (wave >= half && wave < 2 * half) {
-            float* dst = lds + (wave - half) * kRowsHeld * D;
-            if constexpr (kMfmaPV) {
-#pragma unroll
-              for (int j = 0; j < kSlices; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[(rbase + i) * D + 16 * j + (lane & 15)] = w.accm[j][i];
-            } else if (lane < LPR) {
-#pragma unroll
-              for (int h = 0; h < kRowsHeld; ++h)
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) dst[h * D + EPL * lane + e] = w.acc[h][e];
-            }
-            if (lane < kMaxHeadsPerGroup) l_lds[wave - half][lane] = w.l_run;
-          }
-          __syncthreads();
-          if (wave < half) {
-            const float* src = lds + wave * kRowsHeld * D;
-            if constexpr (kMfmaPV) {
-#pragma unroll
-              for (int j = 0; j < kSlices; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w.accm[j][i] += src[(rbase + i) * D + 16 * j + (lane & 15)];
-            } else if (lane < LPR) {
-#pragma unroll
-              for (int h = 0; h < kRowsHeld; ++h)
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) w.acc[h][e] += src[h * D + EPL * lane + e];
-            }
-            w.l_run += l_lds[wave][lane & 15];
-          }
-        }
-        if (wave != 0) return;
-      }
-
-      // ---- epilogue (wave 0) ----
-      if (live) {
-        const float nan = __builtin_nanf("");
-        const float inv = w.bad ? nan : 1.0f / w.l_run;
-        const size_t hstride = kSplit ? (size_t)p.num_partitions * D : (size_t)D;
-        float* base = p.out + ((size_t)it.s * H + it.h0) * D;
-        if constexpr (kSplit) base = p.tmp_out + ((size_t)it.s * H + it.h0) * hstride + (size_t)it.part * D;
-        if constexpr (kMfmaPV) {
-          w.write_rows(it.gc, inv, [&](int h, int d, float v) { base[h * hstride + d] = v; });
-        } else {
-          // four consecutive dims per store
-#pragma unroll
-          for (int h = 0; h < kRowsHeld; ++h) {
-            if (h >= it.gc) continue;
-            const float ih = readlane_f(inv, h);
-            if (lane < LPR) {
-              float* dst = base + h * hstride + EPL * lane;
-#pragma unroll
-              for (int e = 0; e < EPL; e += 4)
-                *reinterpret_cast<f32x4_t*>(dst + e) =
-                    f32x4_t{w.acc[h][e] * ih, w.acc[h][e + 1] * ih, w.acc[h][e + 2] * ih, w.acc[h][e + 3] * ih};
-            }
-          }
-        }
-        if constexpr (kSplit) {
-          // lane h holds head h's max and exp-sum
-          if (lane < it.gc) {
-            const size_t row = ((size_t)it.s * H + it.h0 + lane) * p.num_partitions + it.part;
-            p.max_logits[row] = w.bad ? nan : w.m_true * kLn2;
-            p.exp_sums[row] = w.l_run * fast_exp2(w.m_run - w.m_true);
-          }
-        }
-      }
-    }
-
-    if constexpr (!kPool) break;
-    if (p.queue) {
-      unsigned t;
-      if (!take_queue_ticket(p, w, q, &t)) break;
-      it = queue_item(p, q, t, &pooled, &ticket);
-      live = !pooled;
-    } else {
-      if (p.pool_tickets == 0 || !take_ticket(p, w, &ticket)) break;
-      it = ticket_item(p, ticket);
-      pooled = true;
-    }
+  w.reset();
+  if (it.b0 < it.b1) {
+    w.load_q(p, it.s, it.h0, it.gc);
+    w.walk(p, it.s, it.g, it.L, it.b0, it.b1, wave, ptile);
   }
+  w.fold();
+
+  // (head, dim) -> accumulator element held by this lane, for the merge and
+  // the epilogue.  rows: lanes < LPR hold dims EPL*lane..+EPL-1 of heads 0..GH-1.
+  // tiled: every lane holds heads rbase..rbase+3 at dims 16 j + lane%16.
+  if constexpr (NW > 1) {
+    // common max per head, each wave rescales itself, then a fixed-order tree sum
+    w.bad = __syncthreads_or(w.bad);
+    if (lane < kMaxHeadsPerGroup) {
+      m_lds[wave][lane] = w.m_run;
+      t_lds[wave][lane] = w.m_true;
+    }
+    __syncthreads();
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      mx = fmaxf(mx, m_lds[ww][lane & 15]);
+      w.m_true = fmaxf(w.m_true, t_lds[ww][lane & 15]);
+    }
+    const float sc = fast_exp2(w.m_run - mx);
+    w.l_run *= sc;
+    w.scale_heads(sc);
+    w.m_run = mx;
+#pragma unroll
+    for (int half = NW / 2; half >= 1; half /= 2) {
+      __syncthreads();
+      if (wave >= half && wave < 2 * half) {
+        float* dst = lds + (wave - half) * kRowsHeld * D;
+        if constexpr (kMfmaPV) {
+#pragma unroll
+          for (int j = 0; j < kSlices; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(rbase + i) * D + 16 * j + (lane & 15)] = w.accm[j][i];
+        } else if (lane < LPR) {
+#pragma unroll
+          for (int h = 0; h < kRowsHeld; ++h)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) dst[h * D + EPL * lane + e] = w.acc[h][e];
+        }
+        if (lane < kMaxHeadsPerGroup) l_lds[wave - half][lane] = w.l_run;
+      }
+      __syncthreads();
+      if (wave < half) {
+        const float* src = lds + wave * kRowsHeld * D;
+        if constexpr (kMfmaPV) {
+#pragma unroll
+          for (int j = 0; j < kSlices; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w.accm[j][i] += src[(rbase + i) * D + 16 * j + (lane & 15)];
+        } else if (lane < LPR) {
+#pragma unroll
+          for (int h = 0; h < kRowsHeld; ++h)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) w.acc[h][e] += src[h * D + EPL * lane + e];
+        }
+        w.l_run += l_lds[wave][lane & 15];
+      }
+    }
+    if (wave != 0) return;
+  }
+
+  // ---- epilogue (wave 0) ----
+  if (live) write_result<W_, D, kSplit>(p, w, it);
 }
 
 using AttnKernelFn = void (*)(AttnParams);

@@ -13,31 +13,75 @@ constexpr int kBlockTokens = 16;
 // Query heads one workgroup serves: the N width of the 16x16 matrix-core tile.
 constexpr int kMaxHeadsPerGroup = 16;
 
-// Phase-1 load balance.  Two modes share the chunk machinery:
-//  * pool (a launch that fills the GPU once to four times over, but not by a
-//    whole multiple of the compute units): workgroups are launched for the
-//    first partitions only; the remaining partitions are cut into chunks that
-//    workgroups take when they finish their own partition;
-//  * queue (a launch of more than four workgroups per compute unit, at most
-//    kQueueMaxSeqs sequences): a resident grid of 4 workgroups per compute
-//    unit takes the live (sequence, head group, partition) items from a
-//    ticket counter, the last ones cut into chunks.
-// Phase 2 merges chunk entries with partition entries.  The workspace holds
-// the ticket counter, the queue's live-item prefix (for phase 2) and one
-// scratch slot per chunk.
-constexpr int kMaxPoolChunks = 32;    // chunks per pooled partition
-constexpr int kMaxPoolTickets = 512;  // chunks per launch
-constexpr int kQueueMaxSeqs = 1024;
-// counter area: the ticket counter alone in its first 256 bytes, then the
-// queue's live-item count T and the live items before each sequence
-constexpr int kQueueInfoOffset = 64;  // in uint32 (256 bytes)
-constexpr int kPoolCounters = kQueueInfoOffset + 1 + kQueueMaxSeqs;
-// One chunk entry in the scratch area (floats): per head h < 16 of the
-// group its max logit (log2 units; -inf when the chunk holds no token, NaN
-// after a block id outside the pool) at [h], its exp-sum relative to that max
-// at [16 + h], and its normalised partial output row at [kPieceStats + h * D].
-constexpr int kPieceStats = 64;
-__host__ __device__ constexpr int piece_floats(int d) { return kPieceStats + kMaxHeadsPerGroup * d; }
+// Phase-1 load balance: the balanced split.  When a launch's fixed-size
+// partitions would give more workgroups than compute units (and it has at
+// most kBalancedMaxSeqs sequences), phase 1 does not cut each context into
+// partition_size-token partitions.  It lays the live (KV block, head group)
+// units of all sequences end to end -- sequence by sequence, head group by
+// head group, block by block -- and cuts that line into N equal ranges, one
+// per resident one-wave workgroup.  Workgroup j walks units
+// [floor(j B / N), floor((j + 1) B / N)) of the B live units; where its range
+// crosses from one (sequence, head group) into the next, it writes one entry
+// per (sequence, head group) it touched.  An entry is what a partition entry
+// is (max logit, exp-sum, normalised partial output per query head), for a
+// contiguous stretch of blocks rather than a fixed partition; the entries of
+// a (sequence, head group) occupy its partition slots 0, 1, ... in order.  N
+// is capped so that no (sequence, head group) gets more entries than it has
+// partition slots.  Workgroup 0 publishes N, B and the per-sequence block
+// prefix in the workspace's launch-info area, which phase 2 reads to find how
+// many entries each (sequence, head) has.  Nothing in the workspace is read
+// by phase 1, so no state carries from call to call.
+constexpr int kBalancedMaxSeqs = 1024;
+// Resident one-wave workgroups per compute unit that the balanced split
+// launches.
+#ifndef PAD_BALANCED_WGS_PER_CU
+#define PAD_BALANCED_WGS_PER_CU 3
+#endif
+constexpr int kBalancedWgsPerCu = PAD_BALANCED_WGS_PER_CU;
+// Fewest blocks a balanced range holds (a range costs a query load, a table
+// load and an entry write besides its blocks).
+constexpr int kMinRangeBlocks = 8;
+// launch-info words: [0] N, [1] B low 32 bits, [2] B high 32 bits,
+// [3] zero, [4 + s] live blocks before sequence s (per head group), s <= S
+constexpr int kInfoPrefix = 4;
+constexpr int kInfoWords = kInfoPrefix + kBalancedMaxSeqs + 1;
+
+// Whether phase 1 runs the balanced split: one workgroup per partition would
+// give more workgroups than compute units, the batch has at most
+// kBalancedMaxSeqs sequences, every head group has at least two partition
+// slots, and the live blocks per head group fit 31 bits.  Phase 1, phase 2 and
+// the host-side plan derive it from the same sizes and compute-unit count.
+inline bool balanced_split(int64_t num_seqs, int64_t head_groups, int64_t num_partitions, int64_t max_blocks,
+                           int64_t cus) {
+  return num_seqs * head_groups * num_partitions > cus && num_seqs <= kBalancedMaxSeqs && num_partitions >= 2 &&
+         num_seqs * max_blocks < ((int64_t)1 << 31);
+}
+
+// Which range holds unit x (the largest j with floor(j B / N) <= x).
+__host__ __device__ inline uint64_t range_owner(uint64_t x, uint64_t N, uint64_t B) {
+  return ((x + 1) * N - 1) / B;
+}
+
+// N for B units of which one head group holds at most nb_max: at most
+// `wgs` ranges, at least kMinRangeBlocks units per range, and at most
+// `slots` ranges touching any one head group (a head group of nb units meets
+// at most 1 + ceil(nb N / B) ranges, so N nb_max <= (slots - 1) B suffices);
+// above `cus`, a whole multiple of `cus`.  0 when there is nothing to do.
+__host__ __device__ inline unsigned balanced_ranges(uint64_t B, uint64_t nb_max, unsigned wgs, unsigned slots,
+                                                    unsigned cus) {
+  if (B == 0 || nb_max == 0 || slots < 2 || wgs == 0) return 0;
+  uint64_t n = wgs;
+  const uint64_t a = slots - 1;
+  const uint64_t lim = (uint64_t)wgs * nb_max;  // n nb_max <= a B for every n <= wgs once a B >= lim
+  if (B < (lim + a - 1) / a) {
+    const uint64_t cap = a * B / nb_max;  // a B < lim: no overflow
+    if (cap < n) n = cap;
+  }
+  const uint64_t by_size = (B + kMinRangeBlocks - 1) / kMinRangeBlocks;
+  if (by_size < n) n = by_size;
+  if (cus > 0 && n > cus) n = n / cus * cus;
+  return n < 1 ? 1u : (unsigned)n;
+}
 
 // Everything the launchers need, validated and derived on the host.
 struct Plan {
@@ -59,8 +103,7 @@ struct Plan {
   float* max_logits;  // [S, H, NP]
   float* exp_sums;    // [S, H, NP]
   float* tmp_out;     // [S, H, NP, D]
-  unsigned* counters; // [kPoolCounters]: [0] ticket counter (zero between calls); queue info
-  float* scratch;     // [kMaxPoolTickets][piece_floats(D)]: chunk entries
+  unsigned* info;     // [kInfoWords]: the balanced split's launch info
 };
 
 hipError_t launch_phase1(const Plan& plan, const void* query, const void* key_cache,
@@ -76,7 +119,7 @@ hipError_t launch_one_pass(const Plan& plan, float* out, const void* query,
                            hipStream_t stream);
 
 hipError_t launch_workspace_fill(float* max_logits, float* exp_sums, float* tmp_out,
-                                 size_t n_stats, size_t n_tmp, unsigned* counters,
-                                 size_t n_counters, hipStream_t stream);
+                                 size_t n_stats, size_t n_tmp, unsigned* info,
+                                 size_t n_info, hipStream_t stream);
 
 }  // namespace pad

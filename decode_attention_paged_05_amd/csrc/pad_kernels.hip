@@ -31,15 +31,20 @@ namespace {
 // Phase 2: log-sum-exp merge.  Grid (D / kDims, H, S), kThreads threads (one
 // wave or four); the workgroup owns kDims dims of one (sequence, head), as
 // kDims / 4 dim lanes (4 dims each) x G source groups.  Thread t = kDims/4 g + l
-// takes dims 4 l .. 4 l + 3 of sources g, g + G, g + 2 G, ... (a source is a
-// partition entry or a chunk entry).  Every load of a round -- each source's
-// max and exp-sum and its four dims -- is issued before any arithmetic (the
-// merge is latency-bound, not bandwidth-bound).  Each thread keeps a running
-// max, exp-sum and weighted row over its own sources; the source groups are
-// then combined by the same log-sum-exp rule, by shuffles within a wave and
-// through LDS across waves.  Slots past the sequence's source count are read
-// (they exist) but discarded by select, so stale or NaN contents never enter
-// the sums.
+// takes dims 4 l .. 4 l + 3 of entries g, g + G, g + 2 G, ... of the head's
+// partition slots.  Every load of a round -- each entry's max and exp-sum and
+// its four dims -- is issued before any arithmetic (the merge is
+// latency-bound, not bandwidth-bound), and the first round is issued before
+// the entry count is known.  Each thread keeps a running max, exp-sum and
+// weighted row over its own entries; the source groups are then combined by
+// the same log-sum-exp rule, by shuffles within a wave and through LDS across
+// waves.  Slots past the head's entry count are read (they exist) but
+// discarded by select, so stale or NaN contents never enter the sums.
+//
+// Entry count of (sequence s, head h): ceil(L_s / P) for one workgroup per
+// partition; for the balanced split, the ranges that meet its head group,
+// from the launch info phase 1 published (which must match this call's
+// lengths, or the row is NaN).
 // ---------------------------------------------------------------------------
 struct MergeParams {
   float* out;
@@ -52,35 +57,49 @@ struct MergeParams {
   int max_tokens;  // W * block_size
   int partition;
   int num_partitions;
-  // phase-1 pool (pool_chunks == 0: none): partitions >= main_parts arrive as
-  // pool_chunks chunk entries each in `scratch`
-  const float* scratch;
-  int main_parts;
-  int pool_parts;
-  int pool_chunks;
+  int balanced;
+  const unsigned* info;  // balanced: launch info of phase 1
+  int num_seqs;
   int gy_count;
   int head_chunks;
   int group;
-  // phase-1 queue (queue == 0: none): queue_info[0] = T live items,
-  // queue_info[1 + s] = items before sequence s; the last min(T, queue_tail)
-  // items arrive as pool_chunks chunk entries each
-  int queue;
-  int queue_tail;
-  const unsigned* queue_info;
 };
 
 // Merge workgroup shapes: kThreads threads own kDims dims of one (sequence,
 // head); kDims / 4 "dim lanes" (4 dims each) x kThreads / (kDims / 4) source
-// groups.  Sources per round: 256 for 256 threads, 64 for one wave.
-template <int kThreads, int kDims>
+// groups, kRound sources per round of loads.
+template <int kThreads, int kDims, int kRound>
 struct MergeShape {
   static constexpr int kDL = kDims / 4;            // dim lanes
   static constexpr int kG = kThreads / kDL;        // source groups
-  static constexpr int kPerThread = (kThreads == 64 ? 64 : 256) / kG;  // sources per thread per round
+  static constexpr int kPerThread = kRound / kG;   // sources per thread per round
   static constexpr int kChunk = kG * kPerThread;   // sources per round
   static constexpr int kWaves = kThreads / kWave;
   static_assert(kDL >= 1 && kDL <= 16 && (kWave % kDL) == 0, "dim lanes within a wave");
+  static_assert(kPerThread >= 1 && kChunk == kRound, "a round is a whole number of sources per thread");
 };
+
+// Entries to merge for (sequence s, head h): > 0; 0 for an empty sequence
+// (zero row); -1 for a row that must be NaN (a length outside [0, W * 16],
+// or launch info that does not match the lengths).
+__device__ inline int merge_sources(const MergeParams& p, int s, int h) {
+  const int L = p.seq_lens[s];
+  if (L == 0) return 0;
+  if (L < 0 || L > p.max_tokens) return -1;
+  if (!p.balanced) return (L + p.partition - 1) / p.partition;
+  const unsigned N = p.info[0];
+  const uint64_t B = (uint64_t)p.info[1] | ((uint64_t)p.info[2] << 32);
+  const unsigned pre_s = p.info[kInfoPrefix + s];
+  const unsigned pre_s1 = p.info[kInfoPrefix + s + 1];
+  const unsigned pre_all = p.info[kInfoPrefix + p.num_seqs];
+  const unsigned nb = (unsigned)((L + kBlockTokens - 1) / kBlockTokens);
+  if (N == 0 || pre_s1 - pre_s != nb || B != (uint64_t)pre_all * (uint64_t)p.gy_count) return -1;
+  const int g = h / p.group;
+  const int gy = g * p.head_chunks + (h - g * p.group) / kMaxHeadsPerGroup;
+  const uint64_t g0 = (uint64_t)p.gy_count * pre_s + (uint64_t)gy * nb;
+  const uint64_t n = range_owner(g0 + nb - 1, N, B) - range_owner(g0, N, B) + 1;
+  return n > (uint64_t)p.num_partitions ? -1 : (int)n;
+}
 
 // Log-sum-exp combine of (max m, exp-sum l, weighted row a) with another
 // partial; an empty partial has m = -inf, l = 0, a = 0; NaN propagates.
@@ -93,9 +112,9 @@ __device__ inline void lse_combine(float& m, float& l, f32x4_t& a, float m2, flo
   m = M;
 }
 
-template <int kThreads, int kDims>
+template <int kThreads, int kDims, int kRound>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
-  using SH = MergeShape<kThreads, kDims>;
+  using SH = MergeShape<kThreads, kDims, kRound>;
   constexpr int kDL = SH::kDL;
   constexpr int kMergeGroups = SH::kG;
   constexpr int kMergePerThread = SH::kPerThread;
@@ -118,79 +137,29 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
   const float* es = p.exp_sums + row0;
   const float* tmp = p.tmp_out + row0 * D + d0 + 4 * dl;
   float* orow = p.out + ((size_t)s * p.num_heads + h) * D + d0;
-  // Sources: partition entries [0, n_reg), then the chunk entries of the
-  // partitions from n_reg on, C per partition, in scratch slots first_slot,
-  // first_slot + 1, ...
-  const int C = p.pool_chunks;
-  // this head's place among the pooled items and inside a chunk entry
-  const int g = h / p.group;
-  const int within = h - g * p.group;
-  const int hc = within / kMaxHeadsPerGroup;
-  const int hh = within - hc * kMaxHeadsPerGroup;
-  const int gy = g * p.head_chunks + hc;
-  int n_reg, n_src, first_slot;
-  int nvalid = -1;  // sources of this sequence (pool / plain: known after the first round's loads)
-  if (p.queue) {
-    // the sequence's live items are pre_s + gy * np + partition; items from
-    // cut = T - K on are chunked (slot = (item - cut) * C + chunk)
-    const int L = p.seq_lens[s];
-    if (L <= 0 || L > p.max_tokens) {
-      if (tid < kDims) orow[tid] = (L == 0) ? 0.0f : __builtin_nanf("");
-      return;
-    }
-    const int np = (L + p.partition - 1) / p.partition;
-    const unsigned T = p.queue_info[0];
-    const unsigned K = T < (unsigned)p.queue_tail ? T : (unsigned)p.queue_tail;
-    const long long cut = (long long)(T - K);
-    const long long base = (long long)p.queue_info[1 + s] + (long long)gy * np;
-    const long long r = cut - base;
-    n_reg = r <= 0 ? 0 : (r >= np ? np : (int)r);
-    first_slot = (int)((base + n_reg - cut) * C);
-    n_src = n_reg + (np - n_reg) * C;
-    nvalid = n_src;
-  } else if (C > 0) {
-    // pool: partitions [main_parts, NP) of every (sequence, head group), item
-    // (s * gy_count + gy) * pool_parts + pp, slot item * C + chunk
-    n_reg = p.main_parts;
-    n_src = p.main_parts + p.pool_parts * C;
-    first_slot = (s * p.gy_count + gy) * p.pool_parts * C;
-  } else {
-    n_reg = NP;
-    n_src = NP;
-    first_slot = 0;
-  }
-  const int PF = piece_floats(D);
-
   f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
   float lrun = 0.0f;
   float mrun = -INFINITY;  // running max of this thread's sources, log2 units
-  for (int c0 = 0; c0 < n_src; c0 += kMergeChunk) {
-    // one round of loads: sources that exist, whatever the sequence length
+  int nvalid = -1;         // entries of this (sequence, head): known after the first round's loads are issued
+  for (int c0 = 0; c0 < NP; c0 += kMergeChunk) {
+    // one round of loads: slots that exist, whatever the entry count (a slot
+    // past the table reads slot 0, dropped below by select)
     float m2[kMergePerThread], l[kMergePerThread];
     f32x4_t t[kMergePerThread];
 #pragma unroll
     for (int k = 0; k < kMergePerThread; ++k) {
-      // branch-free: pick the three addresses, load unconditionally (a source
-      // past the list reads partition 0's entry, dropped below by select)
       const int i = c0 + pg + kMergeGroups * k;
-      const bool reg = i < n_reg || i >= n_src;
-      const int ir = i < n_reg ? i : 0;
-      const float* q = p.scratch + (size_t)(reg ? 0 : first_slot + (i - n_reg)) * PF;
-      const float* pm = reg ? ml + ir : q + hh;
-      const float* pl = reg ? es + ir : q + 16 + hh;
-      const float* pr = reg ? tmp + (size_t)ir * D : q + kPieceStats + hh * D + d0 + 4 * dl;
-      m2[k] = *pm * (reg ? kLog2e : 1.0f);
-      l[k] = *pl;
-      t[k] = *reinterpret_cast<const f32x4_t*>(pr);
+      const int ir = i < NP ? i : 0;
+      m2[k] = ml[ir] * kLog2e;
+      l[k] = es[ir];
+      t[k] = *reinterpret_cast<const f32x4_t*>(tmp + (size_t)ir * D);
     }
     if (nvalid < 0) {
-      const int L = p.seq_lens[s];
-      if (L <= 0 || L > p.max_tokens) {
-        if (tid < kDims) orow[tid] = (L == 0) ? 0.0f : __builtin_nanf("");
+      nvalid = merge_sources(p, s, h);
+      if (nvalid <= 0) {
+        if (tid < kDims) orow[tid] = (nvalid == 0) ? 0.0f : __builtin_nanf("");
         return;
       }
-      const int np = (L + p.partition - 1) / p.partition;
-      nvalid = C > 0 ? (np <= n_reg ? np : n_reg + (np - n_reg) * C) : np;
     }
     if (c0 >= nvalid) break;
     float cm = -INFINITY;
@@ -206,8 +175,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
 #pragma unroll
     for (int k = 0; k < kMergePerThread; ++k) {
       if (c0 + pg + kMergeGroups * k >= nvalid) continue;
-      // a chunk without tokens (max -inf, exp-sum 0) weighs nothing; a NaN max
-      // (a bad block id in phase 1) poisons the row
+      // an entry without tokens (max -inf, exp-sum 0) weighs nothing; a NaN
+      // max (a bad block id in phase 1) poisons the row
       const float w = m2[k] > -INFINITY ? l[k] * fast_exp2(m2[k] - mrun) : (m2[k] != m2[k] ? m2[k] : 0.0f);
       lrun += w;
       a += w * t[k];
@@ -240,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(float* ml, float* es, float* tmp, size_t n_stats,
-                                                   size_t n_tmp, unsigned* counters, size_t n_counters) {
+                                                   size_t n_tmp, unsigned* info, size_t n_info) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (size_t i = i0; i < n_stats; i += stride) {
@@ -248,7 +217,7 @@ __global__ __launch_bounds__(256) void fill_kernel(float* ml, float* es, float* 
     es[i] = 0.0f;
   }
   for (size_t i = i0; i < n_tmp; i += stride) tmp[i] = 0.0f;
-  for (size_t i = i0; i < n_counters; i += stride) counters[i] = 0u;
+  for (size_t i = i0; i < n_info; i += stride) info[i] = 0u;
 }
 
 // Smallest instantiated accumulator width that holds `heads` heads.
@@ -301,67 +270,17 @@ AttnParams make_params(const Plan& plan, const void* q, const void* k, const voi
   a.max_logits = plan.max_logits;
   a.exp_sums = plan.exp_sums;
   a.tmp_out = plan.tmp_out;
-  a.counters = plan.counters;
-  a.scratch = plan.scratch;
+  a.info = plan.info;
   a.gy_count = plan.num_kv_heads * plan.head_chunks;
+  a.num_cus = device_cus();
   return a;
 }
 
-#ifndef PAD_POOL_CHUNK_BLOCKS
-#define PAD_POOL_CHUNK_BLOCKS 4  // blocks per pooled chunk
-#endif
 
-// The load-balance rule (phase 1 and phase 2 derive the same plan from the
-// same sizes).  With `items` one-wave partition workgroups and C compute units:
-//  * C < items <= 4 C, not a multiple of C (one resident round): pool.  The
-//    first k * C partition workgroups (k = items / C) are launched; the other
-//    partitions of every (sequence, head group) are cut into chunks;
-//  * items > 4 C and at most kQueueMaxSeqs sequences: queue.  4 C resident
-//    workgroups take live items from the ticket counter; up to
-//    kMaxPoolTickets / chunks of the last live items are cut into chunks.
-struct PoolPlan {
-  int main_parts = 0;  // pool: partitions per (sequence, head group) launched as workgroups
-  int pool_parts = 0;
-  int chunks = 0;      // chunks per pooled partition (or queue tail item); 0 = neither mode
-  int chunk_blocks = 0;
-  int tickets = 0;     // pool: chunk tickets
-  bool queue = false;
-  int queue_wgs = 0;   // queue: resident workgroups
-  int queue_tail = 0;  // queue: most tail items cut into chunks
-};
-
-PoolPlan plan_pool(const Plan& plan) {
-  PoolPlan pp;
-  const int np = plan.num_partitions;
-  pp.main_parts = np;
-  if (PAD_SPLIT_WAVES != 1 || plan.counters == nullptr || plan.scratch == nullptr) return pp;
-  const int64_t per_col = (int64_t)plan.num_seqs * plan.num_kv_heads * plan.head_chunks;
-  const int64_t items = per_col * np;
-  const int64_t cus = device_cus();
-  const int pblocks = plan.partition / kBlockTokens;
-  const int cb = PAD_POOL_CHUNK_BLOCKS;
-  const int chunks = (pblocks + cb - 1) / cb;
-  if (chunks > kMaxPoolChunks) return pp;
-  if (items > 4 * cus) {
-    if (plan.num_seqs > kQueueMaxSeqs) return pp;
-    pp.queue = true;
-    pp.queue_wgs = (int)(4 * cus);
-    pp.chunks = chunks;
-    pp.chunk_blocks = cb;
-    pp.queue_tail = kMaxPoolTickets / chunks;
-    return pp;
-  }
-  if (items <= cus || items % cus == 0) return pp;
-  const int64_t main_parts = (items / cus) * cus / per_col;
-  const int64_t pool_parts = np - main_parts;
-  const int64_t tickets = per_col * pool_parts * chunks;
-  if (main_parts < 1 || pool_parts < 1 || tickets > kMaxPoolTickets) return pp;
-  pp.main_parts = (int)main_parts;
-  pp.pool_parts = (int)pool_parts;
-  pp.chunks = chunks;
-  pp.chunk_blocks = cb;
-  pp.tickets = (int)tickets;
-  return pp;
+bool use_balanced(const Plan& plan) {
+  return PAD_SPLIT_WAVES == 1 && plan.info != nullptr &&
+         balanced_split(plan.num_seqs, (int64_t)plan.num_kv_heads * plan.head_chunks, plan.num_partitions,
+                        plan.max_blocks, device_cus());
 }
 
 }  // namespace
@@ -369,16 +288,10 @@ PoolPlan plan_pool(const Plan& plan) {
 hipError_t launch_phase1(const Plan& plan, const void* query, const void* key_cache, const void* value_cache,
                          const int32_t* block_tables, const int32_t* seq_lens, hipStream_t stream) {
   AttnParams a = make_params(plan, query, key_cache, value_cache, block_tables, seq_lens);
-  const PoolPlan pp = plan_pool(plan);
-  a.main_parts = pp.main_parts;
-  a.pool_parts = pp.pool_parts;
-  a.pool_chunks = pp.chunks;
-  a.pool_chunk_blocks = pp.chunk_blocks;
-  a.pool_tickets = pp.tickets;
-  a.queue = pp.queue ? 1 : 0;
-  a.queue_tail = pp.queue_tail;
-  const dim3 grid = pp.queue ? dim3((unsigned)pp.queue_wgs)
-                             : dim3(pp.main_parts, plan.num_kv_heads * plan.head_chunks, plan.num_seqs);
+  const bool bal = use_balanced(plan);
+  a.balanced = bal ? 1 : 0;
+  const dim3 grid = bal ? dim3((unsigned)(kBalancedWgsPerCu * a.num_cus))
+                        : dim3(plan.num_partitions, plan.num_kv_heads * plan.head_chunks, plan.num_seqs);
   const int gh = heads_template(plan.heads_per_wg);
   if (plan.layout == kLayoutTiled)
     return plan.dtype == 0 ? launch_attn_f32_tiled_split(a, plan.head_size, gh, grid, stream)
@@ -421,61 +334,59 @@ hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens, 
   m.max_tokens = plan.max_blocks * kBlockTokens;
   m.partition = plan.partition;
   m.num_partitions = plan.num_partitions;
-  const PoolPlan pp = plan_pool(plan);
-  m.scratch = plan.scratch;
-  m.main_parts = pp.main_parts;
-  m.pool_parts = pp.pool_parts;
-  m.pool_chunks = pp.chunks;
+  m.balanced = use_balanced(plan) ? 1 : 0;
+  m.info = plan.info;
+  m.num_seqs = plan.num_seqs;
   m.gy_count = plan.num_kv_heads * plan.head_chunks;
   m.head_chunks = plan.head_chunks;
   m.group = plan.group;
-  m.queue = pp.queue ? 1 : 0;
-  m.queue_tail = pp.queue_tail;
-  m.queue_info = plan.counters + kQueueInfoOffset;
-  const dim3 grid(plan.head_size / 64, plan.num_heads, plan.num_seqs);
   void* args[] = {&m};
+  const int D = plan.head_size;
+  auto launch = [&](const void* k, int threads, int dims) {
+    return hipLaunchKernel(k, dim3(D / dims, plan.num_heads, plan.num_seqs), dim3(threads), args, 0, stream);
+  };
+#define PAD_MERGE(T, DIMS, R) launch(reinterpret_cast<const void*>(&merge_kernel<T, DIMS, R>), T, DIMS)
 #if PAD_MERGE_SHAPE
-  // fixed shape (tuning builds): 1 <64,64>, 2 <256,16>, 3 <256,32>, 4 <256,64>, 5 <64,16>, 6 <64,32>
-  {
-    const void* k = PAD_MERGE_SHAPE == 1 ? reinterpret_cast<const void*>(&merge_kernel<64, 64>)
-                  : PAD_MERGE_SHAPE == 2 ? reinterpret_cast<const void*>(&merge_kernel<256, 16>)
-                  : PAD_MERGE_SHAPE == 3 ? reinterpret_cast<const void*>(&merge_kernel<256, 32>)
-                  : PAD_MERGE_SHAPE == 4 ? reinterpret_cast<const void*>(&merge_kernel<256, 64>)
-                  : PAD_MERGE_SHAPE == 5 ? reinterpret_cast<const void*>(&merge_kernel<64, 16>)
-                                         : reinterpret_cast<const void*>(&merge_kernel<64, 32>);
-    const int dims = (PAD_MERGE_SHAPE == 2 || PAD_MERGE_SHAPE == 5) ? 16 : (PAD_MERGE_SHAPE == 3 || PAD_MERGE_SHAPE == 6) ? 32 : 64;
-    const int threads = (PAD_MERGE_SHAPE == 1 || PAD_MERGE_SHAPE >= 5) ? 64 : 256;
-    return hipLaunchKernel(k, dim3(plan.head_size / dims, plan.num_heads, plan.num_seqs), dim3(threads), args, 0,
-                           stream);
+  // fixed shape (tuning builds)
+  switch (PAD_MERGE_SHAPE) {
+    case 1: return PAD_MERGE(64, 64, 16);
+    case 2: return PAD_MERGE(64, 32, 64);
+    case 3: return PAD_MERGE(256, 16, 256);
+    case 4: return PAD_MERGE(256, 32, 256);
+    case 5: return PAD_MERGE(256, 64, 256);
+    case 6: return PAD_MERGE(64, 64, 64);
+    default: return PAD_MERGE(64, 16, 16);
   }
 #endif
-  // Measured on 256 compute units (phase 2 alone): one wave on 32 dims for
-  // tables of at most 64 partitions (a batch of 32 sequences up to 32K tokens:
-  // 22 us against 27 us with 64 dims); otherwise 256 threads on 16 dims while
-  // the grid stays within about three workgroups per compute unit (one 100K
-  // sequence), on 32 dims up to about eight (8 x 131072 tokens, MHA: 17.5 us
-  // against 19 us with 64 dims), else on 64 dims.
-  const int64_t rows = (int64_t)plan.num_heads * plan.num_seqs;
+  // Entries per (sequence, head) the first round of loads should cover: for
+  // the balanced split about (ranges + head groups) / head groups when the
+  // sequences are alike (the ranges number 3 per compute unit at most); for
+  // one workgroup per partition up to the table's partition count.
   const int64_t cus = device_cus();
-  if (plan.num_partitions <= 64)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<64, 32>),
-                           dim3(plan.head_size / 32, plan.num_heads, plan.num_seqs), dim3(64), args, 0, stream);
-  if (rows * (plan.head_size / 16) <= 3 * cus)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<256, 16>),
-                           dim3(plan.head_size / 16, plan.num_heads, plan.num_seqs), dim3(256), args, 0, stream);
-  if (rows * (plan.head_size / 32) <= 8 * cus)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<256, 32>),
-                           dim3(plan.head_size / 32, plan.num_heads, plan.num_seqs), dim3(256), args, 0, stream);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<256, 64>), grid, dim3(256), args, 0, stream);
+  const int64_t groups = (int64_t)plan.num_seqs * plan.num_kv_heads * plan.head_chunks;
+  const int64_t expect = m.balanced ? (kBalancedWgsPerCu * cus + groups + groups - 1) / groups : plan.num_partitions;
+  // Measured on 256 compute units (phase 2 alone): one wave on 64 dims with
+  // rounds of 16 entries when a head has few (8 x 131072 MHA tokens or a batch
+  // of 32 sequences under the balanced split); one wave on 32 dims with rounds
+  // of 64 up to 64 entries; otherwise 256 threads on 16 dims while the grid
+  // stays within about three workgroups per compute unit (one 100K sequence),
+  // on 32 dims up to about eight, else on 64 dims.
+  const int64_t rows = (int64_t)plan.num_heads * plan.num_seqs;
+  if (expect <= 16) return PAD_MERGE(64, 64, 16);
+  if (expect <= 64) return PAD_MERGE(64, 32, 64);
+  if (rows * (D / 16) <= 3 * cus) return PAD_MERGE(256, 16, 256);
+  if (rows * (D / 32) <= 8 * cus) return PAD_MERGE(256, 32, 256);
+  return PAD_MERGE(256, 64, 256);
+#undef PAD_MERGE
 }
 
 hipError_t launch_workspace_fill(float* max_logits, float* exp_sums, float* tmp_out, size_t n_stats, size_t n_tmp,
-                                 unsigned* counters, size_t n_counters, hipStream_t stream) {
+                                 unsigned* info, size_t n_info, hipStream_t stream) {
   const size_t n = n_tmp > n_stats ? n_tmp : n_stats;
   size_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks == 0) blocks = 1;
-  void* args[] = {&max_logits, &exp_sums, &tmp_out, &n_stats, &n_tmp, &counters, &n_counters};
+  void* args[] = {&max_logits, &exp_sums, &tmp_out, &n_stats, &n_tmp, &info, &n_info};
   return hipLaunchKernel(reinterpret_cast<const void*>(&fill_kernel), dim3((unsigned)blocks), dim3(256), args, 0,
                          stream);
 }

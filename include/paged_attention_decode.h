@@ -117,11 +117,10 @@ typedef struct pad_dims {
  *   partition_size 0 = one-pass; else tokens per partition, a multiple of block_size
  *   workspace      device buffer of >= paged_attention_decode_workspace_size(...)
  *                  bytes, used only when partition_size > 0 (may be NULL otherwise).
- *                  Initialise it once with paged_attention_decode_workspace_init
- *                  after allocating it: the library keeps a counter there that must
- *                  start at zero (every call leaves it at zero again).  The
- *                  partition entries need no initialisation: phase 1 writes every
- *                  entry phase 2 reads.
+ *                  Its contents need no initialisation: phase 1 writes every
+ *                  entry and record phase 2 reads, and reads nothing from it.
+ *                  (paged_attention_decode_workspace_init sets the defined
+ *                  starting values the pages' workspace message gives.)
  * Sequences with seq_lens[s] == 0 get all-zero output rows.
  */
 int32_t paged_attention_decode(float* out, const void* query, const void* key_cache,
@@ -137,23 +136,26 @@ int32_t paged_attention_decode(float* out, const void* query, const void* key_ca
  * paged_attention_decode.  Partitions at or beyond ceil(seq_lens[s] /
  * partition_size) are left untouched.
  *
- * Load balance, two modes:
- *  - pool: when the launch's partition workgroups fill the GPU's compute
- *    units once to four times over but not by a whole multiple, workgroups
- *    are launched for the first k * num_cus partitions only; the remaining
- *    partitions of every (sequence, KV head) are cut into chunks of 64
- *    tokens, which workgroups take from a counter in the workspace as they
- *    finish their own partition;
- *  - queue: when there are more than four partition workgroups per compute
- *    unit and at most 1024 sequences, a resident grid of 4 workgroups per
- *    compute unit takes the live (sequence, KV head, partition) items from
- *    the counter -- partitions past a sequence's end are never visited --
- *    and the last ones are cut into 64-token chunks.
- * A chunked partition's result is held as its chunks' entries (same three
- * quantities, in the bookkeeping area), not in its max_logits / exp_sums /
- * tmp_output slots; phase 2 merges chunk entries and partition entries
- * alike.  Phase 2 must run on the same device, with the same sizes, to find
- * them.
+ * Load balance (the balanced split).  When one workgroup per partition
+ * would give more workgroups than the GPU has compute units, and there are at
+ * most 1024 sequences and at least two partition slots per head, phase 1
+ * does not use fixed partition_size-token partitions.  It lays the live
+ * (KV block, head group) pairs of all sequences end to end -- sequence by
+ * sequence, head group by head group, block by block; a sequence with length
+ * 0 or outside [0, max_blocks_per_seq * block_size] has none -- and cuts
+ * them into N equal contiguous ranges, one per workgroup of a grid that is
+ * resident all at once (3 per compute unit, N capped so that no head gets
+ * more entries than it has partition slots, and so that a range holds at
+ * least 8 blocks).  Each entry then covers a contiguous run of whole blocks
+ * (the last one cut at seq_lens[s]) instead of partition e's tokens
+ * [e * partition_size, (e + 1) * partition_size); a head's entries still
+ * fill its slots 0, 1, ... in token order, and never more than
+ * ceil(max_blocks_per_seq * block_size / partition_size) of them.
+ * paged_attention_decode_entry_ranges reports, from a host copy of
+ * seq_lens, which slots hold which tokens in either case.  Phase 1 reads
+ * nothing from the workspace; it writes the entries and, for the balanced
+ * split, a small launch record (N, the number of live pairs and the
+ * per-sequence block prefix) that phase 2 reads to find each head's entries.
  */
 int32_t paged_attention_decode_phase1(const void* query, const void* key_cache,
                                       const void* value_cache, const int32_t* block_tables,
@@ -162,12 +164,15 @@ int32_t paged_attention_decode_phase1(const void* query, const void* key_cache,
                                       size_t workspace_bytes, const pad_dims_t* dims, void* stream);
 
 /*
- * Phase 2 alone: log-sum-exp merge of the first ceil(seq_lens[s] /
- * partition_size) partitions of each (sequence, head) in `workspace` into
- * `out` (pooled partitions through their chunk entries).  Reads only entries
- * phase 1 wrote for the same seq_lens.  num_kv_heads, block_size,
- * partition_size and dims must be those of the phase-1 call: they determine
- * where phase 1 put each partition's result.
+ * Phase 2 alone: log-sum-exp merge of each (sequence, head)'s phase-1
+ * entries in `workspace` into `out`: the first ceil(seq_lens[s] /
+ * partition_size) slots, or under the balanced split the slots its launch
+ * record names.  Reads only entries phase 1 wrote for the same seq_lens.
+ * num_kv_heads, block_size, partition_size and dims must be those of the
+ * phase-1 call, on the same device: they determine where phase 1 put each
+ * result.  A balanced-split launch record that does not match this call's
+ * seq_lens (phase 1 not run, or run with other lengths or sizes) makes the
+ * affected rows NaN.
  */
 int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32_t num_kv_heads,
                                       int32_t block_size, int32_t partition_size,
@@ -181,9 +186,7 @@ int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32
  * with NP = ceil(max_blocks_per_seq * block_size / partition_size), the most
  * partitions any sequence can have (the pages' tmp_output, exp_sums and
  * max_logits, second page, workspace-initialisation message), followed by the
- * library's bookkeeping for phase 1's load balance: 4608 bytes of counters
- * (a ticket counter and the live-item counts of the queue mode) and 512 chunk
- * entries of (64 + 16 * head_size) floats.
+ * balanced split's launch record: 4352 bytes (1029 uint32 words).
  * Returns 0 when partition_size == 0 and (size_t)-1 for invalid arguments.
  */
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
@@ -200,8 +203,9 @@ int32_t paged_attention_decode_workspace_layout(int32_t num_seqs, int32_t num_he
 /*
  * Enqueue the workspace's defined starting contents on `stream`: max_logits =
  * -inf, exp_sums = 0, tmp_output = 0 (second page, workspace-initialisation
- * message) and the bookkeeping counter = 0.  Done with a fill kernel, so the
- * call may be captured in a HIP graph.
+ * message) and the launch record = 0.  Done with a fill kernel, so the call
+ * may be captured in a HIP graph.  Not needed for correct results: phase 1
+ * reads nothing from the workspace.
  */
 int32_t paged_attention_decode_workspace_init(void* workspace, size_t workspace_bytes,
                                               int32_t num_seqs, int32_t num_heads,
@@ -223,6 +227,28 @@ int32_t paged_attention_decode_workspace_init(void* workspace, size_t workspace_
 int32_t paged_attention_decode_choose_partition(int32_t num_seqs, int32_t num_heads,
                                                 int32_t num_kv_heads, int32_t max_context_len,
                                                 int32_t block_size, int32_t num_cus);
+
+/*
+ * Where phase 1 puts each (sequence, head)'s results, computed on the host
+ * from a host copy of seq_lens, for a device with num_cus compute units
+ * (the same rule phase 1 applies on the device).  Arrays (row-major, host
+ * memory, caller-owned):
+ *   seq_lens     int32 [num_seqs]
+ *   entry_count  int32 [num_seqs, num_heads]: entries of (s, h); 0 for
+ *                seq_lens[s] == 0, -1 for a length outside the table (those
+ *                rows are written without entries: zeros, NaN)
+ *   entry_begin, entry_end  int32 [num_seqs, num_heads, NP]: token range
+ *                [begin, end) of slot e < entry_count (other slots untouched)
+ * with NP = ceil(max_blocks_per_seq * block_size / partition_size).  Returns
+ * 1 when phase 1 runs the balanced split, 0 for one workgroup per partition
+ * (slot e = tokens [e * partition_size, min((e + 1) * partition_size, L))),
+ * or a negative status for invalid arguments.
+ */
+int32_t paged_attention_decode_entry_ranges(const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                                            int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                                            int32_t block_size, int32_t partition_size, int32_t num_cus,
+                                            int32_t* entry_count, int32_t* entry_begin,
+                                            int32_t* entry_end);
 
 /* Static text for a status code (never NULL). */
 const char* paged_attention_decode_strerror(int32_t status);

@@ -154,74 +154,28 @@ def workspace_views(ws: torch.Tensor, p: gen.Problem, partition_size: int):
     return (f(ml, n).view(S, H, NP), f(es, n).view(S, H, NP), f(tmp, n * D).view(S, H, NP, D))
 
 
-COUNTER_BYTES = 4608    # bookkeeping counter area: ticket counter (256 B), then the queue's live-item prefix
-POOL_SLOTS = 512        # chunk entries in the scratch area
-POOL_CHUNK_BLOCKS = 4   # blocks per chunk
+def device_cus() -> int:
+    return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-def pool_views(ws: torch.Tensor, p: gen.Problem, partition_size: int):
-    """(ticket counter int32 [1], scratch float32 [512, 64 + 16 D]) views of the
-    workspace's bookkeeping area, which follows tmp_output (256-byte aligned)."""
-    _, _, tmp = pad.paged_attention_decode_workspace_layout(p.num_seqs, p.num_heads, p.head_size,
-                                                            p.max_blocks_per_seq, p.block_size, partition_size)
-    NP = -(-p.max_blocks_per_seq * p.block_size // partition_size)
-    n_tmp = p.num_seqs * p.num_heads * NP * p.head_size
-    up = lambda x: -(-x // 256) * 256
-    c_off = tmp + up(4 * n_tmp)
-    s_off = c_off + COUNTER_BYTES
-    piece = 64 + 16 * p.head_size
-    counters = ws[c_off: c_off + 4].view(torch.int32)
-    scratch = ws[s_off: s_off + 4 * POOL_SLOTS * piece].view(torch.float32).view(POOL_SLOTS, piece)
-    assert s_off + 4 * POOL_SLOTS * piece <= ws.numel()
-    return counters, scratch
+def entry_plan(p: gen.Problem, partition_size: int, lens=None):
+    """(balanced, count [S, H], begin [S, H, NP], end [S, H, NP]): which tokens
+    each phase-1 entry slot holds, from the library's host-side plan."""
+    lens = p.seq_lens if lens is None else lens
+    return pad.paged_attention_decode_entry_ranges(lens, p.num_heads, p.num_kv_heads, p.max_blocks_per_seq,
+                                                   p.block_size, partition_size, device_cus())
 
 
-def pool_plan(p: gen.Problem, partition_size: int, cus: int):
-    """The library's phase-1 pool rule for one-wave workgroups: (main partitions,
-    pooled partitions, chunks per pooled partition) or None."""
-    group = p.num_heads // p.num_kv_heads
-    head_chunks = -(-group // 16)
-    per_col = p.num_seqs * p.num_kv_heads * head_chunks
-    NP = -(-p.max_blocks_per_seq * p.block_size // partition_size)
-    items = per_col * NP
-    if items <= cus or items > 4 * cus or items % cus == 0:
-        return None  # (a launch of more than 4 per unit uses the queue, not the pool)
-    main = (items // cus) * cus // per_col
-    pooled = NP - main
-    chunks = -(-(partition_size // 16) // POOL_CHUNK_BLOCKS)
-    if main < 1 or pooled < 1 or chunks > 32 or per_col * pooled * chunks > POOL_SLOTS:
-        return None
-    return main, pooled, chunks
-
-
-def phase1_entries(ws: torch.Tensor, p: gen.Problem, partition_size: int, s: int, h: int):
+def phase1_entries(ws: torch.Tensor, p: gen.Problem, partition_size: int, s: int, h: int, plan=None):
     """Phase-1 results of (sequence s, head h) as [(token lo, token hi, max, exp-sum, row)],
-    max in natural-log units: the workspace entries of the partitions phase 1
-    launched, then the chunk entries of pooled partitions (scratch area)."""
-    P, D = partition_size, p.head_size
-    L = int(p.seq_lens[s])
-    np_ = -(-L // P)
-    plan = pool_plan(p, P, torch.cuda.get_device_properties(0).multi_processor_count)
-    main = plan[0] if plan else np_
-    ml, es, tmp = [t.cpu().numpy().astype(np.float64) for t in workspace_views(ws, p, P)]
-    out = [(q * P, min((q + 1) * P, L), ml[s, h, q], es[s, h, q], tmp[s, h, q]) for q in range(min(np_, main))]
-    if plan and np_ > main:
-        _, pooled, chunks = plan
-        group = p.num_heads // p.num_kv_heads
-        head_chunks = -(-group // 16)
-        g, within = divmod(h, group)
-        hc, hh = divmod(within, 16)
-        gy = g * head_chunks + hc
-        sc = pool_views(ws, p, P)[1].cpu().numpy().astype(np.float64)
-        ct = POOL_CHUNK_BLOCKS * 16
-        for pp in range(np_ - main):
-            for c in range(chunks):
-                slot = ((s * p.num_kv_heads * head_chunks + gy) * pooled + pp) * chunks + c
-                lo = (main + pp) * P + c * ct
-                hi = min(lo + ct, (main + pp + 1) * P, L)
-                row = sc[slot, 64 + hh * D: 64 + (hh + 1) * D]
-                out.append((lo, max(lo, hi), sc[slot, hh] * np.log(2.0), sc[slot, 16 + hh], row))
-    return out
+    max in natural-log units, in slot order."""
+    _, cnt, lo, hi = plan if plan is not None else entry_plan(p, partition_size)
+    ml, es, tmp = workspace_views(ws, p, partition_size)
+    n = int(cnt[s, h])
+    m = ml[s, h, :n].cpu().numpy().astype(np.float64)
+    l = es[s, h, :n].cpu().numpy().astype(np.float64)
+    o = tmp[s, h, :n].cpu().numpy().astype(np.float64)
+    return [(int(lo[s, h, e]), int(hi[s, h, e]), m[e], l[e], o[e]) for e in range(n)]
 
 
 def check_phase1_entries(entries, q, K, V, scale, tol_m=1e-4, tol_l=1e-4, tol_o=2e-3):

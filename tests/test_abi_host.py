@@ -112,8 +112,8 @@ def test_workspace_size_and_layout():
     assert ml == 0 and es % 256 == 0 and tmp % 256 == 0
     assert es >= S * H * np_ * 4 and tmp - es >= S * H * np_ * 4
     size = pad.paged_attention_decode_workspace_size(S, H, D, W, bs, P)
-    # then phase 1's bookkeeping: 4608 bytes of counters and 512 chunk entries of 64 + 16 D floats
-    assert size >= tmp + S * H * np_ * D * 4 + 4608 + 512 * (64 + 16 * D) * 4 and size % 256 == 0
+    # then the balanced split's launch record: 1029 words, 4352 bytes
+    assert size == tmp + S * H * np_ * D * 4 + 4352 and size % 256 == 0
     assert pad.paged_attention_decode_workspace_size(S, H, D, W, bs, 0) == 0
     with pytest.raises(ValueError):
         pad.paged_attention_decode_workspace_size(S, H, D, W, bs, 100)
@@ -131,8 +131,7 @@ def test_workspace_matches_page_figures():
     f32 = 4
     assert es - ml == -(-g["max_logits"] * f32 // 256) * 256
     assert tmp - es == -(-g["exp_sums"] * f32 // 256) * 256
-    bookkeeping = 4608 + 512 * (64 + 16 * g["head_size"]) * f32
-    assert size - tmp == -(-g["tmp_output"] * f32 // 256) * 256 + bookkeeping
+    assert size - tmp == -(-g["tmp_output"] * f32 // 256) * 256 + 4352
 
 
 def test_partition_counts_from_pages():
@@ -246,3 +245,87 @@ def test_prefill_empty_is_a_noop():
                                          ctypes.byref(pdims(num_tokens=0)), None) == 0
     assert B.LIB.paged_attention_prefill_write_kv(None, None, None, None, None, None, None, 4, 16,
                                                   ctypes.byref(pdims(max_query_len=0)), None) == 0
+
+
+# ---------------------------------------------------------------------------
+# where phase 1 puts its entries (the host copy of the device rule)
+# ---------------------------------------------------------------------------
+
+def check_entry_plan(lens, H, Hkv, W, P, cus=256):
+    """The invariants phase 2 relies on, for any lengths: every (sequence, head)
+    with a valid non-empty length has entries that tile [0, L) in slot order,
+    each a run of whole blocks (the last cut at L), no more than NP of them;
+    the heads of one KV head share them."""
+    import numpy as np
+
+    bal, cnt, lo, hi = pad.paged_attention_decode_entry_ranges(lens, H, Hkv, W, 16, P, cus)
+    NP = -(-W * 16 // P)
+    G = H // Hkv
+    for s, L in enumerate(lens):
+        for h in range(H):
+            n = int(cnt[s, h])
+            if L == 0:
+                assert n == 0
+                continue
+            if L < 0 or L > W * 16:
+                assert n == -1
+                continue
+            assert 1 <= n <= NP, (s, h, n, NP)
+            b, e = lo[s, h, :n], hi[s, h, :n]
+            assert b[0] == 0 and e[-1] == L and np.all(b[1:] == e[:-1]) and np.all(e > b), (s, h)
+            assert np.all(b % 16 == 0)
+            if not bal:
+                assert np.array_equal(b, np.arange(n) * P)
+            assert np.array_equal(cnt[s, h], cnt[s, (h // G) * G])
+            assert np.array_equal(b, lo[s, (h // G) * G, :n])
+    items = len(lens) * Hkv * NP
+    expect_bal = items > cus and len(lens) <= 1024 and NP >= 2
+    assert bal == expect_bal
+    return bal, cnt, lo, hi
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_entry_plan_random_batches(seed):
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    S = int(rng.integers(1, 70))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    H = Hkv * int(rng.choice([1, 3, 6, 8]))
+    W = int(rng.integers(1, 3000))
+    P = int(rng.choice([16, 64, 256, 512, 1024]))
+    lens = rng.integers(0, W * 16 + 1, size=S)
+    lens[rng.random(S) < 0.1] = 0
+    if S > 3:
+        lens[1] = W * 16 + 7  # out of contract
+    check_entry_plan(lens.tolist(), H, Hkv, W, P, cus=int(rng.choice([80, 256, 304])))
+
+
+def test_entry_plan_long_context():
+    # one 100 000-token sequence, 24 q / 4 KV heads, P 512: 196 partition slots;
+    # 768 ranges of 32 or 33 blocks; each KV head's 6250 blocks are exactly a
+    # quarter of the 25 000 units, so every head gets 192 entries
+    bal, cnt, lo, hi = check_entry_plan([100000], 24, 4, 6250, 512)
+    assert bal
+    assert set(cnt[0].tolist()) == {192} and cnt.sum() // 6 == 768
+    sizes = (hi[0, 0, :cnt[0, 0]] - lo[0, 0, :cnt[0, 0]])
+    assert set(((sizes + 15) // 16).tolist()) <= {32, 33, 1, 31} and sizes.max() <= 33 * 16
+
+
+def test_entry_plan_workloads():
+    from decode_attention_paged_05_amd import inputs as gen
+
+    for name in ("tiny", "short", "long", "mixed", "stress"):
+        p = gen.make_problem(name)
+        if p.partition_size:
+            check_entry_plan(p.seq_lens.tolist(), p.num_heads, p.num_kv_heads, p.max_blocks_per_seq,
+                             p.partition_size)
+
+
+def test_entry_plan_argument_errors():
+    with pytest.raises(pad.PadError):
+        pad.paged_attention_decode_entry_ranges([10], 24, 4, 10, 16, 0)
+    with pytest.raises(pad.PadError):
+        pad.paged_attention_decode_entry_ranges([10], 24, 5, 10, 16, 512)
+    with pytest.raises(pad.PadError):
+        pad.paged_attention_decode_entry_ranges([10], 24, 4, 10, 16, 512, num_cus=0)

@@ -2,12 +2,14 @@
 and the large-batch serving workload, element by element (bf16 inputs: max
 abs error 2e-3; fp32 inputs: 1e-5).
 
-Tiny, Short, Long and Mixed are compared in full; Stress (8 x 131072 tokens,
-MHA) on sampled (sequence, head) rows that the oracle computes one by one from
-regenerated logical rows, plus properties that hold at any size.
+Tiny, Short, Long, Mixed and Stress are compared in full.  For Stress (8 x
+131072 tokens, MHA) the oracle computes each of the 192 (sequence, head) rows
+on its own from logical rows regenerated from the seed (no host copy of the
+26 GB pool), on a thread pool.
 """
 
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -93,8 +95,8 @@ def test_long_split(layout):
     ref = dp.oracle()
     err = gu.assert_close(out, ref, "bf16", "long")
     log(f"[long] max err {err:.2e}")
-    # phase-1 entries of two heads against the oracle's Phase 1: the 196
-    # partitions, the last ones as chunk entries when phase 1 pools them
+    # phase-1 entries of two heads against the oracle's Phase 1 over the same
+    # tokens (fixed partitions, or the balanced split's block ranges)
     K = oracle.widen(oracle.gather_sequence(dp.kc_host, p.block_tables[0], 100000, 16), "bf16")
     V = oracle.widen(oracle.gather_sequence(dp.vc_host, p.block_tables[0], 100000, 16), "bf16")
     q = oracle.widen(p.query[0], "bf16")
@@ -115,25 +117,44 @@ def test_mixed_split(layout):
     log(f"[mixed] max err {err:.2e}")
 
 
+_STRESS_REF = {}
+
+
+def stress_reference(p):
+    """Oracle rows [S, H, D] of Stress, and for each (s, h) whether its largest
+    logit sits at a x20 outlier key (the rows whose softmax the outliers
+    dominate)."""
+    if "ref" not in _STRESS_REF:
+        def row(sh):
+            s, h = sh
+            k, v = gen.sequence_kv(p, s, h)  # MHA: KV head == query head
+            ref = oracle.attend_logical(p.query[s, h], k, v, p.scale, "bf16")
+            x = oracle.widen(k, "bf16") @ oracle.widen(p.query[s, h], "bf16")
+            return ref, bool(gen.outlier_positions(p, s)[int(np.argmax(x))])
+
+        pairs = [(s, h) for s in range(p.num_seqs) for h in range(p.num_heads)]
+        log(f"[oracle] stress: {len(pairs)} rows")
+        with ThreadPoolExecutor(max_workers=gen.default_threads()) as ex:
+            res = list(ex.map(row, pairs))
+        ref = np.stack([r for r, _ in res]).reshape(p.num_seqs, p.num_heads, p.head_size)
+        dominated = np.array([d for _, d in res]).reshape(p.num_seqs, p.num_heads)
+        _STRESS_REF["ref"] = (ref, dominated)
+    return _STRESS_REF["ref"]
+
+
 @pytest.mark.parametrize("layout", gu.LAYOUTS)
-def test_stress_sampled(layout):
+def test_stress_every_row(layout):
     dp = problem("stress").use(layout)
     p = dp.p
     log(f"[run] stress P=1024 {layout}")
     out = dp.run()
     torch.cuda.synchronize()
-    o = out.cpu().numpy().astype(np.float64)
-    assert np.isfinite(o).all()
-    worst = 0.0
-    for s in (0, 5):
-        for h in (0, 17):
-            k, v = gen.sequence_kv(p, s, h)  # MHA: KV head == query head
-            ref = oracle.attend_logical(p.query[s, h], k, v, p.scale, "bf16")
-            worst = max(worst, float(np.max(np.abs(o[s, h] - ref))))
-    log(f"[stress] sampled max err {worst:.2e}")
-    assert worst <= 2e-3
-    # each output row is a convex combination of V rows: |out| <= max |V| (< 6 for N(0,1) bf16 draws)
-    assert np.abs(o).max() < 8.0
+    ref, dominated = stress_reference(p)
+    # the x20 keys do take over the softmax of some rows: those rows are compared too
+    assert dominated.sum() > 0
+    err = gu.assert_close(out, ref, "bf16", f"stress {layout}")
+    log(f"[stress] all {p.num_seqs * p.num_heads} rows, max err {err:.2e}; "
+        f"{int(dominated.sum())} rows led by an outlier key")
 
 
 @pytest.mark.parametrize("layout", gu.LAYOUTS)
@@ -157,7 +178,7 @@ def test_workspace_garbage_is_never_read(layout):
     ws = dp.workspace(32)
     ml, es, tmp = gu.workspace_views(ws, p, 32)
     for t in (ml, es, tmp):
-        t.view(torch.int32).fill_(-1)  # every partition entry is NaN; the library's counters stay zero
+        t.view(torch.int32).fill_(-1)  # every partition entry is NaN
     a = dp.run(partition_size=32, workspace=ws)
     b = dp.run(partition_size=32)
     assert torch.equal(a, b)
