@@ -24,10 +24,12 @@ PAD_KV_TILED = 1
 STATUS = {
     0: "PAD_OK", -1: "PAD_ERR_NULL", -2: "PAD_ERR_DTYPE", -3: "PAD_ERR_SHAPE",
     -4: "PAD_ERR_UNSUPPORTED", -5: "PAD_ERR_PARTITION", -6: "PAD_ERR_WORKSPACE", -7: "PAD_ERR_ALIGN",
+    -8: "PAD_ERR_TOO_LARGE",
 }
 
 EXPORTED = [
     "paged_attention_decode",
+    "paged_attention_decode_no_alloc",
     "paged_attention_decode_phase1",
     "paged_attention_decode_phase2",
     "paged_attention_decode_workspace_size",
@@ -91,6 +93,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     dims = ctypes.POINTER(PadDims)
     lib.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, sz, dims, vp]
     lib.paged_attention_decode.restype = i32
+    lib.paged_attention_decode_no_alloc.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, dims, vp]
+    lib.paged_attention_decode_no_alloc.restype = i32
     lib.paged_attention_decode_phase1.argtypes = [vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, sz, dims, vp]
     lib.paged_attention_decode_phase1.restype = i32
     lib.paged_attention_decode_phase2.argtypes = [vp, vp, i32, i32, i32, vp, sz, dims, vp]
@@ -224,6 +228,18 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, seq
                                     int(block_size), int(partition_size), ws_ptr, ws_bytes,
                                     ctypes.byref(dims), _stream(stream))
     _check(st, "paged_attention_decode")
+
+
+def paged_attention_decode_no_alloc(out, query, key_cache, value_cache, block_tables, seq_lens, scale: float,
+                                    num_kv_heads: int, block_size: int, partition_size: int, stream=None) -> None:
+    """Decode attention with the library's static workspace (no allocation); see the C header."""
+    _check_tensors(out, query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, block_size)
+    dims = make_dims(query, key_cache, block_tables)
+    st = LIB.paged_attention_decode_no_alloc(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                             _ptr(block_tables), _ptr(seq_lens), float(scale), int(num_kv_heads),
+                                             int(block_size), int(partition_size), ctypes.byref(dims),
+                                             _stream(stream))
+    _check(st, "paged_attention_decode_no_alloc")
 
 
 def paged_attention_decode_phase1(query, key_cache, value_cache, block_tables, seq_lens, scale: float,

@@ -247,6 +247,35 @@ int32_t paged_attention_decode(float* out, const void* query, const void* key_ca
   return status_of(pad::launch_phase2(plan, out, seq_lens, s));
 }
 
+int32_t paged_attention_decode_no_alloc(float* out, const void* query, const void* key_cache,
+                                        const void* value_cache, const int32_t* block_tables,
+                                        const int32_t* seq_lens, float scale, int32_t num_kv_heads,
+                                        int32_t block_size, int32_t partition_size, const pad_dims_t* dims,
+                                        void* stream) {
+  int32_t st = validate(query, key_cache, value_cache, block_tables, seq_lens, scale, num_kv_heads, block_size,
+                        partition_size, dims);
+  if (st != PAD_OK) return st;
+  if (dims->num_seqs == 0) return PAD_OK;
+  if (!out) return PAD_ERR_NULL;
+  if (!aligned16(out)) return PAD_ERR_ALIGN;
+  pad::Plan plan = make_plan(scale, num_kv_heads, partition_size, dims);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (partition_size == 0)
+    return status_of(pad::launch_one_pass(plan, out, query, key_cache, value_cache, block_tables, seq_lens, s));
+  Layout l;
+  if (!workspace_layout(dims->num_seqs, dims->num_heads, dims->head_size, dims->max_blocks_per_seq, block_size,
+                        partition_size, &l))
+    return PAD_ERR_SHAPE;
+  if (l.total > pad::kStaticWorkspaceBytes) return PAD_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  hipError_t e = pad::static_workspace(&ws);
+  if (e != hipSuccess) return status_of(e);
+  if (!attach_workspace(&plan, ws, pad::kStaticWorkspaceBytes)) return PAD_ERR_WORKSPACE;
+  e = pad::launch_phase1(plan, query, key_cache, value_cache, block_tables, seq_lens, s);
+  if (e != hipSuccess) return status_of(e);
+  return status_of(pad::launch_phase2(plan, out, seq_lens, s));
+}
+
 int32_t paged_attention_prefill(float* out, const void* query, const void* key_cache, const void* value_cache,
                                 const int32_t* block_tables, const int32_t* query_start,
                                 const int32_t* context_lens, float scale, int32_t num_kv_heads,
@@ -414,6 +443,7 @@ const char* paged_attention_decode_strerror(int32_t status) {
     case PAD_ERR_PARTITION: return "partition_size must be >= 0 and a multiple of block_size (> 0 for phase calls)";
     case PAD_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than paged_attention_decode_workspace_size()";
     case PAD_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case PAD_ERR_TOO_LARGE: return "the split call needs more workspace than the library's 64 MiB static workspace holds (paged_attention_decode_no_alloc); pass a workspace to paged_attention_decode instead";
     default: break;
   }
   if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

@@ -118,6 +118,11 @@ hipError_t launch_one_pass(const Plan& plan, float* out, const void* query,
                            const int32_t* block_tables, const int32_t* seq_lens,
                            hipStream_t stream);
 
+// Bytes of the library's static device workspace (the allocation-free entry
+// point's), and its address on the current device, looked up once per device.
+constexpr size_t kStaticWorkspaceBytes = (size_t)64 << 20;
+hipError_t static_workspace(void** ptr);
+
 hipError_t launch_workspace_fill(float* max_logits, float* exp_sums, float* tmp_out,
                                  size_t n_stats, size_t n_tmp, unsigned* info,
                                  size_t n_info, hipStream_t stream);

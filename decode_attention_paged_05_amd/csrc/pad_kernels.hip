@@ -391,4 +391,28 @@ hipError_t launch_workspace_fill(float* max_logits, float* exp_sums, float* tmp_
                          stream);
 }
 
+// The workspace of paged_attention_decode_no_alloc: a file-scope device array,
+// one per GPU the library runs on, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is a stand-in, not
+// a device address): static_workspace() looks up each device's address once,
+// with that device current, and every launch takes that pointer.
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+hipError_t static_workspace(void** ptr) {
+  static std::atomic<void*> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 }  // namespace pad

@@ -87,6 +87,7 @@ extern "C" {
 #define PAD_ERR_PARTITION (-5)   /* partition_size negative or not a multiple of block_size */
 #define PAD_ERR_WORKSPACE (-6)   /* split call with a NULL or too small workspace */
 #define PAD_ERR_ALIGN (-7)       /* a device pointer is not 16-byte aligned */
+#define PAD_ERR_TOO_LARGE (-8)   /* paged_attention_decode_no_alloc: workspace beyond its 64 MiB */
 
 /*
  * Problem sizes shared by the entry points.
@@ -128,6 +129,26 @@ int32_t paged_attention_decode(float* out, const void* query, const void* key_ca
                                const int32_t* seq_lens, float scale, int32_t num_kv_heads,
                                int32_t block_size, int32_t partition_size, void* workspace,
                                size_t workspace_bytes, const pad_dims_t* dims, void* stream);
+
+/*
+ * paged_attention_decode without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * split path's workspace is the library's own static device array of 64 MiB
+ * (kept by every GPU the library runs on until the process ends; its address
+ * is looked up once per device).  Arguments, results and errors are those of
+ * paged_attention_decode, plus PAD_ERR_TOO_LARGE (nothing enqueued) when
+ * paged_attention_decode_workspace_size(...) of this call exceeds 64 MiB
+ * (e.g. 24 heads x 256 dims: S x NP up to about 2 700 partition slots).  Every
+ * call on one GPU shares that array: calls whose work may overlap on one GPU
+ * (two streams, two threads) race and must not be made.  Nothing in the array
+ * has to start at zero: phase 1 writes every value phase 2 reads.
+ */
+int32_t paged_attention_decode_no_alloc(float* out, const void* query, const void* key_cache,
+                                        const void* value_cache, const int32_t* block_tables,
+                                        const int32_t* seq_lens, float scale, int32_t num_kv_heads,
+                                        int32_t block_size, int32_t partition_size, const pad_dims_t* dims,
+                                        void* stream);
 
 /*
  * Phase 1 alone (partition_size > 0): per (sequence, KV head, partition)

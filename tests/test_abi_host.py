@@ -329,3 +329,27 @@ def test_entry_plan_argument_errors():
         pad.paged_attention_decode_entry_ranges([10], 24, 5, 10, 16, 512)
     with pytest.raises(pad.PadError):
         pad.paged_attention_decode_entry_ranges([10], 24, 4, 10, 16, 512, num_cus=0)
+
+
+def test_no_alloc_rejects_what_does_not_fit():
+    """The allocation-free entry point checks its workspace need against the
+    static 64 MiB before any HIP call; other errors are those of
+    paged_attention_decode."""
+    def na(d, partition=512, ptrs=None):
+        p = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, t=FAKE, l=FAKE)
+        if ptrs:
+            p.update(ptrs)
+        return B.LIB.paged_attention_decode_no_alloc(p["out"], p["q"], p["k"], p["v"], p["t"], p["l"], 0.0625, 4, 16,
+                                                     partition, ctypes.byref(d), None)
+    big = dims(max_blocks_per_seq=100000)  # 3125 partition slots x 24 heads x 258 floats: 77 MB
+    assert pad.paged_attention_decode_workspace_size(1, 24, 256, 100000, 16, 512) > 64 << 20
+    assert na(big) == -8
+    assert "64 MiB" in B.strerror(-8)
+    assert na(dims(num_seqs=3, max_blocks_per_seq=40000)) == -8
+    assert na(dims(num_seqs=6, max_blocks_per_seq=100000), partition=16) == -8  # the GPU test's case
+    assert na(dims(dtype=7)) == -2
+    assert na(dims(), partition=500) == -5
+    assert na(dims(), ptrs=dict(out=0)) == -1
+    assert na(dims(), ptrs=dict(q=FAKE + 4)) == -7
+    assert B.LIB.paged_attention_decode_no_alloc(None, None, None, None, None, None, 1.0, 4, 16, 512,
+                                                 ctypes.byref(dims(num_seqs=0)), None) == 0
