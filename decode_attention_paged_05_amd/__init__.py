@@ -17,9 +17,11 @@ from ._binding import (  # noqa: F401
     PadError,
     PadPrefillDims,
     alloc_workspace,
+    check_build,
     make_dims,
     make_prefill_dims,
     paged_attention_decode,
+    paged_attention_decode_build_id,
     paged_attention_decode_choose_partition,
     paged_attention_decode_entry_ranges,
     paged_attention_decode_no_alloc,

@@ -38,6 +38,7 @@ EXPORTED = [
     "paged_attention_decode_choose_partition",
     "paged_attention_decode_strerror",
     "paged_attention_decode_entry_ranges",
+    "paged_attention_decode_build_id",
     "paged_attention_prefill",
     "paged_attention_prefill_write_kv",
 ]
@@ -52,6 +53,8 @@ class PadDims(ctypes.Structure):
         ("num_blocks", ctypes.c_int64),
         ("max_blocks_per_seq", ctypes.c_int32),
         ("kv_layout", ctypes.c_int32),
+        ("query_seq_stride", ctypes.c_int64),
+        ("out_seq_stride", ctypes.c_int64),
     ]
 
 
@@ -112,6 +115,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     ip = ctypes.POINTER(ctypes.c_int32)
     lib.paged_attention_decode_entry_ranges.argtypes = [ip, i32, i32, i32, i32, i32, i32, i32, ip, ip, ip]
     lib.paged_attention_decode_entry_ranges.restype = i32
+    lib.paged_attention_decode_build_id.argtypes = []
+    lib.paged_attention_decode_build_id.restype = ctypes.c_char_p
     lib.paged_attention_decode_strerror.argtypes = [i32]
     lib.paged_attention_decode_strerror.restype = ctypes.c_char_p
     pdims = ctypes.POINTER(PadPrefillDims)
@@ -163,6 +168,23 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _seq_rows_ptr(t) -> Optional[int]:
+    """Pointer of a [S, H, D] tensor whose [H, D] rows are contiguous; the
+    sequence stride (passed in pad_dims_t) may be wider."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2] or (t.shape[0] > 1 and
+                                                                          t.stride(0) < t.shape[1] * t.shape[2]):
+        raise ValueError("query / out must be [S, H, D] with contiguous [H, D] rows")
+    return t.data_ptr()
+
+
+def _seq_stride(t) -> int:
+    return int(t.stride(0)) if t is not None and t.shape[0] > 1 else 0
+
+
 def _stream(stream) -> Optional[int]:
     torch = _torch()
     if stream is None:
@@ -179,12 +201,15 @@ def cache_layout(key_cache, value_cache) -> int:
     raise ValueError("key_cache must be 4-D (rows layout) or 5-D (tiled layout)")
 
 
-def make_dims(query, key_cache, block_tables, value_cache=None) -> PadDims:
+def make_dims(query, key_cache, block_tables, value_cache=None, out=None) -> PadDims:
+    """Sizes of a decode call; the sequence strides of query (and out, when
+    given) go into query_seq_stride / out_seq_stride."""
     if query.dim() != 3 or block_tables.dim() != 2:
         raise ValueError("expected query [S,H,D] and block_tables [S,W]")
     S, H, D = query.shape
     layout = PAD_KV_TILED if key_cache.dim() == 5 else PAD_KV_ROWS
-    return PadDims(_dtype_code(query), S, H, D, key_cache.shape[0], block_tables.shape[1], layout)
+    return PadDims(_dtype_code(query), S, H, D, key_cache.shape[0], block_tables.shape[1], layout,
+                   _seq_stride(query), _seq_stride(out))
 
 
 def _check_tensors(out, query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, block_size):
@@ -220,10 +245,10 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, seq
                            stream=None) -> None:
     """Decode attention into ``out`` (float32 [S, H, D]); see the C header for the contract."""
     _check_tensors(out, query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, block_size)
-    dims = make_dims(query, key_cache, block_tables)
+    dims = make_dims(query, key_cache, block_tables, out=out)
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = LIB.paged_attention_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+    st = LIB.paged_attention_decode(_seq_rows_ptr(out), _seq_rows_ptr(query), _ptr(key_cache), _ptr(value_cache),
                                     _ptr(block_tables), _ptr(seq_lens), float(scale), int(num_kv_heads),
                                     int(block_size), int(partition_size), ws_ptr, ws_bytes,
                                     ctypes.byref(dims), _stream(stream))
@@ -234,8 +259,9 @@ def paged_attention_decode_no_alloc(out, query, key_cache, value_cache, block_ta
                                     num_kv_heads: int, block_size: int, partition_size: int, stream=None) -> None:
     """Decode attention with the library's static workspace (no allocation); see the C header."""
     _check_tensors(out, query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, block_size)
-    dims = make_dims(query, key_cache, block_tables)
-    st = LIB.paged_attention_decode_no_alloc(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+    dims = make_dims(query, key_cache, block_tables, out=out)
+    st = LIB.paged_attention_decode_no_alloc(_seq_rows_ptr(out), _seq_rows_ptr(query), _ptr(key_cache),
+                                             _ptr(value_cache),
                                              _ptr(block_tables), _ptr(seq_lens), float(scale), int(num_kv_heads),
                                              int(block_size), int(partition_size), ctypes.byref(dims),
                                              _stream(stream))
@@ -247,7 +273,7 @@ def paged_attention_decode_phase1(query, key_cache, value_cache, block_tables, s
                                   stream=None) -> None:
     _check_tensors(None, query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, block_size)
     dims = make_dims(query, key_cache, block_tables)
-    st = LIB.paged_attention_decode_phase1(_ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+    st = LIB.paged_attention_decode_phase1(_seq_rows_ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
                                            _ptr(seq_lens), float(scale), int(num_kv_heads), int(block_size),
                                            int(partition_size), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(), ctypes.byref(dims),
@@ -257,7 +283,10 @@ def paged_attention_decode_phase1(query, key_cache, value_cache, block_tables, s
 
 def paged_attention_decode_phase2(out, seq_lens, num_kv_heads: int, block_size: int, partition_size: int, workspace,
                                   dims: PadDims, stream=None) -> None:
-    st = LIB.paged_attention_decode_phase2(_ptr(out), _ptr(seq_lens), int(num_kv_heads), int(block_size),
+    """Phase 2 into ``out``; ``dims`` as for phase 1 (its out_seq_stride is taken from ``out``)."""
+    dims = PadDims(*[getattr(dims, f) for f, _ in PadDims._fields_])
+    dims.out_seq_stride = _seq_stride(out)
+    st = LIB.paged_attention_decode_phase2(_seq_rows_ptr(out), _ptr(seq_lens), int(num_kv_heads), int(block_size),
                                            int(partition_size),
                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
                                            ctypes.byref(dims), _stream(stream))
@@ -303,6 +332,24 @@ def paged_attention_decode_choose_partition(num_seqs, num_heads, num_kv_heads, m
 
 def paged_attention_decode_strerror(status: int) -> str:
     return strerror(status)
+
+
+def paged_attention_decode_build_id() -> str:
+    return LIB.paged_attention_decode_build_id().decode()
+
+
+def check_build() -> str:
+    """Raise unless the loaded libpad.so was built from the sources in this tree
+    (its build id equals the hash of csrc/ and include/); returns the id."""
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("_pad_build_hash", os.path.join(PKG, "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    want, got = mod.source_hash(), paged_attention_decode_build_id()
+    if want != got:
+        raise RuntimeError(f"{LIB_PATH} was built from other sources (build id {got}, sources {want}); rebuild it")
+    return got
 
 
 def paged_attention_decode_entry_ranges(seq_lens, num_heads: int, num_kv_heads: int, max_blocks_per_seq: int,

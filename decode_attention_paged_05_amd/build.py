@@ -8,6 +8,7 @@ binding loads it.
 
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -56,8 +57,24 @@ SOURCE_FLAGS = {"pad_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HOST_SOURCES = ["pad_api.cpp"]
 
 
+def source_hash() -> str:
+    """Hash of every file under csrc/ and include/ (names and contents, in name
+    order): the build id the library reports through
+    paged_attention_decode_build_id()."""
+    h = hashlib.sha256()
+    for d in (CSRC, INCLUDE):
+        for name in sorted(os.listdir(d)):
+            path = os.path.join(d, name)
+            if os.path.isfile(path):
+                h.update(os.path.relpath(path, ROOT).encode())
+                with open(path, "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def build(verbose: bool = False, extra_flags=(), out: str = None) -> str:
     cc = hipcc()
+    build_id = [f'-DPAD_SOURCE_HASH="{source_hash()}"']
     out = out or os.path.join(PKG, LIB_NAME)
     with tempfile.TemporaryDirectory(prefix="pad_build_") as tmp:
         jobs, objs = [], []
@@ -68,7 +85,7 @@ def build(verbose: bool = False, extra_flags=(), out: str = None) -> str:
             objs.append(obj)
         for src in HOST_SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            jobs.append([cc, *COMMON, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+            jobs.append([cc, *COMMON, *build_id, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
         workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
         with ThreadPoolExecutor(max_workers=workers) as ex:

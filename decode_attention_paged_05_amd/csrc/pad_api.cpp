@@ -74,6 +74,14 @@ int32_t validate(const void* query, const void* key_cache, const void* value_cac
   // token counts must fit int32 inside the kernels
   if ((int64_t)dims->max_blocks_per_seq * block_size > INT32_MAX / 2) return PAD_ERR_UNSUPPORTED;
   if (partition_size < 0 || partition_size % block_size) return PAD_ERR_PARTITION;
+  // row strides: 0 = contiguous; otherwise at least one sequence's rows, and
+  // rows that stay 16-byte aligned
+  const int64_t row = (int64_t)dims->num_heads * dims->head_size;
+  if ((dims->query_seq_stride != 0 && dims->query_seq_stride < row) ||
+      (dims->out_seq_stride != 0 && dims->out_seq_stride < row))
+    return PAD_ERR_SHAPE;
+  const int64_t elem = dims->dtype == PAD_DTYPE_BF16 ? 2 : 4;
+  if ((dims->query_seq_stride * elem) % 16 || (dims->out_seq_stride * 4) % 16) return PAD_ERR_ALIGN;
   if (dims->num_seqs == 0) return PAD_OK;
   if (!query || !key_cache || !value_cache || !block_tables || !seq_lens) return PAD_ERR_NULL;
   if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) || (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
@@ -97,6 +105,9 @@ pad::Plan make_plan(float scale, int32_t num_kv_heads, int32_t partition_size, c
   p.max_blocks = dims->max_blocks_per_seq;
   p.partition = partition_size;
   p.scale = scale;
+  const int64_t row = (int64_t)dims->num_heads * dims->head_size;
+  p.q_stride = dims->query_seq_stride ? dims->query_seq_stride : row;
+  p.out_stride = dims->out_seq_stride ? dims->out_seq_stride : row;
   return p;
 }
 
@@ -218,6 +229,9 @@ int32_t paged_attention_decode_phase2(float* out, const int32_t* seq_lens, int32
   if (dims->num_seqs > 65535 || dims->num_heads > 65535) return PAD_ERR_UNSUPPORTED;
   if ((int64_t)dims->max_blocks_per_seq * block_size > INT32_MAX / 2) return PAD_ERR_UNSUPPORTED;
   if (partition_size <= 0 || partition_size % block_size) return PAD_ERR_PARTITION;
+  if (dims->out_seq_stride != 0 && dims->out_seq_stride < (int64_t)dims->num_heads * dims->head_size)
+    return PAD_ERR_SHAPE;
+  if ((dims->out_seq_stride * 4) % 16) return PAD_ERR_ALIGN;
   if (dims->num_seqs == 0) return PAD_OK;
   if (!out || !seq_lens) return PAD_ERR_NULL;
   if (!aligned16(out) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u)) return PAD_ERR_ALIGN;
@@ -432,6 +446,12 @@ int32_t paged_attention_decode_entry_ranges(const int32_t* seq_lens, int32_t num
   }
   return bal ? 1 : 0;
 }
+
+#ifndef PAD_SOURCE_HASH
+#define PAD_SOURCE_HASH "unknown"
+#endif
+
+const char* paged_attention_decode_build_id(void) { return PAD_SOURCE_HASH; }
 
 const char* paged_attention_decode_strerror(int32_t status) {
   switch (status) {

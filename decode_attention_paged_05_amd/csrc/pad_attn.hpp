@@ -101,7 +101,9 @@ struct AttnParams {
   const char* value_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* out;         // one-pass output [S, H, D]
+  float* out;         // one-pass output [S, H, D], rows of sequence s at s * out_stride
+  int64_t q_stride;   // elements between consecutive sequences' query rows (>= H * D)
+  int64_t out_stride; // floats between consecutive sequences' output rows (>= H * D)
   float* max_logits;  // split workspace
   float* exp_sums;
   float* tmp_out;
@@ -310,7 +312,7 @@ struct Walker {
   // that the same lane's K load holds.
   __device__ void load_q(const AttnParams& p, int s, int h0, int gc) {
     const int qh = lane & 15;
-    const char* qrow = p.query + ((size_t)s * p.num_heads + h0 + qh) * G_::kRowBytes + 16 * (lane >> 4);
+    const char* qrow = p.query + ((size_t)s * (size_t)p.q_stride + (size_t)(h0 + qh) * D) * DT::kBytes + 16 * (lane >> 4);
 #pragma unroll
     for (int st = 0; st < kSteps; ++st)
       qop[st] = (qh < gc) ? *reinterpret_cast<const u32x4_t*>(qrow + 64 * st) : u32x4_t{0, 0, 0, 0};
@@ -562,7 +564,7 @@ __device__ inline void write_result(const AttnParams& p, const W_& w, const Work
   const float nan = __builtin_nanf("");
   const float inv = w.bad ? nan : 1.0f / w.l_run;
   const size_t hstride = kSplit ? (size_t)p.num_partitions * D : (size_t)D;
-  float* base = p.out + ((size_t)it.s * H + it.h0) * D;
+  float* base = p.out + (size_t)it.s * (size_t)p.out_stride + (size_t)it.h0 * D;
   if constexpr (kSplit) base = p.tmp_out + ((size_t)it.s * H + it.h0) * hstride + (size_t)it.part * D;
   if constexpr (kMfmaPV) {
     w.write_rows(it.gc, inv, [&](int h, int d, float v) { base[h * hstride + d] = v; });
@@ -761,7 +763,7 @@ __global__ __launch_bounds__((NW * kWave)) void attn_kernel(AttnParams p) {
     if (!it.len_ok || it.L == 0) {
       const float fill = it.len_ok ? 0.0f : __builtin_nanf("");
       for (int i = threadIdx.x; i < it.gc * D; i += NW * kWave)
-        p.out[((size_t)it.s * p.num_heads + it.h0 + i / D) * D + (i % D)] = fill;
+        p.out[(size_t)it.s * (size_t)p.out_stride + (size_t)(it.h0 + i / D) * D + (i % D)] = fill;
       return;
     }
     live = true;

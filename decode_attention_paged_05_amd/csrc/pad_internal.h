@@ -99,6 +99,8 @@ struct Plan {
   int partition;      // P tokens (0 = one-pass)
   int num_partitions; // NP = ceil(W * 16 / P) (0 for one-pass)
   float scale;        // softmax scale
+  int64_t q_stride;   // elements between sequences' query rows
+  int64_t out_stride; // floats between sequences' output rows
   // workspace arrays (split only)
   float* max_logits;  // [S, H, NP]
   float* exp_sums;    // [S, H, NP]

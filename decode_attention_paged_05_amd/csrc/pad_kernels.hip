@@ -47,7 +47,8 @@ namespace {
 // lengths, or the row is NaN).
 // ---------------------------------------------------------------------------
 struct MergeParams {
-  float* out;
+  float* out;              // rows of sequence s at s * out_stride
+  int64_t out_stride;
   const int32_t* seq_lens;
   const float* max_logits;
   const float* exp_sums;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
   const float* ml = p.max_logits + row0;
   const float* es = p.exp_sums + row0;
   const float* tmp = p.tmp_out + row0 * D + d0 + 4 * dl;
-  float* orow = p.out + ((size_t)s * p.num_heads + h) * D + d0;
+  float* orow = p.out + (size_t)s * (size_t)p.out_stride + (size_t)h * D + d0;
   f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
   float lrun = 0.0f;
   float mrun = -INFINITY;  // running max of this thread's sources, log2 units
@@ -258,6 +259,8 @@ AttnParams make_params(const Plan& plan, const void* q, const void* k, const voi
   a.block_tables = tables;
   a.seq_lens = lens;
   a.num_blocks = plan.num_blocks;
+  a.q_stride = plan.q_stride;
+  a.out_stride = plan.out_stride;
   a.num_seqs = plan.num_seqs;
   a.num_heads = plan.num_heads;
   a.num_kv_heads = plan.num_kv_heads;
@@ -325,6 +328,7 @@ hipError_t launch_one_pass(const Plan& plan, float* out, const void* query, cons
 hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens, hipStream_t stream) {
   MergeParams m{};
   m.out = out;
+  m.out_stride = plan.out_stride;
   m.seq_lens = seq_lens;
   m.max_logits = plan.max_logits;
   m.exp_sums = plan.exp_sums;

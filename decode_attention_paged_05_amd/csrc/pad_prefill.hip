@@ -278,8 +278,11 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   const int ctx = a.context_lens[s];
   const int wg_tok0 = qt * (kRowsPerWave * TW);
   const int tok0 = wg_tok0 + (rg / HC) * kRowsPerWave;
+  // out of contract: bad offsets or sizes, or a chunk longer than the grid
+  // covers (n_s > max_query_len), whose rows past the grid no workgroup writes
   const bool bad_seq = ctx < 0 || n < 0 || q_lo < 0 || q_hi > a.num_tokens ||
-                       (int64_t)ctx + n > (int64_t)a.max_blocks * kBlockTokens;
+                       (int64_t)ctx + n > (int64_t)a.max_blocks * kBlockTokens ||
+                       (int64_t)n > (int64_t)gridDim.x * (kRowsPerWave * TW);
   // the whole workgroup leaves together (it shares barriers below)
   if (wg_tok0 >= max(n, 0)) return;
 
@@ -631,7 +634,10 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
   const int per_token = a.num_kv_heads * chunks;
   const int flat = blockIdx.x * 256 + threadIdx.x;
   const int i = flat / per_token;
-  if (i >= n || ctx < 0 || q_lo < 0) return;
+  // a chunk longer than the grid covers (n_s > max_query_len) is out of
+  // contract: none of its tokens is written
+  const int64_t covered = (int64_t)gridDim.x * 256 / per_token;
+  if (i >= n || ctx < 0 || q_lo < 0 || (int64_t)n > covered) return;
   const int rem = flat - i * per_token;
   const int g = rem / chunks;
   const int c = rem - g * chunks;
@@ -668,14 +674,20 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
   }
 }
 
+// Launch and return this launch's own status (not a stale error another call
+// left on the thread).
+template <class Args>
+hipError_t launch_args(const void* fn, dim3 grid, dim3 block, const Args& a, hipStream_t stream) {
+  void* args[] = {const_cast<Args*>(&a)};
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
 template <int D>
 hipError_t launch_prefill_d(const PrefillArgs& a, int hc, dim3 grid, hipStream_t stream) {
-  switch (hc) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, dim3(kWaves * kWave), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, dim3(kWaves * kWave), 0, stream, a); break;
-    default: hipLaunchKernelGGL((prefill_kernel<D, 4>), grid, dim3(kWaves * kWave), 0, stream, a); break;
-  }
-  return hipGetLastError();
+  const void* fn = hc == 1   ? reinterpret_cast<const void*>(&prefill_kernel<D, 1>)
+                   : hc == 2 ? reinterpret_cast<const void*>(&prefill_kernel<D, 2>)
+                             : reinterpret_cast<const void*>(&prefill_kernel<D, 4>);
+  return launch_args(fn, grid, dim3(kWaves * kWave), a, stream);
 }
 
 }  // namespace
@@ -721,18 +733,11 @@ hipError_t launch_write_kv(const WriteKvArgs& a, int num_seqs, int max_query_len
   const int64_t threads = (int64_t)max_query_len * per_token;
   if (num_seqs == 0 || threads == 0) return hipSuccess;
   const dim3 grid((unsigned)((threads + 255) / 256), num_seqs);
-  if (elem_bytes == 2) {
-    if (layout == kKvRows)
-      hipLaunchKernelGGL((write_kv_kernel<2, kKvRows>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((write_kv_kernel<2, kKvTiled>), grid, dim3(256), 0, stream, a);
-  } else {
-    if (layout == kKvRows)
-      hipLaunchKernelGGL((write_kv_kernel<4, kKvRows>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((write_kv_kernel<4, kKvTiled>), grid, dim3(256), 0, stream, a);
-  }
-  return hipGetLastError();
+  const void* fn = elem_bytes == 2 ? (layout == kKvRows ? reinterpret_cast<const void*>(&write_kv_kernel<2, kKvRows>)
+                                                         : reinterpret_cast<const void*>(&write_kv_kernel<2, kKvTiled>))
+                                   : (layout == kKvRows ? reinterpret_cast<const void*>(&write_kv_kernel<4, kKvRows>)
+                                                        : reinterpret_cast<const void*>(&write_kv_kernel<4, kKvTiled>));
+  return launch_args(fn, grid, dim3(256), a, stream);
 }
 
 }  // namespace pad

@@ -25,10 +25,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Pointers named as device pointers must be device memory of the current HIP
- * device (e.g. torch CUDA tensors), contiguous, 16-byte aligned.  Layouts
- * (row-major, innermost last):
- *   out          float32 [num_seqs, num_heads, head_size]
- *   query        dtype   [num_seqs, num_heads, head_size]
+ * device (e.g. torch CUDA tensors), 16-byte aligned, contiguous except for the
+ * sequence strides of query and out (pad_dims_t).  Layouts (row-major,
+ * innermost last):
+ *   out          float32 [num_seqs, num_heads, head_size] (sequence stride out_seq_stride)
+ *   query        dtype   [num_seqs, num_heads, head_size] (sequence stride query_seq_stride)
  *   key_cache    dtype   PAD_KV_ROWS:  [num_blocks, num_kv_heads, block_size, head_size]
  *                        PAD_KV_TILED: [num_blocks, num_kv_heads, head_size/x, block_size, x]
  *                                      with x = 16 bytes of elements (8 bf16, 4 fp32)
@@ -98,6 +99,14 @@ extern "C" {
  *   num_blocks         physical blocks in the KV pool, >= 1
  *   max_blocks_per_seq W >= 1, the block-table row width
  *   kv_layout          PAD_KV_ROWS | PAD_KV_TILED (key_cache and value_cache)
+ *   query_seq_stride   elements from sequence s's query rows to sequence s+1's;
+ *                      0 = num_heads * head_size (contiguous).  Within a sequence
+ *                      the [num_heads, head_size] rows are contiguous.  Lets
+ *                      query be a view of a wider buffer, e.g. the query part
+ *                      of a fused QKV projection [S, (H + 2 Hkv) * D].  Must be
+ *                      0 or >= num_heads * head_size, and a multiple of 16 bytes.
+ *   out_seq_stride     likewise for out (float32 elements), e.g. a slice of a
+ *                      wider activation buffer; 0 = contiguous.
  */
 typedef struct pad_dims {
   int32_t dtype;
@@ -107,6 +116,8 @@ typedef struct pad_dims {
   int64_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t kv_layout;
+  int64_t query_seq_stride;
+  int64_t out_seq_stride;
 } pad_dims_t;
 
 /*
@@ -270,6 +281,14 @@ int32_t paged_attention_decode_entry_ranges(const int32_t* seq_lens, int32_t num
                                             int32_t block_size, int32_t partition_size, int32_t num_cus,
                                             int32_t* entry_count, int32_t* entry_begin,
                                             int32_t* entry_end);
+
+/*
+ * The library's build id: the first 16 hex digits of a SHA-256 over the
+ * names and contents of the source files (csrc/ and include/) it was built
+ * from, fixed at build time (never NULL).  Lets a caller or a test check that
+ * the loaded binary was built from the sources at hand.
+ */
+const char* paged_attention_decode_build_id(void);
 
 /* Static text for a status code (never NULL). */
 const char* paged_attention_decode_strerror(int32_t status);

@@ -43,8 +43,10 @@
  * context_lens[s] + n_s <= max_blocks_per_seq * block_size; block_tables[s, j]
  * lies in [0, num_blocks) for j < ceil((context_lens[s] + n_s) / block_size).
  * A violation never faults: the attention writes NaN rows for that sequence
- * (only rows inside [0, num_tokens)), and the chunk write skips tokens whose
- * slot would fall outside the table or the pool.
+ * (only rows inside [0, num_tokens), and for n_s > max_query_len only the
+ * first rows the launch grid covers, at least max_query_len of them), and the
+ * chunk write skips a sequence with n_s > max_query_len entirely and tokens
+ * whose slot would fall outside the table or the pool.
  */
 #ifndef PAGED_ATTENTION_PREFILL_H
 #define PAGED_ATTENTION_PREFILL_H

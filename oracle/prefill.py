@@ -73,21 +73,26 @@ def prefill_attention(query, key_cache, value_cache, block_tables, query_start, 
     return out
 
 
-def prefill_rows(query_rows, K_rows, V_rows, ctx: int, first: int, scale, dtype) -> np.ndarray:
+def prefill_rows(query_rows, K_rows, V_rows, ctx: int, first, scale, dtype) -> np.ndarray:
     """Outputs of chosen chunk tokens of one (sequence, head) from unpaged rows.
 
-    query_rows [m, D] are the rows of chunk tokens first .. first + m - 1;
-    K_rows, V_rows [>= ctx + first + m, D] the sequence's logical keys and
-    values of its KV head.  Used for sampled checks at sizes where the full
+    query_rows [m, D] are the rows of chunk tokens ``first .. first + m - 1``
+    (``first`` an int), or of the chunk tokens listed in ``first`` (a sequence
+    of m token indices); K_rows, V_rows [>= ctx + last token + 1, D] the
+    sequence's logical keys and values of its KV head.  Chunk token t sees
+    positions 0 .. ctx + t.  Used for sampled checks at sizes where the full
     oracle is too slow.
     """
     q = widen(query_rows, dtype)
     K = widen(K_rows, dtype)
     V = widen(V_rows, dtype)
     sc = float(np.float32(scale))
+    tokens = (np.arange(q.shape[0]) + int(first)) if np.ndim(first) == 0 else np.asarray(first, dtype=np.int64)
+    if tokens.shape != (q.shape[0],):
+        raise ValueError("one token index per query row")
     out = np.empty((q.shape[0], K.shape[1]))
     for r in range(q.shape[0]):
-        visible = ctx + first + r + 1
+        visible = ctx + int(tokens[r]) + 1
         out[r] = attend(q[r], K[:visible], V[:visible], sc)
     return out
 

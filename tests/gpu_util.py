@@ -15,6 +15,7 @@ TOL = {"f32": 1e-5, "bf16": 2e-3}
 def require_gpu():
     if not torch.cuda.is_available():
         raise RuntimeError("GPU tests need a ROCm GPU (run with -m 'not gpu' on a CPU-only host)")
+    pad.check_build()  # the library under test was built from these sources
 
 
 def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:

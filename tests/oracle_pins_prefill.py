@@ -266,6 +266,14 @@ def pin_prefill_rows(orc):
                     assert got.shape == (m, sh["D"])
                     assert np.max(np.abs(got - full[rows, h])) <= 1e-12, ("prefill_rows vs plain", s, first, h)
                     assert np.max(np.abs(got - want[rows, h])) <= 1e-12, ("prefill_rows vs brute force", s, h)
+            # a list of token indices in any order: each row as the plain oracle gives it
+            toks = np.array([n - 2, 0, 3, 1])
+            for h in range(sh["H"]):
+                g = h // group
+                got = orc.prefill_rows(c["q"][lo + toks, h], c["lk"][s][g], c["lv"][s][g], ctx, toks, scale,
+                                       sh["dtype"])
+                assert np.max(np.abs(got - full[lo + toks, h])) <= 1e-12, ("prefill_rows at listed tokens", s, h)
+                assert np.max(np.abs(got - want[lo + toks, h])) <= 1e-12, ("listed tokens vs brute force", s, h)
 
 
 ALL_PINS = [pin_prefill_brute_force, pin_prefill_two_phase, pin_prefill_decode_reduction, pin_prefill_sdpa,

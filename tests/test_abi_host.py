@@ -353,3 +353,23 @@ def test_no_alloc_rejects_what_does_not_fit():
     assert na(dims(), ptrs=dict(q=FAKE + 4)) == -7
     assert B.LIB.paged_attention_decode_no_alloc(None, None, None, None, None, None, 1.0, 4, 16, 512,
                                                  ctypes.byref(dims(num_seqs=0)), None) == 0
+
+
+def test_library_built_from_these_sources():
+    """The loaded library's build id is the hash of csrc/ and include/ as they
+    stand (a stale build fails here before any GPU run)."""
+    bid = pad.check_build()
+    assert len(bid) == 16 and int(bid, 16) >= 0
+
+
+def test_sequence_strides_validated():
+    """query_seq_stride / out_seq_stride: 0 (contiguous) or at least one
+    sequence's rows, and a whole number of 16-byte units."""
+    row = 24 * 256
+    assert call(d=dims(query_seq_stride=row - 8)) == -3
+    assert call(d=dims(out_seq_stride=row - 4)) == -3
+    assert call(d=dims(query_seq_stride=-row)) == -3
+    assert call(d=dims(query_seq_stride=row + 4)) == -7  # 8 bytes past a multiple of 16 (bf16)
+    assert call(d=dims(out_seq_stride=row + 2)) == -7
+    d = dims(out_seq_stride=row - 4)
+    assert B.LIB.paged_attention_decode_phase2(FAKE, FAKE, 4, 16, 512, FAKE, 1 << 30, ctypes.byref(d), None) == -3

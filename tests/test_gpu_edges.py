@@ -387,3 +387,36 @@ def test_two_streams_two_workspaces():
     torch.cuda.synchronize()
     gu.assert_close(oa, ra, "bf16", "stream a")
     gu.assert_close(ob, rb, "bf16", "stream b")
+
+
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+@pytest.mark.parametrize("P", [0, 64, 512])
+def test_strided_query_and_out(P, layout):
+    """query as the query part of a fused QKV projection [S, (H + 2 Hkv) * D]
+    and out as a slice of a wider buffer: bitwise equal to contiguous tensors,
+    nothing written outside the slice (one-pass, one workgroup per partition,
+    the balanced split; the phase entry points too)."""
+    lens = [700, 33, 1500, 0, 2100, 16]
+    dp = gu.DeviceProblem(custom(lens, P=P or 512, W=140)).use(layout)
+    p = dp.p
+    S, H, Hkv, D = p.num_seqs, p.num_heads, p.num_kv_heads, p.head_size
+    ref = dp.run(partition_size=P)
+    qkv = torch.full((S, (H + 2 * Hkv) * D), float("nan"), dtype=dp.query.dtype, device="cuda")
+    qkv[:, :H * D] = dp.query.reshape(S, H * D)
+    q_view = qkv[:, :H * D].view(S, H, D)
+    wide = torch.full((S, H * D + 96), -3.0, dtype=torch.float32, device="cuda")
+    out_view = wide[:, 32:32 + H * D].view(S, H, D)
+    assert q_view.stride(0) == (H + 2 * Hkv) * D and out_view.stride(0) == H * D + 96
+    ws = dp.workspace(P) if P else None
+    pad.paged_attention_decode(out_view, q_view, dp.kc, dp.vc, dp.tables, dp.lens, p.scale, Hkv, 16, P, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_view, ref), f"strided views differ (P={P})"
+    assert torch.all(wide[:, :32] == -3.0) and torch.all(wide[:, 32 + H * D:] == -3.0), "wrote outside the slice"
+    gu.assert_close(out_view, dp.oracle(), "bf16", f"strided P={P}")
+    if P:
+        wide.fill_(-3.0)
+        pad.paged_attention_decode_phase1(q_view, dp.kc, dp.vc, dp.tables, dp.lens, p.scale, Hkv, 16, P, ws)
+        pad.paged_attention_decode_phase2(out_view, dp.lens, Hkv, 16, P, ws, pad.make_dims(q_view, dp.kc, dp.tables))
+        torch.cuda.synchronize()
+        assert torch.equal(out_view, ref), "phase entry points with strided views"
+        assert torch.all(wide[:, :32] == -3.0) and torch.all(wide[:, 32 + H * D:] == -3.0)

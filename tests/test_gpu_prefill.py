@@ -174,37 +174,56 @@ def test_write_then_prefill_matches_two_phase_form():
 
 
 def _sampled_check(pp: gen.PrefillProblem, got: torch.Tensor, rows_per_seq, heads):
-    """Oracle rows computed one by one from the logical K/V of each sequence."""
+    """Oracle rows computed from the logical K/V of each sequence (one oracle
+    call per (sequence, head) over the listed chunk tokens, on a thread pool)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     Hkv, H = pp.spec.num_kv_heads, pp.spec.num_heads
     G = H // Hkv
-    worst = 0.0
+    g_host = got.double().cpu().numpy()
+    jobs = []
     for s in range(pp.num_seqs):
         n, c, lo = int(pp.query_lens[s]), int(pp.context_lens[s]), int(pp.query_start[s])
-        toks = sorted({t for t in rows_per_seq(n) if 0 <= t < n})
-        if not toks:
-            continue
-        for g in sorted({h // G for h in heads}):
-            K, V = gen.sequence_kv(pp.pool, s, g)
-            for h in [h for h in heads if h // G == g]:
-                for t in toks:
-                    want = oracle.prefill_rows(pp.query[lo + t:lo + t + 1, h], K, V, c, t, pp.scale,
-                                               pp.spec.dtype)[0]
-                    worst = max(worst, float(np.max(np.abs(got[lo + t, h].double().cpu().numpy() - want))))
-    return worst
+        toks = np.array(sorted({t for t in rows_per_seq(n) if 0 <= t < n}), dtype=np.int64)
+        if toks.size:
+            jobs += [(s, h, n, c, lo, toks) for h in heads]
+    kv = {}
+
+    def rows_kv(s, g):
+        if (s, g) not in kv:
+            kv[(s, g)] = gen.sequence_kv(pp.pool, s, g)
+        return kv[(s, g)]
+
+    for s, g in sorted({(j[0], j[1] // G) for j in jobs}):
+        rows_kv(s, g)
+
+    def err(job):
+        s, h, n, c, lo, toks = job
+        K, V = kv[(s, h // G)]
+        want = oracle.prefill_rows(pp.query[lo + toks, h], K, V, c, toks, pp.scale, pp.spec.dtype)
+        return float(np.max(np.abs(g_host[lo + toks, h] - want)))
+
+    with ThreadPoolExecutor(max_workers=gen.default_threads()) as ex:
+        return max(ex.map(err, jobs), default=0.0)
 
 
 def _edge_rows(n):
     return [0, 1, 15, 16, 31, 32, 33, 63, 64, 65, 127, 128, n // 2, n - 65, n - 64, n - 33, n - 32, n - 2, n - 1]
 
 
+def _every_64th_and_edges(n):
+    return list(range(0, n, 64)) + _edge_rows(n)
+
+
 def test_prefill_full_size_sampled():
     """8192 new tokens over a 32768-token prefix (the timed workload, same launch):
-    every row finite, sampled rows against the oracle."""
+    every row finite; every 64th chunk token and the tile edges of all 24 heads
+    against the oracle (147 tokens x 24 heads)."""
     pp = gen.make_prefill_problem("prefill")
     dp = DevicePrefill(pp, keep_host=False)
     got = dp.run()
     assert bool(torch.isfinite(got).all())
-    assert _sampled_check(pp, got, _edge_rows, heads=(0, 5, 6, 13, 23)) <= TOL["bf16"]
+    assert _sampled_check(pp, got, _every_64th_and_edges, heads=range(pp.spec.num_heads)) <= TOL["bf16"]
 
 
 def test_prefill_ragged_batch_sampled():
@@ -236,6 +255,45 @@ def test_prefill_block_outside_pool_gives_nan_rows():
     keep = np.r_[0:lo, hi:pp.num_tokens]
     g = got[keep].double().cpu().numpy()
     assert np.max(np.abs(g - want[keep])) <= TOL["bf16"]
+
+
+def test_prefill_chunk_longer_than_max_query_len():
+    """A chunk longer than max_query_len is out of contract: the attention
+    makes the rows the grid covers NaN and leaves the rest untouched, the
+    chunk write writes none of its tokens; the other sequences are exact."""
+    pp = gen.make_prefill_problem("prefill_small")  # chunks (50, 1, 77, 128, 0)
+    dp = DevicePrefill(pp)
+    want = dp.oracle()
+    mq = 64  # the grid covers 64 tokens a sequence (heads 24 / 4, D 256: 64 per workgroup)
+    out = torch.full(tuple(pp.query.shape), 7.0, dtype=torch.float32, device="cuda")
+    pad.paged_attention_prefill(out, dp.query, dp.dp.kc, dp.dp.vc, dp.dp.tables, dp.qs, dp.ctx, pp.scale, 4, 16, mq)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    for s in (2, 3):  # 77 and 128 tokens
+        lo, hi = int(pp.query_start[s]), int(pp.query_start[s + 1])
+        assert bool(torch.isnan(o[lo:lo + mq]).all()), s
+        assert bool((o[lo + mq:hi] == 7.0).all()), s
+    keep = np.r_[0:int(pp.query_start[2])]
+    assert np.max(np.abs(o[keep].double().numpy() - want[keep])) <= TOL["bf16"]
+    # the chunk write: sequences 2 and 3 untouched, 0 and 1 written
+    key, value = pp.chunk_kv()
+    kc_ctx = _poison_chunk_slots(dp.dp.kc_host, pp)
+    vc_ctx = _poison_chunk_slots(dp.dp.vc_host, pp)
+    kc = _upload(kc_ctx, "tiled", "bf16", "k")
+    vc = _upload(vc_ctx, "tiled", "bf16", "v")
+    before = kc.clone()
+    pad.paged_attention_prefill_write_kv(kc, vc, to_device(key, "bf16"), to_device(value, "bf16"), dp.dp.tables,
+                                         dp.qs, dp.ctx, 4, 16, mq)
+    torch.cuda.synchronize()
+    full_k = _upload(dp.dp.kc_host, "tiled", "bf16", "k")
+    for s in range(4):
+        ids = torch.as_tensor(sorted({int(pp.pool.block_tables[s, p // 16]) for p in
+                                      range(int(pp.context_lens[s]), int(pp.context_lens[s] + pp.query_lens[s]))}),
+                              dtype=torch.long, device="cuda")
+        if s in (2, 3):
+            assert torch.equal(kc[ids].view(torch.int16), before[ids].view(torch.int16)), f"sequence {s} written"
+        elif ids.numel():
+            assert torch.equal(kc[ids].view(torch.int16), full_k[ids].view(torch.int16)), f"sequence {s} not written"
 
 
 def test_prefill_rejects_unsupported():

@@ -103,9 +103,10 @@ def _rows_with(visible_of=None, swap=False, unrounded=False):
         K = dec.widen(V_rows if swap else K_rows, dtype)
         V = dec.widen(K_rows if swap else V_rows, dtype)
         sc = float(scale) if unrounded else float(np.float32(scale))
+        toks = (np.arange(q.shape[0]) + int(first)) if np.ndim(first) == 0 else np.asarray(first)
         out = np.empty((q.shape[0], K.shape[1]))
         for r in range(q.shape[0]):
-            visible = visible_of(ctx, first, r) if visible_of else ctx + first + r + 1
+            visible = visible_of(ctx, int(toks[r]), r) if visible_of else ctx + int(toks[r]) + 1
             out[r] = dec.attend(q[r], K[:visible], V[:visible], sc)
         return out
     return f
@@ -122,9 +123,9 @@ MUTANTS = [
     ("prefix_attention_two_phase", _two_phase_with(skip_context=True), "context phase skipped"),
     ("write_chunk", _write_off_by_one, "chunk written one slot late"),
     ("write_chunk", _write_ignoring_context, "chunk written from position 0"),
-    ("prefill_rows", _rows_with(lambda ctx, first, r: ctx + first + r + 2), "rows: one token into the future"),
-    ("prefill_rows", _rows_with(lambda ctx, first, r: ctx + first + r), "rows: own token excluded"),
-    ("prefill_rows", _rows_with(lambda ctx, first, r: ctx + r + 1), "rows: window start ignored"),
+    ("prefill_rows", _rows_with(lambda ctx, t, r: ctx + t + 2), "rows: one token into the future"),
+    ("prefill_rows", _rows_with(lambda ctx, t, r: ctx + t), "rows: own token excluded"),
+    ("prefill_rows", _rows_with(lambda ctx, t, r: ctx + r + 1), "rows: window start ignored"),
     ("prefill_rows", _rows_with(swap=True), "rows: keys and values swapped"),
     ("prefill_rows", _rows_with(unrounded=True), "rows: scale not rounded to float32"),
 ]
