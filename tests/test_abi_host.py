@@ -373,3 +373,82 @@ def test_sequence_strides_validated():
     assert call(d=dims(out_seq_stride=row + 2)) == -7
     d = dims(out_seq_stride=row - 4)
     assert B.LIB.paged_attention_decode_phase2(FAKE, FAKE, 4, 16, 512, FAKE, 1 << 30, ctypes.byref(d), None) == -3
+
+
+def _model_entry_plan(lens, H, Hkv, W, P, cus, wgs_per_cu=3, min_blocks=8):
+    """The balanced split written out in Python from its description: the live
+    (block, head group) units laid end to end, N equal ranges, one entry per
+    (range, head group) they share, slot = range - owner of the head group's
+    first unit.  Returns (balanced, {(s, h): [(lo, hi), ...]})."""
+    import math
+
+    G = H // Hkv
+    chunks = -(-G // 16)
+    gyc = Hkv * chunks
+    NP = -(-W * 16 // P)
+    S = len(lens)
+    if not (S * gyc * NP > cus and S <= 1024 and NP >= 2 and S * W < 2**31):
+        plan = {}
+        for s, L in enumerate(lens):
+            if 0 < L <= W * 16:
+                for h in range(H):
+                    plan[(s, h)] = [(e * P, min((e + 1) * P, L)) for e in range(-(-L // P))]
+        return False, plan
+    nb = [(-(-L // 16) if 0 < L <= W * 16 else 0) for L in lens]
+    B = gyc * sum(nb)
+    if B == 0:
+        return True, {}
+    nmax = max(nb)
+    n = wgs_per_cu * cus
+    n = min(n, (NP - 1) * B // nmax)            # at most NP entries a head group
+    n = min(n, -(-B // min_blocks))             # at least min_blocks units a range
+    if n > cus:
+        n = n // cus * cus
+    N = max(n, 1)
+    starts = [j * B // N for j in range(N + 1)]
+    plan = {}
+    off = 0
+    for s in range(S):
+        for gy in range(gyc):
+            g0, g1 = off, off + nb[s]
+            off = g1
+            if nb[s] == 0:
+                continue
+            pieces = []
+            for j in range(N):
+                a, b = max(starts[j], g0), min(starts[j + 1], g1)
+                if a < b:
+                    pieces.append((j, (a - g0) * 16, min((b - g0) * 16, lens[s])))
+            first = pieces[0][0]
+            assert all(j - first == k for k, (j, _, _) in enumerate(pieces))
+            g = gy // chunks
+            hc = gy % chunks
+            for h in range(g * G + hc * 16, g * G + min(G, hc * 16 + 16)):
+                plan[(s, h)] = [(lo, hi) for _, lo, hi in pieces]
+    return True, plan
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_entry_plan_matches_model(seed):
+    """The library's host plan equals the Python model of the balanced split
+    (and of one workgroup per partition) slot for slot."""
+    import numpy as np
+
+    rng = np.random.default_rng(100 + seed)
+    S = int(rng.integers(1, 50))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    H = Hkv * int(rng.choice([1, 3, 6, 20]))
+    W = int(rng.integers(1, 2500))
+    P = int(rng.choice([16, 64, 512, 1024]))
+    cus = int(rng.choice([80, 256, 304]))
+    lens = rng.integers(0, W * 16 + 1, size=S)
+    lens[rng.random(S) < 0.15] = 0
+    bal, cnt, lo, hi = pad.paged_attention_decode_entry_ranges(lens, H, Hkv, W, 16, P, cus)
+    mbal, model = _model_entry_plan(lens.tolist(), H, Hkv, W, P, cus)
+    assert bal == mbal
+    for s in range(S):
+        for h in range(H):
+            want = model.get((s, h), [])
+            n = int(cnt[s, h])
+            assert n == (len(want) if lens[s] > 0 else 0), (s, h)
+            assert [(int(lo[s, h, e]), int(hi[s, h, e])) for e in range(n)] == want, (s, h)
