@@ -420,3 +420,18 @@ def test_strided_query_and_out(P, layout):
         torch.cuda.synchronize()
         assert torch.equal(out_view, ref), "phase entry points with strided views"
         assert torch.all(wide[:, :32] == -3.0) and torch.all(wide[:, 32 + H * D:] == -3.0)
+
+
+def test_more_than_1024_sequences_split():
+    """1 100 short sequences: more than the balanced split takes, so phase 1
+    runs one workgroup per partition (and the merge counts ceil(L / P))."""
+    rng = np.random.default_rng(17)
+    lens = rng.integers(0, 200, size=1100).tolist()
+    dp = gu.DeviceProblem(custom(lens, H=8, Hkv=2, D=64, P=64, W=13))
+    p = dp.p
+    bal, *_ = gu.entry_plan(p, 64)
+    assert not bal
+    ref = dp.oracle()
+    for layout in gu.LAYOUTS:
+        log(f"[run] 1100 sequences, P=64, {layout}")
+        gu.assert_close(dp.use(layout).run(), ref, "bf16", f"1100 sequences {layout}")
