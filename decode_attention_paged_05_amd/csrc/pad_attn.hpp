@@ -57,6 +57,7 @@
 #include <type_traits>
 
 #include "pad_internal.h"
+#include "pad_lane_ops.h"
 
 namespace pad {
 
@@ -411,8 +412,7 @@ struct Walker {
           bm = fmaxf(bm, x[i]);
         }
         // lanes l, l^16, l^32, l^48 share a head column
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        bm = group_max(bm);
         m_true = fmaxf(m_true, bm);
         if (__ballot(bm > m_run + kLazyLog2) != 0) {
           // raise the reference of every head to its running max
@@ -489,8 +489,7 @@ struct Walker {
 #pragma unroll
           for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
     }
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = group_sum(l_run);
   }
 
   // Normalised rows of heads [0, gc): store(h, d, value) with value scaled by
