@@ -44,7 +44,7 @@ def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_paged_05_amd", "csrc")
     files = sorted(glob.glob(os.path.join(csrc, "pad_attn*")) +
-                   [os.path.join(csrc, n) for n in ("pad_kernels.hip", "pad_internal.h")])
+                   [os.path.join(csrc, n) for n in ("pad_kernels.hip", "pad_internal.h", "pad_lane_ops.h")])
     for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
