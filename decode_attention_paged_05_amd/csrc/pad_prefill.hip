@@ -225,12 +225,6 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   __shared__ __attribute__((aligned(16))) char kv_lds[kBufs * kStepBytes];
   // the logits a wave leaves for its partner: [step parity][row group][block][column tile][lane]
   __shared__ f32x4_t xs_lds[kSolo ? 1 : 2][kSolo ? 1 : kRowGroups][2][2][kWave];
-  // Paired waves (D = 256) keep one of their Q^T operands -- column tile 1,
-  // last 32 dims -- in LDS instead of registers, 16 bytes per lane.  In
-  // registers it was the one value the allocator spilled, and its reload in
-  // every step cost a scratch round trip (8 % of the kernel); two operands
-  // in LDS measured slower than one.
-  __shared__ u32x4_t q_lds[kSolo ? 1 : kWaves][kWave];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -291,8 +285,8 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     return;
   }
 
-  // Q^T operand, held in registers for the whole walk (one of them in LDS at
-  // D = 256, q_lds): column tile ct, step ks -> the row's dims 32 ks + 8 lg .. + 8
+  // Q^T operand, held in registers for the whole walk: column tile ct, step
+  // ks -> the row's dims 32 ks + 8 lg .. + 8
   u32x4_t qop[2][KS];
   {
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
@@ -307,7 +301,6 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
         if (a.negate_q) v ^= u32x4_t{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
         qop[ct][ks] = row_ok[ct] ? v : u32x4_t{0u, 0u, 0u, 0u};
       }
-      if (!kSolo && ct == 1) q_lds[wave][lane] = qop[1][KS - 1];
     }
   }
 
@@ -403,7 +396,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
       const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kv + k_lane + 1024 * ks);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const u32x4_t qb = (!kSolo && ct == 1 && ks == KS - 1) ? q_lds[wave][lane] : qop[ct][ks];
+        const u32x4_t qb = qop[ct][ks];
         r[ct] = mfma_bf16(kf, qb, r[ct]);
       }
     }
@@ -430,7 +423,16 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   // st, and retires all reads of the buffer the next copies reuse); then the
   // softmax of step st, this wave's logits of step st + 1, the copies of step
   // st + 2 and the P.V of step st.
-  for (int st = 0; st < nsteps; ++st) {
+  //
+  // Only the last step can hold V positions the walk does not hold (every
+  // earlier step ends at least one block before the end of the keys), so it
+  // alone runs the masked P.V, as separate code after the loop.  With the
+  // choice made per step inside the loop, the two P.V forms met at a join
+  // where the compiler kept the accumulators in two register sets and copied
+  // all of them on every step (32 64-bit moves); that also held 44 more
+  // registers at D = 256 and made the allocator spill a query operand.  Taken
+  // out of the loop: 7 % faster at D = 256, 5-7 % at D = 128.
+  auto iter = [&](int st, auto last) {
     // paired waves need K of step st + 1 now; solo waves only step st
     if (kSolo && st + 1 < nsteps)
       __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
@@ -574,12 +576,10 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
         }
       }
     };
-    if ((b0 + 2) * kBlockTokens > v_end)
-      pv(std::true_type{});
-    else
-      pv(std::false_type{});
-  }
-
+    pv(last);
+  };
+  for (int st = 0; st + 1 < nsteps; ++st) iter(st, std::false_type{});
+  if (nsteps > 0) iter(nsteps - 1, std::true_type{});
   // every wave's block-id checks count for the whole workgroup's tiles
   bad = __syncthreads_or(bad);
   float inv[2];
