@@ -195,6 +195,29 @@ __device__ inline void remap_workgroup(int HG, int* bx, int* by, int* bz) {
   *bz = U / NX / NG;
 }
 
+// Sequence order of a batch.  The dispatcher starts workgroups in linear-id
+// order, and a batch ends with its last long walk: a heavy sequence whose
+// workgroups come last leaves most compute units idle at the end.  For up to
+// kOrderMaxSeqs sequences every workgroup ranks the sequences by their
+// longest walk (context + chunk tokens, ties by index), heaviest first, and
+// serves the sequence of rank z; larger batches keep the given order.  Returns
+// the sequence of rank z.  Uses `key` and `seq` (kOrderMaxSeqs entries each)
+// and two workgroup barriers; every thread of the workgroup must call it.
+constexpr int kOrderMaxSeqs = 64;
+__device__ inline int sequence_of_rank(const PrefillArgs& a, int nseq, int z, int64_t* key, int* seq) {
+  const int t = threadIdx.x;
+  if (t < nseq) key[t] = (int64_t)a.context_lens[t] + (a.query_start[t + 1] - a.query_start[t]);
+  __syncthreads();
+  if (t < nseq) {
+    const int64_t k = key[t];
+    int rank = 0;
+    for (int j = 0; j < nseq; ++j) rank += (key[j] > k) || (key[j] == k && j < t);
+    seq[rank] = t;  // a strict total order: every rank gets one sequence
+  }
+  __syncthreads();
+  return seq[z];
+}
+
 template <int D, int HC>
 __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) {
   // Up to D = 128 the registers hold a wave's output rows over all of D: each
@@ -233,7 +256,11 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   const int lg = lane >> 4;              // lane group
   int bx, by, bz;
   remap_workgroup(a.head_groups, &bx, &by, &bz);
-  const int s = bz;
+  __shared__ int64_t order_key[kOrderMaxSeqs];
+  __shared__ int order_seq[kOrderMaxSeqs];
+  const int s = (gridDim.z > 1 && gridDim.z <= kOrderMaxSeqs)
+                    ? __builtin_amdgcn_readfirstlane(sequence_of_rank(a, gridDim.z, bz, order_key, order_seq))
+                    : bz;
   const int g = by / a.head_groups;
   const int h = g * a.group + (by % a.head_groups) * HC + rg % HC;
   const int qt = gridDim.x - 1 - bx;  // longest walks first
