@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     paged_attention_decode,
     paged_attention_decode_build_id,
     paged_attention_decode_choose_partition,
+    paged_attention_decode_choose_partition_for_batch,
     paged_attention_decode_entry_ranges,
     paged_attention_decode_no_alloc,
     paged_attention_decode_phase1,

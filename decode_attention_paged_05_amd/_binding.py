@@ -36,6 +36,7 @@ EXPORTED = [
     "paged_attention_decode_workspace_layout",
     "paged_attention_decode_workspace_init",
     "paged_attention_decode_choose_partition",
+    "paged_attention_decode_choose_partition_for_batch",
     "paged_attention_decode_strerror",
     "paged_attention_decode_entry_ranges",
     "paged_attention_decode_build_id",
@@ -112,6 +113,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode_workspace_init.restype = i32
     lib.paged_attention_decode_choose_partition.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.paged_attention_decode_choose_partition.restype = i32
+    lib.paged_attention_decode_choose_partition_for_batch.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, i32]
+    lib.paged_attention_decode_choose_partition_for_batch.restype = i32
     ip = ctypes.POINTER(ctypes.c_int32)
     lib.paged_attention_decode_entry_ranges.argtypes = [ip, i32, i32, i32, i32, i32, i32, i32, ip, ip, ip]
     lib.paged_attention_decode_entry_ranges.restype = i32
@@ -327,6 +330,22 @@ def paged_attention_decode_choose_partition(num_seqs, num_heads, num_kv_heads, m
                                                     num_cus)
     if r < 0:
         raise PadError(r, "paged_attention_decode_choose_partition")
+    return int(r)
+
+
+def paged_attention_decode_choose_partition_for_batch(num_seqs, num_heads, num_kv_heads, head_size, dtype: str,
+                                                      max_context_len, total_context_len, block_size,
+                                                      num_cus=256) -> int:
+    """Partition size for a batch of (possibly) unequal lengths: ``dtype`` is
+    "bf16" or "f32", ``total_context_len`` the sum of the sequence lengths."""
+    code = {"f32": PAD_DTYPE_F32, "bf16": PAD_DTYPE_BF16}.get(dtype)
+    if code is None:
+        raise ValueError(f"dtype must be 'bf16' or 'f32', not {dtype!r}")
+    r = LIB.paged_attention_decode_choose_partition_for_batch(num_seqs, num_heads, num_kv_heads, head_size, code,
+                                                              max_context_len, total_context_len, block_size,
+                                                              num_cus)
+    if r < 0:
+        raise PadError(r, "paged_attention_decode_choose_partition_for_batch")
     return int(r)
 
 

@@ -352,6 +352,33 @@ int32_t paged_attention_prefill_write_kv(void* key_cache, void* value_cache, con
                                         static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// Constants of the batch rule below, fitted on MI355X (256 compute units; 24
+// query / 4 KV heads, head 256, bf16; batches of 64 and 256 sequences of
+// 1024 or 4096 tokens with one sequence 1-16 times as long):
+constexpr double kBatchBytesPerSec = 6.5e12;  // one-pass over a batch of equal lengths
+constexpr double kWalkBytesPerSec1 = 21e9;    // one one-wave workgroup walking its context alone
+constexpr double kWalkBytesPerSec4 = 55e9;    // one four-wave workgroup walking alone
+constexpr double kSplitFixedSec = 30e-6;      // what the split costs beyond one-pass on equal lengths:
+constexpr double kSplitShare = 0.06;          // a fixed part and a share of the step
+
+// The largest partition size in {2048, ..., 128} whose slots
+// let the balanced split keep at least two workgroups per compute unit on the
+// longest sequence: N nb_max <= (NP - 1) B with N = 2 num_cus ranges,
+// nb_max = max_ctx / 16 and B = total / 16 x the workgroups per sequence.
+// 128 when none does.  (Smaller sizes cost workspace: S x H x NP entries.)
+int32_t partition_for_lengths(int64_t max_ctx, int64_t total, int64_t wgs_per_seq, int32_t num_cus) {
+  static const int32_t kSizes[] = {2048, 1024, 512, 256, 128};
+  for (int32_t p : kSizes) {
+    const int64_t np = (max_ctx + p - 1) / p;
+    if (np >= 2 && (np - 1) * total * wgs_per_seq >= 2 * (int64_t)num_cus * max_ctx) return p;
+  }
+  return 128;
+}
+
+}  // namespace
+
 int32_t paged_attention_decode_choose_partition(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                                 int32_t max_context_len, int32_t block_size, int32_t num_cus) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || max_context_len < 0 ||
@@ -362,21 +389,48 @@ int32_t paged_attention_decode_choose_partition(int32_t num_seqs, int32_t num_he
   const int64_t group = num_heads / num_kv_heads;
   const int64_t chunks = (group + pad::kMaxHeadsPerGroup - 1) / pad::kMaxHeadsPerGroup;
   const int64_t wg_one_pass = (int64_t)num_seqs * num_kv_heads * chunks;
-  // Fitted by a sweep on 256 compute units (24 q / 4 KV heads, head 256, bf16;
-  // batch 1-256, context 512-100K): the one-pass form wins once the batch
-  // alone gives every compute unit a workgroup (it also saves the workspace
-  // round trip), and for contexts of one partition or less; otherwise the
-  // largest partition that still yields about 1.5 workgroups per compute unit
-  // was the fastest or within a few percent of it.
+  // Fitted by timing sweeps on 256 compute units (24 q / 4 KV heads, head
+  // 256, bf16): the one-pass form wins once the batch alone gives every
+  // compute unit a workgroup (it also saves the workspace round trip), and
+  // for contexts of one partition or less.  Otherwise phase 1 runs the
+  // balanced split, and the partition size only sets how many slots a head
+  // has: the largest size that still leaves the split two workgroups per
+  // compute unit was the fastest or within 1 % of it (batch 1-16, context
+  // 2048-100K).
   if (wg_one_pass >= num_cus || max_context_len <= 512) return 0;
-  const int64_t target = 3 * (int64_t)num_cus / 2;
-  static const int32_t kSizes[] = {2048, 1024, 512, 256, 128};
-  for (int32_t p : kSizes) {
-    if (p % block_size) continue;
-    const int64_t parts = (max_context_len + p - 1) / p;
-    if (parts >= 2 && wg_one_pass * parts >= target) return p;
-  }
-  return 128;
+  return partition_for_lengths(max_context_len, (int64_t)num_seqs * max_context_len, num_kv_heads * chunks, num_cus);
+}
+
+int32_t paged_attention_decode_choose_partition_for_batch(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                                          int32_t head_size, int32_t dtype,
+                                                          int32_t max_context_len, int64_t total_context_len,
+                                                          int32_t block_size, int32_t num_cus) {
+  const int32_t base = paged_attention_decode_choose_partition(num_seqs, num_heads, num_kv_heads, max_context_len,
+                                                               block_size, num_cus);
+  if (base < 0) return base;
+  if (head_size != 64 && head_size != 128 && head_size != 256) return PAD_ERR_UNSUPPORTED;
+  if (dtype != PAD_DTYPE_F32 && dtype != PAD_DTYPE_BF16) return PAD_ERR_DTYPE;
+  if (total_context_len < max_context_len || total_context_len > (int64_t)num_seqs * max_context_len)
+    return PAD_ERR_SHAPE;
+  if (num_seqs == 0 || max_context_len == 0) return 0;
+  const int64_t group = num_heads / num_kv_heads;
+  const int64_t chunks = (group + pad::kMaxHeadsPerGroup - 1) / pad::kMaxHeadsPerGroup;
+  const int64_t wgs_per_seq = (int64_t)num_kv_heads * chunks;
+  if (num_seqs > pad::kBalancedMaxSeqs) return base;  // no balanced split: the fixed rule
+  if (base > 0) return partition_for_lengths(max_context_len, total_context_len, wgs_per_seq, num_cus);
+  if (max_context_len <= 512) return 0;
+  // One-pass: the step lasts at least until the workgroup of the longest
+  // sequence has walked the tokens it has beyond the others, mostly alone at
+  // the end.  The split shares those tokens among all workgroups for a fixed
+  // cost; it is chosen when the one-pass tail is larger.
+  const double bytes_per_token = 2.0 * head_size * (dtype == PAD_DTYPE_BF16 ? 2 : 4);
+  const int64_t wgs = (int64_t)num_seqs * wgs_per_seq;
+  const double walk = wgs >= 4 * (int64_t)num_cus ? kWalkBytesPerSec1 : kWalkBytesPerSec4;
+  const double mean = (double)total_context_len / num_seqs;
+  const double tail = (max_context_len - mean) * bytes_per_token / walk;
+  const double step = (double)total_context_len * num_kv_heads * bytes_per_token / kBatchBytesPerSec;
+  if (tail <= kSplitFixedSec + kSplitShare * step) return 0;
+  return partition_for_lengths(max_context_len, total_context_len, wgs_per_seq, num_cus);
 }
 
 int32_t paged_attention_decode_entry_ranges(const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,

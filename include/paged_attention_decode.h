@@ -246,19 +246,47 @@ int32_t paged_attention_decode_workspace_init(void* workspace, size_t workspace_
                                               void* stream);
 
 /*
- * One-pass versus split choice for a batch, sized for a GPU with `num_cus`
- * compute units (256 on MI355X).  Returns 0 (one-pass) when the batch's
- * (sequence, KV head) workgroups already give every compute unit one, or the
- * context is at most 512 tokens; otherwise the largest partition size in
- * {2048, 1024, 512, 256, 128} whose partition workgroups number at least
- * 1.5 x num_cus (else 128).  The first page's two-pass message weighs
+ * One-pass versus split choice for a batch of equal lengths, sized for a GPU
+ * with `num_cus` compute units (256 on MI355X).  Returns 0 (one-pass) when
+ * the batch's (sequence, KV head) workgroups already give every compute unit
+ * one, or the context is at most 512 tokens.  Otherwise phase 1 runs the
+ * balanced split, where the partition size only bounds the slots of a head:
+ * this returns the largest size in {2048, 1024, 512, 256, 128} whose slots
+ * still let the split keep two workgroups per compute unit,
+ * (ceil(max_context_len / P) - 1) x num_seqs x workgroups per sequence >=
+ * 2 x num_cus (else 128).  The first page's two-pass message weighs
  * partition count against workgroups per compute unit for a 16-unit GPU;
- * this rule redoes that for num_cus units, fitted by a timing sweep over batch
- * 1-256 and context 512-100K.  Negative status on invalid arguments.
+ * this rule redoes that for num_cus units, fitted by timing sweeps over
+ * batch 1-256 and context 512-100K.  Negative status on invalid arguments.
  */
 int32_t paged_attention_decode_choose_partition(int32_t num_seqs, int32_t num_heads,
                                                 int32_t num_kv_heads, int32_t max_context_len,
                                                 int32_t block_size, int32_t num_cus);
+
+/*
+ * The same choice for a batch whose lengths may differ, told also the head
+ * size, the element type (PAD_DTYPE_*) and the batch's total context
+ * (the sum of its sequence lengths, known to the caller on the host).  Where
+ * paged_attention_decode_choose_partition picks one-pass because the batch
+ * fills the compute units, one workgroup walks each (sequence, KV head)
+ * alone, and the tokens the longest sequence has beyond the mean set the
+ * step's end.  When that tail is longer than the split costs beyond
+ * one-pass (about 30 us plus 6 % of the step on MI355X; measured on batches
+ * of 64 and 256 with one sequence 1-16 times the others' length), this
+ * returns a split partition size instead.  For any split it returns the
+ * largest size in {2048, ..., 128} whose slots let the balanced split
+ * spread the longest sequence over two workgroups per compute unit:
+ * (ceil(max_context_len / P) - 1) x total_context_len x workgroups per
+ * sequence >= 2 x num_cus x max_context_len.  Batches above 1024 sequences get the fixed rule.  With
+ * total_context_len = num_seqs * max_context_len (equal lengths) one-pass
+ * choices are the fixed rule's.  Negative status on invalid arguments,
+ * among them a total below the maximum or above num_seqs times it.
+ */
+int32_t paged_attention_decode_choose_partition_for_batch(int32_t num_seqs, int32_t num_heads,
+                                                          int32_t num_kv_heads, int32_t head_size,
+                                                          int32_t dtype, int32_t max_context_len,
+                                                          int64_t total_context_len, int32_t block_size,
+                                                          int32_t num_cus);
 
 /*
  * Where phase 1 puts each (sequence, head)'s results, computed on the host

@@ -8,6 +8,7 @@ import json
 import os
 import re
 
+import numpy as np
 import pytest
 
 import decode_attention_paged_05_amd as pad
@@ -145,15 +146,17 @@ def test_partition_counts_from_pages():
 
 
 @pytest.mark.parametrize("S,H,Hkv,ctx,expect", [
-    (1, 24, 4, 100000, 1024),     # one long sequence: 4 KV heads x 98 partitions >= 1.5 x 256 workgroups
-    (1, 24, 4, 32768, 256),       # 4 x 128 partitions
-    (1, 24, 4, 8192, 128),        # 4 x 64 partitions of 128 still below 384 workgroups -> smallest
-    (4, 24, 4, 100000, 2048),     # 16 x 49 partitions
-    (16, 24, 4, 2048, 256),       # 64 x 8 partitions
+    # split sizes: the largest P with (ceil(ctx / P) - 1) x S x workgroups per sequence >= 2 x 256
+    (1, 24, 4, 100000, 512),      # 195 x 4 = 780 >= 512 (1024: 97 x 4 = 388 is too few)
+    (1, 24, 4, 32768, 128),       # 255 x 4; 256 would give 127 x 4 = 508
+    (1, 24, 4, 8192, 128),        # none reaches 512: the smallest
+    (4, 24, 4, 100000, 2048),     # 48 x 16
+    (16, 24, 4, 2048, 128),       # 15 x 64; 256 would give 7 x 64
+    (16, 24, 4, 8192, 512),       # 15 x 64
     (64, 24, 4, 8192, 0),         # 256 (seq, KV head) workgroups: one per compute unit -> one-pass
     (256, 24, 4, 2048, 0),        # large batch
-    (8, 24, 24, 131072, 2048),    # MHA: 192 workgroups x 64 partitions
-    (32, 24, 4, 32768, 2048),     # 128 workgroups x 16 partitions
+    (8, 24, 24, 131072, 2048),    # MHA: 63 x 8 x 24
+    (32, 24, 4, 32768, 2048),     # 15 x 128
     (4, 24, 4, 512, 0),           # one partition's worth of context
     (1, 24, 4, 200, 0),
     (0, 24, 4, 100, 0),
@@ -167,6 +170,64 @@ def test_choose_partition_invalid():
         pad.paged_attention_decode_choose_partition(1, 24, 5, 100, 16, 256)
     with pytest.raises(pad.PadError):
         pad.paged_attention_decode_choose_partition(1, 24, 4, 100, 32, 256)
+
+
+# (S, max, total, expected): the batch rule's choices on the batches it was
+# timed on (24 q / 4 KV heads, head 256, bf16, 256 compute units); each pick
+# was the fastest measured size or within 4 % of it
+@pytest.mark.parametrize("S,mx,total,expect", [
+    (256, 2048, 256 * 2048, 0),                 # equal lengths: one-pass
+    (64, 8192, 64 * 8192, 0),
+    (1024, 512, 1024 * 512, 0),
+    (256, 65536, 255 * 1024 + 65536, 2048),     # one-pass 3421 us, split 279 us
+    (132, 32768, 128 * 2048 + 4 * 32768, 2048),  # 781 us against 285 us
+    (64, 3072, 63 * 1024 + 3072, 256),          # 91 us against 72 us
+    (64, 2048, 63 * 1024 + 2048, 0),            # 75 us; the best split 72 us
+    (256, 2048, 255 * 1024 + 2048, 1024),       # 231 us against 213 us
+    (256, 32202, 1659008, 2048),                # log-uniform lengths: 2057 us against 1111 us
+    (1, 100000, 100000, 512),
+])
+def test_choose_partition_for_batch(S, mx, total, expect):
+    assert pad.paged_attention_decode_choose_partition_for_batch(S, 24, 4, 256, "bf16", mx, total, 16, 256) == expect
+
+
+def test_choose_partition_for_batch_equal_lengths_and_slots():
+    rng = np.random.default_rng(8)
+    for _ in range(300):
+        S = int(rng.integers(1, 600))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        H = Hkv * int(rng.choice([1, 2, 6, 20]))
+        mx = int(rng.integers(1, 200000))
+        fixed = pad.paged_attention_decode_choose_partition(S, H, Hkv, mx, 16, 256)
+        # equal lengths: the fixed rule's choice
+        assert pad.paged_attention_decode_choose_partition_for_batch(S, H, Hkv, 128, "bf16", mx, S * mx, 16,
+                                                                     256) == fixed
+        total = int(rng.integers(mx, S * mx + 1))
+        P = pad.paged_attention_decode_choose_partition_for_batch(S, H, Hkv, 128, "bf16", mx, total, 16, 256)
+        assert P in (0, 128, 256, 512, 1024, 2048)
+        if fixed == 0 and mx <= 512:
+            assert P == 0
+        if P:
+            wgs = Hkv * -(-(H // Hkv) // 16)
+            ok = lambda p: (-(-mx // p) - 1) * total * wgs >= 2 * 256 * mx and -(-mx // p) >= 2
+            # the largest size whose slots keep two workgroups per compute unit (else 128)
+            assert ok(P) or P == 128
+            assert all(not ok(q) for q in (256, 512, 1024, 2048) if q > P)
+
+
+def test_choose_partition_for_batch_invalid():
+    f = pad.paged_attention_decode_choose_partition_for_batch
+    with pytest.raises(pad.PadError):
+        f(4, 24, 4, 256, "bf16", 1000, 999, 16, 256)       # total below the maximum
+    with pytest.raises(pad.PadError):
+        f(4, 24, 4, 256, "bf16", 1000, 4001, 16, 256)      # total above S x maximum
+    with pytest.raises(pad.PadError):
+        f(4, 24, 4, 96, "bf16", 1000, 2000, 16, 256)       # head size
+    with pytest.raises(pad.PadError):
+        f(4, 24, 5, 256, "bf16", 1000, 2000, 16, 256)      # heads not a multiple of KV heads
+    with pytest.raises(ValueError):
+        f(4, 24, 4, 256, "f16", 1000, 2000, 16, 256)
+    assert B.LIB.paged_attention_decode_choose_partition_for_batch(4, 24, 4, 256, 7, 1000, 2000, 16, 256) < 0
 
 
 def test_strerror_never_null():

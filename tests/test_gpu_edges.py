@@ -47,6 +47,21 @@ def test_ragged_and_empty(P, layout):
     assert torch.all(out[0] == 0)
 
 
+@pytest.mark.parametrize("layout", gu.LAYOUTS)
+def test_skewed_batch_at_the_batch_rule_choice(layout):
+    """64 sequences, one 16 times as long as the others: the batch rule turns
+    the fixed rule's one-pass choice into a split; both against the oracle."""
+    lens = [256] * 63 + [4096]
+    P = pad.paged_attention_decode_choose_partition_for_batch(64, 24, 4, 256, "bf16", max(lens), sum(lens), 16, 256)
+    assert pad.paged_attention_decode_choose_partition(64, 24, 4, max(lens), 16, 256) == 0
+    assert P > 0
+    dp = gu.DeviceProblem(custom(lens, P=P, seed=23)).use(layout)
+    ref = dp.oracle()
+    for part in (P, 0):
+        log(f"[run] skewed batch P={part} {layout}")
+        gu.assert_close(dp.run(partition_size=part), ref, "bf16", f"skewed batch P={part}")
+
+
 SHAPES = [
     dict(H=32, Hkv=1, D=128, dtype="bf16"),   # 32 heads per KV head: two head chunks
     dict(H=8, Hkv=8, D=64, dtype="bf16"),     # MHA
