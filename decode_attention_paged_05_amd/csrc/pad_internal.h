@@ -108,6 +108,9 @@ struct Plan {
   unsigned* info;     // [kInfoWords]: the balanced split's launch info
 };
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus();
+
 hipError_t launch_phase1(const Plan& plan, const void* query, const void* key_cache,
                          const void* value_cache, const int32_t* block_tables,
                          const int32_t* seq_lens, hipStream_t stream);

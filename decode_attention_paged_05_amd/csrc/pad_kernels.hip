@@ -12,6 +12,25 @@
 
 namespace pad {
 
+// Compute units of the current device, cached per device ordinal.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();  // our own failed query: do not leave it behind
+    return 256;
+  }
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 hipError_t launch_attn_bf16_rows_split(const AttnParams& a, int d, int gh, dim3 grid, hipStream_t stream);
 hipError_t launch_attn_f32_rows_split(const AttnParams& a, int d, int gh, dim3 grid, hipStream_t stream);
 hipError_t launch_attn_bf16_tiled_split(const AttnParams& a, int d, int gh, dim3 grid, hipStream_t stream);
@@ -231,24 +250,6 @@ int heads_template(int heads) {
   return 16;
 }
 
-// Compute units of the current device, cached per device ordinal.
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-    (void)hipGetLastError();  // our own failed query: do not leave it behind
-    return 256;
-  }
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
-    (void)hipGetLastError();
-    cus = 256;
-  }
-  cache[dev].store(cus, std::memory_order_relaxed);
-  return cus;
-}
 
 AttnParams make_params(const Plan& plan, const void* q, const void* k, const void* v, const int32_t* tables,
                        const int32_t* lens) {

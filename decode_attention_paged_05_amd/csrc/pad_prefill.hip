@@ -218,12 +218,14 @@ __device__ inline int sequence_of_rank(const PrefillArgs& a, int nseq, int z, in
   return seq[z];
 }
 
-template <int D, int HC>
+template <int D, int HC, bool SOLO>
 __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) {
-  // Up to D = 128 the registers hold a wave's output rows over all of D: each
-  // wave then owns its 32 rows alone (8 row groups, 256 rows per workgroup),
-  // forms both logit tiles of a step itself, and nothing is exchanged.
-  constexpr bool kSolo = D <= 128;
+  // Solo layout: a wave holds its 32 output rows over all of D and owns them
+  // alone (8 row groups, 256 rows per workgroup); it forms both logit tiles of
+  // a step itself, and nothing is exchanged.  Paired layout (D = 256 only):
+  // two waves share 32 rows, one half of D each (4 row groups, 128 rows).
+  static_assert(SOLO || D == 256, "the paired layout serves head size 256");
+  constexpr bool kSolo = SOLO;
   constexpr int RG = kSolo ? 2 * kRowGroups : kRowGroups;  // 32-row groups per workgroup
   constexpr int TW = RG / HC;            // 32-token groups per workgroup
   constexpr int KS = D / 32;             // QK steps (32 dims each)
@@ -680,12 +682,30 @@ hipError_t launch_args(const void* fn, dim3 grid, dim3 block, const Args& a, hip
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
-template <int D>
+template <int D, bool SOLO>
 hipError_t launch_prefill_d(const PrefillArgs& a, int hc, dim3 grid, hipStream_t stream) {
-  const void* fn = hc == 1   ? reinterpret_cast<const void*>(&prefill_kernel<D, 1>)
-                   : hc == 2 ? reinterpret_cast<const void*>(&prefill_kernel<D, 2>)
-                             : reinterpret_cast<const void*>(&prefill_kernel<D, 4>);
+  const void* fn = hc == 1   ? reinterpret_cast<const void*>(&prefill_kernel<D, 1, SOLO>)
+                   : hc == 2 ? reinterpret_cast<const void*>(&prefill_kernel<D, 2, SOLO>)
+                             : reinterpret_cast<const void*>(&prefill_kernel<D, 4, SOLO>);
   return launch_args(fn, grid, dim3(kWaves * kWave), a, stream);
+}
+
+// Chunk tokens per workgroup: 32-row groups (8 solo, 4 paired) x 32 tokens / HC.
+int tokens_per_wg(int hc, bool solo) { return kRowsPerWave * (solo ? 2 * kRowGroups : kRowGroups) / hc; }
+
+// Whether head size 256 runs the solo layout.  Solo serves 256 rows per
+// workgroup and measured 1.18 times the paired layout's rate (8192 new tokens
+// over 32768, 24 query / 4 KV heads: 863 against 729 TFLOP/s), but its
+// workgroups are twice as large, so fewer of them share the longest chunk:
+// on a 4-sequence batch whose longest chunk gave 288 solo workgroups (one
+// round of 256 and a tail of 32) it ran 533 against 608 TFLOP/s.  Rule:
+// solo unless rounding the longest chunk's workgroups up to whole rounds of
+// the compute units costs more than the rate gains.
+bool solo_at_256(int max_query_len, int hc, int y, int cus) {
+  const int64_t np = (int64_t)((max_query_len + tokens_per_wg(hc, false) - 1) / tokens_per_wg(hc, false)) * y;
+  const int64_t ns = (int64_t)((max_query_len + tokens_per_wg(hc, true) - 1) / tokens_per_wg(hc, true)) * y;
+  const int64_t rp = (np + cus - 1) / cus, rs = (ns + cus - 1) / cus;
+  return rs * 2 * 100 <= rp * 118;
 }
 
 }  // namespace
@@ -696,10 +716,13 @@ int prefill_heads_per_wg(int group) {
   return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
 }
 
-int prefill_tokens_per_wg(int group, int head_size) {
-  const int row_groups = head_size <= 128 ? 2 * kRowGroups : kRowGroups;
-  return kRowsPerWave * row_groups / prefill_heads_per_wg(group);
+bool prefill_solo(int head_size, int group, int num_kv_heads, int max_query_len) {
+  if (head_size <= 128) return true;
+  const int hc = prefill_heads_per_wg(group);
+  return solo_at_256(max_query_len, hc, num_kv_heads * (group / hc), device_cus());
 }
+
+int prefill_tokens_per_wg(int group, bool solo) { return tokens_per_wg(prefill_heads_per_wg(group), solo); }
 
 hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
                           hipStream_t stream) {
@@ -714,14 +737,16 @@ hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_l
   const float qs = args.qscale * kLog2e;
   a.negate_q = qs < 0.0f ? 1 : 0;
   a.qscale = qs < 0.0f ? -qs : (qs > 0.0f ? qs : 1.17549435e-38f);
-  const int tpw = prefill_tokens_per_wg(a.group, head_size);
+  const bool solo = prefill_solo(head_size, a.group, a.num_kv_heads, max_query_len);
+  const int tpw = prefill_tokens_per_wg(a.group, solo);
   const int tiles = (max_query_len + tpw - 1) / tpw;
   if (num_seqs == 0 || tiles == 0) return hipSuccess;
   const dim3 grid(tiles, a.num_kv_heads * a.head_groups, num_seqs);
   switch (head_size) {
-    case 64: return launch_prefill_d<64>(a, hc, grid, stream);
-    case 128: return launch_prefill_d<128>(a, hc, grid, stream);
-    default: return launch_prefill_d<256>(a, hc, grid, stream);
+    case 64: return launch_prefill_d<64, true>(a, hc, grid, stream);
+    case 128: return launch_prefill_d<128, true>(a, hc, grid, stream);
+    default:
+      return solo ? launch_prefill_d<256, true>(a, hc, grid, stream) : launch_prefill_d<256, false>(a, hc, grid, stream);
   }
 }
 

@@ -49,9 +49,12 @@ struct WriteKvArgs {
   int64_t num_blocks;
 };
 
-// Query heads and chunk tokens one prefill workgroup serves.
+// Query heads and chunk tokens one prefill workgroup serves, and whether a
+// launch runs the solo layout (256 rows per workgroup; always below head size
+// 256) or the paired one (128 rows).
 int prefill_heads_per_wg(int group);
-int prefill_tokens_per_wg(int group, int head_size);
+bool prefill_solo(int head_size, int group, int num_kv_heads, int max_query_len);
+int prefill_tokens_per_wg(int group, bool solo);
 
 hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
                           hipStream_t stream);

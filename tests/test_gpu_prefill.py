@@ -278,6 +278,29 @@ def test_prefill_batch_above_the_ordering_cap():
     assert max_err(dp.run(), dp.oracle()) <= TOL["bf16"]
 
 
+def test_prefill_layouts_agree_bitwise():
+    """Head size 256 has two layouts: paired (two waves share 32 rows, 128 rows
+    per workgroup) and solo (a wave owns 32 rows over all of D, 256 rows).  The
+    launcher picks by the longest chunk's workgroup count: with 24 / 4 heads a
+    max_query_len of 700 gives 132 paired or 72 solo workgroups (one round of
+    256 compute units either way: paired), 8192 gives 1536 or 768 (6 rounds
+    against 3: solo).  Every output element sees the same matrix-core sequence
+    in both, so one batch run with either bound gives the same bits."""
+    spec = gen.PrefillSpec("layouts", context_lens=(1000, 0, 37), query_lens=(700, 129, 300), num_heads=24,
+                           num_kv_heads=4, head_size=256, dtype="bf16", seed=24)
+    pp = gen.make_prefill_problem(spec)
+    dp = DevicePrefill(pp)
+    outs = []
+    for mql in (700, 8192):
+        out = torch.full(tuple(pp.query.shape), float("nan"), dtype=torch.float32, device="cuda")
+        pad.paged_attention_prefill(out, dp.query, dp.dp.kc, dp.dp.vc, dp.dp.tables, dp.qs, dp.ctx, pp.scale,
+                                    spec.num_kv_heads, 16, mql)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
+    assert max_err(outs[1], dp.oracle()) <= TOL["bf16"]
+
+
 def test_prefill_block_outside_pool_gives_nan_rows():
     """A block id outside the pool (out of contract) makes that sequence's rows
     NaN and leaves the other sequences exact; nothing faults."""
