@@ -13,12 +13,15 @@
 // same keys as one range, in 32-key steps, with the same running max / sum.
 //
 // Work decomposition.  A workgroup of 8 waves serves one (sequence, KV head,
-// HC query heads of its group, 128 / HC chunk tokens): four row groups of 32
-// query rows (32 consecutive chunk tokens of one head, as two 16-row column
-// tiles), each owned by a pair of waves.  (Up to D = 128 a wave holds its rows
-// over all of D: 8 row groups of one wave, 256 / HC tokens, each wave forming
-// both logit tiles itself -- the "solo" layout; the rest of this note
-// describes the paired one.)  The workgroup walks the keys its
+// HC query heads of its group, a run of chunk tokens) in one of two layouts.
+// Solo (every head size): 8 row groups of 32 query rows (32 consecutive chunk
+// tokens of one head, as two 16-row column tiles), 256 / HC tokens; each wave
+// holds its rows over all of D and forms both logit tiles of a step itself.
+// Paired (head size 256, chosen per launch when the solo layout's larger
+// workgroups would leave the compute units a long tail): four row groups,
+// 128 / HC tokens, each owned by a pair of waves; the rest of this note
+// describes the paired one, of which solo is the exchange-free case.  The
+// workgroup walks the keys its
 // last row can see in 32-key steps (two 16-token blocks).  Each wave of a
 // pair forms the logits of half of the step's keys, over all of D, and
 // leaves them in LDS for its partner; both then run the softmax over the whole
