@@ -40,11 +40,14 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 
 def kernel_source_hash() -> str:
     """Hash of the sources that determine the decode kernels' code (phase 1, the
-    merge, their launchers and shared definitions)."""
+    merge, their launchers and shared definitions, and the build script with
+    their compiler flags)."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "decode_attention_paged_05_amd", "csrc")
+    pkg = os.path.join(ROOT, "decode_attention_paged_05_amd")
+    csrc = os.path.join(pkg, "csrc")
     files = sorted(glob.glob(os.path.join(csrc, "pad_attn*")) +
-                   [os.path.join(csrc, n) for n in ("pad_kernels.hip", "pad_internal.h", "pad_lane_ops.h")])
+                   [os.path.join(csrc, n) for n in ("pad_kernels.hip", "pad_internal.h", "pad_lane_ops.h")] +
+                   [os.path.join(pkg, "build.py")])
     for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())

@@ -49,11 +49,16 @@ def _run(cmd, verbose):
 
 DEVICE_SOURCES = ["pad_kernels.hip", "pad_prefill.hip"] + [f"pad_attn_{dt}_{lay}_{form}.hip" for dt in ("bf16", "f32")
                                                              for lay in ("rows", "tiled") for form in ("split", "one_pass")]
-# Per-source device flags.  The prefill kernel accumulates in ordinary vector
-# registers rather than accumulation registers: its lazy softmax rescale
-# multiplies the accumulators on the vector ALU, and the accumulation-register
-# form made the compiler copy all of them across on every key step.
-SOURCE_FLAGS = {"pad_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source device flags.  The attention kernels accumulate in ordinary vector
+# registers rather than accumulation registers: their lazy softmax rescale
+# multiplies the accumulators on the vector ALU.  In the accumulation-register
+# form the compiler copied the prefill accumulators across on every key step,
+# and moved the decode P.V accumulators between the two register files (about
+# 60 moves per 16-token block of phase 1, half its vector instructions);
+# without them phase 1 measured about 0.5 us faster on the 100K-token step
+# and every decode kernel needs fewer registers.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+SOURCE_FLAGS = {src: VGPR_FORM for src in DEVICE_SOURCES if src.startswith(("pad_prefill", "pad_attn_"))}
 HOST_SOURCES = ["pad_api.cpp"]
 
 
