@@ -33,9 +33,12 @@ constexpr int kMaxHeadsPerGroup = 16;
 // by phase 1, so no state carries from call to call.
 constexpr int kBalancedMaxSeqs = 1024;
 // Resident one-wave workgroups per compute unit that the balanced split
-// launches.
+// launches.  Two measured faster than three on every split workload (100K
+// tokens 71.4-71.6 against 72.1-72.3 us per step; 32 mixed sequences 344
+// against 349 us; 8 x 131072 MHA 3 748 against 3 779 us): phase 1 is as fast,
+// and the merge has a third fewer entries.  One was 13 % slower.
 #ifndef PAD_BALANCED_WGS_PER_CU
-#define PAD_BALANCED_WGS_PER_CU 3
+#define PAD_BALANCED_WGS_PER_CU 2
 #endif
 constexpr int kBalancedWgsPerCu = PAD_BALANCED_WGS_PER_CU;
 // Fewest blocks a balanced range holds (a range costs a query load, a table

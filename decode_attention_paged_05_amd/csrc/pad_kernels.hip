@@ -365,7 +365,8 @@ hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens, 
 #endif
   // Entries per (sequence, head) the first round of loads should cover: for
   // the balanced split about (ranges + head groups) / head groups when the
-  // sequences are alike (the ranges number 3 per compute unit at most); for
+  // sequences are alike (the ranges number kBalancedWgsPerCu per compute unit
+  // at most); for
   // one workgroup per partition up to the table's partition count.
   const int64_t cus = device_cus();
   const int64_t groups = (int64_t)plan.num_seqs * plan.num_kv_heads * plan.head_chunks;

@@ -176,7 +176,7 @@ int32_t paged_attention_decode_no_alloc(float* out, const void* query, const voi
  * sequence, head group by head group, block by block; a sequence with length
  * 0 or outside [0, max_blocks_per_seq * block_size] has none -- and cuts
  * them into N equal contiguous ranges, one per workgroup of a grid that is
- * resident all at once (3 per compute unit, N capped so that no head gets
+ * resident all at once (2 per compute unit, N capped so that no head gets
  * more entries than it has partition slots, and so that a range holds at
  * least 8 blocks).  Each entry then covers a contiguous run of whole blocks
  * (the last one cut at seq_lens[s]) instead of partition e's tokens

@@ -364,13 +364,14 @@ def test_entry_plan_random_batches(seed):
 
 def test_entry_plan_long_context():
     # one 100 000-token sequence, 24 q / 4 KV heads, P 512: 196 partition slots;
-    # 768 ranges of 32 or 33 blocks; each KV head's 6250 blocks are exactly a
-    # quarter of the 25 000 units, so every head gets 192 entries
+    # 512 ranges (two per compute unit) of 48 or 49 blocks; each KV head's 6250
+    # blocks are exactly a quarter of the 25 000 units, so every head gets 128
+    # entries
     bal, cnt, lo, hi = check_entry_plan([100000], 24, 4, 6250, 512)
     assert bal
-    assert set(cnt[0].tolist()) == {192} and cnt.sum() // 6 == 768
+    assert set(cnt[0].tolist()) == {128} and cnt.sum() // 6 == 512
     sizes = (hi[0, 0, :cnt[0, 0]] - lo[0, 0, :cnt[0, 0]])
-    assert set(((sizes + 15) // 16).tolist()) <= {32, 33, 1, 31} and sizes.max() <= 33 * 16
+    assert set(((sizes + 15) // 16).tolist()) <= {48, 49} and sizes.max() <= 49 * 16
 
 
 def test_entry_plan_workloads():
@@ -436,7 +437,7 @@ def test_sequence_strides_validated():
     assert B.LIB.paged_attention_decode_phase2(FAKE, FAKE, 4, 16, 512, FAKE, 1 << 30, ctypes.byref(d), None) == -3
 
 
-def _model_entry_plan(lens, H, Hkv, W, P, cus, wgs_per_cu=3, min_blocks=8):
+def _model_entry_plan(lens, H, Hkv, W, P, cus, wgs_per_cu=2, min_blocks=8):
     """The balanced split written out in Python from its description: the live
     (block, head group) units laid end to end, N equal ranges, one entry per
     (range, head group) they share, slot = range - owner of the head group's

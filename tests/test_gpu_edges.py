@@ -227,7 +227,8 @@ def test_long_balanced_every_entry(layout):
         assert entries[0][0] == 0 and entries[-1][1] == 99000
         assert all(a[1] == b[0] for a, b in zip(entries, entries[1:])), "entries must tile the context"
         if gu.device_cus() == 256:
-            assert len(entries) in (192, 193)
+            # 512 ranges (two per compute unit) over 4 heads' equal shares
+            assert len(entries) in (128, 129)
         gu.check_phase1_entries(entries, q[h], K[h // 6], V[h // 6], p.scale)
 
 
