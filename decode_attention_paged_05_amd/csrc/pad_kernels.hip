@@ -371,16 +371,17 @@ hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens, 
   const int64_t cus = device_cus();
   const int64_t groups = (int64_t)plan.num_seqs * plan.num_kv_heads * plan.head_chunks;
   const int64_t expect = m.balanced ? (kBalancedWgsPerCu * cus + groups + groups - 1) / groups : plan.num_partitions;
-  // Measured on 256 compute units (phase 2 alone): one wave on 64 dims with
-  // rounds of 16 entries when a head has few (8 x 131072 MHA tokens or a batch
-  // of 32 sequences under the balanced split); one wave on 32 dims with rounds
-  // of 64 up to 64 entries; otherwise 256 threads on 16 dims while the grid
-  // stays within about three workgroups per compute unit (one 100K sequence),
-  // on 32 dims up to about eight, else on 64 dims.
+  // Measured on 256 compute units: one wave on 64 dims with rounds of 16
+  // entries when a head has few (8 x 131072 MHA tokens or a batch of 32
+  // sequences under the balanced split); one wave on 32 dims with rounds of 64
+  // up to 64 entries; otherwise 256 threads on 32 dims while the grid stays
+  // within about eight workgroups per compute unit, else on 64 dims.  (One
+  // 100K sequence, 128 entries per head: 32 dims 70.5-71.0 us per step, 16
+  // dims 71.4-71.9 us, 64 dims 71.2 us; with three phase-1 workgroups per
+  // compute unit and 192 entries, 16 dims had been the fastest.)
   const int64_t rows = (int64_t)plan.num_heads * plan.num_seqs;
   if (expect <= 16) return PAD_MERGE(64, 64, 16);
   if (expect <= 64) return PAD_MERGE(64, 32, 64);
-  if (rows * (D / 16) <= 3 * cus) return PAD_MERGE(256, 16, 256);
   if (rows * (D / 32) <= 8 * cus) return PAD_MERGE(256, 32, 256);
   return PAD_MERGE(256, 64, 256);
 #undef PAD_MERGE
