@@ -33,14 +33,21 @@ constexpr int kMaxHeadsPerGroup = 16;
 // by phase 1, so no state carries from call to call.
 constexpr int kBalancedMaxSeqs = 1024;
 // Resident one-wave workgroups per compute unit that the balanced split
-// launches.  Two measured faster than three on every split workload (100K
-// tokens 71.4-71.6 against 72.1-72.3 us per step; 32 mixed sequences 344
-// against 349 us; 8 x 131072 MHA 3 748 against 3 779 us): phase 1 is as fast,
-// and the merge has a third fewer entries.  One was 13 % slower.
-#ifndef PAD_BALANCED_WGS_PER_CU
-#define PAD_BALANCED_WGS_PER_CU 2
+// launches, by cache layout.  Tiled: two measured faster than three on every
+// split workload (100K tokens 71.4-71.6 against 72.1-72.3 us per step; 32
+// mixed sequences 344 against 349 us; 8 x 131072 MHA 3 748 against 3 779
+// us): phase 1 is as fast, and the merge has a third fewer entries; one was
+// 13 % slower.  Rows (P.V on the vector ALUs, four times the vector work per
+// block): three, 72.5-72.7 against 74.3-74.8 us with two on the 100K step.
+#ifndef PAD_BALANCED_WGS_PER_CU_TILED
+#define PAD_BALANCED_WGS_PER_CU_TILED 2
 #endif
-constexpr int kBalancedWgsPerCu = PAD_BALANCED_WGS_PER_CU;
+#ifndef PAD_BALANCED_WGS_PER_CU_ROWS
+#define PAD_BALANCED_WGS_PER_CU_ROWS 3
+#endif
+constexpr int balanced_wgs_per_cu(int kv_layout) {
+  return kv_layout == 1 ? PAD_BALANCED_WGS_PER_CU_TILED : PAD_BALANCED_WGS_PER_CU_ROWS;  // 1: PAD_KV_TILED
+}
 // Fewest blocks a balanced range holds (a range costs a query load, a table
 // load and an entry write besides its blocks).
 constexpr int kMinRangeBlocks = 8;

@@ -176,7 +176,8 @@ int32_t paged_attention_decode_no_alloc(float* out, const void* query, const voi
  * sequence, head group by head group, block by block; a sequence with length
  * 0 or outside [0, max_blocks_per_seq * block_size] has none -- and cuts
  * them into N equal contiguous ranges, one per workgroup of a grid that is
- * resident all at once (2 per compute unit, N capped so that no head gets
+ * resident all at once (2 per compute unit for the tiled layout, 3 for the
+ * rows layout, N capped so that no head gets
  * more entries than it has partition slots, and so that a range holds at
  * least 8 blocks).  Each entry then covers a contiguous run of whole blocks
  * (the last one cut at seq_lens[s]) instead of partition e's tokens
@@ -290,7 +291,9 @@ int32_t paged_attention_decode_choose_partition_for_batch(int32_t num_seqs, int3
 
 /*
  * Where phase 1 puts each (sequence, head)'s results, computed on the host
- * from a host copy of seq_lens, for a device with num_cus compute units
+ * from a host copy of seq_lens, for a cache in kv_layout (PAD_KV_*: the
+ * balanced split launches two workgroups per compute unit for the tiled
+ * layout, three for the rows layout) on a device with num_cus compute units
  * (the same rule phase 1 applies on the device).  Arrays (row-major, host
  * memory, caller-owned):
  *   seq_lens     int32 [num_seqs]
@@ -306,8 +309,8 @@ int32_t paged_attention_decode_choose_partition_for_batch(int32_t num_seqs, int3
  */
 int32_t paged_attention_decode_entry_ranges(const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
                                             int32_t num_kv_heads, int32_t max_blocks_per_seq,
-                                            int32_t block_size, int32_t partition_size, int32_t num_cus,
-                                            int32_t* entry_count, int32_t* entry_begin,
+                                            int32_t block_size, int32_t partition_size, int32_t kv_layout,
+                                            int32_t num_cus, int32_t* entry_count, int32_t* entry_begin,
                                             int32_t* entry_end);
 
 /*

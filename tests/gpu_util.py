@@ -159,18 +159,20 @@ def device_cus() -> int:
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-def entry_plan(p: gen.Problem, partition_size: int, lens=None):
+def entry_plan(p: gen.Problem, partition_size: int, lens=None, layout: str = "tiled"):
     """(balanced, count [S, H], begin [S, H, NP], end [S, H, NP]): which tokens
-    each phase-1 entry slot holds, from the library's host-side plan."""
+    each phase-1 entry slot holds, from the library's host-side plan for a
+    cache in `layout`."""
     lens = p.seq_lens if lens is None else lens
     return pad.paged_attention_decode_entry_ranges(lens, p.num_heads, p.num_kv_heads, p.max_blocks_per_seq,
-                                                   p.block_size, partition_size, device_cus())
+                                                   p.block_size, partition_size, device_cus(), layout)
 
 
-def phase1_entries(ws: torch.Tensor, p: gen.Problem, partition_size: int, s: int, h: int, plan=None):
+def phase1_entries(ws: torch.Tensor, p: gen.Problem, partition_size: int, s: int, h: int, plan=None,
+                   layout: str = "tiled"):
     """Phase-1 results of (sequence s, head h) as [(token lo, token hi, max, exp-sum, row)],
-    max in natural-log units, in slot order."""
-    _, cnt, lo, hi = plan if plan is not None else entry_plan(p, partition_size)
+    max in natural-log units, in slot order (the plan of a cache in `layout`)."""
+    _, cnt, lo, hi = plan if plan is not None else entry_plan(p, partition_size, layout=layout)
     ml, es, tmp = workspace_views(ws, p, partition_size)
     n = int(cnt[s, h])
     m = ml[s, h, :n].cpu().numpy().astype(np.float64)

@@ -312,14 +312,14 @@ def test_prefill_empty_is_a_noop():
 # where phase 1 puts its entries (the host copy of the device rule)
 # ---------------------------------------------------------------------------
 
-def check_entry_plan(lens, H, Hkv, W, P, cus=256):
+def check_entry_plan(lens, H, Hkv, W, P, cus=256, layout="tiled"):
     """The invariants phase 2 relies on, for any lengths: every (sequence, head)
     with a valid non-empty length has entries that tile [0, L) in slot order,
     each a run of whole blocks (the last cut at L), no more than NP of them;
     the heads of one KV head share them."""
     import numpy as np
 
-    bal, cnt, lo, hi = pad.paged_attention_decode_entry_ranges(lens, H, Hkv, W, 16, P, cus)
+    bal, cnt, lo, hi = pad.paged_attention_decode_entry_ranges(lens, H, Hkv, W, 16, P, cus, layout)
     NP = -(-W * 16 // P)
     G = H // Hkv
     for s, L in enumerate(lens):
@@ -359,7 +359,8 @@ def test_entry_plan_random_batches(seed):
     lens[rng.random(S) < 0.1] = 0
     if S > 3:
         lens[1] = W * 16 + 7  # out of contract
-    check_entry_plan(lens.tolist(), H, Hkv, W, P, cus=int(rng.choice([80, 256, 304])))
+    check_entry_plan(lens.tolist(), H, Hkv, W, P, cus=int(rng.choice([80, 256, 304])),
+                     layout=str(rng.choice(["tiled", "rows"])))
 
 
 def test_entry_plan_long_context():
@@ -372,6 +373,9 @@ def test_entry_plan_long_context():
     assert set(cnt[0].tolist()) == {128} and cnt.sum() // 6 == 512
     sizes = (hi[0, 0, :cnt[0, 0]] - lo[0, 0, :cnt[0, 0]])
     assert set(((sizes + 15) // 16).tolist()) <= {48, 49} and sizes.max() <= 49 * 16
+    # the rows layout launches three workgroups per compute unit: 768 ranges of 32 or 33 blocks
+    bal, cnt, lo, hi = check_entry_plan([100000], 24, 4, 6250, 512, layout="rows")
+    assert bal and set(cnt[0].tolist()) == {192} and cnt.sum() // 6 == 768
 
 
 def test_entry_plan_workloads():
@@ -391,6 +395,11 @@ def test_entry_plan_argument_errors():
         pad.paged_attention_decode_entry_ranges([10], 24, 5, 10, 16, 512)
     with pytest.raises(pad.PadError):
         pad.paged_attention_decode_entry_ranges([10], 24, 4, 10, 16, 512, num_cus=0)
+    with pytest.raises(ValueError):
+        pad.paged_attention_decode_entry_ranges([10], 24, 4, 10, 16, 512, layout="nhd")
+    lens = (ctypes.c_int32 * 1)(10)
+    out = (ctypes.c_int32 * 64)()
+    assert B.LIB.paged_attention_decode_entry_ranges(lens, 1, 24, 4, 10, 16, 512, 7, 256, out, out, out) < 0
 
 
 def test_no_alloc_rejects_what_does_not_fit():
@@ -503,10 +512,11 @@ def test_entry_plan_matches_model(seed):
     W = int(rng.integers(1, 2500))
     P = int(rng.choice([16, 64, 512, 1024]))
     cus = int(rng.choice([80, 256, 304]))
+    layout = ("tiled", "rows")[seed % 2]
     lens = rng.integers(0, W * 16 + 1, size=S)
     lens[rng.random(S) < 0.15] = 0
-    bal, cnt, lo, hi = pad.paged_attention_decode_entry_ranges(lens, H, Hkv, W, 16, P, cus)
-    mbal, model = _model_entry_plan(lens.tolist(), H, Hkv, W, P, cus)
+    bal, cnt, lo, hi = pad.paged_attention_decode_entry_ranges(lens, H, Hkv, W, 16, P, cus, layout)
+    mbal, model = _model_entry_plan(lens.tolist(), H, Hkv, W, P, cus, wgs_per_cu=2 if layout == "tiled" else 3)
     assert bal == mbal
     for s in range(S):
         for h in range(H):

@@ -179,7 +179,7 @@ def run_checked(dp, P, what, expect_balanced=True):
     torch.cuda.synchronize()
     ref = dp.oracle()
     gu.assert_close(out, ref, p.dtype, what)
-    plan = gu.entry_plan(p, P)
+    plan = gu.entry_plan(p, P, layout=dp.layout)
     if gu.device_cus() == 256:
         assert plan[0] == expect_balanced, f"{what}: balanced split expected {expect_balanced}"
     for s in sorted({0, p.num_seqs - 1, p.num_seqs // 2}):
@@ -218,7 +218,7 @@ def test_long_balanced_every_entry(layout):
     ws = garbage_workspace(dp, 512)
     dp.run(workspace=ws)
     torch.cuda.synchronize()
-    plan = gu.entry_plan(p, 512)
+    plan = gu.entry_plan(p, 512, layout=layout)
     K = oracle.widen(oracle.gather_sequence(dp.kc_host, p.block_tables[0], 99000, 16), "bf16")
     V = oracle.widen(oracle.gather_sequence(dp.vc_host, p.block_tables[0], 99000, 16), "bf16")
     q = oracle.widen(p.query[0], "bf16")
@@ -227,8 +227,8 @@ def test_long_balanced_every_entry(layout):
         assert entries[0][0] == 0 and entries[-1][1] == 99000
         assert all(a[1] == b[0] for a, b in zip(entries, entries[1:])), "entries must tile the context"
         if gu.device_cus() == 256:
-            # 512 ranges (two per compute unit) over 4 heads' equal shares
-            assert len(entries) in (128, 129)
+            # 512 ranges (two per compute unit, tiled) or 768 (three, rows) over 4 heads' equal shares
+            assert len(entries) in ((128, 129) if layout == "tiled" else (192, 193))
         gu.check_phase1_entries(entries, q[h], K[h // 6], V[h // 6], p.scale)
 
 

@@ -101,7 +101,7 @@ def test_long_split(layout):
     V = oracle.widen(oracle.gather_sequence(dp.vc_host, p.block_tables[0], 100000, 16), "bf16")
     q = oracle.widen(p.query[0], "bf16")
     for h in (0, 13):
-        entries = gu.phase1_entries(ws, p, 512, 0, h)
+        entries = gu.phase1_entries(ws, p, 512, 0, h, layout=layout)
         covered = sorted((lo, hi) for lo, hi, *_ in entries if hi > lo)
         assert covered[0][0] == 0 and covered[-1][1] == 100000
         assert all(a[1] == b[0] for a, b in zip(covered, covered[1:])), "entries must tile the context"
