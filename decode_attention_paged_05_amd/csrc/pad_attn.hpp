@@ -176,7 +176,13 @@ constexpr float kLazyLog2 = 8.0f;
 
 // Build-time tuning knobs (defaults are the tuned values).
 #ifndef PAD_RING_MAX
-#define PAD_RING_MAX 2  // most blocks a wave keeps in flight
+// most blocks a wave keeps in flight; 0: by layout and head size.  Tiled
+// layout: 2 at head size 256 (3 measured slower on the 100K step) and 4
+// below, where a block is 8 KB or less (at 100K tokens, 64 / 8 heads of 64:
+// 57.1 against 48.1 us per step; 32 / 8 heads of 128: 74.6 against 73.4 us;
+// 8 was slower than 4 at both).  Rows layout: 2 (4 spills registers at head
+// size 128).
+#define PAD_RING_MAX 0
 #endif
 #ifndef PAD_SPLIT_WAVES
 #define PAD_SPLIT_WAVES 1  // waves per phase-1 workgroup
@@ -221,9 +227,10 @@ struct TileMap {
   // and the accumulator in ~400 of the 512 registers one wave per SIMD owns
   template <int GH>
   static constexpr int ring() {
+    constexpr int cap = PAD_RING_MAX ? PAD_RING_MAX : (LAYOUT == kLayoutTiled && D < 256 ? 4 : 2);
     constexpr int fixed = G_::kSteps * 4 + acc_vgprs<GH>() + 48;
     constexpr int r = (400 - fixed) / kStageVgprs;
-    return r < 1 ? 1 : (r > PAD_RING_MAX ? PAD_RING_MAX : r);
+    return r < 1 ? 1 : (r > cap ? cap : r);
   }
 };
 
