@@ -363,16 +363,18 @@ constexpr double kWalkBytesPerSec4 = 55e9;    // one four-wave workgroup walking
 constexpr double kSplitFixedSec = 30e-6;      // what the split costs beyond one-pass on equal lengths:
 constexpr double kSplitShare = 0.06;          // a fixed part and a share of the step
 
-// The largest partition size in {2048, ..., 128} whose slots
-// let the balanced split keep at least two workgroups per compute unit on the
-// longest sequence: N nb_max <= (NP - 1) B with N = 2 num_cus ranges,
-// nb_max = max_ctx / 16 and B = total / 16 x the workgroups per sequence.
-// 128 when none does.  (Smaller sizes cost workspace: S x H x NP entries.)
+// The largest partition size in {2048, ..., 128} whose slots let the
+// balanced split launch its full width on the longest sequence, whatever the
+// layout and head size (up to kBalancedWgsPerCuMax workgroups per compute
+// unit): N nb_max <= (NP - 1) B with N = 4 num_cus ranges, nb_max = max_ctx /
+// 16 and B = total / 16 x the workgroups per sequence.  128 when none does.
+// (Smaller sizes cost workspace: S x H x NP entries.)
 int32_t partition_for_lengths(int64_t max_ctx, int64_t total, int64_t wgs_per_seq, int32_t num_cus) {
   static const int32_t kSizes[] = {2048, 1024, 512, 256, 128};
   for (int32_t p : kSizes) {
     const int64_t np = (max_ctx + p - 1) / p;
-    if (np >= 2 && (np - 1) * total * wgs_per_seq >= 2 * (int64_t)num_cus * max_ctx) return p;
+    if (np >= 2 && (np - 1) * total * wgs_per_seq >= (int64_t)pad::kBalancedWgsPerCuMax * num_cus * max_ctx)
+      return p;
   }
   return 128;
 }
@@ -394,9 +396,8 @@ int32_t paged_attention_decode_choose_partition(int32_t num_seqs, int32_t num_he
   // compute unit a workgroup (it also saves the workspace round trip), and
   // for contexts of one partition or less.  Otherwise phase 1 runs the
   // balanced split, and the partition size only sets how many slots a head
-  // has: the largest size that still leaves the split two workgroups per
-  // compute unit was the fastest or within 1 % of it (batch 1-16, context
-  // 2048-100K).
+  // has: the largest size that leaves the split its full width was the
+  // fastest or within 1 % of it (batch 1-16, context 2048-100K).
   if (wg_one_pass >= num_cus || max_context_len <= 512) return 0;
   return partition_for_lengths(max_context_len, (int64_t)num_seqs * max_context_len, num_kv_heads * chunks, num_cus);
 }
@@ -434,13 +435,15 @@ int32_t paged_attention_decode_choose_partition_for_batch(int32_t num_seqs, int3
 }
 
 int32_t paged_attention_decode_entry_ranges(const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
-                                            int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t block_size,
-                                            int32_t partition_size, int32_t kv_layout, int32_t num_cus,
-                                            int32_t* entry_count, int32_t* entry_begin, int32_t* entry_end) {
+                                            int32_t num_kv_heads, int32_t head_size, int32_t max_blocks_per_seq,
+                                            int32_t block_size, int32_t partition_size, int32_t kv_layout,
+                                            int32_t num_cus, int32_t* entry_count, int32_t* entry_begin,
+                                            int32_t* entry_end) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || max_blocks_per_seq <= 0 ||
       num_cus <= 0)
     return PAD_ERR_SHAPE;
   if (kv_layout != PAD_KV_ROWS && kv_layout != PAD_KV_TILED) return PAD_ERR_UNSUPPORTED;
+  if (head_size != 64 && head_size != 128 && head_size != 256) return PAD_ERR_UNSUPPORTED;
   if (block_size != pad::kBlockTokens) return PAD_ERR_UNSUPPORTED;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PAD_ERR_UNSUPPORTED;
   if (partition_size <= 0 || partition_size % block_size) return PAD_ERR_PARTITION;
@@ -463,7 +466,8 @@ int32_t paged_attention_decode_entry_ranges(const int32_t* seq_lens, int32_t num
     pre[s + 1] = pre[s] + nb;
   }
   const uint64_t B = pre[S] * (uint64_t)gyc;
-  const uint64_t N = bal ? pad::balanced_ranges(B, nb_max, (unsigned)(pad::balanced_wgs_per_cu(kv_layout) * num_cus),
+  const uint64_t N = bal ? pad::balanced_ranges(B, nb_max,
+                                                (unsigned)(pad::balanced_wgs_per_cu(kv_layout, head_size) * num_cus),
                                                 (unsigned)np, (unsigned)num_cus)
                          : 0;
   for (int64_t s = 0; s < S; ++s) {

@@ -176,8 +176,8 @@ int32_t paged_attention_decode_no_alloc(float* out, const void* query, const voi
  * sequence, head group by head group, block by block; a sequence with length
  * 0 or outside [0, max_blocks_per_seq * block_size] has none -- and cuts
  * them into N equal contiguous ranges, one per workgroup of a grid that is
- * resident all at once (2 per compute unit for the tiled layout, 3 for the
- * rows layout, N capped so that no head gets
+ * resident all at once (2 per compute unit for the tiled layout at head
+ * size 256, 4 below, 3 for the rows layout, N capped so that no head gets
  * more entries than it has partition slots, and so that a range holds at
  * least 8 blocks).  Each entry then covers a contiguous run of whole blocks
  * (the last one cut at seq_lens[s]) instead of partition e's tokens
@@ -253,9 +253,10 @@ int32_t paged_attention_decode_workspace_init(void* workspace, size_t workspace_
  * one, or the context is at most 512 tokens.  Otherwise phase 1 runs the
  * balanced split, where the partition size only bounds the slots of a head:
  * this returns the largest size in {2048, 1024, 512, 256, 128} whose slots
- * still let the split keep two workgroups per compute unit,
+ * let the split launch its full width (up to four workgroups per compute
+ * unit, depending on the layout and head size),
  * (ceil(max_context_len / P) - 1) x num_seqs x workgroups per sequence >=
- * 2 x num_cus (else 128).  The first page's two-pass message weighs
+ * 4 x num_cus (else 128).  The first page's two-pass message weighs
  * partition count against workgroups per compute unit for a 16-unit GPU;
  * this rule redoes that for num_cus units, fitted by timing sweeps over
  * batch 1-256 and context 512-100K.  Negative status on invalid arguments.
@@ -276,9 +277,9 @@ int32_t paged_attention_decode_choose_partition(int32_t num_seqs, int32_t num_he
  * of 64 and 256 with one sequence 1-16 times the others' length), this
  * returns a split partition size instead.  For any split it returns the
  * largest size in {2048, ..., 128} whose slots let the balanced split
- * spread the longest sequence over two workgroups per compute unit:
+ * launch its full width on the longest sequence:
  * (ceil(max_context_len / P) - 1) x total_context_len x workgroups per
- * sequence >= 2 x num_cus x max_context_len.  Batches above 1024 sequences get the fixed rule.  With
+ * sequence >= 4 x num_cus x max_context_len.  Batches above 1024 sequences get the fixed rule.  With
  * total_context_len = num_seqs * max_context_len (equal lengths) one-pass
  * choices are the fixed rule's.  Negative status on invalid arguments,
  * among them a total below the maximum or above num_seqs times it.
@@ -291,9 +292,10 @@ int32_t paged_attention_decode_choose_partition_for_batch(int32_t num_seqs, int3
 
 /*
  * Where phase 1 puts each (sequence, head)'s results, computed on the host
- * from a host copy of seq_lens, for a cache in kv_layout (PAD_KV_*: the
- * balanced split launches two workgroups per compute unit for the tiled
- * layout, three for the rows layout) on a device with num_cus compute units
+ * from a host copy of seq_lens, for heads of head_size and a cache in
+ * kv_layout (PAD_KV_*: the balanced split launches two workgroups per compute
+ * unit for the tiled layout at head size 256, four below, and three for the
+ * rows layout) on a device with num_cus compute units
  * (the same rule phase 1 applies on the device).  Arrays (row-major, host
  * memory, caller-owned):
  *   seq_lens     int32 [num_seqs]
@@ -308,9 +310,10 @@ int32_t paged_attention_decode_choose_partition_for_batch(int32_t num_seqs, int3
  * or a negative status for invalid arguments.
  */
 int32_t paged_attention_decode_entry_ranges(const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
-                                            int32_t num_kv_heads, int32_t max_blocks_per_seq,
-                                            int32_t block_size, int32_t partition_size, int32_t kv_layout,
-                                            int32_t num_cus, int32_t* entry_count, int32_t* entry_begin,
+                                            int32_t num_kv_heads, int32_t head_size,
+                                            int32_t max_blocks_per_seq, int32_t block_size,
+                                            int32_t partition_size, int32_t kv_layout, int32_t num_cus,
+                                            int32_t* entry_count, int32_t* entry_begin,
                                             int32_t* entry_end);
 
 /*

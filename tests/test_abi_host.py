@@ -146,13 +146,13 @@ def test_partition_counts_from_pages():
 
 
 @pytest.mark.parametrize("S,H,Hkv,ctx,expect", [
-    # split sizes: the largest P with (ceil(ctx / P) - 1) x S x workgroups per sequence >= 2 x 256
-    (1, 24, 4, 100000, 512),      # 195 x 4 = 780 >= 512 (1024: 97 x 4 = 388 is too few)
-    (1, 24, 4, 32768, 128),       # 255 x 4; 256 would give 127 x 4 = 508
-    (1, 24, 4, 8192, 128),        # none reaches 512: the smallest
-    (4, 24, 4, 100000, 2048),     # 48 x 16
-    (16, 24, 4, 2048, 128),       # 15 x 64; 256 would give 7 x 64
-    (16, 24, 4, 8192, 512),       # 15 x 64
+    # split sizes: the largest P with (ceil(ctx / P) - 1) x S x workgroups per sequence >= 4 x 256
+    (1, 24, 4, 100000, 256),      # 390 x 4 = 1560 >= 1024 (512: 195 x 4 = 780 is too few)
+    (1, 24, 4, 32768, 128),       # none reaches 1024 (128: 255 x 4 = 1020): the smallest
+    (1, 24, 4, 8192, 128),
+    (4, 24, 4, 100000, 1024),     # 97 x 16 (2048: 48 x 16 = 768)
+    (16, 24, 4, 2048, 128),       # none: the smallest
+    (16, 24, 4, 8192, 256),       # 31 x 64 (512: 15 x 64 = 960)
     (64, 24, 4, 8192, 0),         # 256 (seq, KV head) workgroups: one per compute unit -> one-pass
     (256, 24, 4, 2048, 0),        # large batch
     (8, 24, 24, 131072, 2048),    # MHA: 63 x 8 x 24
@@ -173,19 +173,18 @@ def test_choose_partition_invalid():
 
 
 # (S, max, total, expected): the batch rule's choices on the batches it was
-# timed on (24 q / 4 KV heads, head 256, bf16, 256 compute units); each pick
-# was the fastest measured size or within 4 % of it
+# timed on (24 q / 4 KV heads, head 256, bf16, 256 compute units)
 @pytest.mark.parametrize("S,mx,total,expect", [
     (256, 2048, 256 * 2048, 0),                 # equal lengths: one-pass
     (64, 8192, 64 * 8192, 0),
     (1024, 512, 1024 * 512, 0),
-    (256, 65536, 255 * 1024 + 65536, 2048),     # one-pass 3421 us, split 279 us
-    (132, 32768, 128 * 2048 + 4 * 32768, 2048),  # 781 us against 285 us
-    (64, 3072, 63 * 1024 + 3072, 256),          # 91 us against 72 us
+    (256, 65536, 255 * 1024 + 65536, 1024),     # one-pass 3421 us, split 279 us
+    (132, 32768, 128 * 2048 + 4 * 32768, 1024),  # 781 us against 284 us
+    (64, 3072, 63 * 1024 + 3072, 128),          # one-pass 91 us
     (64, 2048, 63 * 1024 + 2048, 0),            # 75 us; the best split 72 us
-    (256, 2048, 255 * 1024 + 2048, 1024),       # 231 us against 213 us
+    (256, 2048, 255 * 1024 + 2048, 512),        # 231 us against 218 us
     (256, 32202, 1659008, 2048),                # log-uniform lengths: 2057 us against 1111 us
-    (1, 100000, 100000, 512),
+    (1, 100000, 100000, 256),
 ])
 def test_choose_partition_for_batch(S, mx, total, expect):
     assert pad.paged_attention_decode_choose_partition_for_batch(S, 24, 4, 256, "bf16", mx, total, 16, 256) == expect
@@ -209,8 +208,8 @@ def test_choose_partition_for_batch_equal_lengths_and_slots():
             assert P == 0
         if P:
             wgs = Hkv * -(-(H // Hkv) // 16)
-            ok = lambda p: (-(-mx // p) - 1) * total * wgs >= 2 * 256 * mx and -(-mx // p) >= 2
-            # the largest size whose slots keep two workgroups per compute unit (else 128)
+            ok = lambda p: (-(-mx // p) - 1) * total * wgs >= 4 * 256 * mx and -(-mx // p) >= 2
+            # the largest size whose slots let the split launch its full width (else 128)
             assert ok(P) or P == 128
             assert all(not ok(q) for q in (256, 512, 1024, 2048) if q > P)
 
@@ -312,14 +311,14 @@ def test_prefill_empty_is_a_noop():
 # where phase 1 puts its entries (the host copy of the device rule)
 # ---------------------------------------------------------------------------
 
-def check_entry_plan(lens, H, Hkv, W, P, cus=256, layout="tiled"):
+def check_entry_plan(lens, H, Hkv, W, P, cus=256, layout="tiled", D=256):
     """The invariants phase 2 relies on, for any lengths: every (sequence, head)
     with a valid non-empty length has entries that tile [0, L) in slot order,
     each a run of whole blocks (the last cut at L), no more than NP of them;
     the heads of one KV head share them."""
     import numpy as np
 
-    bal, cnt, lo, hi = pad.paged_attention_decode_entry_ranges(lens, H, Hkv, W, 16, P, cus, layout)
+    bal, cnt, lo, hi = pad.paged_attention_decode_entry_ranges(lens, H, Hkv, W, 16, P, cus, layout, D)
     NP = -(-W * 16 // P)
     G = H // Hkv
     for s, L in enumerate(lens):
@@ -360,7 +359,7 @@ def test_entry_plan_random_batches(seed):
     if S > 3:
         lens[1] = W * 16 + 7  # out of contract
     check_entry_plan(lens.tolist(), H, Hkv, W, P, cus=int(rng.choice([80, 256, 304])),
-                     layout=str(rng.choice(["tiled", "rows"])))
+                     layout=str(rng.choice(["tiled", "rows"])), D=int(rng.choice([64, 128, 256])))
 
 
 def test_entry_plan_long_context():
@@ -376,6 +375,9 @@ def test_entry_plan_long_context():
     # the rows layout launches three workgroups per compute unit: 768 ranges of 32 or 33 blocks
     bal, cnt, lo, hi = check_entry_plan([100000], 24, 4, 6250, 512, layout="rows")
     assert bal and set(cnt[0].tolist()) == {192} and cnt.sum() // 6 == 768
+    # smaller heads in the tiled layout, four: 1024 ranges of 48 or 49 blocks (P 256 leaves the slots)
+    bal, cnt, lo, hi = check_entry_plan([100000], 64, 8, 6250, 256, D=64)
+    assert bal and set(cnt[0].tolist()) == {128} and cnt.sum() // 8 == 1024
 
 
 def test_entry_plan_workloads():
@@ -397,9 +399,11 @@ def test_entry_plan_argument_errors():
         pad.paged_attention_decode_entry_ranges([10], 24, 4, 10, 16, 512, num_cus=0)
     with pytest.raises(ValueError):
         pad.paged_attention_decode_entry_ranges([10], 24, 4, 10, 16, 512, layout="nhd")
+    with pytest.raises(pad.PadError):
+        pad.paged_attention_decode_entry_ranges([10], 24, 4, 10, 16, 512, head_size=96)
     lens = (ctypes.c_int32 * 1)(10)
     out = (ctypes.c_int32 * 64)()
-    assert B.LIB.paged_attention_decode_entry_ranges(lens, 1, 24, 4, 10, 16, 512, 7, 256, out, out, out) < 0
+    assert B.LIB.paged_attention_decode_entry_ranges(lens, 1, 24, 4, 256, 10, 16, 512, 7, 256, out, out, out) < 0
 
 
 def test_no_alloc_rejects_what_does_not_fit():
@@ -513,10 +517,13 @@ def test_entry_plan_matches_model(seed):
     P = int(rng.choice([16, 64, 512, 1024]))
     cus = int(rng.choice([80, 256, 304]))
     layout = ("tiled", "rows")[seed % 2]
+    D = (64, 128, 256)[seed % 3]
     lens = rng.integers(0, W * 16 + 1, size=S)
     lens[rng.random(S) < 0.15] = 0
-    bal, cnt, lo, hi = pad.paged_attention_decode_entry_ranges(lens, H, Hkv, W, 16, P, cus, layout)
-    mbal, model = _model_entry_plan(lens.tolist(), H, Hkv, W, P, cus, wgs_per_cu=2 if layout == "tiled" else 3)
+    bal, cnt, lo, hi = pad.paged_attention_decode_entry_ranges(lens, H, Hkv, W, 16, P, cus, layout, D)
+    # workgroups per compute unit: tiled 2 at head size 256 and 4 below, rows 3
+    wpc = 3 if layout == "rows" else (2 if D == 256 else 4)
+    mbal, model = _model_entry_plan(lens.tolist(), H, Hkv, W, P, cus, wgs_per_cu=wpc)
     assert bal == mbal
     for s in range(S):
         for h in range(H):
