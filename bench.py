@@ -160,11 +160,20 @@ def run_prefill(args) -> int:
     qs = torch.from_numpy(pp.query_start).to(dev)
     ctx = torch.from_numpy(pp.context_lens).to(dev)
     out = torch.empty(tuple(pp.query.shape), dtype=torch.float32, device=dev)
+    form = args.prefill_form
+    if form == "auto":
+        n_ranges = pad.paged_attention_prefill_split_ranges(spec.head_size, spec.num_heads, spec.num_kv_heads)
+        form = "split" if pad.paged_attention_prefill_choose_split(
+            pp.context_lens, pp.query_lens, spec.num_heads, spec.num_kv_heads, spec.head_size, n_ranges) else "grid"
+    split = form == "split"
+    ws = (pad.alloc_prefill_split_workspace(pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size,
+                                            pp.max_query_len, dev) if split else None)
     torch.cuda.synchronize()
     flops = pp.flops()
     desc = (f"{args.config}: {pp.num_seqs} seq, context {list(map(int, pp.context_lens))}, chunk "
             f"{list(map(int, pp.query_lens))} tokens, {spec.num_heads} q / {spec.num_kv_heads} KV heads, head "
-            f"{spec.head_size}, bf16, block 16, tiled layout")
+            f"{spec.head_size}, bf16, block 16, tiled layout, "
+            f"{'split launch' if split else 'one walk per workgroup'}")
     print(f"[bench] {desc}; inputs ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
 
     def step(ev=None):
@@ -172,8 +181,12 @@ def run_prefill(args) -> int:
                                              pp.max_query_len)
         if ev:
             ev[0].record()
-        pad.paged_attention_prefill(out, q, kc, vc, tables, qs, ctx, pp.scale, spec.num_kv_heads, 16,
-                                    pp.max_query_len)
+        if split:
+            pad.paged_attention_prefill_split(out, q, kc, vc, tables, qs, ctx, pp.scale, spec.num_kv_heads, 16,
+                                              pp.max_query_len, ws)
+        else:
+            pad.paged_attention_prefill(out, q, kc, vc, tables, qs, ctx, pp.scale, spec.num_kv_heads, 16,
+                                        pp.max_query_len)
         if ev:
             ev[1].record()
 
@@ -238,7 +251,7 @@ def run_prefill(args) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": desc, "num_tokens": pp.num_tokens, "algorithmic_flops_per_step": flops,
-                   "accumulate": "fp32", "seed": spec.seed},
+                   "accumulate": "fp32", "seed": spec.seed, "form": form},
         "kernels_ms": {"prefill": round(k_ms, 4)},
         "roofline": {
             "bound": "mfma",
@@ -296,6 +309,9 @@ def main() -> int:
     ap.add_argument("--seq-len", type=int, default=None,
                     help="override every sequence's length (table width and pool follow)")
     ap.add_argument("--copies", type=int, default=0, help="KV pool copies to rotate (0: enough for 1.5 GB)")
+    ap.add_argument("--prefill-form", default="auto", choices=["auto", "split", "grid"],
+                    help="prefill workloads: the split launch (long walks cut into pieces, served first), one walk "
+                         "per workgroup, or the library's choice for the workload's lengths")
     ap.add_argument("--layout", default="tiled", choices=["tiled", "rows"],
                     help="KV cache layout: tiled (K 16-byte chunks x tokens, V dims x tokens) or rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")

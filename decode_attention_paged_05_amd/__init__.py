@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     PadDims,
     PadError,
     PadPrefillDims,
+    alloc_prefill_split_workspace,
     alloc_workspace,
     check_build,
     make_dims,
@@ -33,5 +34,9 @@ from ._binding import (  # noqa: F401
     paged_attention_decode_workspace_layout,
     paged_attention_decode_workspace_size,
     paged_attention_prefill,
+    paged_attention_prefill_choose_split,
+    paged_attention_prefill_split,
+    paged_attention_prefill_split_ranges,
+    paged_attention_prefill_split_workspace_size,
     paged_attention_prefill_write_kv,
 )

@@ -41,6 +41,10 @@ EXPORTED = [
     "paged_attention_decode_entry_ranges",
     "paged_attention_decode_build_id",
     "paged_attention_prefill",
+    "paged_attention_prefill_choose_split",
+    "paged_attention_prefill_split",
+    "paged_attention_prefill_split_ranges",
+    "paged_attention_prefill_split_workspace_size",
     "paged_attention_prefill_write_kv",
 ]
 
@@ -125,6 +129,14 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     pdims = ctypes.POINTER(PadPrefillDims)
     lib.paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, pdims, vp]
     lib.paged_attention_prefill.restype = i32
+    lib.paged_attention_prefill_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, pdims, vp, sz, vp]
+    lib.paged_attention_prefill_split.restype = i32
+    lib.paged_attention_prefill_choose_split.argtypes = [ip, ip, i32, i32, i32, i32, i32]
+    lib.paged_attention_prefill_choose_split.restype = i32
+    lib.paged_attention_prefill_split_ranges.argtypes = [i32, i32, i32]
+    lib.paged_attention_prefill_split_ranges.restype = i32
+    lib.paged_attention_prefill_split_workspace_size.argtypes = [pdims, i32, i32]
+    lib.paged_attention_prefill_split_workspace_size.restype = sz
     lib.paged_attention_prefill_write_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, pdims, vp]
     lib.paged_attention_prefill_write_kv.restype = i32
     del i64
@@ -475,6 +487,65 @@ def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, qu
                                      _ptr(block_tables), _ptr(query_start), _ptr(context_lens), float(scale),
                                      int(num_kv_heads), int(block_size), ctypes.byref(dims), _stream(stream))
     _check(st, "paged_attention_prefill")
+
+
+def paged_attention_prefill_split_ranges(head_size: int, num_heads: int, num_kv_heads: int) -> int:
+    """Ranges the balanced split cuts a prefill launch into on the current device."""
+    n = LIB.paged_attention_prefill_split_ranges(int(head_size), int(num_heads), int(num_kv_heads))
+    _check(n if n < 0 else 0, "paged_attention_prefill_split_ranges")
+    return n
+
+
+def paged_attention_prefill_choose_split(context_lens, query_lens, num_heads: int, num_kv_heads: int,
+                                         head_size: int, num_ranges: int) -> bool:
+    """Whether the split launch serves these lengths (host sequences of ints) better than the plain one."""
+    import numpy as np
+    c = np.ascontiguousarray(context_lens, dtype=np.int32)
+    q = np.ascontiguousarray(query_lens, dtype=np.int32)
+    if c.shape != q.shape or c.ndim != 1:
+        raise ValueError("context_lens and query_lens must be 1-D of one length")
+    ip = ctypes.POINTER(ctypes.c_int32)
+    r = LIB.paged_attention_prefill_choose_split(c.ctypes.data_as(ip), q.ctypes.data_as(ip), int(c.size),
+                                                 int(num_heads), int(num_kv_heads), int(head_size), int(num_ranges))
+    _check(r if r < 0 else 0, "paged_attention_prefill_choose_split")
+    return r == 1
+
+
+def paged_attention_prefill_split_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
+                                                 max_query_len: int, num_ranges: int) -> int:
+    dims = PadPrefillDims(PAD_DTYPE_BF16, int(num_seqs), 0, int(num_heads), int(head_size), int(max_query_len), 1, 1,
+                          PAD_KV_TILED)
+    n = LIB.paged_attention_prefill_split_workspace_size(ctypes.byref(dims), int(num_kv_heads), int(num_ranges))
+    if n == ctypes.c_size_t(-1).value:
+        raise PadError(-3, "paged_attention_prefill_split_workspace_size (sizes out of range)")
+    return n
+
+
+def alloc_prefill_split_workspace(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
+                                  max_query_len: int, device=None):
+    """Allocate (torch, uint8) a workspace for paged_attention_prefill_split on the current device."""
+    torch = _torch()
+    n = paged_attention_prefill_split_workspace_size(
+        num_seqs, num_heads, num_kv_heads, head_size, max_query_len,
+        paged_attention_prefill_split_ranges(head_size, num_heads, num_kv_heads))
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def paged_attention_prefill_split(out, query, key_cache, value_cache, block_tables, query_start, context_lens,
+                                  scale: float, num_kv_heads: int, block_size: int, max_query_len: int, workspace,
+                                  stream=None) -> None:
+    """paged_attention_prefill with the launch's work cut into equal ranges (``workspace``: uint8 tensor)."""
+    torch = _torch()
+    _check_prefill(query, key_cache, value_cache, block_tables, query_start, context_lens, num_kv_heads,
+                   block_size, None)
+    if out.dtype != torch.float32 or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must be float32 with the shape of query")
+    dims = make_prefill_dims(query, key_cache, block_tables, max_query_len)
+    st = LIB.paged_attention_prefill_split(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                           _ptr(block_tables), _ptr(query_start), _ptr(context_lens), float(scale),
+                                           int(num_kv_heads), int(block_size), ctypes.byref(dims), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "paged_attention_prefill_split")
 
 
 def paged_attention_prefill_write_kv(key_cache, value_cache, key, value, block_tables, query_start, context_lens,

@@ -322,6 +322,85 @@ int32_t paged_attention_prefill(float* out, const void* query, const void* key_c
                                        static_cast<hipStream_t>(stream)));
 }
 
+int32_t paged_attention_prefill_split_ranges(int32_t head_size, int32_t num_heads, int32_t num_kv_heads) {
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return PAD_ERR_SHAPE;
+  if (head_size != 64 && head_size != 128 && head_size != 256) return PAD_ERR_UNSUPPORTED;
+  return pad::prefill_split_ranges(head_size, num_heads / num_kv_heads);
+}
+
+size_t paged_attention_prefill_split_workspace_size(const pad_prefill_dims_t* dims, int32_t num_kv_heads,
+                                                    int32_t num_ranges) {
+  if (!dims || num_ranges <= 0 || num_kv_heads <= 0 || dims->num_seqs < 0 || dims->max_query_len < 0 ||
+      dims->num_heads <= 0 || dims->num_heads % num_kv_heads != 0 ||
+      (dims->head_size != 64 && dims->head_size != 128 && dims->head_size != 256))
+    return (size_t)-1;
+  return pad::prefill_split_workspace_bytes(dims->num_seqs, num_kv_heads, dims->num_heads / num_kv_heads,
+                                            dims->head_size, dims->max_query_len, num_ranges);
+}
+
+int32_t paged_attention_prefill_choose_split(const int32_t* context_lens, const int32_t* query_lens,
+                                             int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                             int32_t head_size, int32_t num_ranges) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || num_ranges <= 0)
+    return PAD_ERR_SHAPE;
+  if (head_size != 64 && head_size != 128 && head_size != 256) return PAD_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return 0;
+  if (!context_lens || !query_lens) return PAD_ERR_NULL;
+  for (int s = 0; s < num_seqs; ++s)
+    if (context_lens[s] < 0 || query_lens[s] < 0) return PAD_ERR_SHAPE;
+  return pad::prefill_split_cuts(context_lens, query_lens, num_seqs, num_kv_heads, num_heads / num_kv_heads,
+                                 num_ranges) ? 1 : 0;
+}
+
+int32_t paged_attention_prefill_split(float* out, const void* query, const void* key_cache, const void* value_cache,
+                                      const int32_t* block_tables, const int32_t* query_start,
+                                      const int32_t* context_lens, float scale, int32_t num_kv_heads,
+                                      int32_t block_size, const pad_prefill_dims_t* dims, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  int32_t st = validate_prefill(dims, num_kv_heads, block_size, true);
+  if (st != PAD_OK) return st;
+  if (!std::isfinite(scale)) return PAD_ERR_SHAPE;
+  if (dims->num_seqs == 0 || dims->num_tokens == 0 || dims->max_query_len == 0) return PAD_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !query_start || !context_lens)
+    return PAD_ERR_NULL;
+  if (!workspace) return PAD_ERR_WORKSPACE;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned16(workspace) || !aligned4(block_tables) || !aligned4(query_start) || !aligned4(context_lens))
+    return PAD_ERR_ALIGN;
+  const int group = dims->num_heads / num_kv_heads;
+  const int ranges = pad::prefill_split_ranges(dims->head_size, group);
+  // the walk kernel's grid is 32-bit, the merge's second dimension 16-bit
+  const int hg = group / pad::prefill_heads_per_wg(group);
+  if (pad::prefill_split_grid(dims->num_seqs, num_kv_heads, group, dims->max_query_len, ranges) > INT32_MAX ||
+      hg * 8 > 65535)
+    return PAD_ERR_UNSUPPORTED;
+  // the plan's 64-bit step count: S x KV heads x head groups x tiles x steps per tile
+  const int tpw = pad::prefill_tokens_per_wg(group, true);
+  const unsigned __int128 tiles = ((unsigned)dims->max_query_len + tpw - 1) / tpw;
+  const unsigned __int128 steps = ((unsigned __int128)dims->max_blocks_per_seq * block_size + 31) / 32;
+  if ((unsigned __int128)dims->num_seqs * num_kv_heads * hg * tiles * steps >> 62) return PAD_ERR_UNSUPPORTED;
+  if ((size_t)workspace_bytes < pad::prefill_split_workspace_bytes(dims->num_seqs, num_kv_heads, group,
+                                                                   dims->head_size, dims->max_query_len, ranges))
+    return PAD_ERR_WORKSPACE;
+  pad::PrefillArgs a{};
+  a.out = out;
+  a.query = static_cast<const char*>(query);
+  a.key_cache = static_cast<const char*>(key_cache);
+  a.value_cache = static_cast<const char*>(value_cache);
+  a.block_tables = block_tables;
+  a.query_start = query_start;
+  a.context_lens = context_lens;
+  a.qscale = scale;
+  a.num_tokens = dims->num_tokens;
+  a.num_heads = dims->num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.num_blocks = dims->num_blocks;
+  return status_of(pad::launch_prefill_split(a, dims->num_seqs, dims->max_query_len, dims->head_size, ranges,
+                                             workspace, static_cast<hipStream_t>(stream)));
+}
+
 int32_t paged_attention_prefill_write_kv(void* key_cache, void* value_cache, const void* key, const void* value,
                                          const int32_t* block_tables, const int32_t* query_start,
                                          const int32_t* context_lens, int32_t num_kv_heads,

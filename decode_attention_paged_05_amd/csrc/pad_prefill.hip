@@ -57,6 +57,8 @@
 // are ordered so that those sharing K/V tiles share an XCD's L2
 // (remap_workgroup).
 #include <hip/hip_runtime.h>
+#include <limits.h>
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -79,6 +81,7 @@ constexpr int kRowsPerWave = 32;   // two 16-row column tiles
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.0f;  // headroom of the lazy softmax reference
+constexpr float kNoKeysMax = -1e30f;  // reference max of a row that has seen no key
 
 // s_waitcnt immediate: at most n vector-memory loads outstanding and every
 // LDS access done (export counter left at its maximum)
@@ -221,8 +224,35 @@ __device__ inline int sequence_of_rank(const PrefillArgs& a, int nseq, int z, in
   return seq[z];
 }
 
+// LDS of a walk: the ring of K/V step buffers, and the logits a paired wave
+// leaves for its partner ([step parity][row group][block][column tile][lane]).
+template <int D, bool SOLO>
+struct WalkLds {
+  static constexpr int kTileStride = kBlockTokens * D * 2 + 64;
+  static constexpr int kBufs = 3;
+  __attribute__((aligned(16))) char kv[kBufs * 4 * kTileStride];
+  f32x4_t xs[SOLO ? 1 : 2][SOLO ? 1 : kRowGroups][2][2][kWave];
+};
+
+// Where a walk leaves its rows: the output itself (normalised), or, for a
+// piece of a walk split between workgroups, a partial slot (unnormalised rows
+// and each row's running max and sum, combined by merge_kernel).  Slot layout
+// for the solo layout: rows [wave][column tile][16-dim tile][lane] as float4
+// (lane = 16 lane-group + row), stats [wave][column tile][row][max, sum].
+struct WalkOut {
+  float* part;   // null: final rows into the output
+  float* stats;
+};
+
+// Walks steps [st_lo, min(st_hi, its walk's steps)) of one workgroup's rows --
+// sequence s (chunk rows q_lo .., n tokens over ctx cached), head group `by`
+// (KV head by / head_groups), token tile qt -- and leaves the rows in `dst`.
+// `poison` writes NaN rows instead (a sequence out of contract).  All threads
+// of the workgroup call it with the same arguments; st_lo must lie below the
+// walk's step count.
 template <int D, int HC, bool SOLO>
-__global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) {
+__device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, int qt, int q_lo, int n, int ctx,
+                                          int st_lo, int st_hi, bool poison, WalkOut dst, WalkLds<D, SOLO>& L) {
   // Solo layout: a wave holds its 32 output rows over all of D and owns them
   // alone (8 row groups, 256 rows per workgroup); it forms both logit tiles of
   // a step itself, and nothing is exchanged.  Paired layout (D = 256 only):
@@ -250,38 +280,19 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   // issued in.  Issued late, the prefix attention measured 8 % faster at
   // D = 256 (where a spilled register was then reloaded in every step), 7 %
   // at D = 128 and, once the block ids came by scalar loads, 6 % at D = 64.
-  __shared__ __attribute__((aligned(16))) char kv_lds[kBufs * kStepBytes];
-  // the logits a wave leaves for its partner: [step parity][row group][block][column tile][lane]
-  __shared__ f32x4_t xs_lds[kSolo ? 1 : 2][kSolo ? 1 : kRowGroups][2][2][kWave];
+  static_assert(WalkLds<D, SOLO>::kTileStride == kTileStride && WalkLds<D, SOLO>::kBufs == kBufs, "LDS shape");
+  char* const kv_lds = L.kv;
+  auto& xs_lds = L.xs;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int rg = kSolo ? wave : wave >> 1;   // row group
   const int dh = kSolo ? 0 : wave & 1;       // half of D this wave accumulates
   const int lg = lane >> 4;              // lane group
-  int bx, by, bz;
-  remap_workgroup(a.head_groups, &bx, &by, &bz);
-  __shared__ int64_t order_key[kOrderMaxSeqs];
-  __shared__ int order_seq[kOrderMaxSeqs];
-  const int s = (gridDim.z > 1 && gridDim.z <= kOrderMaxSeqs)
-                    ? __builtin_amdgcn_readfirstlane(sequence_of_rank(a, gridDim.z, bz, order_key, order_seq))
-                    : bz;
   const int g = by / a.head_groups;
   const int h = g * a.group + (by % a.head_groups) * HC + rg % HC;
-  const int qt = gridDim.x - 1 - bx;  // longest walks first
-  const int q_lo = a.query_start[s];
-  const int q_hi = a.query_start[s + 1];
-  const int n = q_hi - q_lo;
-  const int ctx = a.context_lens[s];
   const int wg_tok0 = qt * (kRowsPerWave * TW);
   const int tok0 = wg_tok0 + (rg / HC) * kRowsPerWave;
-  // out of contract: bad offsets or sizes, or a chunk longer than the grid
-  // covers (n_s > max_query_len), whose rows past the grid no workgroup writes
-  const bool bad_seq = ctx < 0 || n < 0 || q_lo < 0 || q_hi > a.num_tokens ||
-                       (int64_t)ctx + n > (int64_t)a.max_blocks * kBlockTokens ||
-                       (int64_t)n > (int64_t)gridDim.x * (kRowsPerWave * TW);
-  // the whole workgroup leaves together (it shares barriers below)
-  if (wg_tok0 >= max(n, 0)) return;
 
   // rows of this wave: column tile ct, lane -> chunk token tok0 + 16 ct + lane%16
   int rpos[2];
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
       }
     }
   };
-  if (bad_seq) {
+  if (poison) {
     // out-of-contract sizes: NaN rows, within the output's bounds
     f32x4_t o[2][DT];
     const float nan[2] = {NAN, NAN};
@@ -341,6 +352,9 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   const int kend = ctx + min(wg_tok0 + kRowsPerWave * TW, n);
   const int nblk = (kend + kBlockTokens - 1) / kBlockTokens;
   const int nsteps = (nblk + 1) / 2;
+  // the steps this call walks
+  const int lo = st_lo;
+  const int hi = min(st_hi, nsteps);
   // keys below a wave's first row position are visible to all its rows
   const int diag_from = ctx + tok0;
   // V is zeroed from here on: the tail slots of the sequence's last block, and
@@ -372,7 +386,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     const int blk = 2 * step + my_b;
     return blk < nblk ? table_c[blk] : 0;
   };
-  int next_id = fetch_id(0);
+  int next_id = fetch_id(lo);
   // V tiles are stored with the two 16-byte halves of every other group of 8
   // dims swapped (16-byte chunk c of the tile lands at c ^ ((c >> 4) & 1)), so
   // that the V operand reads of a half-wave hit distinct banks
@@ -409,7 +423,12 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_ref[2] = {-INFINITY, -INFINITY};
+  // The reference max starts at a finite floor, not -inf: a piece of a split
+  // walk that starts past key 0 can hold rows that see none of its keys, and
+  // their weights exp2(-inf - ref) must come out 0, not NaN.  The first keys
+  // a row sees always lift the reference (the rescale factor exp2(floor - max)
+  // is then 0, as from -inf), so whole walks give the same bits either way.
+  float m_ref[2] = {kNoKeysMax, kNoKeysMax};
   float l_run[2] = {0.0f, 0.0f};
 
   // Tile kb of a step's S^T (16 of its 32 keys x the wave's 32 rows, over all
@@ -434,20 +453,20 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     }
   };
   constexpr int kLead = kBufs - 1;  // iteration st issues the copies of step st + kLead
-  for (int k = 0; k < kLead && k < nsteps; ++k) {
-    issue(k, kv_lds + k * kStepBytes);
+  for (int k = lo; k < lo + kLead && k < hi; ++k) {
+    issue(k, kv_lds + (k % kBufs) * kStepBytes);
   }
   // step 0's logits (paired waves: formed ahead, for the exchange)
   if constexpr (!kSolo) {
-    if (nsteps > 1)
+    if (hi - lo > 1)
       __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
     else
       __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
     workgroup_barrier();
     f32x4_t first[2];
-    qk_block(kv_lds, first);
+    qk_block(kv_lds + (lo % kBufs) * kStepBytes, first);
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) xs_lds[0][rg][kb][ct][lane] = first[ct];
+    for (int ct = 0; ct < 2; ++ct) xs_lds[lo & 1][rg][kb][ct][lane] = first[ct];
   }
 
   // Iteration st: wait for the copies of step st + 1 (this wave's; the
@@ -466,7 +485,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
   // out of the loop: 7 % faster at D = 256, 5-7 % at D = 128.
   auto iter = [&](int st, auto last) {
     // paired waves need K of step st + 1 now; solo waves only step st
-    if (kSolo && st + 1 < nsteps)
+    if (kSolo && st + 1 < hi)
       __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
     else
       __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
@@ -571,7 +590,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     // ---- this wave's logits of the next step, for the pair (issued after
     // the softmax, so that the matrix cores work through them while P.V's
     // operands are read)
-    if (!kSolo && st + 1 < nsteps) {
+    if (!kSolo && st + 1 < hi) {
       f32x4_t next[2];
       qk_block(kv_lds + ((st + 1) % kBufs) * kStepBytes, next);
 #pragma unroll
@@ -579,7 +598,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     }
 
     // ---- the copies of step st + 2 (here, after the logits of step st + 1)
-    if (st + kLead < nsteps) {
+    if (st + kLead < hi) {
       issue(st + kLead, kv_lds + ((st + kLead) % kBufs) * kStepBytes);
     }
 
@@ -618,18 +637,408 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) 
     pv(last);
     if constexpr (kPvPriority) __builtin_amdgcn_s_setprio(0);
   };
-  for (int st = 0; st + 1 < nsteps; ++st) iter(st, std::false_type{});
-  if (nsteps > 0) iter(nsteps - 1, std::true_type{});
-  // every wave's block-id checks count for the whole workgroup's tiles
+  for (int st = lo; st + 1 < hi; ++st) iter(st, std::false_type{});
+  if (hi > lo) iter(hi - 1, std::true_type{});
+  // every wave's block-id checks count for the whole workgroup's tiles (and
+  // the barrier retires every LDS read before a next walk's copies)
   bad = __syncthreads_or(bad);
+  float l[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) l[ct] = group_sum(l_run[ct]);
+  if (dst.part) {
+    // a piece of a split walk: unnormalised rows, and each row's reference
+    // max (log2 units of the scaled logits) and sum; NaN sums mark a bad block id
+    float* po = dst.part + (size_t)wave * (2 * DT * kWave * 4);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f32x4_t*>(po + ((ct * DT + dt) * kWave + lane) * 4) = o[ct][dt];
+    if (lg == 0 && dh == 0) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        float* ps = dst.stats + ((rg * 2 + ct) * 16 + lane) * 2;
+        ps[0] = m_ref[ct];
+        ps[1] = bad ? NAN : l[ct];
+      }
+    }
+    return;
+  }
   float inv[2];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const float l = group_sum(l_run[ct]);
-    inv[ct] = bad ? NAN : 1.0f / l;
-  }
+  for (int ct = 0; ct < 2; ++ct) inv[ct] = bad ? NAN : 1.0f / l[ct];
   store_rows(o, inv);
 }
+
+// One workgroup per (token tile, head group, sequence), longest walks first.
+template <int D, int HC, bool SOLO>
+__global__ __launch_bounds__(kWaves * kWave) void prefill_kernel(PrefillArgs a) {
+  constexpr int TPW = kRowsPerWave * (SOLO ? 2 * kRowGroups : kRowGroups) / HC;  // chunk tokens per workgroup
+  int bx, by, bz;
+  remap_workgroup(a.head_groups, &bx, &by, &bz);
+  __shared__ int64_t order_key[kOrderMaxSeqs];
+  __shared__ int order_seq[kOrderMaxSeqs];
+  const int s = (gridDim.z > 1 && gridDim.z <= kOrderMaxSeqs)
+                    ? __builtin_amdgcn_readfirstlane(sequence_of_rank(a, gridDim.z, bz, order_key, order_seq))
+                    : bz;
+  const int qt = gridDim.x - 1 - bx;  // longest walks first
+  const int q_lo = a.query_start[s];
+  const int q_hi = a.query_start[s + 1];
+  const int n = q_hi - q_lo;
+  const int ctx = a.context_lens[s];
+  // out of contract: bad offsets or sizes, or a chunk longer than the grid
+  // covers (n_s > max_query_len), whose rows past the grid no workgroup writes
+  const bool bad_seq = ctx < 0 || n < 0 || q_lo < 0 || q_hi > a.num_tokens ||
+                       (int64_t)ctx + n > (int64_t)a.max_blocks * kBlockTokens ||
+                       (int64_t)n > (int64_t)gridDim.x * TPW;
+  // the whole workgroup leaves together (it shares barriers)
+  if (qt * TPW >= max(n, 0)) return;
+  __shared__ WalkLds<D, SOLO> lds;
+  walk_rows<D, HC, SOLO>(a, s, by, qt, q_lo, n, ctx, 0, INT_MAX, bad_seq, WalkOut{nullptr, nullptr}, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Split launch.  In a batch whose walks differ in length, the longest walks
+// decide when the launch ends while most compute units sit idle.  The split
+// launch cuts every walk longer than C steps into k = ceil(steps / C) pieces
+// of equal length -- C is the launch's total steps over kSplitRounds rounds of
+// its resident workgroups -- and serves the pieces before the whole walks:
+// the dispatcher, which starts workgroups in order as compute units free up,
+// then evens the units out.  A unit (a piece or a whole walk of one KV head,
+// for its HG head chunks) is listed by split_plan_kernel in this order:
+//   1. the pieces: by piece index j, then sequence (longest walk first), then
+//      tile (longest first), then KV head.  Pieces with one index start at
+//      nearly the same key, so the workgroups that run together read the same
+//      K/V tiles through L2;
+//   2. the whole walks: by sequence, tile (longest first), KV head.
+// Each piece leaves its unnormalised rows in a partial slot, and
+// split_merge_kernel combines the pieces of a cut walk by their log-sum-exp.
+// ---------------------------------------------------------------------------
+#ifndef PAD_PREFILL_SPLIT_ROUNDS
+#define PAD_PREFILL_SPLIT_ROUNDS 4
+#endif
+constexpr int kSplitRounds = PAD_PREFILL_SPLIT_ROUNDS;  // rounds of resident workgroups the pieces fill
+// Walks are cut only when the longest is above 1 / kSplitShare of a resident
+// workgroup's fair share (total steps / N): below that the dispatcher's
+// longest-first order already evens the compute units out.
+#ifndef PAD_PREFILL_SPLIT_SHARE
+#define PAD_PREFILL_SPLIT_SHARE 2
+#endif
+constexpr int kSplitShare = PAD_PREFILL_SPLIT_SHARE;
+constexpr int kSplitMaxPieces = 32;  // pieces of one walk, at most
+constexpr int kSplitMinSteps = 16;   // C, at least
+constexpr int kSplitRows = 2 * kRowGroups * kRowsPerWave;  // rows of a solo workgroup
+constexpr int kSplitStatFloats = 2 * kSplitRows;
+constexpr int kSplitPlanThreads = 1024;
+
+// header words the plan writes
+enum { kHdrUnits = 0, kHdrPieces, kHdrCutWalks, kHdrStep, kHdrMaxPieces, kHdrCutSeqs, kHdrWords = 16 };
+
+struct PrefillSplit {
+  int32_t* hdr;        // [kHdrWords]
+  int4* units;         // [units_cap]: {sequence, tile, KV head, j << 16 | k}
+  int32_t* order;      // [S]: sequence of each rank (longest walk first)
+  int32_t* cut_idx;    // [S]: rank of the sequence among those with cut walks, or -1
+  int32_t* cut_seq;    // [cut_seq_cap]: sequence of each such rank
+  int32_t* pair_off;   // [kSplitMaxPieces x cut_seq_cap]: first unit of (piece index, cut sequence)
+  float* part;         // [slots_cap] slots of 256 rows x D floats
+  float* stats;        // [slots_cap] slots of 256 rows x (max, sum)
+  int num_seqs;
+  int max_query_len;
+  int ranges;          // N, resident workgroups of the walk kernel
+  int tokens_per_wg;   // TPW, a multiple of 32
+  int units_cap;
+  int cut_walk_cap;    // bound on cut walks: the merge grid
+  int cut_seq_cap;
+  int slots_cap;
+};
+
+// 32-key steps of token tile t (its last row sees keys 0 .. ctx + min((t + 1) TPW, n) - 1).
+__host__ __device__ inline int64_t tile_steps(int64_t t, int64_t ctx, int64_t n, int64_t tpw) {
+  const int64_t e = (t + 1) * tpw;
+  return (ctx + (e < n ? e : n) + 31) / 32;
+}
+
+// Tiles (of T) whose walks take more than thr steps: the longest ones, since
+// the steps grow with the tile.
+__device__ inline int tiles_above(int64_t thr, int64_t ctx, int64_t n, int64_t tpw, int T) {
+  int lo = 0, hi = T;  // the first tile above thr
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_steps(mid, ctx, n, tpw) > thr) hi = mid; else lo = mid + 1;
+  }
+  return T - lo;
+}
+
+// Whether sequence s is inside the contract (its walks are served).
+__device__ inline bool split_seq_ok(const PrefillArgs& a, const PrefillSplit& p, int s, int* q_lo, int* n,
+                                    int* ctx) {
+  *q_lo = a.query_start[s];
+  const int q_hi = a.query_start[s + 1];
+  *n = q_hi - *q_lo;
+  *ctx = a.context_lens[s];
+  return *ctx >= 0 && *n >= 0 && *q_lo >= 0 && q_hi <= a.num_tokens && *n <= p.max_query_len &&
+         (int64_t)*ctx + *n <= (int64_t)a.max_blocks * kBlockTokens;
+}
+
+// Exclusive scan of one value per thread over the workgroup (kSplitPlanThreads
+// threads); returns the thread's offset and leaves the total in *total.
+__device__ inline int plan_scan(int v, int* wave_sum, int* total) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) wave_sum[w] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int k = 0; k < kSplitPlanThreads / kWave; ++k) {
+    if (k < w) before += wave_sum[k];
+    all += wave_sum[k];
+  }
+  __syncthreads();  // wave_sum is reused by the next scan
+  *total = all;
+  return before + x - v;
+}
+
+// One workgroup: the unit list.
+__global__ __launch_bounds__(kSplitPlanThreads) void split_plan_kernel(PrefillArgs a, PrefillSplit p) {
+  __shared__ int wave_sum[kSplitPlanThreads / kWave];
+  __shared__ unsigned long long total_steps;
+  __shared__ int max_steps;
+  __shared__ int64_t rank_key[kSplitPlanThreads];
+  const int tid = threadIdx.x;
+  const int S = p.num_seqs, Hkv = a.num_kv_heads, HG = a.head_groups;
+  const int64_t tpw = p.tokens_per_wg;
+  if (tid == 0) {
+    total_steps = 0;
+    max_steps = 0;
+  }
+  __syncthreads();
+  // (1) total steps (all head groups) and the longest walk
+  for (int s = tid; s < S; s += kSplitPlanThreads) {
+    int q_lo, n, ctx;
+    if (!split_seq_ok(a, p, s, &q_lo, &n, &ctx) || n == 0) continue;
+    const int T = (int)((n + tpw - 1) / tpw);
+    unsigned long long steps = 0;  // sum over the tiles
+    for (int t = 0; t < T; ++t) steps += (unsigned long long)tile_steps(t, ctx, n, tpw);
+    atomicAdd(&total_steps, steps * (unsigned long long)(Hkv * HG));
+    atomicMax(&max_steps, (int)tile_steps(T - 1, ctx, n, tpw));
+  }
+  __syncthreads();
+  const int64_t B = (int64_t)total_steps;
+  const int64_t rounds = (int64_t)kSplitRounds * p.ranges;
+  int64_t C = (B + rounds - 1) / rounds;
+  C = max(C, (int64_t)(max_steps + kSplitMaxPieces - 1) / kSplitMaxPieces);
+  C = max(C, (int64_t)kSplitMinSteps);
+  if ((int64_t)max_steps * kSplitShare * p.ranges <= B) C = max(C, (int64_t)max_steps);  // no walk is cut
+  const int kmax = max_steps > C ? (int)((max_steps + C - 1) / C) : 1;
+  // (2) serving order: longest walk (context + chunk) first; sequences out of
+  // contract or without tokens last.  Past kSplitPlanThreads sequences, the
+  // given order.
+  if (S <= kSplitPlanThreads) {
+    if (tid < S) {
+      int q_lo, n, ctx;
+      rank_key[tid] = split_seq_ok(a, p, tid, &q_lo, &n, &ctx) && n > 0 ? (int64_t)ctx + n : -1;
+    }
+    __syncthreads();
+    if (tid < S) {
+      const int64_t k = rank_key[tid];
+      int r = 0;
+      for (int j = 0; j < S; ++j) r += (rank_key[j] > k) || (rank_key[j] == k && j < tid);
+      p.order[r] = tid;
+    }
+  } else {
+    for (int s = tid; s < S; s += kSplitPlanThreads) p.order[s] = s;
+  }
+  __syncthreads();  // order is read back below (global writes of this workgroup)
+  // (3) the sequences with cut walks, in serving order
+  int n_cut = 0;
+  for (int base = 0; base < S; base += kSplitPlanThreads) {
+    const int r = base + tid;
+    int cut = 0, s = -1;
+    if (r < S) {
+      s = p.order[r];
+      int q_lo, n, ctx;
+      cut = split_seq_ok(a, p, s, &q_lo, &n, &ctx) && n > 0 && tile_steps((n + tpw - 1) / tpw - 1, ctx, n, tpw) > C;
+    }
+    int tot;
+    const int o = n_cut + plan_scan(cut, wave_sum, &tot);
+    if (r < S) {
+      p.cut_idx[s] = cut ? o : -1;
+      if (cut) p.cut_seq[o] = s;
+    }
+    n_cut += tot;
+  }
+  __syncthreads();  // cut_seq is read back below
+  // (4) the pieces: pair (j, c) = (piece index, cut sequence c) holds, for
+  // every KV head, the tiles whose walks have a piece j (the longest ones)
+  const int pairs = kmax * n_cut;
+  int n_pieces = 0, n_first = 0;
+  for (int base = 0; base < pairs; base += kSplitPlanThreads) {
+    const int q = base + tid;
+    int cnt = 0, s = 0, j = 0, c = 0, ctx = 0, n = 0, q_lo = 0, T = 0;
+    if (q < pairs) {
+      j = q / n_cut;
+      c = q - j * n_cut;
+      s = p.cut_seq[c];
+      split_seq_ok(a, p, s, &q_lo, &n, &ctx);
+      T = (int)((n + tpw - 1) / tpw);
+      cnt = Hkv * tiles_above((j > 0 ? j : 1) * C, ctx, n, tpw, T);
+    }
+    int tot, tot_first;
+    const int o = n_pieces + plan_scan(cnt, wave_sum, &tot);
+    plan_scan(j == 0 ? cnt : 0, wave_sum, &tot_first);
+    if (q < pairs) {
+      p.pair_off[j * p.cut_seq_cap + c] = o;
+      for (int i = 0; i < cnt; ++i) {
+        const int t = T - 1 - i / Hkv;
+        const int k = (int)((tile_steps(t, ctx, n, tpw) + C - 1) / C);
+        p.units[o + i] = make_int4(s, t, i % Hkv, (j << 16) | k);
+      }
+    }
+    n_pieces += tot;
+    n_first += tot_first;
+  }
+  // (5) the whole walks, after the pieces
+  int placed = 0;
+  for (int base = 0; base < S; base += kSplitPlanThreads) {
+    const int r = base + tid;
+    int cnt = 0, s = 0, T = 0, above = 0;
+    if (r < S) {
+      s = p.order[r];
+      int q_lo, n, ctx;
+      if (split_seq_ok(a, p, s, &q_lo, &n, &ctx) && n > 0) {
+        T = (int)((n + tpw - 1) / tpw);
+        above = tiles_above(C, ctx, n, tpw, T);
+        cnt = Hkv * (T - above);
+      }
+    }
+    int tot;
+    const int o = n_pieces + placed + plan_scan(cnt, wave_sum, &tot);
+    for (int i = 0; i < cnt; ++i) p.units[o + i] = make_int4(s, T - above - 1 - i / Hkv, i % Hkv, 1);
+    placed += tot;
+  }
+  if (tid == 0) {
+    p.hdr[kHdrUnits] = n_pieces + placed;
+    p.hdr[kHdrPieces] = n_pieces;
+    p.hdr[kHdrCutWalks] = n_first;
+    p.hdr[kHdrStep] = (int)C;
+    p.hdr[kHdrMaxPieces] = kmax;
+    p.hdr[kHdrCutSeqs] = n_cut;
+  }
+}
+
+// Unit and head chunk of this workgroup.  The HG workgroups of a unit (its
+// head chunks, which read the same K/V tiles) get linear ids 8 apart: the
+// dispatcher deals linear ids to the 8 XCDs in turn, so they share one L2.
+// The grid is a whole number of units.
+__device__ inline void split_unit_of(int HG, int* unit, int* hp) {
+  const int L = blockIdx.x, N = gridDim.x;
+  const int M = N / (8 * HG) * (8 * HG);
+  const int c = L & 7, k = L >> 3;
+  if (L < M) {
+    *unit = (k / HG) * 8 + c;
+    *hp = k % HG;
+  } else {
+    *unit = M / HG + (L - M) / HG;
+    *hp = (L - M) % HG;
+  }
+}
+
+template <int D, int HC>
+__global__ __launch_bounds__(kWaves * kWave) void split_walk_kernel(PrefillArgs a, PrefillSplit p) {
+  __shared__ WalkLds<D, true> lds;
+  int U, hp;
+  split_unit_of(a.head_groups, &U, &hp);
+  if (U >= p.hdr[kHdrUnits]) return;
+  const int4 u = p.units[U];
+  const int s = u.x, t = u.y, g = u.z, j = u.w >> 16, k = u.w & 0xffff;
+  const int q_lo = a.query_start[s];
+  const int n = a.query_start[s + 1] - q_lo;
+  const int ctx = a.context_lens[s];
+  const int64_t st = tile_steps(t, ctx, n, p.tokens_per_wg);
+  const int lo = (int)(j * st / k), hi = (int)((j + 1) * st / k);
+  WalkOut dst{nullptr, nullptr};
+  if (k > 1) {
+    const size_t slot = (size_t)U * a.head_groups + hp;
+    dst.part = p.part + slot * ((size_t)kSplitRows * D);
+    dst.stats = p.stats + slot * kSplitStatFloats;
+  }
+  walk_rows<D, HC, true>(a, s, g * a.head_groups + hp, t, q_lo, n, ctx, lo, hi, false, dst, lds);
+}
+
+// Workgroup (x, 8 hp + rg): x < cut_walk_cap: the cut walk x (the unit of its
+// first piece), head chunk hp, row group rg (32 rows over all of D): combine
+// its pieces.  x >= cut_walk_cap: NaN rows of sequence x - cut_walk_cap if it
+// is out of contract (its first min(n, max_query_len) chunk rows inside the
+// output).
+template <int D, int HC>
+__global__ __launch_bounds__(256) void split_merge_kernel(PrefillArgs a, PrefillSplit p) {
+  constexpr int DT = D / 16;
+  constexpr int TPW = kSplitRows / HC;
+  const int tid = threadIdx.x;
+  const int x = blockIdx.x;
+  const int hp = blockIdx.y / (2 * kRowGroups), rg = blockIdx.y % (2 * kRowGroups);
+  if (x >= p.cut_walk_cap) {
+    const int s = x - p.cut_walk_cap;
+    int q_lo, n, ctx;
+    if (split_seq_ok(a, p, s, &q_lo, &n, &ctx)) return;
+    const int64_t rows = n < 0 ? 0 : (n < p.max_query_len ? n : p.max_query_len);
+    const int64_t per_row = (int64_t)a.num_heads * (D / 4);
+    for (int64_t f = (int64_t)blockIdx.y * 256 + tid; f < rows * per_row; f += 256 * (int64_t)gridDim.y) {
+      const int64_t row = (int64_t)q_lo + f / per_row;
+      if (row < 0 || row >= a.num_tokens) continue;
+      *reinterpret_cast<f32x4_t*>(a.out + row * a.num_heads * D + (f % per_row) * 4) = f32x4_t{NAN, NAN, NAN, NAN};
+    }
+    return;
+  }
+  if (x >= p.hdr[kHdrCutWalks]) return;
+  const int4 u = p.units[x];  // piece 0 of the walk
+  const int s = u.x, t = u.y, g = u.z, k = u.w & 0xffff;
+  const int q_lo = a.query_start[s];
+  const int n = a.query_start[s + 1] - q_lo;
+  const int T = (n + TPW - 1) / TPW;
+  const int c = p.cut_idx[s];
+  const int within = (T - 1 - t) * a.num_kv_heads + g;  // the walk's place in each of its pairs
+  const int i = tid >> 3, ct = i >> 4, l16 = i & 15, qg = tid & 7;
+  const size_t stat_off = ((size_t)(rg * 2 + ct) * 16 + l16) * 2;
+  auto slot_of = [&](int j) {
+    return (size_t)(p.pair_off[j * p.cut_seq_cap + c] + within) * a.head_groups + hp;
+  };
+  float M = -INFINITY;
+  for (int j = 0; j < k; ++j) M = fmaxf(M, p.stats[slot_of(j) * kSplitStatFloats + stat_off]);
+  float l = 0.0f;
+  f32x4_t acc[D / 32];
+#pragma unroll
+  for (int q = 0; q < D / 32; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < k; ++j) {
+    const size_t slot = slot_of(j);
+    const float* st = p.stats + slot * kSplitStatFloats + stat_off;
+    // a piece without keys for this row (max kNoKeysMax) weighs exp2(-1e30 -
+    // M) = 0 beside one with keys; a NaN sum propagates
+    const float wgt = __builtin_amdgcn_exp2f(st[0] - M);
+    l += wgt * st[1];
+    const float* po = p.part + slot * ((size_t)kSplitRows * D) + (size_t)rg * (2 * DT * kWave * 4);
+#pragma unroll
+    for (int q = 0; q < D / 32; ++q) {
+      const int d4 = qg + 8 * q;  // 4-dim quad: dims 4 d4 .. = 16 (d4 >> 2) + 4 (d4 & 3) + e
+      const int lane = (d4 & 3) * 16 + l16;
+      acc[q] += wgt * *reinterpret_cast<const f32x4_t*>(po + (((size_t)ct * DT + (d4 >> 2)) * kWave + lane) * 4);
+    }
+  }
+  const int tok = t * TPW + (rg / HC) * kRowsPerWave + 16 * ct + l16;
+  const int64_t row = (int64_t)q_lo + tok;
+  if (tok >= n || row >= a.num_tokens) return;
+  const int h = g * a.group + hp * HC + rg % HC;
+  float* dst = a.out + ((size_t)row * a.num_heads + h) * D;
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int q = 0; q < D / 32; ++q) *reinterpret_cast<f32x4_t*>(dst + 4 * (qg + 8 * q)) = acc[q] * inv;
+}
+
 
 // Chunk write: key/value rows [T, Hkv, D] of the chunk tokens go to the cache
 // slots of their positions.  One thread per 16 bytes of one (token, KV head)
@@ -735,19 +1144,151 @@ bool prefill_solo(int head_size, int group, int num_kv_heads, int max_query_len)
 
 int prefill_tokens_per_wg(int group, bool solo) { return tokens_per_wg(prefill_heads_per_wg(group), solo); }
 
-hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
-                          hipStream_t stream) {
+namespace {
+
+// The kernels' view of the arguments: head groups per KV head, and the scale.
+// The kernels apply the scale in the exp2 argument and take maxima over the
+// raw logits, which needs a positive scale: a negative one moves onto the
+// query's sign, and 0 becomes the smallest normal float (for logits below
+// 2^100 in magnitude every weight is then exp2 of less than 2^-26, which
+// rounds to 1, as with 0).
+PrefillArgs kernel_args(const PrefillArgs& args) {
   PrefillArgs a = args;
-  const int hc = prefill_heads_per_wg(a.group);
-  a.head_groups = a.group / hc;
-  // The kernel applies the scale in the exp2 argument and takes maxima over the
-  // raw logits, which needs a positive scale: a negative one moves onto the
-  // query's sign, and 0 becomes the smallest normal float (for logits below
-  // 2^100 in magnitude every weight is then exp2 of less than 2^-26, which
-  // rounds to 1, as with 0)
+  a.head_groups = a.group / prefill_heads_per_wg(a.group);
   const float qs = args.qscale * kLog2e;
   a.negate_q = qs < 0.0f ? 1 : 0;
   a.qscale = qs < 0.0f ? -qs : (qs > 0.0f ? qs : 1.17549435e-38f);
+  return a;
+}
+
+const void* split_walk_fn(int head_size, int hc) {
+#define PAD_SPLIT_FN(DD)                                                                  \
+  (hc == 1   ? reinterpret_cast<const void*>(&split_walk_kernel<DD, 1>)                  \
+   : hc == 2 ? reinterpret_cast<const void*>(&split_walk_kernel<DD, 2>)                  \
+             : reinterpret_cast<const void*>(&split_walk_kernel<DD, 4>))
+  return head_size == 64 ? PAD_SPLIT_FN(64) : head_size == 128 ? PAD_SPLIT_FN(128) : PAD_SPLIT_FN(256);
+#undef PAD_SPLIT_FN
+}
+
+const void* split_merge_fn(int head_size, int hc) {
+#define PAD_MERGE_FN(DD)                                                                  \
+  (hc == 1   ? reinterpret_cast<const void*>(&split_merge_kernel<DD, 1>)                 \
+   : hc == 2 ? reinterpret_cast<const void*>(&split_merge_kernel<DD, 2>)                 \
+             : reinterpret_cast<const void*>(&split_merge_kernel<DD, 4>))
+  return head_size == 64 ? PAD_MERGE_FN(64) : head_size == 128 ? PAD_MERGE_FN(128) : PAD_MERGE_FN(256);
+#undef PAD_MERGE_FN
+}
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of a split launch.  Bounds (rounds = kSplitRounds x N, C >= the
+// total steps / rounds): a cut walk has more than C steps, so fewer than
+// rounds / HG walks are cut, in fewer than rounds / (Hkv HG) sequences; a cut
+// walk's k = ceil(steps / C) pieces number under 2 steps / C, so fewer than
+// 2 rounds / HG pieces; whole walks are at most S x Hkv x ceil(max_query_len / TPW).
+struct SplitLayout {
+  int64_t units_cap, cut_walk_cap, cut_seq_cap, slots_cap;
+  size_t units, order, cut_idx, cut_seq, pair_off, stats, part, bytes;
+};
+SplitLayout split_layout(int num_seqs, int num_kv_heads, int group, int head_size, int max_query_len, int ranges) {
+  const int64_t hg = group / prefill_heads_per_wg(group);
+  const int64_t tpw = tokens_per_wg(prefill_heads_per_wg(group), true);
+  const int64_t rounds = (int64_t)kSplitRounds * ranges;
+  SplitLayout l;
+  l.units_cap = (int64_t)num_seqs * num_kv_heads * ((max_query_len + tpw - 1) / tpw) + 2 * rounds / hg + 2;
+  l.cut_walk_cap = rounds / hg + 1;
+  l.cut_seq_cap = std::min<int64_t>(num_seqs, rounds / (hg * num_kv_heads) + 1);
+  l.slots_cap = (2 * rounds / hg + 2) * hg;
+  l.units = 256;  // the header
+  l.order = l.units + align256((size_t)l.units_cap * 16);
+  l.cut_idx = l.order + align256((size_t)num_seqs * 4);
+  l.cut_seq = l.cut_idx + align256((size_t)num_seqs * 4);
+  l.pair_off = l.cut_seq + align256((size_t)l.cut_seq_cap * 4);
+  l.stats = l.pair_off + align256((size_t)kSplitMaxPieces * l.cut_seq_cap * 4);
+  l.part = l.stats + align256((size_t)l.slots_cap * kSplitStatFloats * 4);
+  l.bytes = l.part + (size_t)l.slots_cap * kSplitRows * head_size * 4;
+  return l;
+}
+
+}  // namespace
+
+int prefill_split_ranges(int head_size, int group) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_walk_fn(head_size, prefill_heads_per_wg(group)),
+                                                   kWaves * kWave, 0) != hipSuccess ||
+      per_cu < 1) {
+    (void)hipGetLastError();  // our own failed query: do not leave it behind
+    per_cu = 1;
+  }
+  return per_cu * device_cus();
+}
+
+size_t prefill_split_workspace_bytes(int num_seqs, int num_kv_heads, int group, int head_size, int max_query_len,
+                                     int ranges) {
+  return split_layout(num_seqs, num_kv_heads, group, head_size, max_query_len, ranges).bytes;
+}
+
+bool prefill_split_cuts(const int32_t* context_lens, const int32_t* query_lens, int num_seqs, int num_kv_heads,
+                        int group, int ranges) {
+  const int64_t hg = group / prefill_heads_per_wg(group);
+  const int64_t tpw = tokens_per_wg(prefill_heads_per_wg(group), true);
+  int64_t total = 0, longest = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int64_t ctx = context_lens[s], n = query_lens[s];
+    if (n <= 0) continue;
+    const int64_t T = (n + tpw - 1) / tpw;
+    for (int64_t t = 0; t < T; ++t) total += tile_steps(t, ctx, n, tpw);
+    longest = std::max(longest, tile_steps(T - 1, ctx, n, tpw));
+  }
+  // the plan kernel's rule
+  return longest * kSplitShare * ranges > total * num_kv_heads * hg;
+}
+
+int64_t prefill_split_grid(int num_seqs, int num_kv_heads, int group, int max_query_len, int ranges) {
+  const SplitLayout l = split_layout(num_seqs, num_kv_heads, group, 256, max_query_len, ranges);
+  return l.units_cap * (group / prefill_heads_per_wg(group));
+}
+
+hipError_t launch_prefill_split(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
+                                int ranges, void* workspace, hipStream_t stream) {
+  if (num_seqs == 0) return hipSuccess;
+  const PrefillArgs a = kernel_args(args);
+  const int hc = prefill_heads_per_wg(a.group);
+  const SplitLayout l = split_layout(num_seqs, a.num_kv_heads, a.group, head_size, max_query_len, ranges);
+  char* base = static_cast<char*>(workspace);
+  PrefillSplit p{};
+  p.hdr = reinterpret_cast<int32_t*>(base);
+  p.units = reinterpret_cast<int4*>(base + l.units);
+  p.order = reinterpret_cast<int32_t*>(base + l.order);
+  p.cut_idx = reinterpret_cast<int32_t*>(base + l.cut_idx);
+  p.cut_seq = reinterpret_cast<int32_t*>(base + l.cut_seq);
+  p.pair_off = reinterpret_cast<int32_t*>(base + l.pair_off);
+  p.stats = reinterpret_cast<float*>(base + l.stats);
+  p.part = reinterpret_cast<float*>(base + l.part);
+  p.num_seqs = num_seqs;
+  p.max_query_len = max_query_len;
+  p.ranges = ranges;
+  p.tokens_per_wg = tokens_per_wg(hc, true);
+  p.units_cap = (int)l.units_cap;
+  p.cut_walk_cap = (int)l.cut_walk_cap;
+  p.cut_seq_cap = (int)l.cut_seq_cap;
+  p.slots_cap = (int)l.slots_cap;
+  void* kargs[] = {const_cast<PrefillArgs*>(&a), &p};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&split_plan_kernel), dim3(1),
+                                 dim3(kSplitPlanThreads), kargs, 0, stream);
+  if (e != hipSuccess) return e;
+  e = hipLaunchKernel(split_walk_fn(head_size, hc), dim3((unsigned)(l.units_cap * a.head_groups)),
+                      dim3(kWaves * kWave), kargs, 0, stream);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(split_merge_fn(head_size, hc),
+                         dim3((unsigned)(l.cut_walk_cap + num_seqs), (unsigned)(2 * kRowGroups * a.head_groups)),
+                         dim3(256), kargs, 0, stream);
+}
+
+hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
+                          hipStream_t stream) {
+  const PrefillArgs a = kernel_args(args);
+  const int hc = prefill_heads_per_wg(a.group);
   const bool solo = prefill_solo(head_size, a.group, a.num_kv_heads, max_query_len);
   const int tpw = prefill_tokens_per_wg(a.group, solo);
   const int tiles = (max_query_len + tpw - 1) / tpw;

@@ -59,6 +59,20 @@ int prefill_tokens_per_wg(int group, bool solo);
 hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
                           hipStream_t stream);
 
+// Split launch of the prefix attention (solo layout): the resident
+// workgroups of its walk kernel on the current device (N), the workspace it
+// needs, and the launch (plan, walks, merge).
+int prefill_split_ranges(int head_size, int group);
+size_t prefill_split_workspace_bytes(int num_seqs, int num_kv_heads, int group, int head_size, int max_query_len,
+                                     int ranges);
+// whether a split launch over these lengths cuts any walk (host arrays)
+bool prefill_split_cuts(const int32_t* context_lens, const int32_t* query_lens, int num_seqs, int num_kv_heads,
+                        int group, int ranges);
+// workgroups of the walk kernel (a bound on its units x head chunks)
+int64_t prefill_split_grid(int num_seqs, int num_kv_heads, int group, int max_query_len, int ranges);
+hipError_t launch_prefill_split(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
+                                int ranges, void* workspace, hipStream_t stream);
+
 hipError_t launch_write_kv(const WriteKvArgs& args, int num_seqs, int max_query_len, int elem_bytes, int layout,
                            hipStream_t stream);
 

@@ -104,6 +104,73 @@ int32_t paged_attention_prefill(float* out, const void* query, const void* key_c
                                 int32_t block_size, const pad_prefill_dims_t* dims, void* stream);
 
 /*
+ * Split launch of the same prefix attention, for batches whose walks differ
+ * in length.  It applies the first page's two-pass message (partitions of the
+ * keys accumulated in parallel, then combined by log-sum-exp rescaling) and
+ * its even-share note (about the same work for every workgroup) to the
+ * prefill walks.  A walk is the key range of one workgroup's rows: one
+ * sequence, one KV head's query heads (or a chunk of them), one tile of chunk
+ * tokens, in 32-key steps up to the tile's last position.  Every walk longer
+ * than C steps -- C = the launch's total steps over 4 N, N =
+ * paged_attention_prefill_split_ranges() -- is cut into ceil(steps / C)
+ * pieces of equal length, which are served first (longest sequence first);
+ * the whole walks follow.  No walk is cut when the longest is at most half
+ * of the total steps over N (see paged_attention_prefill_choose_split).  Pieces leave unnormalised rows in the workspace
+ * and a merge combines them.  Same operation, arguments and contract as
+ * paged_attention_prefill, except:
+ *   workspace        device memory of at least workspace_bytes bytes, 16-byte
+ *                    aligned; contents on entry do not matter (every byte read
+ *                    is written first by the same call); two calls in flight
+ *                    must not share it
+ *   workspace_bytes  >= paged_attention_prefill_split_workspace_size(dims,
+ *                    num_kv_heads, N), else PAD_ERR_WORKSPACE
+ * A sequence with n_s > max_query_len is out of contract here for any
+ * excess: its first max_query_len rows (inside the output) are NaN.  Results
+ * agree with paged_attention_prefill's to fp32 rounding (a cut walk's partial
+ * sums are added in another order), not bit for bit; walks that are not cut
+ * give the same bits.  PAD_ERR_UNSUPPORTED also for launches whose unit list
+ * would pass 2^31 workgroups.  Enqueues three kernels on `stream`.
+ */
+int32_t paged_attention_prefill_split(float* out, const void* query, const void* key_cache, const void* value_cache,
+                                      const int32_t* block_tables, const int32_t* query_start,
+                                      const int32_t* context_lens, float scale, int32_t num_kv_heads,
+                                      int32_t block_size, const pad_prefill_dims_t* dims, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
+ * N for paged_attention_prefill_split on the current HIP device: its compute
+ * units times the split walk kernel's resident workgroups per unit at this
+ * head size.  PAD_ERR_SHAPE or PAD_ERR_UNSUPPORTED (negative) for sizes the
+ * prefill attention rejects.
+ */
+int32_t paged_attention_prefill_split_ranges(int32_t head_size, int32_t num_heads, int32_t num_kv_heads);
+
+/*
+ * Which launch serves these lengths better: 1 for paged_attention_prefill_split
+ * (some walk is longer than half of a resident workgroup's fair share of the
+ * launch's steps, so the split cuts it), 0 for paged_attention_prefill (the
+ * split would cut nothing; the one-walk-per-workgroup launch then measured
+ * 1 to 3 % faster).  context_lens and query_lens are HOST arrays of
+ * num_seqs entries (>= 0); num_ranges is N of this device
+ * (paged_attention_prefill_split_ranges).  Negative status for bad sizes.
+ * Host-only; no HIP call.
+ */
+int32_t paged_attention_prefill_choose_split(const int32_t* context_lens, const int32_t* query_lens,
+                                             int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                             int32_t head_size, int32_t num_ranges);
+
+/*
+ * Workspace bytes of paged_attention_prefill_split for these sizes (num_seqs,
+ * num_heads, head_size and max_query_len of dims) and N = num_ranges: the
+ * unit list (whole walks and pieces: at most num_seqs x num_kv_heads x
+ * ceil(max_query_len / tokens per walk) + 8 N / head chunks), and partial
+ * slots of 256 rows x (head_size + 2) floats for at most 8 N pieces.
+ * (size_t)-1 for sizes out of range.  Host-only; no HIP call.
+ */
+size_t paged_attention_prefill_split_workspace_size(const pad_prefill_dims_t* dims, int32_t num_kv_heads,
+                                                    int32_t num_ranges);
+
+/*
  * Store the chunk's keys and values in the cache: row query_start[s] + i of
  * `key` / `value` goes to position context_lens[s] + i of sequence s, that
  * is to block block_tables[s, p / block_size], slot p % block_size, in the

@@ -298,6 +298,75 @@ def test_prefill_write_argument_errors(kw, status):
     assert write_call(**kw) == status
 
 
+def split_call(ws=FAKE, ws_bytes=1 << 30, d=None, ptrs=None):
+    p = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, t=FAKE, qs=FAKE, c=FAKE)
+    if ptrs:
+        p.update(ptrs)
+    return B.LIB.paged_attention_prefill_split(p["out"], p["q"], p["kc"], p["vc"], p["t"], p["qs"], p["c"], 0.1, 4,
+                                               16, ctypes.byref(d or pdims()), ws, ws_bytes, None)
+
+
+def test_prefill_split_argument_errors():
+    """Validation of the split launch, all before any HIP call: the prefill
+    checks, then the workspace pointer and its alignment."""
+    assert split_call(d=pdims(head_size=96)) == -4
+    assert split_call(d=pdims(dtype=0)) == -4
+    assert split_call(ptrs=dict(q=0)) == -1
+    assert split_call(ws=None) == -6
+    assert split_call(ws=FAKE + 8) == -7
+    assert split_call(ws=None, d=pdims(num_seqs=0)) == 0  # nothing to do: no workspace needed
+
+
+def walk_steps(ctx, n, tpw):
+    """32-key steps of every token tile's walk: the tile's last row sees
+    positions 0 .. ctx + min((t + 1) tpw, n) - 1."""
+    return [-(-(ctx + min((t + 1) * tpw, n)) // 32) for t in range(-(-n // tpw))]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefill_choose_split_rule(seed):
+    """The split is chosen exactly when the longest walk is more than half of
+    a resident workgroup's share of all walks' steps (every KV head and head
+    chunk walks the same steps)."""
+    rng = np.random.default_rng(seed)
+    S = int(rng.integers(1, 40))
+    ctx = rng.integers(0, 40000, S) * (rng.random(S) < 0.8)
+    qn = rng.integers(0, 3000, S)
+    H, Hkv, D, N = [(24, 4, 256, 256), (32, 8, 128, 256), (64, 8, 64, 512), (12, 12, 128, 256)][seed % 4]
+    G = H // Hkv
+    hc = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+    tpw = 256 // hc
+    steps = [st for c, n in zip(ctx, qn) for st in walk_steps(int(c), int(n), tpw)]
+    want = bool(steps) and max(steps) * 2 * N > sum(steps) * Hkv * (G // hc)
+    assert pad.paged_attention_prefill_choose_split(ctx, qn, H, Hkv, D, N) == want
+
+
+def test_prefill_choose_split_workloads():
+    """One chunk over a long prefix: its walks are short beside the total (no
+    cut, the plain launch); the ragged batch: its 33 000-key walks are cut."""
+    from decode_attention_paged_05_amd import inputs as gen
+
+    for name, want in (("prefill", False), ("prefill_batch", True)):
+        pp = gen.make_prefill_problem(name)
+        s = pp.spec
+        assert pad.paged_attention_prefill_choose_split(pp.context_lens, pp.query_lens, s.num_heads, s.num_kv_heads,
+                                                        s.head_size, 256) == want, name
+    with pytest.raises(pad.PadError):
+        pad.paged_attention_prefill_choose_split([5, -1], [3, 3], 24, 4, 256, 256)
+
+
+def test_prefill_split_workspace_size():
+    size = pad.paged_attention_prefill_split_workspace_size
+    base = size(4, 24, 4, 256, 3000, 256)
+    assert base > 0
+    assert size(8, 24, 4, 256, 3000, 256) > base  # more sequences: more whole walks listed
+    assert size(4, 24, 4, 128, 3000, 256) < base  # smaller partial slots
+    # partial slots: 8 N pieces of 256 rows x D floats bound the size from below
+    assert base >= 8 * 256 * 256 * 256 * 4
+    with pytest.raises(pad.PadError):
+        size(4, 24, 5, 256, 3000, 256)
+
+
 def test_prefill_empty_is_a_noop():
     assert B.LIB.paged_attention_prefill(None, None, None, None, None, None, None, 1.0, 4, 16,
                                          ctypes.byref(pdims(num_seqs=0)), None) == 0

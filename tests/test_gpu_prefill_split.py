@@ -1,0 +1,174 @@
+"""The balanced split of the prefix attention on the GPU, against the oracle.
+
+Every call goes through the C ABI (``paged_attention_prefill_split``): the
+launch's walks are cut into equal ranges, cut walks leave pieces in the
+workspace and a merge combines them.  The cases make the cuts fall everywhere:
+walks cut into many pieces (more ranges than steps, so empty ranges too),
+boundaries on walk starts, sequences without steps, and the two prefill
+workloads the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_paged_05_amd as pad
+from decode_attention_paged_05_amd import inputs as gen
+from tests.gpu_util import TOL
+from tests.test_gpu_prefill import (PREFILL_SHAPES, DevicePrefill, _every_64th_and_edges, _edge_rows,
+                                    _sampled_check, max_err)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_split(dp: DevicePrefill, ws=None, out=None, tables=None, mql=None, scale=None):
+    pp = dp.pp
+    spec = pp.spec
+    if ws is None:
+        ws = pad.alloc_prefill_split_workspace(pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size,
+                                               pp.max_query_len if mql is None else mql)
+    if out is None:
+        out = torch.full(tuple(pp.query.shape), float("nan"), dtype=torch.float32, device="cuda")
+    pad.paged_attention_prefill_split(out, dp.query, dp.dp.kc, dp.dp.vc, dp.dp.tables if tables is None else tables,
+                                      dp.qs, dp.ctx, pp.scale if scale is None else scale, spec.num_kv_heads, 16,
+                                      pp.max_query_len if mql is None else mql, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_split_small_ragged():
+    dp = DevicePrefill(gen.make_prefill_problem("prefill_small"))
+    assert max_err(run_split(dp), dp.oracle()) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("H,Hkv,D,ctx,qn", PREFILL_SHAPES, ids=lambda v: str(v))
+def test_split_shapes(H, Hkv, D, ctx, qn):
+    """Every head grouping and head size; the split agrees with the oracle and
+    with the one-walk-per-workgroup launch."""
+    spec = gen.PrefillSpec("shape", context_lens=ctx, query_lens=qn, num_heads=H, num_kv_heads=Hkv, head_size=D,
+                           dtype="bf16", seed=hash((H, Hkv, D, ctx, qn)) % 1000)
+    dp = DevicePrefill(gen.make_prefill_problem(spec))
+    got = run_split(dp)
+    assert max_err(got, dp.oracle()) <= TOL["bf16"]
+    assert float((got - dp.run()).abs().max()) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("ctx,qn", [((5000,), (40,)), ((0, 3000, 0), (1, 17, 2)), ((70000,), (300,))],
+                         ids=["one-walk", "tiny-walks", "long"])
+def test_split_cuts_walks_into_many_pieces(ctx, qn):
+    """Few, long walks against hundreds of ranges: each walk is cut into many
+    pieces (ranges of one or two steps, some empty), all merged."""
+    spec = gen.PrefillSpec("cuts", context_lens=ctx, query_lens=qn, num_heads=4, num_kv_heads=1, head_size=64,
+                           dtype="bf16", seed=sum(ctx) % 997)
+    dp = DevicePrefill(gen.make_prefill_problem(spec))
+    assert max_err(run_split(dp), dp.oracle()) <= TOL["bf16"]
+
+
+def test_split_sequences_without_work():
+    """Empty chunks around the ones with work: their (no) rows, and the others exact."""
+    spec = gen.PrefillSpec("empty", context_lens=(100, 0, 5000, 7, 0), query_lens=(0, 0, 129, 0, 33), num_heads=8,
+                           num_kv_heads=2, head_size=128, dtype="bf16", seed=51)
+    dp = DevicePrefill(gen.make_prefill_problem(spec))
+    assert max_err(run_split(dp), dp.oracle()) <= TOL["bf16"]
+
+
+def test_split_workspace_contents_do_not_matter():
+    """Every workspace byte the call reads it writes first: NaN-filled and
+    random workspaces, and a second call on the same one, give the same bits."""
+    dp = DevicePrefill(gen.make_prefill_problem(gen.PrefillSpec(
+        "ws", context_lens=(3000, 10, 700), query_lens=(100, 300, 64), num_heads=24, num_kv_heads=4, head_size=256,
+        dtype="bf16", seed=52)))
+    spec = dp.pp.spec
+    ws = pad.alloc_prefill_split_workspace(dp.pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size,
+                                           dp.pp.max_query_len)
+    ws.view(torch.uint8).fill_(0xFF)  # NaN floats, all-ones counters and offsets
+    a = run_split(dp, ws=ws)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda"))
+    b = run_split(dp, ws=ws)
+    c = run_split(dp, ws=ws)
+    assert torch.equal(a, b) and torch.equal(b, c)
+    assert max_err(a, dp.oracle()) <= TOL["bf16"]
+
+
+def test_split_ragged_batch_sampled():
+    """The 4-sequence batch workload the benchmark times, same launch."""
+    pp = gen.make_prefill_problem("prefill_batch")
+    dp = DevicePrefill(pp, keep_host=False)
+    got = run_split(dp)
+    assert bool(torch.isfinite(got).all())
+    assert _sampled_check(pp, got, _every_64th_and_edges, heads=(0, 5, 7, 12, 17, 23)) <= TOL["bf16"]
+
+
+def test_split_full_size_sampled():
+    """8192 new tokens over a 32768-token prefix: every 64th chunk token and the
+    tile edges of all 24 heads against the oracle."""
+    pp = gen.make_prefill_problem("prefill")
+    dp = DevicePrefill(pp, keep_host=False)
+    got = run_split(dp)
+    assert bool(torch.isfinite(got).all())
+    assert _sampled_check(pp, got, _every_64th_and_edges, heads=range(pp.spec.num_heads)) <= TOL["bf16"]
+
+
+def test_split_out_of_contract_sequences():
+    """A block id outside the pool makes that sequence's rows NaN (through the
+    merge when its walks are cut); a chunk longer than max_query_len gets its
+    first max_query_len rows NaN and the rest untouched; others exact."""
+    pp = gen.make_prefill_problem("prefill_small")  # chunks (50, 1, 77, 128, 0)
+    dp = DevicePrefill(pp)
+    want = dp.oracle()
+    tables = dp.dp.tables.clone()
+    tables[0, 1] = pp.pool.num_blocks + 5
+    got = run_split(dp, tables=tables)
+    lo, hi = int(pp.query_start[0]), int(pp.query_start[1])
+    assert bool(torch.isnan(got[lo:hi]).all())
+    keep = np.r_[hi:pp.num_tokens]
+    assert np.max(np.abs(got[keep].double().cpu().numpy() - want[keep])) <= TOL["bf16"]
+    mq = 64
+    out = torch.full(tuple(pp.query.shape), 7.0, dtype=torch.float32, device="cuda")
+    run_split(dp, out=out, mql=mq)
+    o = out.cpu()
+    for s in (2, 3):  # 77 and 128 tokens
+        lo, hi = int(pp.query_start[s]), int(pp.query_start[s + 1])
+        assert bool(torch.isnan(o[lo:lo + mq]).all()), s
+        assert bool((o[lo + mq:hi] == 7.0).all()), s
+    keep = np.r_[0:int(pp.query_start[2])]
+    assert np.max(np.abs(o[keep].double().numpy() - want[keep])) <= TOL["bf16"]
+
+
+def test_split_rejects_a_small_workspace():
+    dp = DevicePrefill(gen.make_prefill_problem("prefill_small"), keep_host=False)
+    spec = dp.pp.spec
+    need = pad.paged_attention_prefill_split_workspace_size(
+        dp.pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size, dp.pp.max_query_len,
+        pad.paged_attention_prefill_split_ranges(spec.head_size, spec.num_heads, spec.num_kv_heads))
+    with pytest.raises(pad.PadError):
+        run_split(dp, ws=torch.empty(need - 256, dtype=torch.uint8, device="cuda"))
+
+
+def test_split_graph_capture_replays():
+    """The three kernels captured in a HIP graph: every replay, with eager work
+    in between, equals the eager result bitwise."""
+    dp = DevicePrefill(gen.make_prefill_problem("prefill_small"))
+    pp, spec = dp.pp, dp.pp.spec
+    ws = pad.alloc_prefill_split_workspace(pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size,
+                                           pp.max_query_len)
+    eager = run_split(dp, ws=ws)
+    out = torch.empty_like(eager)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+
+    def step():
+        pad.paged_attention_prefill_split(out, dp.query, dp.dp.kc, dp.dp.vc, dp.dp.tables, dp.qs, dp.ctx, pp.scale,
+                                          spec.num_kv_heads, 16, pp.max_query_len, ws)
+
+    with torch.cuda.stream(stream):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+    for r in range(4):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r}"
+        assert torch.equal(run_split(dp, ws=ws), eager)
