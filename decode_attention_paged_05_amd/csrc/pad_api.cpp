@@ -369,10 +369,9 @@ int32_t paged_attention_prefill_split(float* out, const void* query, const void*
     return PAD_ERR_ALIGN;
   const int group = dims->num_heads / num_kv_heads;
   const int ranges = pad::prefill_split_ranges(dims->head_size, group);
-  // the walk kernel's grid is 32-bit, the merge's second dimension 16-bit
+  // the walk kernel's grid is 32-bit
   const int hg = group / pad::prefill_heads_per_wg(group);
-  if (pad::prefill_split_grid(dims->num_seqs, num_kv_heads, group, dims->max_query_len, ranges) > INT32_MAX ||
-      hg * 8 > 65535)
+  if (pad::prefill_split_grid(dims->num_seqs, num_kv_heads, group, dims->max_query_len, ranges) > INT32_MAX)
     return PAD_ERR_UNSUPPORTED;
   // the plan's 64-bit step count: S x KV heads x head groups x tiles x steps per tile
   const int tpw = pad::prefill_tokens_per_wg(group, true);

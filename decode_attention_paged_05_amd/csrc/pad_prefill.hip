@@ -748,7 +748,6 @@ struct PrefillSplit {
   int ranges;          // N, resident workgroups of the walk kernel
   int tokens_per_wg;   // TPW, a multiple of 32
   int units_cap;
-  int cut_walk_cap;    // bound on cut walks: the merge grid
   int cut_seq_cap;
   int slots_cap;
 };
@@ -757,6 +756,14 @@ struct PrefillSplit {
 __host__ __device__ inline int64_t tile_steps(int64_t t, int64_t ctx, int64_t n, int64_t tpw) {
   const int64_t e = (t + 1) * tpw;
   return (ctx + (e < n ? e : n) + 31) / 32;
+}
+
+// Steps of all of a sequence's walks (one head group): the tiles before the
+// last are full, and tile t of them takes ceil(ctx / 32) + (t + 1) TPW / 32.
+__host__ __device__ inline int64_t seq_walk_steps(int64_t ctx, int64_t n, int64_t tpw) {
+  if (n <= 0) return 0;
+  const int64_t T = (n + tpw - 1) / tpw;
+  return (T - 1) * ((ctx + 31) / 32) + (tpw / 32) * ((T - 1) * T / 2) + tile_steps(T - 1, ctx, n, tpw);
 }
 
 // Tiles (of T) whose walks take more than thr steps: the longest ones, since
@@ -803,29 +810,49 @@ __device__ inline int plan_scan(int v, int* wave_sum, int* total) {
   return before + x - v;
 }
 
-// One workgroup: the unit list.
+// One workgroup: the unit list.  Up to kSplitPlanThreads sequences, their
+// sizes, order and cut list live in LDS.
 __global__ __launch_bounds__(kSplitPlanThreads) void split_plan_kernel(PrefillArgs a, PrefillSplit p) {
   __shared__ int wave_sum[kSplitPlanThreads / kWave];
   __shared__ unsigned long long total_steps;
   __shared__ int max_steps;
   __shared__ int64_t rank_key[kSplitPlanThreads];
+  __shared__ int c_ctx[kSplitPlanThreads], c_n[kSplitPlanThreads];
+  __shared__ int c_order[kSplitPlanThreads], c_cut[kSplitPlanThreads];
   const int tid = threadIdx.x;
   const int S = p.num_seqs, Hkv = a.num_kv_heads, HG = a.head_groups;
   const int64_t tpw = p.tokens_per_wg;
+  const bool cached = S <= kSplitPlanThreads;
+  int* const order = cached ? c_order : p.order;
+  int* const cut_seq = cached ? c_cut : p.cut_seq;
+  // context and chunk length of sequence s; chunk 0 for one out of contract
+  auto seq = [&](int s, int* ctx, int* n) {
+    if (cached) {
+      *ctx = c_ctx[s];
+      *n = c_n[s];
+    } else {
+      int q_lo;
+      if (!split_seq_ok(a, p, s, &q_lo, n, ctx)) *n = 0;
+    }
+  };
   if (tid == 0) {
     total_steps = 0;
     max_steps = 0;
   }
+  if (cached && tid < S) {
+    int q_lo, n, ctx;
+    const bool ok = split_seq_ok(a, p, tid, &q_lo, &n, &ctx);
+    c_ctx[tid] = ctx;
+    c_n[tid] = ok ? n : 0;
+  }
   __syncthreads();
   // (1) total steps (all head groups) and the longest walk
   for (int s = tid; s < S; s += kSplitPlanThreads) {
-    int q_lo, n, ctx;
-    if (!split_seq_ok(a, p, s, &q_lo, &n, &ctx) || n == 0) continue;
-    const int T = (int)((n + tpw - 1) / tpw);
-    unsigned long long steps = 0;  // sum over the tiles
-    for (int t = 0; t < T; ++t) steps += (unsigned long long)tile_steps(t, ctx, n, tpw);
-    atomicAdd(&total_steps, steps * (unsigned long long)(Hkv * HG));
-    atomicMax(&max_steps, (int)tile_steps(T - 1, ctx, n, tpw));
+    int n, ctx;
+    seq(s, &ctx, &n);
+    if (n == 0) continue;
+    atomicAdd(&total_steps, (unsigned long long)seq_walk_steps(ctx, n, tpw) * (unsigned long long)(Hkv * HG));
+    atomicMax(&max_steps, (int)tile_steps((n + tpw - 1) / tpw - 1, ctx, n, tpw));
   }
   __syncthreads();
   const int64_t B = (int64_t)total_steps;
@@ -838,37 +865,35 @@ __global__ __launch_bounds__(kSplitPlanThreads) void split_plan_kernel(PrefillAr
   // (2) serving order: longest walk (context + chunk) first; sequences out of
   // contract or without tokens last.  Past kSplitPlanThreads sequences, the
   // given order.
-  if (S <= kSplitPlanThreads) {
-    if (tid < S) {
-      int q_lo, n, ctx;
-      rank_key[tid] = split_seq_ok(a, p, tid, &q_lo, &n, &ctx) && n > 0 ? (int64_t)ctx + n : -1;
-    }
+  if (cached) {
+    if (tid < S) rank_key[tid] = c_n[tid] > 0 ? (int64_t)c_ctx[tid] + c_n[tid] : -1;
     __syncthreads();
     if (tid < S) {
       const int64_t k = rank_key[tid];
       int r = 0;
       for (int j = 0; j < S; ++j) r += (rank_key[j] > k) || (rank_key[j] == k && j < tid);
-      p.order[r] = tid;
+      order[r] = tid;
     }
   } else {
-    for (int s = tid; s < S; s += kSplitPlanThreads) p.order[s] = s;
+    for (int s = tid; s < S; s += kSplitPlanThreads) order[s] = s;
   }
-  __syncthreads();  // order is read back below (global writes of this workgroup)
+  __syncthreads();  // order is read back below
   // (3) the sequences with cut walks, in serving order
   int n_cut = 0;
   for (int base = 0; base < S; base += kSplitPlanThreads) {
     const int r = base + tid;
     int cut = 0, s = -1;
     if (r < S) {
-      s = p.order[r];
-      int q_lo, n, ctx;
-      cut = split_seq_ok(a, p, s, &q_lo, &n, &ctx) && n > 0 && tile_steps((n + tpw - 1) / tpw - 1, ctx, n, tpw) > C;
+      s = order[r];
+      int n, ctx;
+      seq(s, &ctx, &n);
+      cut = n > 0 && tile_steps((n + tpw - 1) / tpw - 1, ctx, n, tpw) > C;
     }
     int tot;
     const int o = n_cut + plan_scan(cut, wave_sum, &tot);
     if (r < S) {
       p.cut_idx[s] = cut ? o : -1;
-      if (cut) p.cut_seq[o] = s;
+      if (cut) cut_seq[o] = s;
     }
     n_cut += tot;
   }
@@ -879,12 +904,12 @@ __global__ __launch_bounds__(kSplitPlanThreads) void split_plan_kernel(PrefillAr
   int n_pieces = 0, n_first = 0;
   for (int base = 0; base < pairs; base += kSplitPlanThreads) {
     const int q = base + tid;
-    int cnt = 0, s = 0, j = 0, c = 0, ctx = 0, n = 0, q_lo = 0, T = 0;
+    int cnt = 0, s = 0, j = 0, c = 0, ctx = 0, n = 0, T = 0;
     if (q < pairs) {
       j = q / n_cut;
       c = q - j * n_cut;
-      s = p.cut_seq[c];
-      split_seq_ok(a, p, s, &q_lo, &n, &ctx);
+      s = cut_seq[c];
+      seq(s, &ctx, &n);
       T = (int)((n + tpw - 1) / tpw);
       cnt = Hkv * tiles_above((j > 0 ? j : 1) * C, ctx, n, tpw, T);
     }
@@ -908,9 +933,10 @@ __global__ __launch_bounds__(kSplitPlanThreads) void split_plan_kernel(PrefillAr
     const int r = base + tid;
     int cnt = 0, s = 0, T = 0, above = 0;
     if (r < S) {
-      s = p.order[r];
-      int q_lo, n, ctx;
-      if (split_seq_ok(a, p, s, &q_lo, &n, &ctx) && n > 0) {
+      s = order[r];
+      int n, ctx;
+      seq(s, &ctx, &n);
+      if (n > 0) {
         T = (int)((n + tpw - 1) / tpw);
         above = tiles_above(C, ctx, n, tpw, T);
         cnt = Hkv * (T - above);
@@ -925,7 +951,7 @@ __global__ __launch_bounds__(kSplitPlanThreads) void split_plan_kernel(PrefillAr
     p.hdr[kHdrUnits] = n_pieces + placed;
     p.hdr[kHdrPieces] = n_pieces;
     p.hdr[kHdrCutWalks] = n_first;
-    p.hdr[kHdrStep] = (int)C;
+    p.hdr[kHdrStep] = (int)min(C, (int64_t)INT_MAX);
     p.hdr[kHdrMaxPieces] = kmax;
     p.hdr[kHdrCutSeqs] = n_cut;
   }
@@ -970,32 +996,21 @@ __global__ __launch_bounds__(kWaves * kWave) void split_walk_kernel(PrefillArgs 
   walk_rows<D, HC, true>(a, s, g * a.head_groups + hp, t, q_lo, n, ctx, lo, hi, false, dst, lds);
 }
 
-// Workgroup (x, 8 hp + rg): x < cut_walk_cap: the cut walk x (the unit of its
-// first piece), head chunk hp, row group rg (32 rows over all of D): combine
-// its pieces.  x >= cut_walk_cap: NaN rows of sequence x - cut_walk_cap if it
-// is out of contract (its first min(n, max_query_len) chunk rows inside the
-// output).
+// Merge grid: (8 HG, kMergeWalkRows + kMergeSeqRows).  Workgroup (8 hp + rg,
+// y < kMergeWalkRows) combines, for head chunk hp and row group rg (32 rows
+// over all of D), the pieces of cut walks y, y + kMergeWalkRows, ... (walk w
+// = the unit of its first piece); the HG x 8 workgroups of one walk are
+// adjacent in the dispatch order.  Rows y >= kMergeWalkRows write the NaN rows
+// of sequences out of contract (their first min(n, max_query_len) chunk rows
+// inside the output).
+constexpr int kMergeWalkRows = 128;
+constexpr int kMergeSeqRows = 16;
+
 template <int D, int HC>
-__global__ __launch_bounds__(256) void split_merge_kernel(PrefillArgs a, PrefillSplit p) {
+__device__ inline void merge_walk(const PrefillArgs& a, const PrefillSplit& p, int x, int hp, int rg) {
   constexpr int DT = D / 16;
   constexpr int TPW = kSplitRows / HC;
   const int tid = threadIdx.x;
-  const int x = blockIdx.x;
-  const int hp = blockIdx.y / (2 * kRowGroups), rg = blockIdx.y % (2 * kRowGroups);
-  if (x >= p.cut_walk_cap) {
-    const int s = x - p.cut_walk_cap;
-    int q_lo, n, ctx;
-    if (split_seq_ok(a, p, s, &q_lo, &n, &ctx)) return;
-    const int64_t rows = n < 0 ? 0 : (n < p.max_query_len ? n : p.max_query_len);
-    const int64_t per_row = (int64_t)a.num_heads * (D / 4);
-    for (int64_t f = (int64_t)blockIdx.y * 256 + tid; f < rows * per_row; f += 256 * (int64_t)gridDim.y) {
-      const int64_t row = (int64_t)q_lo + f / per_row;
-      if (row < 0 || row >= a.num_tokens) continue;
-      *reinterpret_cast<f32x4_t*>(a.out + row * a.num_heads * D + (f % per_row) * 4) = f32x4_t{NAN, NAN, NAN, NAN};
-    }
-    return;
-  }
-  if (x >= p.hdr[kHdrCutWalks]) return;
   const int4 u = p.units[x];  // piece 0 of the walk
   const int s = u.x, t = u.y, g = u.z, k = u.w & 0xffff;
   const int q_lo = a.query_start[s];
@@ -1008,25 +1023,50 @@ __global__ __launch_bounds__(256) void split_merge_kernel(PrefillArgs a, Prefill
   auto slot_of = [&](int j) {
     return (size_t)(p.pair_off[j * p.cut_seq_cap + c] + within) * a.head_groups + hp;
   };
-  float M = -INFINITY;
-  for (int j = 0; j < k; ++j) M = fmaxf(M, p.stats[slot_of(j) * kSplitStatFloats + stat_off]);
-  float l = 0.0f;
+  // Pieces four at a time, every load of a group in flight together, with a
+  // running max: the sums are rescaled when a group raises it.  A group's
+  // places past the last piece repeat the last piece with weight 0.
+  float M = -INFINITY, l = 0.0f;
   f32x4_t acc[D / 32];
 #pragma unroll
   for (int q = 0; q < D / 32; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = 0; j < k; ++j) {
-    const size_t slot = slot_of(j);
-    const float* st = p.stats + slot * kSplitStatFloats + stat_off;
-    // a piece without keys for this row (max kNoKeysMax) weighs exp2(-1e30 -
-    // M) = 0 beside one with keys; a NaN sum propagates
-    const float wgt = __builtin_amdgcn_exp2f(st[0] - M);
-    l += wgt * st[1];
-    const float* po = p.part + slot * ((size_t)kSplitRows * D) + (size_t)rg * (2 * DT * kWave * 4);
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    size_t sl[4];
+    float mj[4], lj[4];
+    f32x4_t oj[4][D / 32];
 #pragma unroll
-    for (int q = 0; q < D / 32; ++q) {
-      const int d4 = qg + 8 * q;  // 4-dim quad: dims 4 d4 .. = 16 (d4 >> 2) + 4 (d4 & 3) + e
-      const int lane = (d4 & 3) * 16 + l16;
-      acc[q] += wgt * *reinterpret_cast<const f32x4_t*>(po + (((size_t)ct * DT + (d4 >> 2)) * kWave + lane) * 4);
+    for (int e = 0; e < 4; ++e) sl[e] = slot_of(min(j0 + e, k - 1));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float* st = p.stats + sl[e] * kSplitStatFloats + stat_off;
+      mj[e] = st[0];
+      lj[e] = st[1];
+      const float* po = p.part + sl[e] * ((size_t)kSplitRows * D) + (size_t)rg * (2 * DT * kWave * 4);
+#pragma unroll
+      for (int q = 0; q < D / 32; ++q) {
+        const int d4 = qg + 8 * q;  // 4-dim quad: dims 4 d4 .. = 16 (d4 >> 2) + 4 (d4 & 3) + e
+        const int lane = (d4 & 3) * 16 + l16;
+        oj[e][q] = *reinterpret_cast<const f32x4_t*>(po + (((size_t)ct * DT + (d4 >> 2)) * kWave + lane) * 4);
+      }
+    }
+    float m4 = mj[0];
+#pragma unroll
+    for (int e = 1; e < 4; ++e) m4 = fmaxf(m4, mj[e]);
+    if (m4 > M) {
+      const float r = __builtin_amdgcn_exp2f(M - m4);  // 0 for the first group
+      l *= r;
+#pragma unroll
+      for (int q = 0; q < D / 32; ++q) acc[q] *= r;
+      M = m4;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // a piece without keys for this row (max kNoKeysMax) weighs exp2(-1e30 -
+      // M) = 0 beside one with keys; a NaN sum propagates
+      const float w = j0 + e < k ? __builtin_amdgcn_exp2f(mj[e] - M) : 0.0f;
+      l += w * lj[e];
+#pragma unroll
+      for (int q = 0; q < D / 32; ++q) acc[q] += w * oj[e][q];
     }
   }
   const int tok = t * TPW + (rg / HC) * kRowsPerWave + 16 * ct + l16;
@@ -1037,6 +1077,27 @@ __global__ __launch_bounds__(256) void split_merge_kernel(PrefillArgs a, Prefill
   const float inv = 1.0f / l;
 #pragma unroll
   for (int q = 0; q < D / 32; ++q) *reinterpret_cast<f32x4_t*>(dst + 4 * (qg + 8 * q)) = acc[q] * inv;
+}
+
+template <int D, int HC>
+__global__ __launch_bounds__(256) void split_merge_kernel(PrefillArgs a, PrefillSplit p) {
+  const int hp = blockIdx.x / (2 * kRowGroups), rg = blockIdx.x % (2 * kRowGroups);
+  if ((int)blockIdx.y < kMergeWalkRows) {
+    const int walks = p.hdr[kHdrCutWalks];
+    for (int x = blockIdx.y; x < walks; x += kMergeWalkRows) merge_walk<D, HC>(a, p, x, hp, rg);
+    return;
+  }
+  const int64_t per_row = (int64_t)a.num_heads * (D / 4);
+  for (int s = blockIdx.y - kMergeWalkRows; s < p.num_seqs; s += gridDim.y - kMergeWalkRows) {
+    int q_lo, n, ctx;
+    if (split_seq_ok(a, p, s, &q_lo, &n, &ctx)) continue;
+    const int64_t rows = n < 0 ? 0 : (n < p.max_query_len ? n : p.max_query_len);
+    for (int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x; f < rows * per_row; f += 256 * (int64_t)gridDim.x) {
+      const int64_t row = (int64_t)q_lo + f / per_row;
+      if (row < 0 || row >= a.num_tokens) continue;
+      *reinterpret_cast<f32x4_t*>(a.out + row * a.num_heads * D + (f % per_row) * 4) = f32x4_t{NAN, NAN, NAN, NAN};
+    }
+  }
 }
 
 
@@ -1187,7 +1248,7 @@ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // walk's k = ceil(steps / C) pieces number under 2 steps / C, so fewer than
 // 2 rounds / HG pieces; whole walks are at most S x Hkv x ceil(max_query_len / TPW).
 struct SplitLayout {
-  int64_t units_cap, cut_walk_cap, cut_seq_cap, slots_cap;
+  int64_t units_cap, cut_seq_cap, slots_cap;
   size_t units, order, cut_idx, cut_seq, pair_off, stats, part, bytes;
 };
 SplitLayout split_layout(int num_seqs, int num_kv_heads, int group, int head_size, int max_query_len, int ranges) {
@@ -1196,7 +1257,6 @@ SplitLayout split_layout(int num_seqs, int num_kv_heads, int group, int head_siz
   const int64_t rounds = (int64_t)kSplitRounds * ranges;
   SplitLayout l;
   l.units_cap = (int64_t)num_seqs * num_kv_heads * ((max_query_len + tpw - 1) / tpw) + 2 * rounds / hg + 2;
-  l.cut_walk_cap = rounds / hg + 1;
   l.cut_seq_cap = std::min<int64_t>(num_seqs, rounds / (hg * num_kv_heads) + 1);
   l.slots_cap = (2 * rounds / hg + 2) * hg;
   l.units = 256;  // the header
@@ -1236,9 +1296,8 @@ bool prefill_split_cuts(const int32_t* context_lens, const int32_t* query_lens, 
   for (int s = 0; s < num_seqs; ++s) {
     const int64_t ctx = context_lens[s], n = query_lens[s];
     if (n <= 0) continue;
-    const int64_t T = (n + tpw - 1) / tpw;
-    for (int64_t t = 0; t < T; ++t) total += tile_steps(t, ctx, n, tpw);
-    longest = std::max(longest, tile_steps(T - 1, ctx, n, tpw));
+    total += seq_walk_steps(ctx, n, tpw);
+    longest = std::max(longest, tile_steps((n + tpw - 1) / tpw - 1, ctx, n, tpw));
   }
   // the plan kernel's rule
   return longest * kSplitShare * ranges > total * num_kv_heads * hg;
@@ -1270,7 +1329,6 @@ hipError_t launch_prefill_split(const PrefillArgs& args, int num_seqs, int max_q
   p.ranges = ranges;
   p.tokens_per_wg = tokens_per_wg(hc, true);
   p.units_cap = (int)l.units_cap;
-  p.cut_walk_cap = (int)l.cut_walk_cap;
   p.cut_seq_cap = (int)l.cut_seq_cap;
   p.slots_cap = (int)l.slots_cap;
   void* kargs[] = {const_cast<PrefillArgs*>(&a), &p};
@@ -1280,9 +1338,10 @@ hipError_t launch_prefill_split(const PrefillArgs& args, int num_seqs, int max_q
   e = hipLaunchKernel(split_walk_fn(head_size, hc), dim3((unsigned)(l.units_cap * a.head_groups)),
                       dim3(kWaves * kWave), kargs, 0, stream);
   if (e != hipSuccess) return e;
+  const unsigned seq_rows = (unsigned)std::min(num_seqs, kMergeSeqRows);
   return hipLaunchKernel(split_merge_fn(head_size, hc),
-                         dim3((unsigned)(l.cut_walk_cap + num_seqs), (unsigned)(2 * kRowGroups * a.head_groups)),
-                         dim3(256), kargs, 0, stream);
+                         dim3((unsigned)(2 * kRowGroups * a.head_groups), kMergeWalkRows + seq_rows), dim3(256),
+                         kargs, 0, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
