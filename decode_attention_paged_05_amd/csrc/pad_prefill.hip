@@ -56,6 +56,11 @@
 // need it (the diagonal, the end of the walk), in separate code.  Workgroups
 // are ordered so that those sharing K/V tiles share an XCD's L2
 // (remap_workgroup).
+//
+// Two launches run this walk (walk_rows): prefill_kernel, one workgroup per
+// walk; and the split launch (split_plan_kernel, split_walk_kernel,
+// split_merge_kernel), which cuts walks much longer than the launch's
+// average into pieces that run first and are combined by their log-sum-exp.
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <algorithm>

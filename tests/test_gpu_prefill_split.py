@@ -172,3 +172,32 @@ def test_split_graph_capture_replays():
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {r}"
         assert torch.equal(run_split(dp, ws=ws), eager)
+
+
+def test_split_more_sequences_than_the_plan_caches():
+    """1 100 sequences: past the plan's 1 024 sequences in LDS, its tables live
+    in the workspace and the sequences keep their given order."""
+    rng = np.random.default_rng(61)
+    S = 1100
+    ctx = tuple(int(v) for v in rng.integers(0, 300, S))
+    qn = tuple(int(v) for v in rng.integers(0, 9, S))
+    spec = gen.PrefillSpec("many", context_lens=ctx, query_lens=qn, num_heads=8, num_kv_heads=2, head_size=128,
+                           dtype="bf16", seed=61)
+    dp = DevicePrefill(gen.make_prefill_problem(spec))
+    assert max_err(run_split(dp), dp.oracle()) <= TOL["bf16"]
+
+
+def test_split_many_cut_sequences():
+    """400 sequences whose one walk each is cut: more (piece index, sequence)
+    pairs than the plan's 1 024 threads, so its pair loop takes several rounds."""
+    rng = np.random.default_rng(62)
+    S = 400
+    ctx = tuple(int(v) for v in rng.integers(1900, 2100, S))
+    qn = tuple(int(v) for v in rng.integers(1, 4, S))
+    spec = gen.PrefillSpec("cutmany", context_lens=ctx, query_lens=qn, num_heads=4, num_kv_heads=1, head_size=64,
+                           dtype="bf16", seed=62)
+    pp = gen.make_prefill_problem(spec)
+    n_ranges = pad.paged_attention_prefill_split_ranges(64, 4, 1)
+    assert pad.paged_attention_prefill_choose_split(pp.context_lens, pp.query_lens, 4, 1, 64, n_ranges)
+    dp = DevicePrefill(pp)
+    assert max_err(run_split(dp), dp.oracle()) <= TOL["bf16"]
