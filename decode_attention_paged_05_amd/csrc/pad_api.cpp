@@ -348,7 +348,7 @@ int32_t paged_attention_prefill_choose_split(const int32_t* context_lens, const 
   if (!context_lens || !query_lens) return PAD_ERR_NULL;
   for (int s = 0; s < num_seqs; ++s)
     if (context_lens[s] < 0 || query_lens[s] < 0) return PAD_ERR_SHAPE;
-  return pad::prefill_split_cuts(context_lens, query_lens, num_seqs, num_kv_heads, num_heads / num_kv_heads,
+  return pad::prefill_split_pays(context_lens, query_lens, num_seqs, num_kv_heads, num_heads / num_kv_heads,
                                  num_ranges) ? 1 : 0;
 }
 

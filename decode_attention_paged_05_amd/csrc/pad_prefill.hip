@@ -64,6 +64,7 @@
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <algorithm>
+#include <atomic>
 #include <math.h>
 #include <stdint.h>
 
@@ -193,7 +194,7 @@ __device__ inline void remap_workgroup(int HG, int* bx, int* by, int* bz) {
   }
   const int N = NX * NY * NZ;
   const int M = N / (8 * HG) * (8 * HG);
-  int U, hp;  // unit = (token tile, KV head, sequence); head group within it
+  int U, hp;  // unit = (KV head, token tile, sequence), KV head fastest; head group within it
   if (L < M) {
     U = (k / HG) * 8 + c;
     hp = k % HG;
@@ -201,9 +202,9 @@ __device__ inline void remap_workgroup(int HG, int* bx, int* by, int* bz) {
     U = M / HG + (L - M) / HG;
     hp = (L - M) % HG;
   }
-  *bx = U % NX;
-  *by = ((U / NX) % NG) * HG + hp;
-  *bz = U / NX / NG;
+  *by = (U % NG) * HG + hp;
+  *bx = (U / NG) % NX;
+  *bz = U / NG / NX;
 }
 
 // Sequence order of a batch.  The dispatcher starts workgroups in linear-id
@@ -1278,12 +1279,24 @@ SplitLayout split_layout(int num_seqs, int num_kv_heads, int group, int head_siz
 }  // namespace
 
 int prefill_split_ranges(int head_size, int group) {
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_walk_fn(head_size, prefill_heads_per_wg(group)),
-                                                   kWaves * kWave, 0) != hipSuccess ||
-      per_cu < 1) {
-    (void)hipGetLastError();  // our own failed query: do not leave it behind
-    per_cu = 1;
+  // resident walk workgroups per CU, per device, head size and head chunk
+  // (queried once: the occupancy query costs microseconds of host time)
+  static std::atomic<int> cache[64][3][3];
+  const int hc = prefill_heads_per_wg(group);
+  const int di = head_size == 64 ? 0 : head_size == 128 ? 1 : 2, ci = hc == 1 ? 0 : hc == 2 ? 1 : 2;
+  int dev = 0;
+  const bool cacheable = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64;
+  if (!cacheable) (void)hipGetLastError();
+  int per_cu = cacheable ? cache[dev][di][ci].load(std::memory_order_relaxed) : 0;
+  if (per_cu <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_walk_fn(head_size, hc), kWaves * kWave, 0) !=
+            hipSuccess ||
+        per_cu < 1) {
+      (void)hipGetLastError();  // our own failed query: do not leave it behind
+      per_cu = 1;
+    } else if (cacheable) {
+      cache[dev][di][ci].store(per_cu, std::memory_order_relaxed);
+    }
   }
   return per_cu * device_cus();
 }
@@ -1293,19 +1306,22 @@ size_t prefill_split_workspace_bytes(int num_seqs, int num_kv_heads, int group, 
   return split_layout(num_seqs, num_kv_heads, group, head_size, max_query_len, ranges).bytes;
 }
 
-bool prefill_split_cuts(const int32_t* context_lens, const int32_t* query_lens, int num_seqs, int num_kv_heads,
+bool prefill_split_pays(const int32_t* context_lens, const int32_t* query_lens, int num_seqs, int num_kv_heads,
                         int group, int ranges) {
   const int64_t hg = group / prefill_heads_per_wg(group);
   const int64_t tpw = tokens_per_wg(prefill_heads_per_wg(group), true);
   int64_t total = 0, longest = 0;
+  int busy = 0;  // sequences with chunk tokens
   for (int s = 0; s < num_seqs; ++s) {
     const int64_t ctx = context_lens[s], n = query_lens[s];
     if (n <= 0) continue;
+    ++busy;
     total += seq_walk_steps(ctx, n, tpw);
     longest = std::max(longest, tile_steps((n + tpw - 1) / tpw - 1, ctx, n, tpw));
   }
-  // the plan kernel's rule
-  return longest * kSplitShare * ranges > total * num_kv_heads * hg;
+  // a batch: the split's longest-first unit list beat the plain launch's
+  // order; one sequence: only when the plan would cut a walk (its rule)
+  return busy > 1 || longest * kSplitShare * ranges > total * num_kv_heads * hg;
 }
 
 int64_t prefill_split_grid(int num_seqs, int num_kv_heads, int group, int max_query_len, int ranges) {

@@ -147,10 +147,12 @@ int32_t paged_attention_prefill_split_ranges(int32_t head_size, int32_t num_head
 
 /*
  * Which launch serves these lengths better: 1 for paged_attention_prefill_split
- * (some walk is longer than half of a resident workgroup's fair share of the
- * launch's steps, so the split cuts it), 0 for paged_attention_prefill (the
- * split would cut nothing; the one-walk-per-workgroup launch then measured
- * 1 to 3 % faster).  context_lens and query_lens are HOST arrays of
+ * when more than one sequence has chunk tokens (its longest-first unit list
+ * measured 0 to 40 % faster on ragged batches, and 3 % slower on one of the
+ * twelve batches timed), or when some walk is longer than half of a resident
+ * workgroup's fair share of the launch's steps (the split cuts it); 0 for
+ * paged_attention_prefill otherwise (one sequence whose walks are all short:
+ * the one-walk-per-workgroup launch measured 1 to 3 % faster there).  context_lens and query_lens are HOST arrays of
  * num_seqs entries (>= 0); num_ranges is N of this device
  * (paged_attention_prefill_split_ranges).  Negative status for bad sizes.
  * Host-only; no HIP call.

@@ -325,9 +325,10 @@ def walk_steps(ctx, n, tpw):
 
 @pytest.mark.parametrize("seed", range(6))
 def test_prefill_choose_split_rule(seed):
-    """The split is chosen exactly when the longest walk is more than half of
-    a resident workgroup's share of all walks' steps (every KV head and head
-    chunk walks the same steps)."""
+    """The split is chosen for a batch (more than one sequence with chunk
+    tokens), and for one sequence exactly when its longest walk is more than
+    half of a resident workgroup's share of all walks' steps (every KV head
+    and head chunk walks the same steps)."""
     rng = np.random.default_rng(seed)
     S = int(rng.integers(1, 40))
     ctx = rng.integers(0, 40000, S) * (rng.random(S) < 0.8)
@@ -337,13 +338,20 @@ def test_prefill_choose_split_rule(seed):
     hc = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
     tpw = 256 // hc
     steps = [st for c, n in zip(ctx, qn) for st in walk_steps(int(c), int(n), tpw)]
-    want = bool(steps) and max(steps) * 2 * N > sum(steps) * Hkv * (G // hc)
+    busy = int(np.count_nonzero(qn))
+    want = busy > 1 or (bool(steps) and max(steps) * 2 * N > sum(steps) * Hkv * (G // hc))
     assert pad.paged_attention_prefill_choose_split(ctx, qn, H, Hkv, D, N) == want
+    # one sequence alone: the cut rule decides
+    for s in range(min(S, 8)):
+        one = walk_steps(int(ctx[s]), int(qn[s]), tpw)
+        want1 = bool(one) and max(one) * 2 * N > sum(one) * Hkv * (G // hc)
+        assert pad.paged_attention_prefill_choose_split(ctx[s:s + 1], qn[s:s + 1], H, Hkv, D, N) == want1
 
 
 def test_prefill_choose_split_workloads():
     """One chunk over a long prefix: its walks are short beside the total (no
-    cut, the plain launch); the ragged batch: its 33 000-key walks are cut."""
+    cut, the plain launch); the ragged batch: the split; one short chunk over a
+    long context (few, long walks): the split, which cuts them."""
     from decode_attention_paged_05_amd import inputs as gen
 
     for name, want in (("prefill", False), ("prefill_batch", True)):
@@ -351,6 +359,9 @@ def test_prefill_choose_split_workloads():
         s = pp.spec
         assert pad.paged_attention_prefill_choose_split(pp.context_lens, pp.query_lens, s.num_heads, s.num_kv_heads,
                                                         s.head_size, 256) == want, name
+    assert pad.paged_attention_prefill_choose_split([100000], [256], 24, 4, 256, 256)
+    assert pad.paged_attention_prefill_choose_split([100000, 7], [256, 0], 24, 4, 128, 256)  # one busy: cut
+    assert not pad.paged_attention_prefill_choose_split([32768, 7], [8192, 0], 24, 4, 256, 256)  # one busy: no cut
     with pytest.raises(pad.PadError):
         pad.paged_attention_prefill_choose_split([5, -1], [3, 3], 24, 4, 256, 256)
 
