@@ -737,25 +737,26 @@ constexpr int kSplitRows = 2 * kRowGroups * kRowsPerWave;  // rows of a solo wor
 constexpr int kSplitStatFloats = 2 * kSplitRows;
 constexpr int kSplitPlanThreads = 1024;
 
-// header words the plan writes
+// Header words the plan writes (int32 at the workspace's start): units
+// listed, pieces among them (listed first), cut walks, C, the most pieces of
+// one walk, sequences with cut walks.  The walk and merge kernels read the
+// first and third; tests read them all.
 enum { kHdrUnits = 0, kHdrPieces, kHdrCutWalks, kHdrStep, kHdrMaxPieces, kHdrCutSeqs, kHdrWords = 16 };
 
 struct PrefillSplit {
   int32_t* hdr;        // [kHdrWords]
-  int4* units;         // [units_cap]: {sequence, tile, KV head, j << 16 | k}
-  int32_t* order;      // [S]: sequence of each rank (longest walk first)
+  int4* units;         // {sequence, tile, KV head, j << 16 | k}
+  int32_t* order;      // [S]: sequence of each rank (longest walk first), past the plan's LDS
   int32_t* cut_idx;    // [S]: rank of the sequence among those with cut walks, or -1
-  int32_t* cut_seq;    // [cut_seq_cap]: sequence of each such rank
+  int32_t* cut_seq;    // [cut_seq_cap]: sequence of each such rank, past the plan's LDS
   int32_t* pair_off;   // [kSplitMaxPieces x cut_seq_cap]: first unit of (piece index, cut sequence)
-  float* part;         // [slots_cap] slots of 256 rows x D floats
-  float* stats;        // [slots_cap] slots of 256 rows x (max, sum)
+  float* part;         // partial slots of 256 rows x D floats
+  float* stats;        // partial slots of 256 rows x (max, sum)
   int num_seqs;
   int max_query_len;
   int ranges;          // N, resident workgroups of the walk kernel
   int tokens_per_wg;   // TPW, a multiple of 32
-  int units_cap;
   int cut_seq_cap;
-  int slots_cap;
 };
 
 // 32-key steps of token tile t (its last row sees keys 0 .. ctx + min((t + 1) TPW, n) - 1).
@@ -1349,9 +1350,7 @@ hipError_t launch_prefill_split(const PrefillArgs& args, int num_seqs, int max_q
   p.max_query_len = max_query_len;
   p.ranges = ranges;
   p.tokens_per_wg = tokens_per_wg(hc, true);
-  p.units_cap = (int)l.units_cap;
   p.cut_seq_cap = (int)l.cut_seq_cap;
-  p.slots_cap = (int)l.slots_cap;
   void* kargs[] = {const_cast<PrefillArgs*>(&a), &p};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&split_plan_kernel), dim3(1),
                                  dim3(kSplitPlanThreads), kargs, 0, stream);

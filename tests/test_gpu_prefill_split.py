@@ -201,3 +201,48 @@ def test_split_many_cut_sequences():
     assert pad.paged_attention_prefill_choose_split(pp.context_lens, pp.query_lens, 4, 1, 64, n_ranges)
     dp = DevicePrefill(pp)
     assert max_err(run_split(dp), dp.oracle()) <= TOL["bf16"]
+
+
+def plan_model(ctx, qn, H, Hkv, N, mql):
+    """The plan's decisions restated: C, the walks it cuts and the units it lists."""
+    G = H // Hkv
+    hc = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+    hg, tpw = G // hc, 256 // hc
+    walks = []  # (sequence, tile, steps) of sequences inside the contract
+    for s, (c, n) in enumerate(zip(ctx, qn)):
+        if 0 < n <= mql:
+            walks += [(s, t, -(-(c + min((t + 1) * tpw, n)) // 32)) for t in range(-(-n // tpw))]
+    B = sum(st for _, _, st in walks) * Hkv * hg
+    L = max((st for _, _, st in walks), default=0)
+    C = max(-(-B // (4 * N)), -(-L // 32), 16)
+    if L * 2 * N <= B:
+        C = max(C, L)
+    ks = [-(-st // C) for _, _, st in walks]
+    cut = [k for k in ks if k > 1]
+    pieces = Hkv * sum(cut)
+    whole = Hkv * sum(1 for k in ks if k == 1)
+    return {"units": pieces + whole, "pieces": pieces, "cut_walks": Hkv * len(cut), "C": C,
+            "max_pieces": max(ks) if L > C else 1, "cut_seqs": len({s for (s, _, _), k in zip(walks, ks) if k > 1})}
+
+
+@pytest.mark.parametrize("name", ["prefill_batch", "prefill", "prefill_small", "skewed"])
+def test_split_plan_matches_model(name):
+    """The plan's header (units, pieces, cut walks, C, most pieces of a walk,
+    sequences with cut walks) against a restatement of its rule."""
+    if name == "skewed":
+        spec = gen.PrefillSpec("skewed", context_lens=(60000,) + (500,) * 15, query_lens=(1024,) + (256,) * 15,
+                               num_heads=24, num_kv_heads=4, head_size=256, dtype="bf16", seed=63)
+        pp = gen.make_prefill_problem(spec)
+    else:
+        pp = gen.make_prefill_problem(name)
+    spec = pp.spec
+    dp = DevicePrefill(pp, keep_host=False)
+    ws = pad.alloc_prefill_split_workspace(pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size,
+                                           pp.max_query_len)
+    run_split(dp, ws=ws)
+    hdr = ws[:24].cpu().numpy().view(np.int32)
+    N = pad.paged_attention_prefill_split_ranges(spec.head_size, spec.num_heads, spec.num_kv_heads)
+    want = plan_model([int(v) for v in pp.context_lens], [int(v) for v in pp.query_lens], spec.num_heads,
+                      spec.num_kv_heads, N, pp.max_query_len)
+    got = dict(zip(["units", "pieces", "cut_walks", "C", "max_pieces", "cut_seqs"], [int(v) for v in hdr]))
+    assert got == want
