@@ -167,7 +167,7 @@ def run_prefill(args) -> int:
             pp.context_lens, pp.query_lens, spec.num_heads, spec.num_kv_heads, spec.head_size, n_ranges) else "grid"
     split = form == "split"
     ws = (pad.alloc_prefill_split_workspace(pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size,
-                                            pp.max_query_len, dev) if split else None)
+                                            pp.max_query_len, tables.shape[1], dev) if split else None)
     torch.cuda.synchronize()
     flops = pp.flops()
     desc = (f"{args.config}: {pp.num_seqs} seq, context {list(map(int, pp.context_lens))}, chunk "

@@ -512,9 +512,9 @@ def paged_attention_prefill_choose_split(context_lens, query_lens, num_heads: in
 
 
 def paged_attention_prefill_split_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
-                                                 max_query_len: int, num_ranges: int) -> int:
-    dims = PadPrefillDims(PAD_DTYPE_BF16, int(num_seqs), 0, int(num_heads), int(head_size), int(max_query_len), 1, 1,
-                          PAD_KV_TILED)
+                                                 max_query_len: int, max_blocks_per_seq: int, num_ranges: int) -> int:
+    dims = PadPrefillDims(PAD_DTYPE_BF16, int(num_seqs), 0, int(num_heads), int(head_size), int(max_query_len), 1,
+                          int(max_blocks_per_seq), PAD_KV_TILED)
     n = LIB.paged_attention_prefill_split_workspace_size(ctypes.byref(dims), int(num_kv_heads), int(num_ranges))
     if n == ctypes.c_size_t(-1).value:
         raise PadError(-3, "paged_attention_prefill_split_workspace_size (sizes out of range)")
@@ -522,11 +522,11 @@ def paged_attention_prefill_split_workspace_size(num_seqs: int, num_heads: int, 
 
 
 def alloc_prefill_split_workspace(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
-                                  max_query_len: int, device=None):
+                                  max_query_len: int, max_blocks_per_seq: int, device=None):
     """Allocate (torch, uint8) a workspace for paged_attention_prefill_split on the current device."""
     torch = _torch()
     n = paged_attention_prefill_split_workspace_size(
-        num_seqs, num_heads, num_kv_heads, head_size, max_query_len,
+        num_seqs, num_heads, num_kv_heads, head_size, max_query_len, max_blocks_per_seq,
         paged_attention_prefill_split_ranges(head_size, num_heads, num_kv_heads))
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
 

@@ -331,11 +331,12 @@ int32_t paged_attention_prefill_split_ranges(int32_t head_size, int32_t num_head
 size_t paged_attention_prefill_split_workspace_size(const pad_prefill_dims_t* dims, int32_t num_kv_heads,
                                                     int32_t num_ranges) {
   if (!dims || num_ranges <= 0 || num_kv_heads <= 0 || dims->num_seqs < 0 || dims->max_query_len < 0 ||
-      dims->num_heads <= 0 || dims->num_heads % num_kv_heads != 0 ||
+      dims->max_blocks_per_seq <= 0 || dims->num_heads <= 0 || dims->num_heads % num_kv_heads != 0 ||
       (dims->head_size != 64 && dims->head_size != 128 && dims->head_size != 256))
     return (size_t)-1;
   return pad::prefill_split_workspace_bytes(dims->num_seqs, num_kv_heads, dims->num_heads / num_kv_heads,
-                                            dims->head_size, dims->max_query_len, num_ranges);
+                                            dims->head_size, dims->max_query_len, dims->max_blocks_per_seq,
+                                            num_ranges);
 }
 
 int32_t paged_attention_prefill_choose_split(const int32_t* context_lens, const int32_t* query_lens,
@@ -371,7 +372,8 @@ int32_t paged_attention_prefill_split(float* out, const void* query, const void*
   const int ranges = pad::prefill_split_ranges(dims->head_size, group);
   // the walk kernel's grid is 32-bit
   const int hg = group / pad::prefill_heads_per_wg(group);
-  if (pad::prefill_split_grid(dims->num_seqs, num_kv_heads, group, dims->max_query_len, ranges) > INT32_MAX)
+  if (pad::prefill_split_grid(dims->num_seqs, num_kv_heads, group, dims->max_query_len, dims->max_blocks_per_seq,
+                              ranges) > INT32_MAX)
     return PAD_ERR_UNSUPPORTED;
   // the plan's 64-bit step count: S x KV heads x head groups x tiles x steps per tile
   const int tpw = pad::prefill_tokens_per_wg(group, true);
@@ -379,7 +381,8 @@ int32_t paged_attention_prefill_split(float* out, const void* query, const void*
   const unsigned __int128 steps = ((unsigned __int128)dims->max_blocks_per_seq * block_size + 31) / 32;
   if ((unsigned __int128)dims->num_seqs * num_kv_heads * hg * tiles * steps >> 62) return PAD_ERR_UNSUPPORTED;
   if ((size_t)workspace_bytes < pad::prefill_split_workspace_bytes(dims->num_seqs, num_kv_heads, group,
-                                                                   dims->head_size, dims->max_query_len, ranges))
+                                                                   dims->head_size, dims->max_query_len,
+                                                                   dims->max_blocks_per_seq, ranges))
     return PAD_ERR_WORKSPACE;
   pad::PrefillArgs a{};
   a.out = out;

@@ -1250,22 +1250,32 @@ const void* split_merge_fn(int head_size, int hc) {
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace of a split launch.  Bounds (rounds = kSplitRounds x N, C >= the
-// total steps / rounds): a cut walk has more than C steps, so fewer than
-// rounds / HG walks are cut, in fewer than rounds / (Hkv HG) sequences; a cut
-// walk's k = ceil(steps / C) pieces number under 2 steps / C, so fewer than
-// 2 rounds / HG pieces; whole walks are at most S x Hkv x ceil(max_query_len / TPW).
+// total steps / rounds; walks W = S x Hkv x ceil(max_query_len / TPW) at
+// most): a cut walk has more than C steps, so fewer than rounds / HG walks
+// are cut, in fewer than rounds / (Hkv HG) sequences; a cut walk's k =
+// ceil(steps / C) pieces number under 2 steps / C, and, as C >= 16, at most
+// ceil(Lmax / 16) (Lmax = the longest walk the block table allows; none is
+// cut below 17 steps) and kSplitMaxPieces: fewer than min(2 rounds / HG,
+// kmax W) pieces.
 struct SplitLayout {
   int64_t units_cap, cut_seq_cap, slots_cap;
   size_t units, order, cut_idx, cut_seq, pair_off, stats, part, bytes;
 };
-SplitLayout split_layout(int num_seqs, int num_kv_heads, int group, int head_size, int max_query_len, int ranges) {
+SplitLayout split_layout(int num_seqs, int num_kv_heads, int group, int head_size, int max_query_len, int max_blocks,
+                         int ranges) {
   const int64_t hg = group / prefill_heads_per_wg(group);
   const int64_t tpw = tokens_per_wg(prefill_heads_per_wg(group), true);
   const int64_t rounds = (int64_t)kSplitRounds * ranges;
   SplitLayout l;
-  l.units_cap = (int64_t)num_seqs * num_kv_heads * ((max_query_len + tpw - 1) / tpw) + 2 * rounds / hg + 2;
+  const int64_t walks = (int64_t)num_seqs * num_kv_heads * ((max_query_len + tpw - 1) / tpw);
+  const int64_t longest = ((int64_t)max_blocks * kBlockTokens + 31) / 32;
+  const int64_t kmax = longest > kSplitMinSteps
+                           ? std::min<int64_t>(kSplitMaxPieces, (longest + kSplitMinSteps - 1) / kSplitMinSteps)
+                           : 0;
+  const int64_t pieces = std::min<int64_t>(2 * rounds / hg + 2, kmax * walks);
+  l.units_cap = walks + pieces;
   l.cut_seq_cap = std::min<int64_t>(num_seqs, rounds / (hg * num_kv_heads) + 1);
-  l.slots_cap = (2 * rounds / hg + 2) * hg;
+  l.slots_cap = pieces * hg;
   l.units = 256;  // the header
   l.order = l.units + align256((size_t)l.units_cap * 16);
   l.cut_idx = l.order + align256((size_t)num_seqs * 4);
@@ -1303,8 +1313,8 @@ int prefill_split_ranges(int head_size, int group) {
 }
 
 size_t prefill_split_workspace_bytes(int num_seqs, int num_kv_heads, int group, int head_size, int max_query_len,
-                                     int ranges) {
-  return split_layout(num_seqs, num_kv_heads, group, head_size, max_query_len, ranges).bytes;
+                                     int max_blocks, int ranges) {
+  return split_layout(num_seqs, num_kv_heads, group, head_size, max_query_len, max_blocks, ranges).bytes;
 }
 
 bool prefill_split_pays(const int32_t* context_lens, const int32_t* query_lens, int num_seqs, int num_kv_heads,
@@ -1325,8 +1335,9 @@ bool prefill_split_pays(const int32_t* context_lens, const int32_t* query_lens, 
   return busy > 1 || longest * kSplitShare * ranges > total * num_kv_heads * hg;
 }
 
-int64_t prefill_split_grid(int num_seqs, int num_kv_heads, int group, int max_query_len, int ranges) {
-  const SplitLayout l = split_layout(num_seqs, num_kv_heads, group, 256, max_query_len, ranges);
+int64_t prefill_split_grid(int num_seqs, int num_kv_heads, int group, int max_query_len, int max_blocks,
+                           int ranges) {
+  const SplitLayout l = split_layout(num_seqs, num_kv_heads, group, 256, max_query_len, max_blocks, ranges);
   return l.units_cap * (group / prefill_heads_per_wg(group));
 }
 
@@ -1335,7 +1346,8 @@ hipError_t launch_prefill_split(const PrefillArgs& args, int num_seqs, int max_q
   if (num_seqs == 0) return hipSuccess;
   const PrefillArgs a = kernel_args(args);
   const int hc = prefill_heads_per_wg(a.group);
-  const SplitLayout l = split_layout(num_seqs, a.num_kv_heads, a.group, head_size, max_query_len, ranges);
+  const SplitLayout l = split_layout(num_seqs, a.num_kv_heads, a.group, head_size, max_query_len, a.max_blocks,
+                                     ranges);
   char* base = static_cast<char*>(workspace);
   PrefillSplit p{};
   p.hdr = reinterpret_cast<int32_t*>(base);

@@ -64,13 +64,13 @@ hipError_t launch_prefill(const PrefillArgs& args, int num_seqs, int max_query_l
 // needs, and the launch (plan, walks, merge).
 int prefill_split_ranges(int head_size, int group);
 size_t prefill_split_workspace_bytes(int num_seqs, int num_kv_heads, int group, int head_size, int max_query_len,
-                                     int ranges);
+                                     int max_blocks, int ranges);
 // whether the split launch serves these lengths (host arrays) better: a
 // batch of more than one sequence with chunk tokens, or walks it would cut
 bool prefill_split_pays(const int32_t* context_lens, const int32_t* query_lens, int num_seqs, int num_kv_heads,
                         int group, int ranges);
 // workgroups of the walk kernel (a bound on its units x head chunks)
-int64_t prefill_split_grid(int num_seqs, int num_kv_heads, int group, int max_query_len, int ranges);
+int64_t prefill_split_grid(int num_seqs, int num_kv_heads, int group, int max_query_len, int max_blocks, int ranges);
 hipError_t launch_prefill_split(const PrefillArgs& args, int num_seqs, int max_query_len, int head_size,
                                 int ranges, void* workspace, hipStream_t stream);
 

@@ -163,10 +163,13 @@ int32_t paged_attention_prefill_choose_split(const int32_t* context_lens, const 
 
 /*
  * Workspace bytes of paged_attention_prefill_split for these sizes (num_seqs,
- * num_heads, head_size and max_query_len of dims) and N = num_ranges: the
- * unit list (whole walks and pieces: at most num_seqs x num_kv_heads x
- * ceil(max_query_len / tokens per walk) + 8 N / head chunks), and partial
- * slots of 256 rows x (head_size + 2) floats for at most 8 N pieces.
+ * num_heads, head_size, max_query_len and max_blocks_per_seq of dims) and
+ * N = num_ranges: the unit list (at most W = num_seqs x num_kv_heads x
+ * ceil(max_query_len / tokens per walk) walks, and fewer than
+ * min(8 N / head chunks, k W) pieces, k = the pieces a walk of the block
+ * table's width can be cut into: 0 below 512 positions, at most 32), and
+ * partial slots of 256 rows x (head_size + 2) floats, one per piece and head
+ * chunk.
  * (size_t)-1 for sizes out of range.  Host-only; no HIP call.
  */
 size_t paged_attention_prefill_split_workspace_size(const pad_prefill_dims_t* dims, int32_t num_kv_heads,

@@ -368,14 +368,16 @@ def test_prefill_choose_split_workloads():
 
 def test_prefill_split_workspace_size():
     size = pad.paged_attention_prefill_split_workspace_size
-    base = size(4, 24, 4, 256, 3000, 256)
+    base = size(4, 24, 4, 256, 3000, 2063, 256)  # the ragged batch: contexts up to 33 000 positions
     assert base > 0
-    assert size(8, 24, 4, 256, 3000, 256) > base  # more sequences: more whole walks listed
-    assert size(4, 24, 4, 128, 3000, 256) < base  # smaller partial slots
-    # partial slots: 8 N pieces of 256 rows x D floats bound the size from below
-    assert base >= 8 * 256 * 256 * 256 * 4
+    assert size(8, 24, 4, 256, 3000, 2063, 256) > base  # more sequences: more whole walks listed
+    assert size(4, 24, 4, 128, 3000, 2063, 256) < base  # smaller partial slots
+    # the batch's 376 pieces x 3 head chunks fit: 1 128 slots of 256 rows x 256 floats
+    assert base >= 1128 * 256 * 256 * 4
+    # no walk of a 16-block table can be cut (at most 8 steps): no partial slots at all
+    assert size(4, 24, 4, 256, 3000, 16, 256) < 1 << 20
     with pytest.raises(pad.PadError):
-        size(4, 24, 5, 256, 3000, 256)
+        size(4, 24, 5, 256, 3000, 2063, 256)
 
 
 def test_prefill_empty_is_a_noop():

@@ -26,7 +26,7 @@ def run_split(dp: DevicePrefill, ws=None, out=None, tables=None, mql=None, scale
     spec = pp.spec
     if ws is None:
         ws = pad.alloc_prefill_split_workspace(pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size,
-                                               pp.max_query_len if mql is None else mql)
+                                               pp.max_query_len if mql is None else mql, dp.dp.tables.shape[1])
     if out is None:
         out = torch.full(tuple(pp.query.shape), float("nan"), dtype=torch.float32, device="cuda")
     pad.paged_attention_prefill_split(out, dp.query, dp.dp.kc, dp.dp.vc, dp.dp.tables if tables is None else tables,
@@ -80,7 +80,7 @@ def test_split_workspace_contents_do_not_matter():
         dtype="bf16", seed=52)))
     spec = dp.pp.spec
     ws = pad.alloc_prefill_split_workspace(dp.pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size,
-                                           dp.pp.max_query_len)
+                                           dp.pp.max_query_len, dp.dp.tables.shape[1])
     ws.view(torch.uint8).fill_(0xFF)  # NaN floats, all-ones counters and offsets
     a = run_split(dp, ws=ws)
     ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda"))
@@ -140,7 +140,8 @@ def test_split_rejects_a_small_workspace():
     spec = dp.pp.spec
     need = pad.paged_attention_prefill_split_workspace_size(
         dp.pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size, dp.pp.max_query_len,
-        pad.paged_attention_prefill_split_ranges(spec.head_size, spec.num_heads, spec.num_kv_heads))
+        dp.dp.tables.shape[1], pad.paged_attention_prefill_split_ranges(spec.head_size, spec.num_heads,
+                                                                          spec.num_kv_heads))
     with pytest.raises(pad.PadError):
         run_split(dp, ws=torch.empty(need - 256, dtype=torch.uint8, device="cuda"))
 
@@ -151,7 +152,7 @@ def test_split_graph_capture_replays():
     dp = DevicePrefill(gen.make_prefill_problem("prefill_small"))
     pp, spec = dp.pp, dp.pp.spec
     ws = pad.alloc_prefill_split_workspace(pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size,
-                                           pp.max_query_len)
+                                           pp.max_query_len, dp.dp.tables.shape[1])
     eager = run_split(dp, ws=ws)
     out = torch.empty_like(eager)
     stream = torch.cuda.Stream()
@@ -238,7 +239,7 @@ def test_split_plan_matches_model(name):
     spec = pp.spec
     dp = DevicePrefill(pp, keep_host=False)
     ws = pad.alloc_prefill_split_workspace(pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size,
-                                           pp.max_query_len)
+                                           pp.max_query_len, dp.dp.tables.shape[1])
     run_split(dp, ws=ws)
     hdr = ws[:24].cpu().numpy().view(np.int32)
     N = pad.paged_attention_prefill_split_ranges(spec.head_size, spec.num_heads, spec.num_kv_heads)
