@@ -111,13 +111,14 @@ int32_t paged_attention_prefill(float* out, const void* query, const void* key_c
  * prefill walks.  A walk is the key range of one workgroup's rows: one
  * sequence, one KV head's query heads (or a chunk of them), one tile of chunk
  * tokens, in 32-key steps up to the tile's last position.  Every walk longer
- * than C steps -- C = the launch's total steps over 4 N, N =
- * paged_attention_prefill_split_ranges() -- is cut into ceil(steps / C)
- * pieces of equal length, which are served first (longest sequence first);
- * the whole walks follow.  No walk is cut when the longest is at most half
- * of the total steps over N (see paged_attention_prefill_choose_split).  Pieces leave unnormalised rows in the workspace
- * and a merge combines them.  Same operation, arguments and contract as
- * paged_attention_prefill, except:
+ * than C steps -- C = the launch's total steps over 4 N (N =
+ * paged_attention_prefill_split_ranges()), at least 16 and at least the
+ * longest walk over 32 -- is cut into ceil(steps / C) pieces of equal
+ * length, which are served first (longest sequence first); the whole walks
+ * follow.  No walk is cut when the longest is at most half of the total
+ * steps over N (see paged_attention_prefill_choose_split).  Pieces leave
+ * unnormalised rows in the workspace and a merge combines them.  Same
+ * operation, arguments and contract as paged_attention_prefill, except:
  *   workspace        device memory of at least workspace_bytes bytes, 16-byte
  *                    aligned; contents on entry do not matter (every byte read
  *                    is written first by the same call); two calls in flight
@@ -152,10 +153,10 @@ int32_t paged_attention_prefill_split_ranges(int32_t head_size, int32_t num_head
  * twelve batches timed), or when some walk is longer than half of a resident
  * workgroup's fair share of the launch's steps (the split cuts it); 0 for
  * paged_attention_prefill otherwise (one sequence whose walks are all short:
- * the one-walk-per-workgroup launch measured 1 to 3 % faster there).  context_lens and query_lens are HOST arrays of
- * num_seqs entries (>= 0); num_ranges is N of this device
- * (paged_attention_prefill_split_ranges).  Negative status for bad sizes.
- * Host-only; no HIP call.
+ * the one-walk-per-workgroup launch measured 1 to 3 % faster there).
+ * context_lens and query_lens are HOST arrays of num_seqs entries (>= 0);
+ * num_ranges is N of this device (paged_attention_prefill_split_ranges).
+ * Negative status for bad sizes.  Host-only; no HIP call.
  */
 int32_t paged_attention_prefill_choose_split(const int32_t* context_lens, const int32_t* query_lens,
                                              int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
@@ -169,8 +170,7 @@ int32_t paged_attention_prefill_choose_split(const int32_t* context_lens, const 
  * min(8 N / head chunks, k W) pieces, k = the pieces a walk of the block
  * table's width can be cut into: 0 below 512 positions, at most 32), and
  * partial slots of 256 rows x (head_size + 2) floats, one per piece and head
- * chunk.
- * (size_t)-1 for sizes out of range.  Host-only; no HIP call.
+ * chunk.  (size_t)-1 for sizes out of range.  Host-only; no HIP call.
  */
 size_t paged_attention_prefill_split_workspace_size(const pad_prefill_dims_t* dims, int32_t num_kv_heads,
                                                     int32_t num_ranges);

@@ -512,6 +512,15 @@ def test_no_alloc_rejects_what_does_not_fit():
                                                  ctypes.byref(dims(num_seqs=0)), None) == 0
 
 
+def test_source_folders_hold_sources_only():
+    """The build id hashes every file under csrc/ and include/: a stray object or
+    listing there gives a library whose id no clean checkout reproduces."""
+    for d, exts in ((os.path.join(ROOT, "decode_attention_paged_05_amd", "csrc"), (".hip", ".hpp", ".h", ".cpp")),
+                    (os.path.join(ROOT, "include"), (".h",))):
+        stray = [n for n in os.listdir(d) if not n.endswith(exts)]
+        assert not stray, f"{d}: {stray}"
+
+
 def test_library_built_from_these_sources():
     """The loaded library's build id is the hash of csrc/ and include/ as they
     stand (a stale build fails here before any GPU run)."""

@@ -247,3 +247,19 @@ def test_split_plan_matches_model(name):
                       spec.num_kv_heads, N, pp.max_query_len)
     got = dict(zip(["units", "pieces", "cut_walks", "C", "max_pieces", "cut_seqs"], [int(v) for v in hdr]))
     assert got == want
+
+
+@pytest.mark.parametrize("H,Hkv,D,ctx,qn", [(24, 4, 256, (0, 37, 200, 16, 5), (50, 1, 77, 128, 0)),
+                                            (8, 4, 128, (0, 64), (200, 17)), (10, 5, 64, (0,), (90,))],
+                         ids=lambda v: str(v))
+def test_split_without_cuts_gives_the_plain_bits(H, Hkv, D, ctx, qn):
+    """Walks the split launch does not cut run the plain launch's walk code over
+    the same steps: the same bits (the plan cuts nothing here; its header says so)."""
+    spec = gen.PrefillSpec("nocut", context_lens=ctx, query_lens=qn, num_heads=H, num_kv_heads=Hkv, head_size=D,
+                           dtype="bf16", seed=64)
+    pp = gen.make_prefill_problem(spec)
+    dp = DevicePrefill(pp, keep_host=False)
+    ws = pad.alloc_prefill_split_workspace(pp.num_seqs, H, Hkv, D, pp.max_query_len, dp.dp.tables.shape[1])
+    got = run_split(dp, ws=ws)
+    assert int(ws[4:8].cpu().numpy().view(np.int32)[0]) == 0  # pieces listed
+    assert torch.equal(got, dp.run())
