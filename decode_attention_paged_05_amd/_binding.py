@@ -120,7 +120,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode_choose_partition_for_batch.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, i32]
     lib.paged_attention_decode_choose_partition_for_batch.restype = i32
     ip = ctypes.POINTER(ctypes.c_int32)
-    lib.paged_attention_decode_entry_ranges.argtypes = [ip, i32, i32, i32, i32, i32, i32, i32, i32, i32, ip, ip, ip]
+    lib.paged_attention_decode_entry_ranges.argtypes = [ip, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, ip, ip,
+                                                        ip]
     lib.paged_attention_decode_entry_ranges.restype = i32
     lib.paged_attention_decode_build_id.argtypes = []
     lib.paged_attention_decode_build_id.restype = ctypes.c_char_p
@@ -385,9 +386,10 @@ def check_build() -> str:
 
 def paged_attention_decode_entry_ranges(seq_lens, num_heads: int, num_kv_heads: int, max_blocks_per_seq: int,
                                         block_size: int, partition_size: int, num_cus: int = 256,
-                                        layout: str = "tiled", head_size: int = 256):
+                                        layout: str = "tiled", head_size: int = 256, dtype: str = "bf16"):
     """Where phase 1 puts each (sequence, head)'s results, for host lengths,
-    heads of ``head_size`` and a cache in ``layout`` ("tiled" or "rows").
+    heads of ``head_size``, elements of ``dtype`` ("bf16" or "f32") and a cache
+    in ``layout`` ("tiled" or "rows").
 
     Returns ``(balanced, count [S, H], begin [S, H, NP], end [S, H, NP])`` as
     NumPy int32 arrays: slot e < count[s, h] of (s, h) holds tokens
@@ -401,6 +403,9 @@ def paged_attention_decode_entry_ranges(seq_lens, num_heads: int, num_kv_heads: 
     kv_layout = {"rows": PAD_KV_ROWS, "tiled": PAD_KV_TILED}.get(layout)
     if kv_layout is None:
         raise ValueError(f"layout must be 'tiled' or 'rows', not {layout!r}")
+    code = {"f32": PAD_DTYPE_F32, "bf16": PAD_DTYPE_BF16}.get(dtype)
+    if code is None:
+        raise ValueError(f"dtype must be 'bf16' or 'f32', not {dtype!r}")
     if partition_size <= 0 or partition_size % block_size:
         raise PadError(-5, "paged_attention_decode_entry_ranges")
     NP = -(-max_blocks_per_seq * block_size // partition_size)
@@ -409,7 +414,7 @@ def paged_attention_decode_entry_ranges(seq_lens, num_heads: int, num_kv_heads: 
     end = np.zeros((S, num_heads, NP), dtype=np.int32)
     ip = ctypes.POINTER(ctypes.c_int32)
     r = LIB.paged_attention_decode_entry_ranges(lens.ctypes.data_as(ip), S, int(num_heads), int(num_kv_heads),
-                                                int(head_size), int(max_blocks_per_seq), int(block_size),
+                                                int(head_size), code, int(max_blocks_per_seq), int(block_size),
                                                 int(partition_size),
                                                 kv_layout, int(num_cus), count.ctypes.data_as(ip),
                                                 begin.ctypes.data_as(ip),

@@ -516,14 +516,15 @@ int32_t paged_attention_decode_choose_partition_for_batch(int32_t num_seqs, int3
 }
 
 int32_t paged_attention_decode_entry_ranges(const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
-                                            int32_t num_kv_heads, int32_t head_size, int32_t max_blocks_per_seq,
-                                            int32_t block_size, int32_t partition_size, int32_t kv_layout,
-                                            int32_t num_cus, int32_t* entry_count, int32_t* entry_begin,
-                                            int32_t* entry_end) {
+                                            int32_t num_kv_heads, int32_t head_size, int32_t dtype,
+                                            int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size,
+                                            int32_t kv_layout, int32_t num_cus, int32_t* entry_count,
+                                            int32_t* entry_begin, int32_t* entry_end) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || max_blocks_per_seq <= 0 ||
       num_cus <= 0)
     return PAD_ERR_SHAPE;
   if (kv_layout != PAD_KV_ROWS && kv_layout != PAD_KV_TILED) return PAD_ERR_UNSUPPORTED;
+  if (dtype != PAD_DTYPE_F32 && dtype != PAD_DTYPE_BF16) return PAD_ERR_DTYPE;
   if (head_size != 64 && head_size != 128 && head_size != 256) return PAD_ERR_UNSUPPORTED;
   if (block_size != pad::kBlockTokens) return PAD_ERR_UNSUPPORTED;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PAD_ERR_UNSUPPORTED;
@@ -548,7 +549,9 @@ int32_t paged_attention_decode_entry_ranges(const int32_t* seq_lens, int32_t num
   }
   const uint64_t B = pre[S] * (uint64_t)gyc;
   const uint64_t N = bal ? pad::balanced_ranges(B, nb_max,
-                                                (unsigned)(pad::balanced_wgs_per_cu(kv_layout, head_size) * num_cus),
+                                                (unsigned)(pad::balanced_wgs_per_cu(kv_layout, head_size,
+                                                                                    dtype == PAD_DTYPE_F32 ? 4 : 2) *
+                                                           num_cus),
                                                 (unsigned)np, (unsigned)num_cus)
                          : 0;
   for (int64_t s = 0; s < S; ++s) {

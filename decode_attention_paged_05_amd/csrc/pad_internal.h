@@ -33,7 +33,8 @@ constexpr int kMaxHeadsPerGroup = 16;
 // by phase 1, so no state carries from call to call.
 constexpr int kBalancedMaxSeqs = 1024;
 // Resident one-wave workgroups per compute unit that the balanced split
-// launches, by cache layout and head size.  Tiled, head size 256: two
+// launches, by cache layout, head size and element size.  Tiled, head size
+// 256, bf16: two
 // measured faster than three on every split workload (100K tokens 71.4-71.6
 // against 72.1-72.3 us per step; 32 mixed sequences 344 against 349 us; 8 x
 // 131072 MHA 3 748 against 3 779 us): phase 1 is as fast, and the merge has a
@@ -42,7 +43,9 @@ constexpr int kBalancedMaxSeqs = 1024;
 // heads of 64: 100K tokens 40.9 against 51.7 us, 16 x 32K 174 against 208 us;
 // heads of 128 unchanged; six slower).  Rows (P.V on the vector ALUs, four
 // times the vector work per block): three, 72.5-72.7 against 74.3-74.8 us
-// with two on the 100K step.
+// with two on the 100K step.  Tiled, head size 256, fp32 (a 32 KB block
+// fills 128 registers: one block in flight per wave): three, 131-134 against
+// 174-177 us with two on the 100K step; four 134 us.
 #ifndef PAD_BALANCED_WGS_PER_CU_TILED
 #define PAD_BALANCED_WGS_PER_CU_TILED 2
 #endif
@@ -52,10 +55,15 @@ constexpr int kBalancedMaxSeqs = 1024;
 #ifndef PAD_BALANCED_WGS_PER_CU_ROWS
 #define PAD_BALANCED_WGS_PER_CU_ROWS 3
 #endif
-constexpr int kBalancedWgsPerCuMax = 4;  // the most of the three (partition sizes leave slots for it)
-constexpr int balanced_wgs_per_cu(int kv_layout, int head_size) {
+#ifndef PAD_BALANCED_WGS_PER_CU_TILED_F32
+#define PAD_BALANCED_WGS_PER_CU_TILED_F32 3
+#endif
+constexpr int kBalancedWgsPerCuMax = 4;  // the most of them (partition sizes leave slots for it)
+constexpr int balanced_wgs_per_cu(int kv_layout, int head_size, int elem_bytes) {
   return kv_layout != 1 ? PAD_BALANCED_WGS_PER_CU_ROWS  // 1: PAD_KV_TILED
-                        : (head_size >= 256 ? PAD_BALANCED_WGS_PER_CU_TILED : PAD_BALANCED_WGS_PER_CU_TILED_SMALL);
+         : head_size < 256 ? PAD_BALANCED_WGS_PER_CU_TILED_SMALL
+         : elem_bytes == 4 ? PAD_BALANCED_WGS_PER_CU_TILED_F32
+                           : PAD_BALANCED_WGS_PER_CU_TILED;
 }
 // Fewest blocks a balanced range holds (a range costs a query load, a table
 // load and an entry write besides its blocks).

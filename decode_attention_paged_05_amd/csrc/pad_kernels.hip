@@ -294,7 +294,8 @@ hipError_t launch_phase1(const Plan& plan, const void* query, const void* key_ca
   AttnParams a = make_params(plan, query, key_cache, value_cache, block_tables, seq_lens);
   const bool bal = use_balanced(plan);
   a.balanced = bal ? 1 : 0;
-  const dim3 grid = bal ? dim3((unsigned)(balanced_wgs_per_cu(plan.layout, plan.head_size) * a.num_cus))
+  const dim3 grid = bal ? dim3((unsigned)(balanced_wgs_per_cu(plan.layout, plan.head_size, plan.dtype == 0 ? 4 : 2) *
+                                          a.num_cus))
                         : dim3(plan.num_partitions, plan.num_kv_heads * plan.head_chunks, plan.num_seqs);
   const int gh = heads_template(plan.heads_per_wg);
   if (plan.layout == kLayoutTiled)
@@ -371,7 +372,8 @@ hipError_t launch_phase2(const Plan& plan, float* out, const int32_t* seq_lens, 
   const int64_t cus = device_cus();
   const int64_t groups = (int64_t)plan.num_seqs * plan.num_kv_heads * plan.head_chunks;
   const int64_t expect =
-      m.balanced ? (pad::balanced_wgs_per_cu(plan.layout, plan.head_size) * cus + groups + groups - 1) / groups
+      m.balanced ? (pad::balanced_wgs_per_cu(plan.layout, plan.head_size, plan.dtype == 0 ? 4 : 2) * cus + groups +
+                    groups - 1) / groups
                  : plan.num_partitions;
   // Measured on 256 compute units: one wave on 64 dims with rounds of 16
   // entries when a head has few (8 x 131072 MHA tokens or a batch of 32

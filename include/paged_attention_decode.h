@@ -177,7 +177,8 @@ int32_t paged_attention_decode_no_alloc(float* out, const void* query, const voi
  * 0 or outside [0, max_blocks_per_seq * block_size] has none -- and cuts
  * them into N equal contiguous ranges, one per workgroup of a grid that is
  * resident all at once (2 per compute unit for the tiled layout at head
- * size 256, 4 below, 3 for the rows layout, N capped so that no head gets
+ * size 256 in bf16, 3 there in fp32, 4 below head size 256, 3 for the rows
+ * layout; N capped so that no head gets
  * more entries than it has partition slots, and so that a range holds at
  * least 8 blocks).  Each entry then covers a contiguous run of whole blocks
  * (the last one cut at seq_lens[s]) instead of partition e's tokens
@@ -292,11 +293,12 @@ int32_t paged_attention_decode_choose_partition_for_batch(int32_t num_seqs, int3
 
 /*
  * Where phase 1 puts each (sequence, head)'s results, computed on the host
- * from a host copy of seq_lens, for heads of head_size and a cache in
- * kv_layout (PAD_KV_*: the balanced split launches two workgroups per compute
- * unit for the tiled layout at head size 256, four below, and three for the
- * rows layout) on a device with num_cus compute units
- * (the same rule phase 1 applies on the device).  Arrays (row-major, host
+ * from a host copy of seq_lens, for heads of head_size, elements of dtype
+ * (PAD_DTYPE_*) and a cache in kv_layout (PAD_KV_*: the balanced split
+ * launches two workgroups per compute unit for the tiled layout at head size
+ * 256 in bf16, three there in fp32, four below head size 256, and three for
+ * the rows layout) on a device with num_cus compute units (the same rule
+ * phase 1 applies on the device).  Arrays (row-major, host
  * memory, caller-owned):
  *   seq_lens     int32 [num_seqs]
  *   entry_count  int32 [num_seqs, num_heads]: entries of (s, h); 0 for
@@ -310,7 +312,7 @@ int32_t paged_attention_decode_choose_partition_for_batch(int32_t num_seqs, int3
  * or a negative status for invalid arguments.
  */
 int32_t paged_attention_decode_entry_ranges(const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
-                                            int32_t num_kv_heads, int32_t head_size,
+                                            int32_t num_kv_heads, int32_t head_size, int32_t dtype,
                                             int32_t max_blocks_per_seq, int32_t block_size,
                                             int32_t partition_size, int32_t kv_layout, int32_t num_cus,
                                             int32_t* entry_count, int32_t* entry_begin,

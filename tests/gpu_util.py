@@ -166,7 +166,7 @@ def entry_plan(p: gen.Problem, partition_size: int, lens=None, layout: str = "ti
     lens = p.seq_lens if lens is None else lens
     return pad.paged_attention_decode_entry_ranges(lens, p.num_heads, p.num_kv_heads, p.max_blocks_per_seq,
                                                    p.block_size, partition_size, device_cus(), layout,
-                                                   p.head_size)
+                                                   p.head_size, p.dtype)
 
 
 def phase1_entries(ws: torch.Tensor, p: gen.Problem, partition_size: int, s: int, h: int, plan=None,

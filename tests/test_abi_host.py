@@ -393,14 +393,14 @@ def test_prefill_empty_is_a_noop():
 # where phase 1 puts its entries (the host copy of the device rule)
 # ---------------------------------------------------------------------------
 
-def check_entry_plan(lens, H, Hkv, W, P, cus=256, layout="tiled", D=256):
+def check_entry_plan(lens, H, Hkv, W, P, cus=256, layout="tiled", D=256, dtype="bf16"):
     """The invariants phase 2 relies on, for any lengths: every (sequence, head)
     with a valid non-empty length has entries that tile [0, L) in slot order,
     each a run of whole blocks (the last cut at L), no more than NP of them;
     the heads of one KV head share them."""
     import numpy as np
 
-    bal, cnt, lo, hi = pad.paged_attention_decode_entry_ranges(lens, H, Hkv, W, 16, P, cus, layout, D)
+    bal, cnt, lo, hi = pad.paged_attention_decode_entry_ranges(lens, H, Hkv, W, 16, P, cus, layout, D, dtype)
     NP = -(-W * 16 // P)
     G = H // Hkv
     for s, L in enumerate(lens):
@@ -441,7 +441,8 @@ def test_entry_plan_random_batches(seed):
     if S > 3:
         lens[1] = W * 16 + 7  # out of contract
     check_entry_plan(lens.tolist(), H, Hkv, W, P, cus=int(rng.choice([80, 256, 304])),
-                     layout=str(rng.choice(["tiled", "rows"])), D=int(rng.choice([64, 128, 256])))
+                     layout=str(rng.choice(["tiled", "rows"])), D=int(rng.choice([64, 128, 256])),
+                     dtype=str(rng.choice(["bf16", "f32"])))
 
 
 def test_entry_plan_long_context():
@@ -460,6 +461,9 @@ def test_entry_plan_long_context():
     # smaller heads in the tiled layout, four: 1024 ranges of 48 or 49 blocks (P 256 leaves the slots)
     bal, cnt, lo, hi = check_entry_plan([100000], 64, 8, 6250, 256, D=64)
     assert bal and set(cnt[0].tolist()) == {128} and cnt.sum() // 8 == 1024
+    # fp32 in the tiled layout at head size 256, three: 768 ranges, as the rows layout
+    bal, cnt, lo, hi = check_entry_plan([100000], 24, 4, 6250, 512, dtype="f32")
+    assert bal and set(cnt[0].tolist()) == {192} and cnt.sum() // 6 == 768
 
 
 def test_entry_plan_workloads():
@@ -483,9 +487,13 @@ def test_entry_plan_argument_errors():
         pad.paged_attention_decode_entry_ranges([10], 24, 4, 10, 16, 512, layout="nhd")
     with pytest.raises(pad.PadError):
         pad.paged_attention_decode_entry_ranges([10], 24, 4, 10, 16, 512, head_size=96)
+    with pytest.raises(ValueError):
+        pad.paged_attention_decode_entry_ranges([10], 24, 4, 10, 16, 512, dtype="f16")
     lens = (ctypes.c_int32 * 1)(10)
     out = (ctypes.c_int32 * 64)()
-    assert B.LIB.paged_attention_decode_entry_ranges(lens, 1, 24, 4, 256, 10, 16, 512, 7, 256, out, out, out) < 0
+    assert B.LIB.paged_attention_decode_entry_ranges(lens, 1, 24, 4, 256, 1, 10, 16, 512, 7, 256, out, out, out) < 0
+    assert B.LIB.paged_attention_decode_entry_ranges(lens, 1, 24, 4, 256, 9, 10, 16, 512, 1, 256, out, out,
+                                                     out) == -2
 
 
 def test_no_alloc_rejects_what_does_not_fit():
