@@ -51,6 +51,10 @@
 //     came out in).  p is split into bf16 hi + lo (two MFMAs), ~2^-16
 //     relative precision.  Lane l holds output dims of row l%16, so the
 //     softmax state and the rescale stay in the lane.
+// The solo layout multiplies P.V in fp16 instead (one MFMA, v_mfma_f32_16x16x32_f16):
+// p rounded to fp16, V converted to fp16 in LDS once per step by the waves
+// that copied it; a V value beyond fp16's range sends the walk to the bf16
+// form above (walk_rows has the details).
 // V elements at positions the walk does not hold are zeroed before the MFMA,
 // so NaN padding never reaches a row.  Masking runs only on the steps that
 // need it (the diagonal, the end of the walk), in separate code.  Workgroups
@@ -79,6 +83,9 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 
 constexpr int kWave = 64;
 constexpr int kWaves = 8;          // waves per workgroup: 4 row groups x 2 halves of D
@@ -88,6 +95,13 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.0f;  // headroom of the lazy softmax reference
 constexpr float kNoKeysMax = -1e30f;  // reference max of a row that has seen no key
+// fp16 P.V in the solo layout (1), or the bf16 hi + lo pair everywhere (0)
+#ifndef PAD_PREFILL_F16_PV
+#define PAD_PREFILL_F16_PV 1
+#endif
+// fp16 weights are formed against the reference less this (log2 units): with
+// the lazy reference's 2^8 of headroom they lie in [0, 2^15]
+constexpr float kF16Shift = 7.0f;
 
 // s_waitcnt immediate: at most n vector-memory loads outstanding and every
 // LDS access done (export counter left at its maximum)
@@ -158,6 +172,10 @@ __device__ inline void* uniform_ptr(const void* ptr) {
 __device__ inline f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                  c, 0, 0, 0);
+}
+__device__ inline f32x4_t mfma_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
 }
 
 // Workgroup order.  The dispatcher deals linear workgroup ids to the 8 XCDs
@@ -230,14 +248,16 @@ __device__ inline int sequence_of_rank(const PrefillArgs& a, int nseq, int z, in
   return seq[z];
 }
 
-// LDS of a walk: the ring of K/V step buffers, and the logits a paired wave
-// leaves for its partner ([step parity][row group][block][column tile][lane]).
+// LDS of a walk: the ring of K/V step buffers, the logits a paired wave
+// leaves for its partner ([step parity][row group][block][column tile][lane]),
+// and the fp16 range flag of the solo layout's F16 pass.
 template <int D, bool SOLO>
 struct WalkLds {
   static constexpr int kTileStride = kBlockTokens * D * 2 + 64;
   static constexpr int kBufs = 3;
   __attribute__((aligned(16))) char kv[kBufs * 4 * kTileStride];
   f32x4_t xs[SOLO ? 1 : 2][SOLO ? 1 : kRowGroups][2][2][kWave];
+  int f16_bad;
 };
 
 // Where a walk leaves its rows: the output itself (normalised), or, for a
@@ -265,6 +285,7 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
   // two waves share 32 rows, one half of D each (4 row groups, 128 rows).
   static_assert(SOLO || D == 256, "the paired layout serves head size 256");
   constexpr bool kSolo = SOLO;
+  constexpr bool kF16 = kSolo && PAD_PREFILL_F16_PV;
   constexpr int RG = kSolo ? 2 * kRowGroups : kRowGroups;  // 32-row groups per workgroup
   constexpr int TW = RG / HC;            // 32-token groups per workgroup
   constexpr int KS = D / 32;             // QK steps (32 dims each)
@@ -371,71 +392,14 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
   const size_t head_off = (size_t)g * kTileBytes;
   const size_t block_stride = (size_t)a.num_kv_heads * kTileBytes;
   bool bad = false;
-
-  // The first wave of pair t copies tile t of each step into LDS: K of the
-  // step's first block, K of its second, V of the first, V of the second; the
-  // second wave of each pair copies nothing.  (Measured: copies issued by four
-  // waves, one per SIMD pair, beat the same copies spread over all eight by
-  // 2.5 %; by one or two waves, they were slower.)
-  const int my_tile = kSolo ? wave & 3 : wave >> 1;  // 0, 1: K of the two blocks; 2, 3: V
-  const bool copier = kSolo ? wave < 4 : dh == 0;
-  const char* pool = (my_tile < 2) ? a.key_cache : a.value_cache;
-  const int my_b = my_tile & 1;
-  // The block table is read-only for the launch: each wave fetches the id of
-  // the block it copies next by a scalar load, one issue ahead.  (Loaded 64 at
-  // a time into a vector register instead, the id load left the loop with a
-  // wait for the whole vector-memory counter at its back edge, which drained
-  // the step's own copies: 3 to 5 % slower.)
-  const int32_t __attribute__((address_space(4)))* table_c =
-      (const int32_t __attribute__((address_space(4)))*)table_row;
-  auto fetch_id = [&](int step) {
-    const int blk = 2 * step + my_b;
-    return blk < nblk ? table_c[blk] : 0;
-  };
-  int next_id = fetch_id(lo);
-  // V tiles are stored with the two 16-byte halves of every other group of 8
-  // dims swapped (16-byte chunk c of the tile lands at c ^ ((c >> 4) & 1)), so
-  // that the V operand reads of a half-wave hit distinct banks
-  const int k_src = 16 * lane;
-  const int v_src = 16 * (lane ^ ((lane >> 4) & 1));
-  const int src_off = my_tile < 2 ? k_src : v_src;
-  auto issue = [&](int step, char* buf) {
-    const int blk = 2 * step + my_b;
-    int phys = next_id;
-    next_id = fetch_id(step + 1);
-    const bool live = blk < nblk;
-    const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
-    bad |= live && !ok;
-    const uint32_t bytes = (live && ok) ? kTileBytes : 0u;
-    if (!ok) phys = 0;
-    const uint64_t base = reinterpret_cast<uint64_t>(pool + (size_t)phys * block_stride + head_off);
-    const u32x4_t rs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base),
-                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) & 0xffffu,
-                        (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kRsrcWord3};
-    lds_char* lds = (lds_char*)(buf + my_tile * kTileStride);
-    if (copier) {
-      static_assert(CH <= 8, "at most two runs of copies per tile");
-      if constexpr (CH <= 4) {
-        lds_copy16_run<CH>(lds, src_off, rs);
-      } else {
-        lds_copy16_run<4>(lds, src_off, rs);
-        lds_copy16_run<CH - 4>(lds + 4096, src_off + 4096, rs);
-      }
-    }
-  };
-
   f32x4_t o[2][DT];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   // The reference max starts at a finite floor, not -inf: a piece of a split
   // walk that starts past key 0 can hold rows that see none of its keys, and
   // their weights exp2(-inf - ref) must come out 0, not NaN.  The first keys
   // a row sees always lift the reference (the rescale factor exp2(floor - max)
   // is then 0, as from -inf), so whole walks give the same bits either way.
-  float m_ref[2] = {kNoKeysMax, kNoKeysMax};
-  float l_run[2] = {0.0f, 0.0f};
+  float m_ref[2];
+  float l_run[2];
 
   // Tile kb of a step's S^T (16 of its 32 keys x the wave's 32 rows, over all
   // of D): the A operand comes straight from the step's K tiles in LDS
@@ -458,193 +422,376 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
       }
     }
   };
+  // V elements stored in LDS with the two 16-byte halves of every other group
+  // of 8 dims swapped (16-byte chunk c of the tile lands at c ^ ((c >> 4) & 1)),
+  // so that the V operand reads of a half-wave hit distinct banks
+  const int k_src = 16 * lane;
+  const int v_src = 16 * (lane ^ ((lane >> 4) & 1));
   constexpr int kLead = kBufs - 1;  // iteration st issues the copies of step st + kLead
-  for (int k = lo; k < lo + kLead && k < hi; ++k) {
-    issue(k, kv_lds + (k % kBufs) * kStepBytes);
-  }
-  // step 0's logits (paired waves: formed ahead, for the exchange)
-  if constexpr (!kSolo) {
-    if (hi - lo > 1)
-      __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
-    workgroup_barrier();
-    f32x4_t first[2];
-    qk_block(kv_lds + (lo % kBufs) * kStepBytes, first);
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) xs_lds[lo & 1][rg][kb][ct][lane] = first[ct];
-  }
 
-  // Iteration st: wait for the copies of step st + 1 (this wave's; the
-  // barrier makes every wave's visible, publishes every wave's logits of step
-  // st, and retires all reads of the buffer the next copies reuse); then the
-  // softmax of step st, this wave's logits of step st + 1, the copies of step
-  // st + 2 and the P.V of step st.
-  //
-  // Only the last step can hold V positions the walk does not hold (every
-  // earlier step ends at least one block before the end of the keys), so it
-  // alone runs the masked P.V, as separate code after the loop.  With the
-  // choice made per step inside the loop, the two P.V forms met at a join
-  // where the compiler kept the accumulators in two register sets and copied
-  // all of them on every step (32 64-bit moves); that also held 44 more
-  // registers at D = 256 and made the allocator spill a query operand.  Taken
-  // out of the loop: 7 % faster at D = 256, 5-7 % at D = 128.
-  auto iter = [&](int st, auto last) {
-    // paired waves need K of step st + 1 now; solo waves only step st
-    if (kSolo && st + 1 < hi)
-      __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
-    workgroup_barrier();
-    const int b0 = 2 * st;  // first block of this step
-    const char* kv = kv_lds + (st % kBufs) * kStepBytes;
-
-    // ---- logits S^T of the step: two blocks x two column tiles, one block
-    // formed by each wave of the pair
-    f32x4_t sc[2][2];
-    if constexpr (kSolo) {
-      // solo waves: kb = 0, so k_lane is tile 0's offset; tile 1's is 64 bytes on
-      qk_block(kv, sc[0]);
-      qk_block(kv + 64, sc[1]);
-    } else {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) sc[b][ct] = xs_lds[st & 1][rg][b][ct][lane];
-    }
-
-    // ---- mask, running max, weights.  Only steps that reach the wave's first
-    // row position (the diagonal) or the end of the keys need the mask.
-    const bool diag = (b0 + 2) * kBlockTokens > diag_from;
-    float x[2][2][4];
-    float bm[2];
-    // separate code for the masked steps, so the common step carries no selects
-    auto logits = [&](auto masked) {
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        bm[ct] = -INFINITY;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = sc[b][ct][i];
-            if constexpr (decltype(masked)::value) {
-              const int jpos = (b0 + (lg >> 1)) * kBlockTokens + 8 * (lg & 1) + 4 * b + i;
-              x[b][ct][i] = (jpos <= rpos[ct] && jpos < kend) ? v : -INFINITY;
-            } else {
-              x[b][ct][i] = v;
-            }
-            bm[ct] = fmaxf(bm[ct], x[b][ct][i]);
-          }
-        bm[ct] = group_max(bm[ct]);
-        // the scale is positive: the max of the scaled logits is the scaled max
-        bm[ct] = bm[ct] > -INFINITY ? bm[ct] * a.qscale : -INFINITY;
-      }
+  // One pass over steps [lo, hi).  F16 (solo layout only): P.V runs on
+  // v_mfma_f32_16x16x32_f16 with one fp16 term for p, and V is converted to
+  // fp16 in LDS once per step, instead of two bf16 products per tile (p split
+  // into hi + lo).  V is exact in fp16 where |v| <= 65504; p is computed
+  // against a reference kF16Shift below the running one, so the weights lie in
+  // [0, 2^15] and a weight below 2^-14 of the largest is all that lands in
+  // fp16's subnormal range.  A V value beyond 65504 (or an infinity) sets a
+  // flag; the pass then returns false, and the walk starts over in the bf16
+  // form.  (The flag is read once, after the last step's barrier: an exit
+  // from the step loop on it made the compiler hold about 90 more registers
+  // and spill at D = 256.)
+  auto run = [&](auto f16_tag) -> bool {
+    constexpr bool F16 = decltype(f16_tag)::value;
+    // Copies.  bf16 form: the first wave of pair t copies tile t of each step
+    // into LDS (K of the step's first block, K of its second, V of the first,
+    // V of the second); the second wave of each pair copies nothing.
+    // (Measured: copies issued by four waves, one per SIMD pair, beat the same
+    // copies spread over all eight by 2.5 %; by one or two waves, they were
+    // slower.)  F16 form: copying wave w (w < 4) takes half w & 1 of block
+    // w >> 1's K tile and of its V tile, so that each of the four converts
+    // the V it copied, on its own SIMD.
+    const int my_tile = kSolo ? wave & 3 : wave >> 1;  // bf16 form: 0, 1: K of the two blocks; 2, 3: V
+    const bool copier = kSolo ? wave < 4 : dh == 0;
+    const int my_b = F16 ? (wave >> 1) & 1 : my_tile & 1;
+    const int my_half = wave & 1;  // F16 form
+    constexpr int kHalfBytes = kTileBytes / 2;
+    const char* pool = (my_tile < 2) ? a.key_cache : a.value_cache;
+    // The block table is read-only for the launch: each wave fetches the id of
+    // the block it copies next by a scalar load, one issue ahead.  (Loaded 64
+    // at a time into a vector register instead, the id load left the loop with
+    // a wait for the whole vector-memory counter at its back edge, which
+    // drained the step's own copies: 3 to 5 % slower.)
+    const int32_t __attribute__((address_space(4)))* table_c =
+        (const int32_t __attribute__((address_space(4)))*)table_row;
+    auto fetch_id = [&](int step) {
+      const int blk = 2 * step + my_b;
+      return blk < nblk ? table_c[blk] : 0;
     };
-    if (diag)
-      logits(std::true_type{});
-    else
-      logits(std::false_type{});
-    // Lazy rescale.  Up to D = 64 it runs every step, branch-free, with a
-    // factor of 1 where the reference stays (the accumulator is 32 floats a
-    // lane there): measured 15 % faster than the branch at D = 64, and 7 to
-    // 10 % slower at D = 128 and 256, where the branch stays.
-    if constexpr (D <= 64) {
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const bool up = bm[ct] > m_ref[ct] + kLazyLog2;
-        const float m_new = up ? bm[ct] : m_ref[ct];
-        const float alpha = up ? __builtin_amdgcn_exp2f(m_ref[ct] - m_new) : 1.0f;  // 0 on a row's first keys
-        l_run[ct] *= alpha;
-        m_ref[ct] = m_new;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
-      }
-    } else if (__builtin_expect(__ballot(bm[0] > m_ref[0] + kLazyLog2 || bm[1] > m_ref[1] + kLazyLog2) != 0, 0)) {
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const float m_new = bm[ct] > m_ref[ct] + kLazyLog2 ? bm[ct] : m_ref[ct];
-        const float alpha = __builtin_amdgcn_exp2f(m_ref[ct] - m_new);  // 0 on a row's first keys
-        l_run[ct] *= alpha;
-        m_ref[ct] = m_new;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
-      }
-    }
-    // p = hi + lo in bf16: hi keeps the top 16 bits of p (truncation, so p - hi
-    // is exact), lo the top 16 bits of the remainder; packed by byte permutes
-    u32x4_t p_hi[2], p_lo[2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int b = k >> 1, i = 2 * (k & 1);
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[b][ct][i], a.qscale, -m_ref[ct]));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[b][ct][i + 1], a.qscale, -m_ref[ct]));
-        l_run[ct] += p0 + p1;
-        const uint32_t u0 = __builtin_bit_cast(uint32_t, p0), u1 = __builtin_bit_cast(uint32_t, p1);
-        const float r0 = p0 - __builtin_bit_cast(float, u0 & 0xffff0000u);
-        const float r1 = p1 - __builtin_bit_cast(float, u1 & 0xffff0000u);
-        hi[k] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-        lo[k] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, r1), __builtin_bit_cast(uint32_t, r0), 0x07060302u);
-      }
-      p_hi[ct] = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
-      p_lo[ct] = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
-    }
-
-    // ---- this wave's logits of the next step, for the pair (issued after
-    // the softmax, so that the matrix cores work through them while P.V's
-    // operands are read)
-    if (!kSolo && st + 1 < hi) {
-      f32x4_t next[2];
-      qk_block(kv_lds + ((st + 1) % kBufs) * kStepBytes, next);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) xs_lds[(st + 1) & 1][rg][kb][ct][lane] = next[ct];
-    }
-
-    // ---- the copies of step st + 2 (here, after the logits of step st + 1)
-    if (st + kLead < hi) {
-      issue(st + kLead, kv_lds + ((st + kLead) % kBufs) * kStepBytes);
-    }
-
-    // ---- O^T += V^T P^T.  V elements at positions the walk does not hold are
-    // zeroed: p is 0 there, but 0 * NaN would poison the row.
-    auto pv = [&](auto masked) {
-      uint32_t vm[4];
-      if constexpr (decltype(masked)::value) {
-        const int pos = (b0 + (lg >> 1)) * kBlockTokens + 8 * (lg & 1);
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          vm[w] = (pos + 2 * w < v_end ? 0xffffu : 0u) | (pos + 2 * w + 1 < v_end ? 0xffff0000u : 0u);
-      }
-      // dim d = 16 dt + lane%16, tokens 8 (lg & 1) .. + 8 of block lg >> 1:
-      // 16-byte chunk 2 d + (lg & 1) of that block's tile, stored swizzled
-      const char* vt = kv + (2 + (lg >> 1)) * kTileStride + 512 * DT * dh + (lane & 15) * 32 +
-                       16 * ((lg & 1) ^ ((lane >> 3) & 1));
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        u32x4_t va = *reinterpret_cast<const u32x4_t*>(vt + 512 * dt);
-        if constexpr (decltype(masked)::value) va = u32x4_t{va[0] & vm[0], va[1] & vm[1], va[2] & vm[2], va[3] & vm[3]};
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          o[ct][dt] = mfma_bf16(va, p_hi[ct], o[ct][dt]);
-          o[ct][dt] = mfma_bf16(va, p_lo[ct], o[ct][dt]);
+    int next_id = fetch_id(lo);
+    const int src_off = my_tile < 2 ? k_src : v_src;
+    auto rsrc = [&](const char* base_pool, int phys, uint32_t bytes) {
+      const uint64_t base = reinterpret_cast<uint64_t>(base_pool + (size_t)phys * block_stride + head_off);
+      return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) & 0xffffu,
+                     (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kRsrcWord3};
+    };
+    auto issue = [&](int step, char* buf) {
+      const int blk = 2 * step + my_b;
+      int phys = next_id;
+      next_id = fetch_id(step + 1);
+      const bool live = blk < nblk;
+      const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
+      bad |= live && !ok;
+      const uint32_t bytes = (live && ok) ? kTileBytes : 0u;
+      if (!ok) phys = 0;
+      if (!copier) return;
+      if constexpr (F16) {
+        const int h_off = my_half * kHalfBytes;
+        lds_copy16_run<CH / 2>((lds_char*)(buf + my_b * kTileStride + h_off), k_src + h_off,
+                               rsrc(a.key_cache, phys, bytes));
+        lds_copy16_run<CH / 2>((lds_char*)(buf + (2 + my_b) * kTileStride + h_off), v_src + h_off,
+                               rsrc(a.value_cache, phys, bytes));
+      } else {
+        const u32x4_t rs = rsrc(pool, phys, bytes);
+        lds_char* lds = (lds_char*)(buf + my_tile * kTileStride);
+        static_assert(CH <= 8, "at most two runs of copies per tile");
+        if constexpr (CH <= 4) {
+          lds_copy16_run<CH>(lds, src_off, rs);
+        } else {
+          lds_copy16_run<4>(lds, src_off, rs);
+          lds_copy16_run<CH - 4>(lds + 4096, src_off + 4096, rs);
         }
       }
     };
-    // At D = 256 solo waves issue their P.V products at raised priority, so
-    // that a wave keeps the matrix core for its whole run of 2 DT products
-    // instead of interleaving with the other waves' logits: measured 3 %
-    // faster there.  The pairs (which trade logits through LDS) and the
-    // smaller head sizes (shorter runs) lose 1 to 2 % with it.
-    constexpr bool kPvPriority = kSolo && D == 256;
-    if constexpr (kPvPriority) __builtin_amdgcn_s_setprio(1);
-    pv(last);
-    if constexpr (kPvPriority) __builtin_amdgcn_s_setprio(0);
+    // F16 form: a copying wave's conversion of the V it copied for `step`, in
+    // place.  Lane l holds 16-byte chunks 64 j + l of its half of the tile:
+    // 8 consecutive tokens of one dim, the first at 8 ((l & 1) ^ ((l >> 4) & 1))
+    // in the block (the swizzle above).  The masked form (a pass's last step)
+    // first zeroes the positions from v_end on, on the walk's last step (the
+    // tail slots of the last block, and an odd walk's second block, which was
+    // not copied).  Returns whether a value lies beyond fp16's range.
+    auto convert_v = [&](int step, char* buf, auto masked) {
+      char* vt = buf + (2 + my_b) * kTileStride + my_half * kHalfBytes + 16 * lane;
+      const int pos0 = (2 * step + my_b) * kBlockTokens + 8 * ((lane & 1) ^ ((lane >> 4) & 1));
+      const bool tail = decltype(masked)::value && step == nsteps - 1;
+      float mx = 0.0f;
+#pragma unroll
+      for (int j = 0; j < CH / 2; ++j) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(vt + 1024 * j);
+        u32x4_t r;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float v0 = __builtin_bit_cast(float, w[k] << 16);
+          float v1 = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+          if (tail) {
+            v0 = pos0 + 2 * k < v_end ? v0 : 0.0f;
+            v1 = pos0 + 2 * k + 1 < v_end ? v1 : 0.0f;
+          }
+          mx = fmaxf(mx, fmaxf(fabsf(v0), fabsf(v1)));
+          r[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{v0, v1}), f16x2_t));
+        }
+        *reinterpret_cast<u32x4_t*>(vt + 1024 * j) = r;
+      }
+      return !(mx <= 65504.0f);
+    };
+
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m_ref[0] = m_ref[1] = kNoKeysMax;
+    l_run[0] = l_run[1] = 0.0f;
+    bad = false;
+    if constexpr (F16) {
+      // the range flag starts clear before any wave can set it
+      if (threadIdx.x == 0) L.f16_bad = 0;
+      __syncthreads();
+    }
+    for (int k = lo; k < lo + kLead && k < hi; ++k) {
+      issue(k, kv_lds + (k % kBufs) * kStepBytes);
+    }
+    // F16: V of step lo (the last step's is converted in its own iteration)
+    if (F16 && copier && lo + 1 < hi) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
+      if (convert_v(lo, kv_lds + (lo % kBufs) * kStepBytes, std::false_type{})) L.f16_bad = 1;
+    }
+    // step 0's logits (paired waves: formed ahead, for the exchange)
+    if constexpr (!kSolo) {
+      if (hi - lo > 1)
+        __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
+      workgroup_barrier();
+      f32x4_t first[2];
+      qk_block(kv_lds + (lo % kBufs) * kStepBytes, first);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) xs_lds[lo & 1][rg][kb][ct][lane] = first[ct];
+    }
+
+    // Iteration st: wait for the copies of step st + 1 (this wave's; the
+    // barrier makes every wave's visible, publishes every wave's logits of step
+    // st, and retires all reads of the buffer the next copies reuse); then the
+    // softmax of step st, this wave's logits of step st + 1, the copies of step
+    // st + 2 and the P.V of step st.
+    //
+    // Only the last step can hold V positions the walk does not hold (every
+    // earlier step ends at least one block before the end of the keys), so it
+    // alone runs the masked P.V, as separate code after the loop.  With the
+    // choice made per step inside the loop, the two P.V forms met at a join
+    // where the compiler kept the accumulators in two register sets and copied
+    // all of them on every step (32 64-bit moves); that also held 44 more
+    // registers at D = 256 and made the allocator spill a query operand.  Taken
+    // out of the loop: 7 % faster at D = 256, 5-7 % at D = 128.
+    auto iter = [&](int st, auto last) {
+      // paired waves need K of step st + 1 now; solo waves only step st
+      if (kSolo && st + 1 < hi)
+        __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
+      workgroup_barrier();
+      const int b0 = 2 * st;  // first block of this step
+      const char* kv = kv_lds + (st % kBufs) * kStepBytes;
+      // F16: the pass's last step converts its own V here (the masked form),
+      // published by a barrier before its P.V: kept out of the loop, the
+      // masking code made the compiler spill at D = 256
+      if constexpr (F16 && decltype(last)::value)
+        if (copier && convert_v(st, kv_lds + (st % kBufs) * kStepBytes, std::true_type{})) L.f16_bad = 1;
+
+      // ---- logits S^T of the step: two blocks x two column tiles, one block
+      // formed by each wave of the pair
+      f32x4_t sc[2][2];
+      if constexpr (kSolo) {
+        // solo waves: kb = 0, so k_lane is tile 0's offset; tile 1's is 64 bytes on
+        qk_block(kv, sc[0]);
+        qk_block(kv + 64, sc[1]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) sc[b][ct] = xs_lds[st & 1][rg][b][ct][lane];
+      }
+
+      // ---- mask, running max, weights.  Only steps that reach the wave's first
+      // row position (the diagonal) or the end of the keys need the mask.
+      const bool diag = (b0 + 2) * kBlockTokens > diag_from;
+      float x[2][2][4];
+      float bm[2];
+      // separate code for the masked steps, so the common step carries no selects
+      auto logits = [&](auto masked) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          bm[ct] = -INFINITY;
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float v = sc[b][ct][i];
+              if constexpr (decltype(masked)::value) {
+                const int jpos = (b0 + (lg >> 1)) * kBlockTokens + 8 * (lg & 1) + 4 * b + i;
+                x[b][ct][i] = (jpos <= rpos[ct] && jpos < kend) ? v : -INFINITY;
+              } else {
+                x[b][ct][i] = v;
+              }
+              bm[ct] = fmaxf(bm[ct], x[b][ct][i]);
+            }
+          bm[ct] = group_max(bm[ct]);
+          // the scale is positive: the max of the scaled logits is the scaled max
+          bm[ct] = bm[ct] > -INFINITY ? bm[ct] * a.qscale : -INFINITY;
+        }
+      };
+      if (diag)
+        logits(std::true_type{});
+      else
+        logits(std::false_type{});
+      // Lazy rescale.  Up to D = 64 it runs every step, branch-free, with a
+      // factor of 1 where the reference stays (the accumulator is 32 floats a
+      // lane there): measured 15 % faster than the branch at D = 64, and 7 to
+      // 10 % slower at D = 128 and 256, where the branch stays.
+      if constexpr (D <= 64) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const bool up = bm[ct] > m_ref[ct] + kLazyLog2;
+          const float m_new = up ? bm[ct] : m_ref[ct];
+          const float alpha = up ? __builtin_amdgcn_exp2f(m_ref[ct] - m_new) : 1.0f;  // 0 on a row's first keys
+          l_run[ct] *= alpha;
+          m_ref[ct] = m_new;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
+        }
+      } else if (__builtin_expect(__ballot(bm[0] > m_ref[0] + kLazyLog2 || bm[1] > m_ref[1] + kLazyLog2) != 0, 0)) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const float m_new = bm[ct] > m_ref[ct] + kLazyLog2 ? bm[ct] : m_ref[ct];
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[ct] - m_new);  // 0 on a row's first keys
+          l_run[ct] *= alpha;
+          m_ref[ct] = m_new;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
+        }
+      }
+      // The weights.  bf16 form: p = hi + lo, hi keeping the top 16 bits of p
+      // (truncation, so p - hi is exact), lo the top 16 bits of the remainder;
+      // packed by byte permutes.  F16 form: p rounded to fp16 (nearest even),
+      // against the reference less kF16Shift.
+      u32x4_t p_hi[2], p_lo[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const float m_sub = F16 ? m_ref[ct] - kF16Shift : m_ref[ct];
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int b = k >> 1, i = 2 * (k & 1);
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[b][ct][i], a.qscale, -m_sub));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[b][ct][i + 1], a.qscale, -m_sub));
+          l_run[ct] += p0 + p1;
+          if constexpr (F16) {
+            hi[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{p0, p1}), f16x2_t));
+          } else {
+            const uint32_t u0 = __builtin_bit_cast(uint32_t, p0), u1 = __builtin_bit_cast(uint32_t, p1);
+            const float r0 = p0 - __builtin_bit_cast(float, u0 & 0xffff0000u);
+            const float r1 = p1 - __builtin_bit_cast(float, u1 & 0xffff0000u);
+            hi[k] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+            lo[k] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, r1), __builtin_bit_cast(uint32_t, r0),
+                                          0x07060302u);
+          }
+        }
+        p_hi[ct] = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (!F16) p_lo[ct] = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+      }
+
+      // ---- this wave's logits of the next step, for the pair (issued after
+      // the softmax, so that the matrix cores work through them while P.V's
+      // operands are read)
+      if (!kSolo && st + 1 < hi) {
+        f32x4_t next[2];
+        qk_block(kv_lds + ((st + 1) % kBufs) * kStepBytes, next);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) xs_lds[(st + 1) & 1][rg][kb][ct][lane] = next[ct];
+      }
+
+      // ---- the copies of step st + 2 (here, after the logits of step st + 1)
+      if (st + kLead < hi) {
+        issue(st + kLead, kv_lds + ((st + kLead) % kBufs) * kStepBytes);
+      }
+
+      // ---- O^T += V^T P^T.  V elements at positions the walk does not hold are
+      // zeroed: p is 0 there, but 0 * NaN would poison the row (the F16 form
+      // zeroed them in its conversion).
+      auto pv = [&](auto masked) {
+        uint32_t vm[4];
+        if constexpr (decltype(masked)::value) {
+          const int pos = (b0 + (lg >> 1)) * kBlockTokens + 8 * (lg & 1);
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            vm[w] = (pos + 2 * w < v_end ? 0xffffu : 0u) | (pos + 2 * w + 1 < v_end ? 0xffff0000u : 0u);
+        }
+        // dim d = 16 dt + lane%16, tokens 8 (lg & 1) .. + 8 of block lg >> 1:
+        // 16-byte chunk 2 d + (lg & 1) of that block's tile, stored swizzled
+        const char* vt = kv + (2 + (lg >> 1)) * kTileStride + 512 * DT * dh + (lane & 15) * 32 +
+                         16 * ((lg & 1) ^ ((lane >> 3) & 1));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          u32x4_t va = *reinterpret_cast<const u32x4_t*>(vt + 512 * dt);
+          if constexpr (decltype(masked)::value)
+            va = u32x4_t{va[0] & vm[0], va[1] & vm[1], va[2] & vm[2], va[3] & vm[3]};
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            if constexpr (F16) {
+              o[ct][dt] = mfma_f16(va, p_hi[ct], o[ct][dt]);
+            } else {
+              o[ct][dt] = mfma_bf16(va, p_hi[ct], o[ct][dt]);
+              o[ct][dt] = mfma_bf16(va, p_lo[ct], o[ct][dt]);
+            }
+          }
+        }
+      };
+      // In the bf16 form at D = 256 solo waves issue their P.V products at
+      // raised priority, so that a wave keeps the matrix core for its whole
+      // run of 2 DT products instead of interleaving with the other waves'
+      // logits: measured 3 % faster there.  The pairs (which trade logits
+      // through LDS) and the smaller head sizes (shorter runs) lose 1 to 2 %
+      // with it, and so does the F16 form, whose run is half as long (0.6 %).
+      constexpr bool kPvPriority = kSolo && D == 256 && !F16;
+      if constexpr (F16 && decltype(last)::value) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
+        workgroup_barrier();
+      }
+      if constexpr (kPvPriority) __builtin_amdgcn_s_setprio(1);
+      if constexpr (F16)
+        pv(std::false_type{});
+      else
+        pv(last);
+      if constexpr (kPvPriority) __builtin_amdgcn_s_setprio(0);
+
+      if constexpr (F16) {
+        // the conversion of step st + 1's V, once this wave's copies of it are
+        // in (those of step st + 2 may still be in flight).  The compiler
+        // barrier keeps its LDS reads out of the P.V above, where they held
+        // enough registers to spill at D = 256.
+        asm volatile("" ::: "memory");
+        if (copier && st + 2 < hi) {
+          __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
+          if (convert_v(st + 1, kv_lds + ((st + 1) % kBufs) * kStepBytes, std::false_type{})) L.f16_bad = 1;
+        }
+      }
+    };
+    for (int st = lo; st + 1 < hi; ++st) iter(st, std::false_type{});
+    if (hi > lo) iter(hi - 1, std::true_type{});
+    // F16: every conversion came before the last step's P.V barrier, so
+    // every wave reads the same flag here
+    return F16 ? __builtin_amdgcn_readfirstlane(L.f16_bad) == 0 : true;
   };
-  for (int st = lo; st + 1 < hi; ++st) iter(st, std::false_type{});
-  if (hi > lo) iter(hi - 1, std::true_type{});
+  bool done = false;
+  if constexpr (kF16) done = run(std::true_type{});
+  if (!done) {
+    if constexpr (kF16) {
+      // the F16 pass stopped: every wave's copies landed and every LDS read
+      // retired before the ring is reused
+      __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
+      workgroup_barrier();
+    }
+    run(std::false_type{});
+  }
   // every wave's block-id checks count for the whole workgroup's tiles (and
   // the barrier retires every LDS read before a next walk's copies)
   bad = __syncthreads_or(bad);
@@ -653,7 +800,8 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
   for (int ct = 0; ct < 2; ++ct) l[ct] = group_sum(l_run[ct]);
   if (dst.part) {
     // a piece of a split walk: unnormalised rows, and each row's reference
-    // max (log2 units of the scaled logits) and sum; NaN sums mark a bad block id
+    // max (log2 units of the scaled logits; that of the weights, so the F16
+    // pass's less kF16Shift) and sum; NaN sums mark a bad block id
     float* po = dst.part + (size_t)wave * (2 * DT * kWave * 4);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
@@ -664,7 +812,7 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         float* ps = dst.stats + ((rg * 2 + ct) * 16 + lane) * 2;
-        ps[0] = m_ref[ct];
+        ps[0] = done ? m_ref[ct] - kF16Shift : m_ref[ct];
         ps[1] = bad ? NAN : l[ct];
       }
     }

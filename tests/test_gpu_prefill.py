@@ -278,27 +278,83 @@ def test_prefill_batch_above_the_ordering_cap():
     assert max_err(dp.run(), dp.oracle()) <= TOL["bf16"]
 
 
-def test_prefill_layouts_agree_bitwise():
+def _run_mql(dp, mql, vc=None):
+    pp = dp.pp
+    out = torch.full(tuple(pp.query.shape), float("nan"), dtype=torch.float32, device="cuda")
+    pad.paged_attention_prefill(out, dp.query, dp.dp.kc, dp.dp.vc if vc is None else vc, dp.dp.tables, dp.qs, dp.ctx,
+                                pp.scale, pp.spec.num_kv_heads, 16, mql)
+    torch.cuda.synchronize()
+    return out
+
+
+_LAYOUT_SPEC = gen.PrefillSpec("layouts", context_lens=(1000, 0, 37), query_lens=(700, 129, 300), num_heads=24,
+                               num_kv_heads=4, head_size=256, dtype="bf16", seed=24)
+_PAIRED_MQL, _SOLO_MQL = 700, 8192
+
+
+def test_prefill_layouts_agree():
     """Head size 256 has two layouts: paired (two waves share 32 rows, 128 rows
     per workgroup) and solo (a wave owns 32 rows over all of D, 256 rows).  The
     launcher picks by the longest chunk's workgroup count: with 24 / 4 heads a
     max_query_len of 700 gives 132 paired or 72 solo workgroups (one round of
     256 compute units either way: paired), 8192 gives 1536 or 768 (6 rounds
-    against 3: solo).  Every output element sees the same matrix-core sequence
-    in both, so one batch run with either bound gives the same bits."""
-    spec = gen.PrefillSpec("layouts", context_lens=(1000, 0, 37), query_lens=(700, 129, 300), num_heads=24,
-                           num_kv_heads=4, head_size=256, dtype="bf16", seed=24)
-    pp = gen.make_prefill_problem(spec)
+    against 3: solo).  Solo multiplies P.V with one fp16 weight, paired with
+    the bf16 hi + lo pair: both within the tolerance of the oracle."""
+    pp = gen.make_prefill_problem(_LAYOUT_SPEC)
     dp = DevicePrefill(pp)
-    outs = []
-    for mql in (700, 8192):
-        out = torch.full(tuple(pp.query.shape), float("nan"), dtype=torch.float32, device="cuda")
-        pad.paged_attention_prefill(out, dp.query, dp.dp.kc, dp.dp.vc, dp.dp.tables, dp.qs, dp.ctx, pp.scale,
-                                    spec.num_kv_heads, 16, mql)
-        torch.cuda.synchronize()
-        outs.append(out)
-    assert torch.equal(outs[0], outs[1])
-    assert max_err(outs[1], dp.oracle()) <= TOL["bf16"]
+    want = dp.oracle()
+    paired, solo = _run_mql(dp, _PAIRED_MQL), _run_mql(dp, _SOLO_MQL)
+    assert max_err(paired, want) <= TOL["bf16"]
+    assert max_err(solo, want) <= TOL["bf16"]
+
+
+def test_prefill_v_beyond_fp16_range_falls_back():
+    """A V value beyond fp16's range (1e6, at sequence 1's last chunk position,
+    which only that sequence's last row sees) makes the solo walk over it
+    start over in the bf16 form: that row equals the paired layout's (bf16
+    throughout) bit for bit, within the bf16 form's relative precision of the
+    oracle, and every other row stays within the tolerance."""
+    pp = gen.make_prefill_problem(_LAYOUT_SPEC)
+    dp = DevicePrefill(pp)
+    s, g, d = 1, 1, 5
+    pos = int(pp.context_lens[s] + pp.query_lens[s] - 1)
+    blk, t = int(pp.pool.block_tables[s, pos // 16]), pos % 16
+    big = torch.tensor(1e6, dtype=torch.bfloat16)
+    dp.dp.vc[blk, g, d, t] = big.cuda()  # tiled V: [blocks, KV heads, D, 16]
+    dp.dp.vc_host[blk, g, t, d] = big.view(torch.int16).numpy().astype(np.uint16)
+    torch.cuda.synchronize()
+    want = dp.oracle()
+    paired, solo = _run_mql(dp, _PAIRED_MQL), _run_mql(dp, _SOLO_MQL)
+    group = pp.spec.num_heads // pp.spec.num_kv_heads
+    row, heads = int(pp.query_start[s + 1]) - 1, slice(g * group, (g + 1) * group)
+    assert torch.equal(solo[row, heads], paired[row, heads])
+    w = want[row, heads]
+    got = solo[row, heads].double().cpu().numpy()
+    assert np.max(np.abs(w)) > 100.0  # the outlier carries the row
+    assert np.all(np.abs(got - w) <= TOL["bf16"] + 1e-4 * np.abs(w))
+    keep = np.ones(want.shape[:2], dtype=bool)
+    keep[row, heads] = False
+    for out in (solo, paired):
+        g_ = out.double().cpu().numpy()
+        assert np.all(np.isfinite(g_))
+        assert np.max(np.abs(g_ - want)[keep]) <= TOL["bf16"]
+
+
+def test_prefill_tail_slots_do_not_reach_rows():
+    """The cache slots past each sequence's last token (the tail of its last
+    block) hold 1e30 instead of NaN: the solo walk zeroes them before its
+    range check and P.V, so the rows keep their bits (an fp16 range failure
+    there would have sent the walk to the bf16 form, with other bits)."""
+    pp = gen.make_prefill_problem(_LAYOUT_SPEC)
+    dp = DevicePrefill(pp, keep_host=False)
+    base = _run_mql(dp, _SOLO_MQL)
+    vc = dp.dp.vc.clone()
+    for s in range(pp.num_seqs):
+        end = int(pp.context_lens[s] + pp.query_lens[s])
+        for pos in range(end, -(-end // 16) * 16):
+            vc[int(pp.pool.block_tables[s, pos // 16]), :, :, pos % 16] = 1e30
+    got = _run_mql(dp, _SOLO_MQL, vc=vc)
+    assert torch.equal(got, base)
 
 
 def test_prefill_block_outside_pool_gives_nan_rows():

@@ -254,7 +254,9 @@ def test_split_plan_matches_model(name):
                          ids=lambda v: str(v))
 def test_split_without_cuts_gives_the_plain_bits(H, Hkv, D, ctx, qn):
     """Walks the split launch does not cut run the plain launch's walk code over
-    the same steps: the same bits (the plan cuts nothing here; its header says so)."""
+    the same steps: the same bits (the plan cuts nothing here; its header says
+    so).  The split launch always takes the solo layout; a max_query_len of
+    8192 makes the plain launch take it at head size 256 too."""
     spec = gen.PrefillSpec("nocut", context_lens=ctx, query_lens=qn, num_heads=H, num_kv_heads=Hkv, head_size=D,
                            dtype="bf16", seed=64)
     pp = gen.make_prefill_problem(spec)
@@ -262,4 +264,8 @@ def test_split_without_cuts_gives_the_plain_bits(H, Hkv, D, ctx, qn):
     ws = pad.alloc_prefill_split_workspace(pp.num_seqs, H, Hkv, D, pp.max_query_len, dp.dp.tables.shape[1])
     got = run_split(dp, ws=ws)
     assert int(ws[4:8].cpu().numpy().view(np.int32)[0]) == 0  # pieces listed
-    assert torch.equal(got, dp.run())
+    plain = torch.full(tuple(pp.query.shape), float("nan"), dtype=torch.float32, device="cuda")
+    pad.paged_attention_prefill(plain, dp.query, dp.dp.kc, dp.dp.vc, dp.dp.tables, dp.qs, dp.ctx, pp.scale, Hkv, 16,
+                                8192)
+    torch.cuda.synchronize()
+    assert torch.equal(got, plain)
