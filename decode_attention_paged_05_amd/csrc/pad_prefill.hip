@@ -86,6 +86,7 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
 
 constexpr int kWave = 64;
 constexpr int kWaves = 8;          // waves per workgroup: 4 row groups x 2 halves of D
@@ -161,6 +162,22 @@ __device__ inline void lds_copy16_run(lds_char* lds, int voffset, u32x4_t rsrc) 
 // the copies in flight); the "memory" clobber keeps the compiler from moving
 // LDS accesses across it.  Callers wait for their own copies and LDS reads first.
 __device__ inline void workgroup_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// max over the four lane groups of a row, as group_max, with v_max_f32 as
+// written: the compiler's fmaxf first quiets signalling NaNs of operands it
+// cannot prove quiet (two more instructions per swap), and these come out of
+// the matrix cores and the lane swaps
+__device__ inline float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ inline float group_max_raw(float v) {
+  float a, b;
+  swap16(v, a, b);
+  swap32(vmax(a, b), a, b);
+  return vmax(a, b);
+}
 
 __device__ inline void* uniform_ptr(const void* ptr) {
   const uint64_t a = reinterpret_cast<uint64_t>(ptr);
@@ -510,29 +527,34 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
     // first zeroes the positions from v_end on, on the walk's last step (the
     // tail slots of the last block, and an odd walk's second block, which was
     // not copied).  Returns whether a value lies beyond fp16's range.
+    // The range check runs on the bf16 bits, two at a time: a magnitude of
+    // 0x4780 (65536) or more is beyond fp16's largest value (the bf16 below it
+    // is 65280), and infinities and NaNs lie above it too.  (As float maxima
+    // it cost two more instructions a pair, which the compiler added to quiet
+    // signalling NaNs; this form and the lane-group max without them measured
+    // 2.5 % faster at D = 256.)
     auto convert_v = [&](int step, char* buf, auto masked) {
       char* vt = buf + (2 + my_b) * kTileStride + my_half * kHalfBytes + 16 * lane;
       const int pos0 = (2 * step + my_b) * kBlockTokens + 8 * ((lane & 1) ^ ((lane >> 4) & 1));
       const bool tail = decltype(masked)::value && step == nsteps - 1;
-      float mx = 0.0f;
+      u16x2_t mx = {0, 0};
 #pragma unroll
       for (int j = 0; j < CH / 2; ++j) {
         const u32x4_t w = *reinterpret_cast<const u32x4_t*>(vt + 1024 * j);
         u32x4_t r;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          float v0 = __builtin_bit_cast(float, w[k] << 16);
-          float v1 = __builtin_bit_cast(float, w[k] & 0xffff0000u);
-          if (tail) {
-            v0 = pos0 + 2 * k < v_end ? v0 : 0.0f;
-            v1 = pos0 + 2 * k + 1 < v_end ? v1 : 0.0f;
-          }
-          mx = fmaxf(mx, fmaxf(fabsf(v0), fabsf(v1)));
+          uint32_t u = w[k];
+          if (tail)
+            u &= (pos0 + 2 * k < v_end ? 0xffffu : 0u) | (pos0 + 2 * k + 1 < v_end ? 0xffff0000u : 0u);
+          mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, u & 0x7fff7fffu));
+          const float v0 = __builtin_bit_cast(float, u << 16);
+          const float v1 = __builtin_bit_cast(float, u & 0xffff0000u);
           r[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{v0, v1}), f16x2_t));
         }
         *reinterpret_cast<u32x4_t*>(vt + 1024 * j) = r;
       }
-      return !(mx <= 65504.0f);
+      return mx[0] >= 0x4780u || mx[1] >= 0x4780u;
     };
 
 #pragma unroll
@@ -634,7 +656,7 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
               }
               bm[ct] = fmaxf(bm[ct], x[b][ct][i]);
             }
-          bm[ct] = group_max(bm[ct]);
+          bm[ct] = group_max_raw(bm[ct]);
           // the scale is positive: the max of the scaled logits is the scaled max
           bm[ct] = bm[ct] > -INFINITY ? bm[ct] * a.qscale : -INFINITY;
         }
@@ -767,13 +789,16 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
         // the conversion of step st + 1's V, once this wave's copies of it are
         // in (those of step st + 2 may still be in flight).  The compiler
         // barrier keeps its LDS reads out of the P.V above, where they held
-        // enough registers to spill at D = 256.
+        // enough registers to spill at D = 256.  (Placed before the P.V
+        // instead, so that the other wave of the SIMD would multiply
+        // meanwhile, the kernel measured 3 % slower.)
         asm volatile("" ::: "memory");
         if (copier && st + 2 < hi) {
           __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
           if (convert_v(st + 1, kv_lds + ((st + 1) % kBufs) * kStepBytes, std::false_type{})) L.f16_bad = 1;
         }
       }
+
     };
     for (int st = lo; st + 1 < hi; ++st) iter(st, std::false_type{});
     if (hi > lo) iter(hi - 1, std::true_type{});
