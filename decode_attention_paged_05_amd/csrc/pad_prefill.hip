@@ -51,7 +51,7 @@
 //     came out in).  p is split into bf16 hi + lo (two MFMAs), ~2^-16
 //     relative precision.  Lane l holds output dims of row l%16, so the
 //     softmax state and the rescale stay in the lane.
-// The solo layout multiplies P.V in fp16 instead (one MFMA, v_mfma_f32_16x16x32_f16):
+// Both layouts multiply P.V in fp16 instead (one MFMA, v_mfma_f32_16x16x32_f16):
 // p rounded to fp16, V converted to fp16 in LDS once per step by the waves
 // that copied it; a V value beyond fp16's range sends the walk to the bf16
 // form above (walk_rows has the details).
@@ -96,7 +96,7 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.0f;  // headroom of the lazy softmax reference
 constexpr float kNoKeysMax = -1e30f;  // reference max of a row that has seen no key
-// fp16 P.V in the solo layout (1), or the bf16 hi + lo pair everywhere (0)
+// fp16 P.V with a bf16 fallback (1), or the bf16 hi + lo pair only (0)
 #ifndef PAD_PREFILL_F16_PV
 #define PAD_PREFILL_F16_PV 1
 #endif
@@ -267,7 +267,7 @@ __device__ inline int sequence_of_rank(const PrefillArgs& a, int nseq, int z, in
 
 // LDS of a walk: the ring of K/V step buffers, the logits a paired wave
 // leaves for its partner ([step parity][row group][block][column tile][lane]),
-// and the fp16 range flag of the solo layout's F16 pass.
+// and the fp16 range flag of the F16 pass.
 template <int D, bool SOLO>
 struct WalkLds {
   static constexpr int kTileStride = kBlockTokens * D * 2 + 64;
@@ -302,7 +302,7 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
   // two waves share 32 rows, one half of D each (4 row groups, 128 rows).
   static_assert(SOLO || D == 256, "the paired layout serves head size 256");
   constexpr bool kSolo = SOLO;
-  constexpr bool kF16 = kSolo && PAD_PREFILL_F16_PV;
+  constexpr bool kF16 = PAD_PREFILL_F16_PV;
   constexpr int RG = kSolo ? 2 * kRowGroups : kRowGroups;  // 32-row groups per workgroup
   constexpr int TW = RG / HC;            // 32-token groups per workgroup
   constexpr int KS = D / 32;             // QK steps (32 dims each)
@@ -446,7 +446,7 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
   const int v_src = 16 * (lane ^ ((lane >> 4) & 1));
   constexpr int kLead = kBufs - 1;  // iteration st issues the copies of step st + kLead
 
-  // One pass over steps [lo, hi).  F16 (solo layout only): P.V runs on
+  // One pass over steps [lo, hi).  F16: P.V runs on
   // v_mfma_f32_16x16x32_f16 with one fp16 term for p, and V is converted to
   // fp16 in LDS once per step, instead of two bf16 products per tile (p split
   // into hi + lo).  V is exact in fp16 where |v| <= 65504; p is computed
@@ -464,11 +464,11 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
     // V of the second); the second wave of each pair copies nothing.
     // (Measured: copies issued by four waves, one per SIMD pair, beat the same
     // copies spread over all eight by 2.5 %; by one or two waves, they were
-    // slower.)  F16 form: copying wave w (w < 4) takes half w & 1 of block
-    // w >> 1's K tile and of its V tile, so that each of the four converts
-    // the V it copied, on its own SIMD.
+    // slower.)  F16 form (both layouts): copying wave w (w < 4) takes half
+    // w & 1 of block w >> 1's K tile and of its V tile, so that each of the
+    // four converts the V it copied, on its own SIMD.
     const int my_tile = kSolo ? wave & 3 : wave >> 1;  // bf16 form: 0, 1: K of the two blocks; 2, 3: V
-    const bool copier = kSolo ? wave < 4 : dh == 0;
+    const bool copier = (kSolo || F16) ? wave < 4 : dh == 0;
     const int my_b = F16 ? (wave >> 1) & 1 : my_tile & 1;
     const int my_half = wave & 1;  // F16 form
     constexpr int kHalfBytes = kTileBytes / 2;
@@ -1355,18 +1355,19 @@ hipError_t launch_prefill_d(const PrefillArgs& a, int hc, dim3 grid, hipStream_t
 int tokens_per_wg(int hc, bool solo) { return kRowsPerWave * (solo ? 2 * kRowGroups : kRowGroups) / hc; }
 
 // Whether head size 256 runs the solo layout.  Solo serves 256 rows per
-// workgroup and measured 1.18 times the paired layout's rate (8192 new tokens
-// over 32768, 24 query / 4 KV heads: 863 against 729 TFLOP/s), but its
-// workgroups are twice as large, so fewer of them share the longest chunk:
-// on a 4-sequence batch whose longest chunk gave 288 solo workgroups (one
-// round of 256 and a tail of 32) it ran 533 against 608 TFLOP/s.  Rule:
-// solo unless rounding the longest chunk's workgroups up to whole rounds of
-// the compute units costs more than the rate gains.
+// workgroup and measured 1.42 times the paired layout's rate (8192 new tokens
+// over 32768, 24 query / 4 KV heads: 1090 against 770 TFLOP/s, both with fp16
+// P.V), but its workgroups are twice as large, so fewer of them share the
+// longest chunk.  Rule: solo unless rounding the longest chunk's workgroups
+// up to whole rounds of the compute units costs more than the rate gains.
+// On a 4-sequence batch whose longest chunk gives 288 solo workgroups (two
+// rounds of 256) against 576 paired ones (three), solo measured 691 to 699
+// against 649 TFLOP/s; paired stays where its whole grid fits one round.
 bool solo_at_256(int max_query_len, int hc, int y, int cus) {
   const int64_t np = (int64_t)((max_query_len + tokens_per_wg(hc, false) - 1) / tokens_per_wg(hc, false)) * y;
   const int64_t ns = (int64_t)((max_query_len + tokens_per_wg(hc, true) - 1) / tokens_per_wg(hc, true)) * y;
   const int64_t rp = (np + cus - 1) / cus, rs = (ns + cus - 1) / cus;
-  return rs * 2 * 100 <= rp * 118;
+  return rs * 2 * 100 <= rp * 142;
 }
 
 }  // namespace

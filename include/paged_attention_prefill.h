@@ -95,13 +95,11 @@ typedef struct pad_prefill_dims {
  *   block_size     tokens per block; must be 16
  * Supported: bf16 query and cache in the PAD_KV_TILED layout (else
  * PAD_ERR_UNSUPPORTED).  Sequences with n_s == 0 produce no rows.
- * Accumulation is fp32.  Where the launch takes the solo layout (every head
- * size; at 256 unless the longest chunk would leave the compute units a long
- * tail), the attention weights enter the P.V product as one fp16 value each
- * (relative rounding at most 2^-11; V is exact in fp16); a walk whose keys
- * hold a V value beyond fp16's range (|v| > 65504, or infinite) is computed
- * again with each weight as a bf16 hi + lo pair (about 2^-16), which the
- * paired layout always uses.  The products are exact and accumulate in
+ * Accumulation is fp32.  The attention weights enter the P.V product as one
+ * fp16 value each (relative rounding at most 2^-11; V is exact in fp16); a
+ * walk whose keys hold a V value beyond fp16's range (|v| > 65504, or
+ * infinite, or NaN) is computed again with each weight as a bf16 hi + lo pair
+ * (about 2^-16 relative).  The products are exact and accumulate in
  * fp32; the fp16 weights' rounding bounds the error by 2^-11 max |v| where
  * every rounding points one way.  Measured maximum error against an fp64
  * reference (bf16 normal inputs): 4.0e-4 over walks of at most 328 keys,
