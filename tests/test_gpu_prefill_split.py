@@ -64,6 +64,35 @@ def test_split_cuts_walks_into_many_pieces(ctx, qn):
     assert max_err(run_split(dp), dp.oracle()) <= TOL["bf16"]
 
 
+def test_split_pieces_mix_fp16_and_fallback():
+    """A V value beyond fp16's range (1e6) in the middle of a 70 000-token
+    context: the plan cuts each walk into pieces, the pieces holding the
+    outlier fall back to the bf16 form and record their own reference, the
+    others stay in fp16 and record theirs 2^7 lower, and the merge combines
+    both kinds.  Every row attends to the outlier: each is within the
+    tolerance of the oracle plus the bf16 form's relative precision."""
+    spec = gen.PrefillSpec("mix", context_lens=(70000,), query_lens=(64,), num_heads=8, num_kv_heads=2,
+                           head_size=128, dtype="bf16", seed=71)
+    pp = gen.make_prefill_problem(spec)
+    dp = DevicePrefill(pp)
+    g, d, pos = 1, 9, 35000
+    blk, t = int(pp.pool.block_tables[0, pos // 16]), pos % 16
+    big = torch.tensor(1e6, dtype=torch.bfloat16)
+    dp.dp.vc[blk, g, d, t] = big.cuda()  # tiled V: [blocks, KV heads, D, 16]
+    dp.dp.vc_host[blk, g, t, d] = big.view(torch.int16).numpy().astype(np.uint16)
+    torch.cuda.synchronize()
+    ws = pad.alloc_prefill_split_workspace(pp.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_size,
+                                           pp.max_query_len, dp.dp.tables.shape[1])
+    got = run_split(dp, ws=ws)
+    assert int(ws[4:8].cpu().numpy().view(np.int32)[0]) > 0  # pieces listed
+    want = dp.oracle()
+    g_ = got.double().cpu().numpy()
+    assert np.all(np.isfinite(g_))
+    group = spec.num_heads // spec.num_kv_heads
+    assert np.max(np.abs(want[:, g * group:(g + 1) * group, d])) > 1.0  # the outlier shows in every such row
+    assert np.all(np.abs(g_ - want) <= TOL["bf16"] + 1e-4 * np.abs(want))
+
+
 def test_split_sequences_without_work():
     """Empty chunks around the ones with work: their (no) rows, and the others exact."""
     spec = gen.PrefillSpec("empty", context_lens=(100, 0, 5000, 7, 0), query_lens=(0, 0, 129, 0, 33), num_heads=8,
