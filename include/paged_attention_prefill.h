@@ -3,9 +3,10 @@
  * (chunked prefill) attention, the step on the other side of decode.
  *
  * Operation (first page, prefill note; second page, the prefix-attention
- * allocator-reuse message and the "pre-gather all context K/V" rewrite): a
- * sequence s already holds context_lens[s] tokens in the paged KV cache and
- * receives a chunk of n_s = query_start[s+1] - query_start[s] new tokens.
+ * allocator-reuse message and the rewrite that gathers the whole context's
+ * K/V before attending): a sequence s already holds context_lens[s] tokens in
+ * the paged KV cache and receives a chunk of n_s = query_start[s+1] -
+ * query_start[s] new tokens.
  * Chunk token i sits at absolute position p = context_lens[s] + i and takes
  * softmax attention over the sequence's positions 0 .. p:
  *

@@ -6,11 +6,11 @@ no code with the GPU library and imports nothing from it.
 
 What it computes.  The first page's prefill note (the path that replaced the
 Triton context-attention kernel) and the second page's prefix-attention
-messages (the allocator-reuse message and the "pre-gather all context K/V"
-rewrite) describe prefill for a sequence that already holds ``ctx`` tokens in
-the paged cache and receives a chunk of ``n`` new tokens: every new token
-attends to all cached context tokens and, causally, to the chunk's tokens up
-to and including itself.  The pages compute it as a K-tiled online softmax in
+messages (the allocator-reuse message and the rewrite that gathers the whole
+context's K/V before attending) describe prefill for a sequence that already
+holds ``ctx`` tokens in the paged cache and receives a chunk of ``n`` new
+tokens: every new token attends to all cached context tokens and, causally,
+to the chunk's tokens up to and including itself.  The pages compute it as a K-tiled online softmax in
 two phases, context tiles first (keys gathered from the cache through the
 block table once), then the chunk's own tiles under the causal mask.
 
