@@ -251,7 +251,8 @@ def run_prefill(args) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": desc, "num_tokens": pp.num_tokens, "algorithmic_flops_per_step": flops,
-                   "accumulate": "fp32", "seed": spec.seed, "form": form},
+                   "accumulate": "fp32", "products": "QK^T bf16 x bf16, P.V fp16 x fp16 (bf16 hi + lo pair where a "
+                   "V value exceeds fp16's range)", "seed": spec.seed, "form": form},
         "kernels_ms": {"prefill": round(k_ms, 4)},
         "roofline": {
             "bound": "mfma",
