@@ -665,22 +665,13 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
         logits(std::true_type{});
       else
         logits(std::false_type{});
-      // Lazy rescale.  Up to D = 64 it runs every step, branch-free, with a
-      // factor of 1 where the reference stays (the accumulator is 32 floats a
-      // lane there): measured 15 % faster than the branch at D = 64, and 7 to
-      // 10 % slower at D = 128 and 256, where the branch stays.
-      if constexpr (D <= 64) {
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const bool up = bm[ct] > m_ref[ct] + kLazyLog2;
-          const float m_new = up ? bm[ct] : m_ref[ct];
-          const float alpha = up ? __builtin_amdgcn_exp2f(m_ref[ct] - m_new) : 1.0f;  // 0 on a row's first keys
-          l_run[ct] *= alpha;
-          m_ref[ct] = m_new;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
-        }
-      } else if (__builtin_expect(__ballot(bm[0] > m_ref[0] + kLazyLog2 || bm[1] > m_ref[1] + kLazyLog2) != 0, 0)) {
+      // Lazy rescale: a uniform branch, taken when some row's max grows past
+      // its reference by more than 2^8.  (Up to D = 64 it once ran every
+      // step, branch-free, with a factor of 1 where the reference stays: 15 %
+      // faster than the branch with the bf16 hi + lo weights, whose register
+      // copies around the branch cost more; with fp16 weights the branch
+      // measured 13 % faster there, 754 -> 854 TFLOP/s.)
+      if (__builtin_expect(__ballot(bm[0] > m_ref[0] + kLazyLog2 || bm[1] > m_ref[1] + kLazyLog2) != 0, 0)) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           const float m_new = bm[ct] > m_ref[ct] + kLazyLog2 ? bm[ct] : m_ref[ct];
