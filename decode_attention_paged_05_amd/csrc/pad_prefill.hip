@@ -466,12 +466,23 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
     // copies spread over all eight by 2.5 %; by one or two waves, they were
     // slower.)  F16 form (both layouts): copying wave w (w < 4) takes half
     // w & 1 of block w >> 1's K tile and of its V tile, so that each of the
-    // four converts the V it copied, on its own SIMD.
+    // four converts the V it copied, on its own SIMD; at D = 256 every wave
+    // copies a quarter (below).
     const int my_tile = kSolo ? wave & 3 : wave >> 1;  // bf16 form: 0, 1: K of the two blocks; 2, 3: V
-    const bool copier = (kSolo || F16) ? wave < 4 : dh == 0;
-    const int my_b = F16 ? (wave >> 1) & 1 : my_tile & 1;
-    const int my_half = wave & 1;  // F16 form
-    constexpr int kHalfBytes = kTileBytes / 2;
+    // F16 form at D = 256: all eight waves copy, a quarter of one block's K
+    // and V tiles each, and convert their own quarter of V, so that the two
+    // waves of a SIMD share the conversion: 2 % faster than four copying
+    // waves there (and 9 % slower at D = 128, whose quarters are single 1 KB
+    // copies; D = 64's tiles do not split in quarters of whole copies).
+    constexpr bool k8 = F16 && D == 256;
+    constexpr int kParts = k8 ? 4 : 2;          // F16 form: parts of a tile, one per copying wave
+    constexpr int kPartBytes = kTileBytes / kParts;
+    constexpr int kPartCopies = CH / kParts;    // 1 KB copies of one part
+    // this wave's copies per step: the two parts (K and V), or one tile
+    constexpr int CPS = F16 ? 2 * kPartCopies : CH;
+    const bool copier = k8 ? true : (kSolo || F16) ? wave < 4 : dh == 0;
+    const int my_b = k8 ? wave >> 2 : F16 ? (wave >> 1) & 1 : my_tile & 1;
+    const int my_part = k8 ? wave & 3 : wave & 1;  // F16 form
     const char* pool = (my_tile < 2) ? a.key_cache : a.value_cache;
     // The block table is read-only for the launch: each wave fetches the id of
     // the block it copies next by a scalar load, one issue ahead.  (Loaded 64
@@ -503,11 +514,11 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
       if (!ok) phys = 0;
       if (!copier) return;
       if constexpr (F16) {
-        const int h_off = my_half * kHalfBytes;
-        lds_copy16_run<CH / 2>((lds_char*)(buf + my_b * kTileStride + h_off), k_src + h_off,
-                               rsrc(a.key_cache, phys, bytes));
-        lds_copy16_run<CH / 2>((lds_char*)(buf + (2 + my_b) * kTileStride + h_off), v_src + h_off,
-                               rsrc(a.value_cache, phys, bytes));
+        const int h_off = my_part * kPartBytes;
+        lds_copy16_run<kPartCopies>((lds_char*)(buf + my_b * kTileStride + h_off), k_src + h_off,
+                                    rsrc(a.key_cache, phys, bytes));
+        lds_copy16_run<kPartCopies>((lds_char*)(buf + (2 + my_b) * kTileStride + h_off), v_src + h_off,
+                                    rsrc(a.value_cache, phys, bytes));
       } else {
         const u32x4_t rs = rsrc(pool, phys, bytes);
         lds_char* lds = (lds_char*)(buf + my_tile * kTileStride);
@@ -534,12 +545,12 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
     // signalling NaNs; this form and the lane-group max without them measured
     // 2.5 % faster at D = 256.)
     auto convert_v = [&](int step, char* buf, auto masked) {
-      char* vt = buf + (2 + my_b) * kTileStride + my_half * kHalfBytes + 16 * lane;
+      char* vt = buf + (2 + my_b) * kTileStride + my_part * kPartBytes + 16 * lane;
       const int pos0 = (2 * step + my_b) * kBlockTokens + 8 * ((lane & 1) ^ ((lane >> 4) & 1));
       const bool tail = decltype(masked)::value && step == nsteps - 1;
       u16x2_t mx = {0, 0};
 #pragma unroll
-      for (int j = 0; j < CH / 2; ++j) {
+      for (int j = 0; j < kPartCopies; ++j) {
         const u32x4_t w = *reinterpret_cast<const u32x4_t*>(vt + 1024 * j);
         u32x4_t r;
 #pragma unroll
@@ -574,13 +585,13 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
     }
     // F16: V of step lo (the last step's is converted in its own iteration)
     if (F16 && copier && lo + 1 < hi) {
-      __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
+      __builtin_amdgcn_s_waitcnt(kWaitVmLds(CPS));
       if (convert_v(lo, kv_lds + (lo % kBufs) * kStepBytes, std::false_type{})) L.f16_bad = 1;
     }
     // step 0's logits (paired waves: formed ahead, for the exchange)
     if constexpr (!kSolo) {
       if (hi - lo > 1)
-        __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
+        __builtin_amdgcn_s_waitcnt(kWaitVmLds(CPS));
       else
         __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
       workgroup_barrier();
@@ -607,7 +618,7 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
     auto iter = [&](int st, auto last) {
       // paired waves need K of step st + 1 now; solo waves only step st
       if (kSolo && st + 1 < hi)
-        __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
+        __builtin_amdgcn_s_waitcnt(kWaitVmLds(CPS));
       else
         __builtin_amdgcn_s_waitcnt(kWaitVmLds(0));
       workgroup_barrier();
@@ -785,7 +796,7 @@ __device__ __forceinline__ void walk_rows(const PrefillArgs& a, int s, int by, i
         // meanwhile, the kernel measured 3 % slower.)
         asm volatile("" ::: "memory");
         if (copier && st + 2 < hi) {
-          __builtin_amdgcn_s_waitcnt(kWaitVmLds(CH));
+          __builtin_amdgcn_s_waitcnt(kWaitVmLds(CPS));
           if (convert_v(st + 1, kv_lds + ((st + 1) % kBufs) * kStepBytes, std::false_type{})) L.f16_bad = 1;
         }
       }
