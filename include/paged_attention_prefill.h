@@ -98,7 +98,7 @@ typedef struct pad_prefill_dims {
  * PAD_ERR_UNSUPPORTED).  Sequences with n_s == 0 produce no rows.
  * Accumulation is fp32.  The attention weights enter the P.V product as one
  * fp16 value each (relative rounding at most 2^-11; V is exact in fp16 down
- * to 2^-14 in magnitude, and below that within 2^-25 absolute); a
+ * to 2^-14 in magnitude, and below that within 2^-14 absolute); a
  * walk whose keys hold a V value beyond fp16's range (|v| > 65504, or
  * infinite, or NaN) is computed again with each weight as a bf16 hi + lo pair
  * (about 2^-16 relative).  The products are exact and accumulate in
