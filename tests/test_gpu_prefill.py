@@ -346,6 +346,45 @@ def test_prefill_v_beyond_fp16_range_falls_back():
     assert torch.equal(solo[others], clean[others])
 
 
+@pytest.mark.parametrize("D", [64, 256])
+def test_prefill_peaked_row_keeps_its_tail(D):
+    """One key 21.5 (log2 units) above 32 767 others, every V value 1: the
+    weighted average must come out 1 (the oracle's definition, with every V
+    equal, reduces to it).  With fp16 weights formed 2^7 below the reference
+    the keys after the dominant one sit in fp16's subnormal range, holding
+    about 1 % of the row's mass; were they flushed to zero, the rows would
+    read 0.9905.  They read 0.9998: each step adds the tail's small weights to
+    an fp32 accumulator holding the dominant one (128), and that rounding,
+    the same in every step, is what is left.  Both launches."""
+    spec = gen.PrefillSpec("peak", context_lens=(32767,), query_lens=(1,), num_heads=4, num_kv_heads=1,
+                           head_size=D, dtype="bf16", seed=81)
+    pp = gen.make_prefill_problem(spec)
+    dp = DevicePrefill(pp, keep_host=False)
+    # logits: q . k = 8 * (-x) for every key but the dominant one (0): with scale
+    # 1 / sqrt(D) the gap in log2 units is 8 x scale log2(e) = 21.46
+    x = 21.46 / (8 * D ** -0.5 * 1.4426950408889634)
+    q = torch.zeros_like(dp.query)
+    q[:, :, 0] = 8.0
+    kc = torch.zeros_like(dp.dp.kc)
+    kc[:, :, 0, :, 0] = -x  # tiled K: [blocks, KV heads, D / 8, 16, 8]; dim 0
+    dom = 5000
+    kc[int(pp.pool.block_tables[0, dom // 16]), 0, 0, dom % 16, 0] = 0.0
+    vc = torch.ones_like(dp.dp.vc)
+    torch.cuda.synchronize()
+    outs = []
+    out = torch.full(tuple(pp.query.shape), float("nan"), dtype=torch.float32, device="cuda")
+    pad.paged_attention_prefill(out, q, kc, vc, dp.dp.tables, dp.qs, dp.ctx, D ** -0.5, 1, 16, pp.max_query_len)
+    outs.append(out)
+    ws = pad.alloc_prefill_split_workspace(pp.num_seqs, 4, 1, D, pp.max_query_len, dp.dp.tables.shape[1])
+    out2 = torch.full(tuple(pp.query.shape), float("nan"), dtype=torch.float32, device="cuda")
+    pad.paged_attention_prefill_split(out2, q, kc, vc, dp.dp.tables, dp.qs, dp.ctx, D ** -0.5, 1, 16,
+                                      pp.max_query_len, ws)
+    outs.append(out2)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert float((o - 1.0).abs().max()) <= TOL["bf16"]
+
+
 def test_prefill_tail_slots_do_not_reach_rows():
     """The cache slots past each sequence's last token (the tail of its last
     block) hold 1e30 instead of NaN: the solo walk zeroes them before its
