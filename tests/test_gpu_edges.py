@@ -291,6 +291,7 @@ BALANCED_SHAPES = [
     ([17900, 16500], 24, 4, 256, "bf16", 1120, 512),   # 2 seqs: a range crosses from one sequence to the next
     ([20380], 8, 8, 128, "bf16", 1280, 512),           # MHA
     ([76793], 8, 2, 64, "f32", 4800, 512),             # fp32
+    ([40000], 24, 4, 256, "f32", 2500, 128),           # fp32 at head 256, tiled: three ranges per CU (768)
     ([38397], 16, 2, 256, "bf16", 2400, 256),          # P 256
     ([300, 290, 17, 5], 8, 8, 64, "bf16", 40, 16),     # little work: ranges of 8 blocks, fewer than the grid
     ([1000] * 40, 8, 4, 128, "bf16", 64, 512),         # two slots per head: the entry cap sets the range count
